@@ -1,0 +1,158 @@
+"""NVFP4 oracle (TEST INFRASTRUCTURE ONLY).
+
+A plain CPU implementation in C (``nvfp4_oracle.c``): table decode of E2M1 and
+E4M3, the fp32 quantisation rule step by step, and the product accumulated in
+fp64. Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package; the GPU library never uses it.
+
+Functions take and return numpy arrays; bf16 tensors are uint16 bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "nvfp4_oracle.c")
+_SO = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+# gcc, -O2, strict IEEE: no fast-math, no contraction of a*b+c into fma.
+CFLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared", "-pthread", "-std=c99"]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle into liboracle.so next to its source."""
+    if force or not os.path.exists(_SO):
+        tmp = _SO + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _SO)
+    return _SO
+
+
+def _L():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            build()
+        lib = ctypes.CDLL(_SO)
+        P, I64 = ctypes.c_void_p, ctypes.c_int64
+        lib.orc_e2m1_value.argtypes = [ctypes.c_int]
+        lib.orc_e2m1_value.restype = ctypes.c_double
+        lib.orc_e4m3_value.argtypes = [ctypes.c_int]
+        lib.orc_e4m3_value.restype = ctypes.c_double
+        lib.orc_e4m3_encode.argtypes = [ctypes.c_float]
+        lib.orc_e4m3_encode.restype = ctypes.c_uint8
+        lib.orc_e2m1_encode.argtypes = [ctypes.c_float]
+        lib.orc_e2m1_encode.restype = ctypes.c_uint8
+        lib.orc_quantize.argtypes = [P, I64, I64, P, P, P]
+        lib.orc_quantize.restype = ctypes.c_int
+        lib.orc_dequant.argtypes = [P, P, ctypes.c_float, I64, I64, P]
+        lib.orc_dequant.restype = None
+        lib.orc_gemv.argtypes = [P, I64, P, P, ctypes.c_float, I64, I64, P, P, ctypes.c_int]
+        lib.orc_gemv.restype = None
+        lib.orc_tile.argtypes = [P, P, I64, I64, P, P]
+        lib.orc_tile.restype = None
+        lib.orc_e4m3_encode_n.argtypes = [P, I64, P]
+        lib.orc_e4m3_encode_n.restype = None
+        lib.orc_e2m1_encode_n.argtypes = [P, I64, P]
+        lib.orc_e2m1_encode_n.restype = None
+        _lib = lib
+    return _lib
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a, a.ctypes.data
+
+
+def e2m1_value(code: int) -> float:
+    return _L().orc_e2m1_value(int(code))
+
+
+def e4m3_value(code: int) -> float:
+    return _L().orc_e4m3_value(int(code))
+
+
+def e4m3_encode(s: float) -> int:
+    return int(_L().orc_e4m3_encode(float(s)))
+
+
+def e2m1_encode(v: float) -> int:
+    return int(_L().orc_e2m1_encode(float(v)))
+
+
+def e4m3_encode_array(s: np.ndarray) -> np.ndarray:
+    a, pa = _c(np.ravel(s), np.float32)
+    out = np.empty(a.size, dtype=np.uint8)
+    _L().orc_e4m3_encode_n(pa, a.size, out.ctypes.data)
+    return out
+
+
+def e2m1_encode_array(v: np.ndarray) -> np.ndarray:
+    a, pa = _c(np.ravel(v), np.float32)
+    out = np.empty(a.size, dtype=np.uint8)
+    _L().orc_e2m1_encode_n(pa, a.size, out.ctypes.data)
+    return out
+
+
+def quantize(W_bits: np.ndarray):
+    """W (uint16 bf16 bits [N][K]) -> (packed uint8 [N][K/2], scales uint8 [N][K/16], gscale float32)."""
+    W, pw = _c(W_bits, np.uint16)
+    N, K = W.shape
+    packed = np.empty((N, K // 2), dtype=np.uint8)
+    scales = np.empty((N, K // 16), dtype=np.uint8)
+    g = np.zeros(1, dtype=np.float32)
+    rc = _L().orc_quantize(pw, N, K, packed.ctypes.data, scales.ctypes.data, g.ctypes.data)
+    if rc != 0:
+        raise ValueError("orc_quantize: bad shape %r" % (W.shape,))
+    return packed, scales, np.float32(g[0])
+
+
+def dequant(packed: np.ndarray, scales: np.ndarray, gscale) -> np.ndarray:
+    packed, pp = _c(packed, np.uint8)
+    scales, ps = _c(scales, np.uint8)
+    N, K = packed.shape[0], packed.shape[1] * 2
+    out = np.empty((N, K), dtype=np.float64)
+    _L().orc_dequant(pp, ps, float(np.float32(gscale)), N, K, out.ctypes.data)
+    return out
+
+
+def gemv(x_bits: np.ndarray, packed: np.ndarray, scales: np.ndarray, gscale, threads: int = 1,
+         with_l1: bool = True):
+    """fp64 product y[M][N] (and the error scale l1[M][N]) for bf16 x [M][K]."""
+    x, px = _c(np.atleast_2d(x_bits), np.uint16)
+    packed, pp = _c(packed, np.uint8)
+    scales, ps = _c(scales, np.uint8)
+    M, K = x.shape
+    N = packed.shape[0]
+    assert packed.shape[1] * 2 == K and scales.shape == (N, K // 16)
+    y = np.empty((M, N), dtype=np.float64)
+    l1 = np.empty((M, N), dtype=np.float64) if with_l1 else None
+    _L().orc_gemv(px, M, pp, ps, float(np.float32(gscale)), N, K, y.ctypes.data,
+                  l1.ctypes.data if with_l1 else None, int(threads))
+    return (y, l1) if with_l1 else y
+
+
+def tile(packed: np.ndarray, scales: np.ndarray):
+    """Canonical -> the GPU library's tiled layout (flat uint8 arrays)."""
+    packed, pp = _c(packed, np.uint8)
+    scales, ps = _c(scales, np.uint8)
+    N, K = packed.shape[0], packed.shape[1] * 2
+    G, C = (N + 7) // 8, (K + 1023) // 1024
+    pt = np.empty(G * C * 4096, dtype=np.uint8)
+    st = np.empty(G * C * 512, dtype=np.uint8)
+    _L().orc_tile(pp, ps, N, K, pt.ctypes.data, st.ctypes.data)
+    return pt, st
+
+
+def tolerance_ok(y_gpu: np.ndarray, y_ref: np.ndarray, l1: np.ndarray, rel: float = 2e-3):
+    """Per-element bound |y_gpu - y_ref| <= rel * l1; returns (ok, worst ratio)."""
+    err = np.abs(np.asarray(y_gpu, dtype=np.float64) - y_ref)
+    bound = rel * l1
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(bound > 0, err / np.where(bound > 0, bound, 1.0), np.where(err > 0, np.inf, 0.0))
+    return bool(np.all(err <= bound)), float(ratio.max() if ratio.size else 0.0)

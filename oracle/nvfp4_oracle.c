@@ -1,0 +1,310 @@
+/*
+ * NVFP4 oracle: TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously-correct CPU implementation of what the NVFP4
+ * decode path computes. Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg may load it; the GPU library never links or calls it, and
+ * this file shares no code, header or table with the GPU sources.
+ *
+ * What is computed and where it comes from
+ * ----------------------------------------
+ * The engine the source pages describe stores weights as NVFP4 "so there is
+ * less data to shuffle" (page "How imp turns a model file into words", Part
+ * one: loading the model) and reads them "without unpacking them to 16 bits"
+ * during the bandwidth-bound decode phase (page "imp" README, the decode
+ * paragraph of the request walkthrough). The engineering log's post "NVFP4 at
+ * the bit level" names the parts of the format: four-bit values and two
+ * scales. The bit-level definition used here:
+ *   - element: FP4 E2M1 (1 sign, 2 exponent bits with bias 1, 1 mantissa
+ *     bit; OCP Microscaling Formats v1.0), magnitudes {0,.5,1,1.5,2,3,4,6};
+ *   - block scale: FP8 E4M3 "fn" (OCP 8-bit floating point: bias 7, no
+ *     infinities, 0x7F/0xFF are NaN, max 448), one per 16 consecutive
+ *     K-elements of a row;
+ *   - tensor scale: one FP32 value, a decode multiplier.
+ * Quantisation rule (fp32, one IEEE rounding per operation):
+ *   gscale = amax|W| / (448*6);  per block: s = (block_amax / 6) / gscale,
+ *   scale code = E4M3(s) rounded to nearest-even, saturating at 448;
+ *   element code = E2M1(w / (E4M3(code)*gscale)) rounded to nearest-even.
+ * Dequantised weight: E2M1(q) * E4M3(sc) * gscale.
+ * Product: y[m][n] = sum_k dequant(W)[n][k] * x[m][k], here in fp64.
+ *
+ * Readings where the definition above leaves a choice (each is listed with
+ * its reason in the project's design notes):
+ *   - element order: even k in the low nibble of each byte;
+ *   - canonical layout: packed [N][K/2], scales [N][K/16], row-major,
+ *     K a multiple of 16 (blocks never straddle rows);
+ *   - an all-zero tensor gives gscale = 0, and any block whose scale code
+ *     is 0x00 gets element codes 0;
+ *   - the sign of an element code is the sign bit of w/d, so small
+ *     negative values encode as 0x8 (-0).
+ *
+ * Pins (tests run without a GPU): E2M1 values against the minifloat
+ * bit-field formula; E4M3 decode against torch.float8_e4m3fn for all 256
+ * codes; E4M3 encode against torch's round-to-nearest-even cast; E2M1 encode
+ * against brute-force nearest search; quantiser round-trip invariants and a
+ * hand-worked example; the product against numpy float64 matmul of the
+ * dequantised matrix and exact power-of-two cases.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------- decode */
+
+/* E2M1 magnitudes for codes 0..7; bit 3 is the sign. */
+static const double E2M1_MAG[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+double orc_e2m1_value(int code) {
+    double m = E2M1_MAG[code & 7];
+    return (code & 8) ? -m : m;
+}
+
+/* E4M3 "fn": sign s, exponent e (4 bits, bias 7), mantissa m (3 bits).
+ * e == 0: subnormal (m/8) * 2^(1-7);  otherwise (1 + m/8) * 2^(e-7);
+ * e == 15 && m == 7: NaN. */
+double orc_e4m3_value(int code) {
+    int s = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0)
+        v = ldexp((double)m / 8.0, 1 - 7);
+    else
+        v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+static double E4M3_TAB[256];
+static double E2M1_TAB[16];
+static pthread_once_t tab_once = PTHREAD_ONCE_INIT;
+
+static void build_tables(void) {
+    for (int c = 0; c < 256; ++c) E4M3_TAB[c] = orc_e4m3_value(c);
+    for (int c = 0; c < 16; ++c) E2M1_TAB[c] = orc_e2m1_value(c);
+}
+
+static void tables(void) { pthread_once(&tab_once, build_tables); }
+
+/* ---------------------------------------------------------------- encode */
+
+/* Nearest finite E4M3 code to s >= 0, ties to the even code (even mantissa
+ * bit), saturating: anything >= 448 (the largest finite value) gives 0x7E.
+ * Positive codes 0x00..0x7E are increasing in value, so the two neighbours
+ * of s are found by walking the table. */
+uint8_t orc_e4m3_encode(float s_in) {
+    tables();
+    double s = (double)s_in;
+    int neg = 0;
+    if (s < 0 || (s == 0 && signbit(s))) { neg = 1; s = -s; }
+    int c;
+    if (!(s < E4M3_TAB[0x7E])) {
+        c = 0x7E;
+    } else {
+        int lo = 0;
+        while (E4M3_TAB[lo + 1] <= s) ++lo;       /* E4M3_TAB[lo] <= s < E4M3_TAB[lo+1] */
+        double dlo = s - E4M3_TAB[lo], dhi = E4M3_TAB[lo + 1] - s;
+        if (dlo < dhi)
+            c = lo;
+        else if (dhi < dlo)
+            c = lo + 1;
+        else
+            c = (lo % 2 == 0) ? lo : lo + 1;
+    }
+    return (uint8_t)(c | (neg ? 0x80 : 0));
+}
+
+/* E2M1 code of v: the nearest of the eight magnitudes, ties to the even code
+ * (even mantissa bit), magnitudes above 6 saturate to 6; the sign bit of the
+ * code is the sign bit of v. Walks the midpoints between neighbours. */
+uint8_t orc_e2m1_encode(float v) {
+    double a = fabs((double)v);
+    int code = 7;
+    for (int i = 0; i < 7; ++i) {
+        double mid = 0.5 * (E2M1_MAG[i] + E2M1_MAG[i + 1]);
+        if (a < mid) { code = i; break; }
+        if (a == mid) { code = (i % 2 == 0) ? i : i + 1; break; }
+    }
+    return (uint8_t)(code | (signbit(v) ? 8 : 0));
+}
+
+/* -------------------------------------------------------------- quantise */
+
+static float bf16_to_f32(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* Quantise W (bf16 bits, [N][K] row-major) into the canonical layout.
+ * Returns 0, or -1 if K is not a multiple of 16 or a size is negative.
+ * Every arithmetic step is one fp32 operation, rounded to nearest-even
+ * (this file is compiled with -ffp-contract=off and without fast-math). */
+int orc_quantize(const uint16_t *W, int64_t N, int64_t K, uint8_t *packed, uint8_t *scales,
+                 float *gscale_out) {
+    tables();
+    if (N < 0 || K < 0 || K % 16 != 0) return -1;
+    /* 1. tensor amax (exact) */
+    float amax = 0.0f;
+    for (int64_t i = 0; i < N * K; ++i) {
+        float a = fabsf(bf16_to_f32(W[i]));
+        if (a > amax) amax = a;
+    }
+    /* 2. tensor scale */
+    if (amax == 0.0f) {
+        *gscale_out = 0.0f;
+        memset(packed, 0, (size_t)(N * K / 2));
+        memset(scales, 0, (size_t)(N * K / 16));
+        return 0;
+    }
+    volatile float gscale = amax / 2688.0f;      /* 448 * 6 */
+    *gscale_out = gscale;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t b = 0; b < K / 16; ++b) {
+            const uint16_t *wb = W + n * K + b * 16;
+            /* 3. block amax and scale */
+            float bamax = 0.0f;
+            for (int j = 0; j < 16; ++j) {
+                float a = fabsf(bf16_to_f32(wb[j]));
+                if (a > bamax) bamax = a;
+            }
+            volatile float t = bamax / 6.0f;
+            volatile float s = t / gscale;
+            uint8_t sc = orc_e4m3_encode(s);
+            float s_dec = (float)E4M3_TAB[sc];
+            scales[n * (K / 16) + b] = sc;
+            /* 4. elements */
+            uint8_t codes[16];
+            for (int j = 0; j < 16; ++j) {
+                if (s_dec == 0.0f) {
+                    codes[j] = 0;
+                } else {
+                    volatile float d = s_dec * gscale;
+                    volatile float v = bf16_to_f32(wb[j]) / d;
+                    codes[j] = orc_e2m1_encode(v);
+                }
+            }
+            /* 5. pack, even k in the low nibble */
+            for (int j = 0; j < 8; ++j)
+                packed[n * (K / 2) + b * 8 + j] = (uint8_t)(codes[2 * j] | (codes[2 * j + 1] << 4));
+        }
+    }
+    return 0;
+}
+
+/* Dequantised weights, fp64 [N][K]. */
+void orc_dequant(const uint8_t *packed, const uint8_t *scales, float gscale, int64_t N, int64_t K,
+                 double *out) {
+    tables();
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            uint8_t byte = packed[n * (K / 2) + k / 2];
+            int q = (k % 2 == 0) ? (byte & 15) : (byte >> 4);
+            out[n * K + k] = E2M1_TAB[q] * E4M3_TAB[scales[n * (K / 16) + k / 16]] * (double)gscale;
+        }
+}
+
+/* --------------------------------------------------------------- product */
+
+typedef struct {
+    const uint16_t *x;
+    const uint8_t *packed, *scales;
+    double gscale;
+    int64_t M, N, K, n0, n1;
+    double *y, *l1;
+} gemv_job;
+
+static void *gemv_rows(void *arg) {
+    const gemv_job *j = (const gemv_job *)arg;
+    const int64_t K = j->K;
+    for (int64_t n = j->n0; n < j->n1; ++n) {
+        const uint8_t *q = j->packed + n * (K / 2);
+        const uint8_t *sc = j->scales + n * (K / 16);
+        for (int64_t m = 0; m < j->M; ++m) {
+            const uint16_t *xm = j->x + m * K;
+            double y = 0.0, l1 = 0.0;
+            for (int64_t b = 0; b < K / 16; ++b) {
+                double s = E4M3_TAB[sc[b]];
+                double inner = 0.0;
+                for (int64_t i = 0; i < 16; ++i) {
+                    int64_t k = b * 16 + i;
+                    uint8_t byte = q[k / 2];
+                    double e = E2M1_TAB[(k % 2 == 0) ? (byte & 15) : (byte >> 4)];
+                    double xv = (double)bf16_to_f32(xm[k]);
+                    inner += e * xv;
+                    l1 += fabs(e * s * j->gscale * xv);
+                }
+                y += s * inner;
+            }
+            j->y[m * j->N + n] = j->gscale * y;
+            if (j->l1) j->l1[m * j->N + n] = l1;
+        }
+    }
+    return 0;
+}
+
+/* y[m][n] = gscale * sum_b E4M3(sc[n][b]) * sum_i E2M1(q[n][16b+i]) * x[m][16b+i]
+ * in fp64, and l1[m][n] = sum_k |dequant(W)[n][k] * x[m][k]| (the scale of
+ * the error bound). x is bf16 bits [M][K]; packed/scales canonical layout.
+ * Rows n are split over `nthreads` threads; each sum runs in k order. */
+void orc_gemv(const uint16_t *x, int64_t M, const uint8_t *packed, const uint8_t *scales,
+              float gscale, int64_t N, int64_t K, double *y, double *l1, int nthreads) {
+    tables();
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if (nthreads > N) nthreads = (int)(N > 0 ? N : 1);
+    pthread_t th[256];
+    gemv_job jobs[256];
+    for (int t = 0; t < nthreads; ++t) {
+        gemv_job j = {x, packed, scales, (double)gscale, M, N, K, N * t / nthreads,
+                      N * (t + 1) / nthreads, y, l1};
+        jobs[t] = j;
+    }
+    for (int t = 1; t < nthreads; ++t) pthread_create(&th[t], 0, gemv_rows, &jobs[t]);
+    gemv_rows(&jobs[0]);
+    for (int t = 1; t < nthreads; ++t) pthread_join(th[t], 0);
+}
+
+/* --------------------------------------------------------- device layout */
+
+/* The GPU library's tiled layout, written out as plain loops so that the
+ * GPU re-tiling can be compared byte for byte. Rows form groups of 8
+ * (G = ceil(N/8)); K forms chunks of 1024 (C = ceil(K/1024)); tile (g, c) is
+ * stored at index g*C + c.
+ *   packed tile, 4096 B: byte r*512 + l*16 + i  =  canonical packed byte
+ *       (row 8g+r, byte (1024c + 32l)/2 + i)      r<8, l<32, i<16
+ *   scale tile, 512 B:   byte l*16 + r*2 + j    =  canonical scale
+ *       (row 8g+r, block 64c + 2l + j)            j<2
+ * Positions outside the tensor (row >= N or k >= K) hold 0. */
+void orc_tile(const uint8_t *packed, const uint8_t *scales, int64_t N, int64_t K, uint8_t *packed_t,
+              uint8_t *scales_t) {
+    int64_t G = (N + 7) / 8, C = (K + 1023) / 1024;
+    for (int64_t g = 0; g < G; ++g)
+        for (int64_t c = 0; c < C; ++c) {
+            uint8_t *pt = packed_t + (g * C + c) * 4096;
+            uint8_t *st = scales_t + (g * C + c) * 512;
+            for (int r = 0; r < 8; ++r)
+                for (int l = 0; l < 32; ++l) {
+                    int64_t row = 8 * g + r;
+                    for (int i = 0; i < 16; ++i) {
+                        int64_t kb = (1024 * c + 32 * l) / 2 + i;      /* byte index in the row */
+                        pt[r * 512 + l * 16 + i] =
+                            (row < N && kb < K / 2) ? packed[row * (K / 2) + kb] : 0;
+                    }
+                    for (int j = 0; j < 2; ++j) {
+                        int64_t blk = 64 * c + 2 * l + j;
+                        st[l * 16 + r * 2 + j] =
+                            (row < N && blk < K / 16) ? scales[row * (K / 16) + blk] : 0;
+                    }
+                }
+        }
+}
+
+/* Element-wise versions of the two encoders, for sweeping many inputs. */
+void orc_e4m3_encode_n(const float *s, int64_t n, uint8_t *out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_encode(s[i]);
+}
+
+void orc_e2m1_encode_n(const float *v, int64_t n, uint8_t *out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_e2m1_encode(v[i]);
+}

@@ -1,0 +1,289 @@
+"""Pins for the CPU oracle: each check compares it with something other than
+itself (the format's bit-field definition, torch's float8_e4m3fn, brute-force
+search, exact rational arithmetic, numpy float64 matmul, a hand-worked
+example), chosen so that a dropped term, a wrong sign or index, a swapped
+nibble or a transposed operand fails at least one of them."""
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import bf16_to_float32, float32_to_bf16_bits, tensor_bits, workload, x_bits
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------- E2M1 values
+def minifloat_value(code, ebits, mbits, bias):
+    """Value of a sign/exponent/mantissa minifloat from its bit fields."""
+    s = code >> (ebits + mbits)
+    e = (code >> mbits) & ((1 << ebits) - 1)
+    m = code & ((1 << mbits) - 1)
+    if e == 0:
+        v = Fraction(m, 1 << mbits) * Fraction(2) ** (1 - bias)
+    else:
+        v = (1 + Fraction(m, 1 << mbits)) * Fraction(2) ** (e - bias)
+    return -v if s else v
+
+
+def test_e2m1_values_match_bit_fields():
+    # E2M1: 1 sign, 2 exponent bits (bias 1), 1 mantissa bit.
+    for c in range(16):
+        assert oracle.e2m1_value(c) == float(minifloat_value(c, 2, 1, 1))
+        assert np.signbit(oracle.e2m1_value(c)) == bool(c & 8)
+    mags = sorted({abs(oracle.e2m1_value(c)) for c in range(16)})
+    assert mags == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+# ----------------------------------------------------------------- E4M3 decode
+def test_e4m3_decode_all_codes_match_torch():
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    for c in range(256):
+        v = oracle.e4m3_value(c)
+        if np.isnan(ref[c]):
+            assert np.isnan(v), c
+        else:
+            assert v == ref[c] and np.signbit(v) == np.signbit(ref[c]), (c, v, ref[c])
+    assert oracle.e4m3_value(0x7E) == 448.0 and oracle.e4m3_value(0x01) == 2.0 ** -9
+    assert np.isnan(oracle.e4m3_value(0x7F)) and np.isnan(oracle.e4m3_value(0xFF))
+
+
+def test_e4m3_decode_matches_bit_fields():
+    for c in range(256):
+        if c & 0x7F == 0x7F:
+            continue
+        assert oracle.e4m3_value(c) == float(minifloat_value(c, 4, 3, 7))
+
+
+# ----------------------------------------------------------------- E4M3 encode
+def _neighbourhood(values, ulps):
+    v = np.asarray(values, dtype=np.float32)
+    bits = v.view(np.int32)
+    out = [(bits + d).view(np.float32) for d in range(-ulps, ulps + 1)]
+    return np.concatenate(out)
+
+
+def test_e4m3_encode_matches_torch_rne():
+    finite = np.array([oracle.e4m3_value(c) for c in range(0x7F)], dtype=np.float64)
+    mids = (finite[:-1] + finite[1:]) / 2
+    pts = np.concatenate([_neighbourhood(finite[1:].astype(np.float32), 3),
+                          _neighbourhood(mids.astype(np.float32), 3),
+                          np.array([0.0, 2.0 ** -10, 1.5 * 2.0 ** -10, 448.0, 460.0, 463.99], np.float32)])
+    rng = np.random.default_rng(0)
+    rnd = np.exp(rng.uniform(np.log(1e-5), np.log(463.0), 2_000_000)).astype(np.float32)
+    s = np.concatenate([pts, rnd])
+    s = s[(s >= 0) & (s < 464.0)]
+    ours = oracle.e4m3_encode_array(s)
+    ref = torch.from_numpy(s).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ours, ref), np.flatnonzero(ours != ref)[:10]
+
+
+def test_e4m3_encode_saturates_and_round_trips():
+    big = np.array([448.0, 449.0, 464.0, 470.0, 1e6, 3e38, np.inf], np.float32)
+    assert np.all(oracle.e4m3_encode_array(big) == 0x7E)
+    for c in range(0x7F):
+        assert oracle.e4m3_encode(oracle.e4m3_value(c)) == c
+
+
+# ----------------------------------------------------------------- E2M1 encode
+def e2m1_bruteforce(v):
+    """Nearest of the 16 codes by exhaustive search; ties to the code whose
+    mantissa bit is 0; |v| > 6 saturates; sign from the sign bit of v."""
+    mags = np.array([float(minifloat_value(c, 2, 1, 1)) for c in range(8)])
+    a = np.abs(v.astype(np.float64))[:, None]
+    d = np.abs(a - mags[None, :])
+    best = d.min(axis=1, keepdims=True)
+    cand = d == best
+    even = cand & (np.arange(8)[None, :] % 2 == 0)
+    code = np.where(even.any(axis=1), np.argmax(even, axis=1), np.argmax(cand, axis=1))
+    return (code | np.where(np.signbit(v), 8, 0)).astype(np.uint8)
+
+
+def test_e2m1_encode_matches_bruteforce():
+    mags = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float32)
+    mids = ((mags[:-1].astype(np.float64) + mags[1:]) / 2).astype(np.float32)
+    pts = np.concatenate([_neighbourhood(mags[1:], 8), _neighbourhood(mids, 8), [0.0, 1e-30, 6.5, 7.0, 100.0]])
+    pts = np.concatenate([pts, -pts, np.float32([-0.0])]).astype(np.float32)
+    rng = np.random.default_rng(1)
+    rnd = rng.uniform(-8, 8, 1_000_000).astype(np.float32)
+    v = np.concatenate([pts, rnd])
+    assert np.array_equal(oracle.e2m1_encode_array(v), e2m1_bruteforce(v))
+
+
+# ------------------------------------------------------------------ quantiser
+def load_worked_example():
+    rows, packed, scales, gscale = [], [], [], None
+    with open(os.path.join(GOLDEN, "quant_worked_example.txt")) as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            key, *vals = line.split()
+            if key == "gscale":
+                gscale = float(vals[0])
+            elif key == "row":
+                rows.append([float(v) for v in vals])
+            elif key == "packed":
+                packed.append([int(v, 16) for v in vals])
+            elif key == "scales":
+                scales.append([int(v, 16) for v in vals])
+    W = np.array(rows, dtype=np.float32)
+    Wb = float32_to_bf16_bits(W)
+    assert np.array_equal(bf16_to_float32(Wb), W) and np.array_equal(np.signbit(bf16_to_float32(Wb)), np.signbit(W))
+    return Wb, np.array(packed, np.uint8), np.array(scales, np.uint8), np.float32(gscale)
+
+
+def test_quantize_worked_example():
+    Wb, packed, scales, g = load_worked_example()
+    p, s, gs = oracle.quantize(Wb)
+    assert gs == g
+    assert np.array_equal(s, scales), (s, scales)
+    assert np.array_equal(p, packed), (p, packed)
+
+
+def check_invariants(Wb, p, s, g):
+    W = bf16_to_float32(Wb).astype(np.float64)
+    N, K = W.shape
+    amax = np.abs(W).max()
+    assert g == np.float32(np.float32(amax) / np.float32(2688.0))
+    assert s.max() <= 0x7E and not np.any(s & 0x80)
+    blk = np.abs(W).reshape(N, K // 16, 16).max(axis=2)
+    n0, b0 = np.unravel_index(np.argmax(blk), blk.shape)
+    assert s[n0, b0] == 0x7E
+    D = oracle.dequant(p, s, g)
+    sdec = np.array([oracle.e4m3_value(c) for c in range(256)])[s]            # [N][K/16]
+    d = np.repeat(sdec * float(g), 16, axis=1)
+    normal = np.repeat(s >= 0x08, 16, axis=1)
+    assert np.all(np.abs(W - D)[normal] <= d[normal] * (1 + 2.0 ** -20))
+    # the largest element of each normal-scale block decodes to +-6 * s_dec * gscale
+    idx = np.argmax(np.abs(W).reshape(N, K // 16, 16), axis=2)
+    q = np.stack([p & 15, p >> 4], axis=2).reshape(N, K // 16, 16)
+    top = np.take_along_axis(q, idx[..., None], axis=2)[..., 0]
+    Wtop = np.take_along_axis(W.reshape(N, K // 16, 16), idx[..., None], axis=2)[..., 0]
+    sel = (s >= 0x08) & (Wtop != 0)
+    assert np.all((top[sel] & 7) == 7)
+    assert np.all(((top[sel] & 8) != 0) == (Wtop[sel] < 0))
+
+
+@pytest.mark.parametrize("name,tname,rows", [("gemv_1024", "w", None), ("dense27b_layer", "down", 256),
+                                             ("lm_head", "w", 512), ("qwen3_0p6b_decode", "L1.q", None)])
+def test_quantize_invariants_on_workloads(name, tname, rows):
+    W = tensor_bits(workload(name).tensor(tname))
+    if rows:
+        W = W[:rows]
+    p, s, g = oracle.quantize(W)
+    check_invariants(W, p, s, g)
+
+
+def test_quantize_degenerate_cases():
+    z = np.zeros((4, 32), np.uint16)
+    p, s, g = oracle.quantize(z)
+    assert g == 0 and not p.any() and not s.any()
+    one = np.zeros((2, 32), np.float32)
+    one[1, 20] = -0.75
+    p, s, g = oracle.quantize(float32_to_bf16_bits(one))
+    assert g == np.float32(0.75) / np.float32(2688)
+    assert list(s.ravel()) == [0, 0, 0, 0x7E]
+    assert p[1, 10] == 0x0F and p[1].sum() == 0x0F        # k=20 is the low nibble of byte 10, code -6
+    const = np.full((1, 16), 0.3, np.float32)
+    p, s, g = oracle.quantize(float32_to_bf16_bits(const))
+    assert s[0, 0] == 0x7E and np.all(p == 0x77)
+    with pytest.raises(ValueError):
+        oracle.quantize(np.zeros((2, 24), np.uint16))
+
+
+# -------------------------------------------------------------------- product
+def dequant_from_bits(p, s, g):
+    """Dequantised weights built independently of the oracle: E2M1 from its
+    bit fields, E4M3 through torch.float8_e4m3fn."""
+    e2 = np.array([float(minifloat_value(c, 2, 1, 1)) for c in range(16)])
+    e4 = torch.from_numpy(np.ascontiguousarray(s)).view(torch.float8_e4m3fn).double().numpy()
+    q = np.stack([p & 15, p >> 4], axis=2).reshape(p.shape[0], -1)
+    return e2[q] * np.repeat(e4, 16, axis=1) * float(g)
+
+
+def test_gemv_matches_numpy_on_tiny_matrices():
+    rng = np.random.default_rng(3)
+    for N, K, M in [(1, 16, 1), (3, 32, 2), (7, 64, 3), (64, 48, 4), (5, 1024 + 16, 2)]:
+        W = float32_to_bf16_bits(rng.normal(0, 0.05, (N, K)).astype(np.float32))
+        x = float32_to_bf16_bits(rng.normal(0, 1, (M, K)).astype(np.float32))
+        p, s, g = oracle.quantize(W)
+        D = dequant_from_bits(p, s, g)
+        xf = bf16_to_float32(x).astype(np.float64)
+        y, l1 = oracle.gemv(x, p, s, g)
+        ref = xf @ D.T
+        assert np.allclose(y, ref, rtol=1e-13, atol=1e-15 * np.abs(D).sum())
+        assert np.allclose(l1, np.abs(xf) @ np.abs(D).T, rtol=1e-13)
+        assert not np.allclose(y, (xf[:, ::-1] @ D.T) if K > 16 else y + 1)
+
+
+def test_gemv_exact_against_rationals():
+    """Worked example weights with power-of-two x: every product and sum is a
+    short binary fraction, so the fp64 result must equal exact rational
+    arithmetic over the bit-field decodes."""
+    Wb, packed, scales, g = load_worked_example()
+    rng = np.random.default_rng(4)
+    x = (2.0 ** rng.integers(-3, 4, (3, 32))) * rng.choice([-1, 1], (3, 32))
+    xb = float32_to_bf16_bits(x.astype(np.float32))
+    y, _ = oracle.gemv(xb, packed, scales, g)
+    e2 = [minifloat_value(c, 2, 1, 1) for c in range(16)]
+    e4 = [minifloat_value(c, 4, 3, 7) for c in range(0x7F)]
+    for m in range(3):
+        for n in range(2):
+            acc = Fraction(0)
+            for k in range(32):
+                q = packed[n, k // 2] >> (4 * (k % 2)) & 15
+                acc += e2[q] * e4[scales[n, k // 16]] * Fraction(float(g)) * Fraction(float(x[m, k]))
+            assert y[m, n] == float(acc)
+
+
+def test_gemv_one_hot_selects_a_column():
+    W = tensor_bits(workload("gemv_1024").tensor("w"))[:64]
+    p, s, g = oracle.quantize(W)
+    D = dequant_from_bits(p, s, g)
+    for k in [0, 1, 15, 16, 17, 511, 1023]:
+        x = np.zeros((1, 1024), np.float32)
+        x[0, k] = 1.0
+        y, _ = oracle.gemv(float32_to_bf16_bits(x), p, s, g)
+        assert np.array_equal(y[0], D[:, k])
+
+
+def test_gemv_threads_do_not_change_results():
+    W = tensor_bits(workload("gemv_1024").tensor("w"))
+    x = x_bits(workload("gemv_1024").x("x"))
+    p, s, g = oracle.quantize(W)
+    y1, l1 = oracle.gemv(x, p, s, g, threads=1)
+    y8, l8 = oracle.gemv(x, p, s, g, threads=8)
+    assert np.array_equal(y1, y8) and np.array_equal(l1, l8)
+
+
+def test_tolerance_helper():
+    ok, r = oracle.tolerance_ok(np.array([1.0, 2.0]), np.array([1.0, 2.001]), np.array([1.0, 1.0]))
+    assert ok and abs(r - 0.5) < 1e-9
+    ok, r = oracle.tolerance_ok(np.array([1.0]), np.array([1.01]), np.array([1.0]))
+    assert not ok
+
+
+# ---------------------------------------------------------------- tiled layout
+def test_tile_matches_reshape_formulation():
+    rng = np.random.default_rng(5)
+    for N, K in [(16, 2048), (24, 1024), (8, 3072)]:
+        p = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+        s = rng.integers(0, 256, (N, K // 16), dtype=np.uint8)
+        pt, st = oracle.tile(p, s)
+        G, C = N // 8, K // 1024
+        ref_p = p.reshape(G, 8, C, 32, 16).transpose(0, 2, 1, 3, 4).ravel()
+        ref_s = s.reshape(G, 8, C, 32, 2).transpose(0, 2, 3, 1, 4).ravel()
+        assert np.array_equal(pt, ref_p) and np.array_equal(st, ref_s)
+
+
+def test_tile_pads_ragged_shapes_with_zeros():
+    N, K = 11, 1024 + 48
+    p = np.arange(N * K // 2, dtype=np.int64).astype(np.uint8).reshape(N, K // 2) | 1
+    s = np.full((N, K // 16), 0x33, np.uint8)
+    pt, st = oracle.tile(p, s)
+    assert pt.size == 2 * 2 * 4096 and st.size == 2 * 2 * 512
+    assert np.count_nonzero(pt) == N * K // 2 and np.count_nonzero(st) == N * K // 16
+    assert np.array_equal(np.sort(pt[pt != 0]), np.sort(p.ravel()))
