@@ -1,0 +1,188 @@
+"""NVFP4 decode path for AMD Instinct MI355X (gfx950): Python binding.
+
+A thin ctypes layer over libfp4.so, the C ABI declared in include/fp4.h.
+It only marshals arguments: every step runs in the library's HIP kernels on
+the tensors' device, on torch's current stream. PyTorch supplies device
+memory and streams. There is no CPU fallback: without the built library the
+import fails, and CPU tensors are rejected.
+
+Names follow the C ABI: quantize, retile, gemv, gemv_multi, gemm_prefill,
+layout_bytes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch  # loads the HIP runtime first; libfp4 then binds to the same one
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp4.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "fp4.h")
+
+ROWMAJOR, TILED = 0, 1
+MAX_PROJ = 8
+_LAYOUTS = {"rowmajor": ROWMAJOR, "tiled": TILED, ROWMAJOR: ROWMAJOR, TILED: TILED}
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libfp4.so is not built: run `python -c 'import __graft_entry__ as g; g.build()'` "
+                      "or `python bit_block_scaled_fp4_amd/build.py`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_P, _I64, _I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+
+
+class _Proj(ctypes.Structure):
+    _fields_ = [("packed", _P), ("scales", _P), ("gscale", _P), ("N", _I64), ("y", _P), ("ldy", _I64)]
+
+
+_lib.fp4_status_string.argtypes = [_I]
+_lib.fp4_status_string.restype = ctypes.c_char_p
+_lib.fp4_layout_bytes.argtypes = [_I64, _I64, _I, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
+_lib.fp4_quantize.argtypes = [_P, _I64, _I64, _I, _P, _P, _P, _P]
+_lib.fp4_retile.argtypes = [_P, _P, _I64, _I64, _P, _P, _P]
+_lib.fp4_gemv.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]
+_lib.fp4_gemv_multi.argtypes = [ctypes.POINTER(_Proj), _I, _P, _I64, _I64, _P]
+_lib.fp4_gemm_prefill.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]
+for _f in ("fp4_layout_bytes", "fp4_quantize", "fp4_retile", "fp4_gemv", "fp4_gemv_multi", "fp4_gemm_prefill"):
+    getattr(_lib, _f).restype = _I
+
+
+class Fp4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, _lib.fp4_status_string(status).decode(), status))
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise Fp4Error(status, where)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor (got %s); there is no CPU path" % (name, t.device))
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s (got %s)" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def layout_bytes(N: int, K: int, layout="tiled"):
+    """(packed_bytes, scale_bytes) for an N x K weight in the given layout."""
+    pb, sb = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(_lib.fp4_layout_bytes(N, K, _LAYOUTS[layout], ctypes.byref(pb), ctypes.byref(sb)), "fp4_layout_bytes")
+    return pb.value, sb.value
+
+
+@dataclass
+class NVFP4Weight:
+    """Quantised weight: packed codes, E4M3 block scales and the fp32 tensor scale (device)."""
+    packed: torch.Tensor
+    scales: torch.Tensor
+    gscale: torch.Tensor
+    N: int
+    K: int
+    layout: int = TILED
+
+
+def quantize(W: torch.Tensor, layout="tiled", out: Optional[NVFP4Weight] = None) -> NVFP4Weight:
+    """fp4_quantize: bf16 W [N][K] -> NVFP4Weight in `layout`."""
+    N, K = W.shape
+    lay = _LAYOUTS[layout]
+    if out is None:
+        pb, sb = layout_bytes(N, K, lay)
+        out = NVFP4Weight(torch.empty(pb, dtype=torch.uint8, device=W.device),
+                          torch.empty(sb, dtype=torch.uint8, device=W.device),
+                          torch.empty(1, dtype=torch.float32, device=W.device), N, K, lay)
+    _check(_lib.fp4_quantize(_dev(W, "W", torch.bfloat16), N, K, lay, _dev(out.packed, "packed", torch.uint8),
+                             _dev(out.scales, "scales", torch.uint8), _dev(out.gscale, "gscale", torch.float32),
+                             _stream(W.device)), "fp4_quantize")
+    return out
+
+
+def retile(w: NVFP4Weight, out: Optional[NVFP4Weight] = None) -> NVFP4Weight:
+    """fp4_retile: canonical (row-major) NVFP4Weight -> tiled copy (gscale shared)."""
+    if w.layout != ROWMAJOR:
+        raise ValueError("retile expects a row-major weight")
+    if out is None:
+        pb, sb = layout_bytes(w.N, w.K, TILED)
+        out = NVFP4Weight(torch.empty(pb, dtype=torch.uint8, device=w.packed.device),
+                          torch.empty(sb, dtype=torch.uint8, device=w.packed.device), w.gscale, w.N, w.K, TILED)
+    _check(_lib.fp4_retile(_dev(w.packed, "packed", torch.uint8), _dev(w.scales, "scales", torch.uint8), w.N, w.K,
+                           _dev(out.packed, "packed_tiled", torch.uint8), _dev(out.scales, "scales_tiled", torch.uint8),
+                           _stream(w.packed.device)), "fp4_retile")
+    return out
+
+
+def _x2d(x: torch.Tensor):
+    if x.dim() == 1:
+        x = x.view(1, -1)
+    return x, x.shape[0], x.shape[1]
+
+
+def gemv(x: torch.Tensor, w: NVFP4Weight, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp4_gemv: y[M][N] = x[M][K] @ dequant(w)^T (fp32), x bf16, w tiled."""
+    x, M, K = _x2d(x)
+    if K != w.K:
+        raise ValueError("x has K=%d, weight has K=%d" % (K, w.K))
+    if out is None:
+        out = torch.empty((M, w.N), dtype=torch.float32, device=x.device)
+    _check(_lib.fp4_gemv(_dev(out, "y", torch.float32), _dev(x, "x", torch.bfloat16), _dev(w.packed, "packed"),
+                         _dev(w.scales, "scales"), _dev(w.gscale, "gscale", torch.float32), M, w.N, K,
+                         _stream(x.device)), "fp4_gemv")
+    return out
+
+
+def gemv_multi(x: torch.Tensor, weights: Sequence[NVFP4Weight], outs: Sequence[torch.Tensor],
+               ldys: Optional[Sequence[int]] = None) -> None:
+    """fp4_gemv_multi: one launch computing outs[i][m][n] (row stride ldys[i]) for every weight."""
+    x, M, K = _x2d(x)
+    n = len(weights)
+    if not 1 <= n <= MAX_PROJ or len(outs) != n:
+        raise ValueError("need 1..%d weights and as many outputs" % MAX_PROJ)
+    arr = (_Proj * n)()
+    for i, (w, y) in enumerate(zip(weights, outs)):
+        if w.K != K:
+            raise ValueError("weight %d has K=%d, x has K=%d" % (i, w.K, K))
+        ldy = ldys[i] if ldys is not None else w.N
+        if y.device.type != "cuda" or y.dtype != torch.float32:
+            raise ValueError("outs[%d] must be a float32 GPU tensor" % i)
+        avail = y.untyped_storage().nbytes() // 4 - y.storage_offset()   # fp32 elements from y's data_ptr on
+        if avail < (M - 1) * ldy + w.N:
+            raise ValueError("outs[%d] is too small for M=%d rows of stride %d" % (i, M, ldy))
+        arr[i] = _Proj(_dev(w.packed, "packed"), _dev(w.scales, "scales"), _dev(w.gscale, "gscale", torch.float32),
+                       w.N, y.data_ptr(), ldy)
+    _check(_lib.fp4_gemv_multi(arr, n, _dev(x, "x", torch.bfloat16), M, K, _stream(x.device)), "fp4_gemv_multi")
+
+
+def gemm_prefill(x: torch.Tensor, w: NVFP4Weight, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp4_gemm_prefill: the same product on bf16 MFMA for prefill-sized M."""
+    x, M, K = _x2d(x)
+    if K != w.K:
+        raise ValueError("x has K=%d, weight has K=%d" % (K, w.K))
+    if out is None:
+        out = torch.empty((M, w.N), dtype=torch.float32, device=x.device)
+    _check(_lib.fp4_gemm_prefill(_dev(out, "y", torch.float32), _dev(x, "x", torch.bfloat16),
+                                 _dev(w.packed, "packed"), _dev(w.scales, "scales"),
+                                 _dev(w.gscale, "gscale", torch.float32), M, w.N, K, _stream(x.device)),
+           "fp4_gemm_prefill")
+    return out
+
+
+def raw():
+    """The ctypes handle of libfp4.so (for tests that call the C ABI directly)."""
+    return _lib
+
+
+__all__ = ["quantize", "retile", "gemv", "gemv_multi", "gemm_prefill", "layout_bytes", "NVFP4Weight",
+           "Fp4Error", "raw", "ROWMAJOR", "TILED", "LIB_PATH", "HEADER_PATH"]

@@ -1,0 +1,204 @@
+// NVFP4 quantisation (load time) and canonical -> tiled re-tiling.
+//
+// The engine shrinks every weight once when the model is loaded (page "How
+// imp turns a model file into words", Part one) and keeps the transformed
+// weights (page "imp" README, the weight-cache note). This file does both on
+// the GPU. The quantised bytes are unique, so each fp32 step below is one
+// IEEE operation rounded to nearest-even: divisions are correctly rounded
+// (-fhip-fp32-correctly-rounded-divide-sqrt) and this file is compiled with
+// -ffp-contract=off so that no multiply is fused into an add.
+//
+// Launch sequence for one tensor, all on the caller's stream:
+//   1. k_amax_init   slot := 0
+//   2. k_amax        slot := max over W of the bf16 magnitude bits (atomic max;
+//                    bf16 magnitudes order like their bit patterns)
+//   3. k_encode      one thread per 16-element block: block scale, codes, pack
+//   4. k_finalize    slot := amax / 2688  (the tensor scale gscale)
+#include "fp4_internal.h"
+
+namespace fp4 {
+namespace {
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t h) { return __uint_as_float(h << 16); }
+
+// fp32 (>= 0) -> E4M3 code, nearest-even, saturating at 448 (code 0x7E).
+// Normal results: round the 24-bit significand to 4 bits. Subnormal results
+// (below 2^-6): the code is the integer nearest to s * 2^9 (ties to even),
+// where 8 means the smallest normal, code 0x08.
+__device__ __forceinline__ uint32_t e4m3_code(float s) {
+  if (!(s < 448.0f)) return 0x7Eu;
+  const uint32_t u = __float_as_uint(s);
+  const int e = (int)(u >> 23) - 127;
+  if (e >= -6) {
+    const uint32_t sig = (u & 0x7FFFFFu) | 0x800000u;
+    uint32_t q = sig >> 20;                 // 8..15
+    const uint32_t rem = sig & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ++q;
+    uint32_t E = (uint32_t)(e + 7);
+    if (q == 16u) { q = 8u; ++E; }
+    return (E << 3) | (q - 8u);
+  }
+  return (uint32_t)__builtin_rintf(s * 512.0f);
+}
+
+// E2M1 code of v: the magnitude code counts the decision thresholds passed
+// (midpoints between the eight magnitudes; at a midpoint the even code
+// wins, hence > at 0.25, 1.25, 2.5, 5 and >= at 0.75, 1.75, 3.5). The sign
+// bit of v becomes bit 3.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = fabsf(v);
+  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                     (uint32_t)(a > 5.0f);
+  return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+__global__ void k_amax_init(uint32_t* slot) { *slot = 0u; }
+
+__global__ __launch_bounds__(256) void k_amax(const uint4* __restrict__ W, int64_t nvec,
+                                              uint32_t* slot) {
+  uint32_t m = 0;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += stride) {
+    const uint4 v = W[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      m = max(m, w[j] & 0x7FFFu);
+      m = max(m, (w[j] >> 16) & 0x7FFFu);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+  if ((threadIdx.x & 63) == 0 && m != 0u) atomicMax(slot, m);
+}
+
+// One thread per 16-element block. For the tiled layout the thread space is
+// the padded one (G*8 rows x C*64 blocks) so padding is written as zeros.
+__global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ W, int64_t N, int64_t K,
+                                                int tiled, uint8_t* __restrict__ packed,
+                                                uint8_t* __restrict__ scales,
+                                                const uint32_t* __restrict__ slot) {
+  const int64_t kb = K / 16;                          // blocks per row
+  const int64_t C = chunks_of(K);
+  const int64_t bpr = tiled ? C * 64 : kb;            // blocks per (padded) row
+  const int64_t rows = tiled ? groups_of(N) * kGroupRows : N;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= rows * bpr) return;
+  const int64_t n = t / bpr, b = t % bpr;
+
+  uint32_t sc = 0, lo = 0, hi = 0;  // scale code, packed bytes 0..3 and 4..7
+  const float amax = bf16_bits_to_float(*slot);
+  if (n < N && b < kb && amax != 0.0f) {
+    const float gscale = amax / 2688.0f;
+    const uint4* src = reinterpret_cast<const uint4*>(W + n * K + b * 16);
+    uint32_t h[16];
+    {
+      const uint4 a = src[0], c = src[1];
+      const uint32_t d[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) { h[2 * j] = d[j] & 0xFFFFu; h[2 * j + 1] = d[j] >> 16; }
+    }
+    uint32_t bm = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) bm = max(bm, h[j] & 0x7FFFu);
+    const float bamax = bf16_bits_to_float(bm);
+    const float s = (bamax / 6.0f) / gscale;
+    sc = e4m3_code(s);
+    const float s_dec = __builtin_amdgcn_cvt_f32_fp8((int)sc, 0);   // OCP E4M3 decode
+    if (s_dec != 0.0f) {
+      const float d = __fmul_rn(s_dec, gscale);
+      uint32_t codes[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) codes[j] = e2m1_code(bf16_bits_to_float(h[j]) / d);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        lo |= (codes[2 * j] | (codes[2 * j + 1] << 4)) << (8 * j);
+        hi |= (codes[8 + 2 * j] | (codes[9 + 2 * j] << 4)) << (8 * j);
+      }
+    }
+  }
+  if (!tiled) {
+    *reinterpret_cast<uint2*>(packed + n * (K / 2) + b * 8) = make_uint2(lo, hi);
+    scales[n * kb + b] = (uint8_t)sc;
+  } else {
+    const int64_t g = n / kGroupRows, r = n % kGroupRows;
+    const int64_t c = b / 64, l = (b % 64) / 2, j = b % 2;
+    const int64_t tile = g * C + c;
+    *reinterpret_cast<uint2*>(packed + tile * kTilePacked + r * 512 + l * 16 + j * 8) = make_uint2(lo, hi);
+    scales[tile * kTileScale + l * 16 + r * 2 + j] = (uint8_t)sc;
+  }
+}
+
+__global__ void k_finalize(uint32_t* slot) {
+  const float amax = bf16_bits_to_float(*slot);
+  *reinterpret_cast<float*>(slot) = amax / 2688.0f;   // 0 stays 0
+}
+
+// One thread per 16-byte lane piece of a packed tile; threads of the first
+// G*C*32 also build the lane's 16 scale bytes.
+__global__ __launch_bounds__(256) void k_retile(const uint8_t* __restrict__ packed,
+                                                const uint8_t* __restrict__ scales, int64_t N,
+                                                int64_t K, uint8_t* __restrict__ packed_t,
+                                                uint8_t* __restrict__ scales_t) {
+  const int64_t G = groups_of(N), C = chunks_of(K);
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= G * C * 256) return;
+  const int64_t tile = t / 256, rl = t % 256, r = rl / 32, l = rl % 32;
+  const int64_t g = tile / C, c = tile % C;
+  const int64_t row = g * kGroupRows + r;
+  const int64_t rb = K / 2;                 // canonical bytes per row
+  const int64_t kbyte = c * 512 + l * 16;   // first byte of this piece in the row
+  uint2 a = make_uint2(0, 0), b = make_uint2(0, 0);
+  if (row < N) {
+    const uint8_t* src = packed + row * rb + kbyte;   // 8-byte aligned (rb % 8 == 0)
+    if (kbyte + 8 <= rb) a = *reinterpret_cast<const uint2*>(src);
+    if (kbyte + 16 <= rb) b = *reinterpret_cast<const uint2*>(src + 8);
+  }
+  *reinterpret_cast<uint4*>(packed_t + tile * kTilePacked + r * 512 + l * 16) = make_uint4(a.x, a.y, b.x, b.y);
+  if (rl < 32) {
+    const int64_t kb = K / 16;
+    uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) {
+      const int64_t row2 = g * kGroupRows + rr;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t blk = c * 64 + rl * 2 + j;
+        const uint32_t v = (row2 < N && blk < kb) ? scales[row2 * kb + blk] : 0u;
+        const int pos = rr * 2 + j;
+        w[pos / 4] |= v << (8 * (pos % 4));
+      }
+    }
+    *reinterpret_cast<uint4*>(scales_t + tile * kTileScale + rl * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const uint16_t* W, int64_t N, int64_t K, bool tiled, uint8_t* packed,
+                           uint8_t* scales, float* gscale, hipStream_t s) {
+  uint32_t* slot = reinterpret_cast<uint32_t*>(gscale);
+  hipLaunchKernelGGL(k_amax_init, dim3(1), dim3(1), 0, s, slot);
+  const int64_t nvec = N * K / 8;
+  const int64_t want = (nvec + 255) / 256;
+  const int grid_amax = (int)(want < 4096 ? want : 4096);
+  hipLaunchKernelGGL(k_amax, dim3(grid_amax), dim3(256), 0, s, reinterpret_cast<const uint4*>(W), nvec, slot);
+  const int64_t rows = tiled ? groups_of(N) * kGroupRows : N;
+  const int64_t bpr = tiled ? chunks_of(K) * 64 : K / 16;
+  const int64_t nthreads = rows * bpr;
+  hipLaunchKernelGGL(k_encode, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0, s, W, N, K,
+                     tiled ? 1 : 0, packed, scales, slot);
+  hipLaunchKernelGGL(k_finalize, dim3(1), dim3(1), 0, s, slot);
+  return hipGetLastError();
+}
+
+hipError_t launch_retile(const uint8_t* packed, const uint8_t* scales, int64_t N, int64_t K,
+                         uint8_t* packed_t, uint8_t* scales_t, hipStream_t s) {
+  const int64_t n = groups_of(N) * chunks_of(K) * 256;
+  hipLaunchKernelGGL(k_retile, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, packed, scales, N, K,
+                     packed_t, scales_t);
+  return hipGetLastError();
+}
+
+}  // namespace fp4

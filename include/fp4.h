@@ -1,0 +1,164 @@
+/*
+ * fp4.h: C ABI of the NVFP4 decode-path library for AMD Instinct MI355X
+ * (gfx950). Built as libfp4.so from bit_block_scaled_fp4_amd/csrc/.
+ *
+ * What it computes. Decode in an LLM engine is bandwidth-bound: every weight
+ * is read once per generated token and the arithmetic is trivial, so the
+ * weights are kept in 4 bits and multiplied without first expanding them to
+ * 16 bits (page "imp" README, the decode paragraph of the request
+ * walkthrough; page "1. The big picture", section "The most important
+ * number in this book", whose ceiling tokens/s <= bandwidth / bytes per token
+ * is the roofline used to judge these kernels). Shrinking the weights at load
+ * time is "the biggest single lever" for decode (page "How imp turns a model
+ * file into words", Part one: loading the model).
+ *
+ * Format (NVFP4: four-bit values and two scales, as the engineering log's post
+ * "NVFP4 at the bit level" describes it):
+ *   - element: FP4 E2M1 (OCP MX v1.0), values {0,0.5,1,1.5,2,3,4,6} with sign,
+ *     two per byte, the even K index in the low nibble;
+ *   - block scale: one FP8 E4M3 (OCP "fn": max 448, no infinities) per 16
+ *     consecutive K elements of a row;
+ *   - tensor scale gscale: one fp32 decode multiplier per tensor.
+ *   dequant(W)[n][k] = E2M1(q[n][k]) * E4M3(sc[n][k/16]) * gscale.
+ *
+ * Shapes. W is [N][K] (N output features, K input features), x is bf16
+ * [M][K] row-major, y is fp32 [M][N] row-major (y[m*ldy + n]).
+ * y[m][n] = sum_k dequant(W)[n][k] * x[m][k]. K must be a multiple of 16.
+ *
+ * Layouts of the quantised weights (see fp4_layout_bytes for sizes):
+ *   FP4_LAYOUT_ROWMAJOR (canonical): packed [N][K/2] bytes, scales [N][K/16]
+ *     bytes, both row-major.
+ *   FP4_LAYOUT_TILED (device layout read by fp4_gemv, fp4_gemv_multi and
+ *     fp4_gemm_prefill): rows form groups of 8 (G = ceil(N/8)), K forms
+ *     chunks of 1024 (C = ceil(K/1024)); tile (g, c) is stored at index
+ *     g*C + c. In a packed tile (4096 B) byte r*512 + l*16 + i holds
+ *     canonical byte (row 8g+r, byte 512c + 16l + i); in a scale tile (512 B)
+ *     byte l*16 + r*2 + j holds the scale of (row 8g+r, block 64c + 2l + j),
+ *     for r < 8, l < 32, i < 16, j < 2. Positions outside the tensor hold 0.
+ *     One 32-lane group thus reads a row's 1024-element chunk as 32
+ *     contiguous 16-byte pieces, two whole 16-element blocks per lane, and
+ *     the 16 scales it needs for 8 rows as one 16-byte load.
+ *
+ * Conventions for every call:
+ *   - Pointers marked "device" are HIP device memory (e.g. a torch CUDA
+ *     tensor's data_ptr()) on the current HIP device; the caller owns every
+ *     buffer; the library allocates nothing and keeps no state between calls.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Calls only
+ *     enqueue work: they never synchronise, and results are ready when the
+ *     stream's work is. gscale is a device pointer, so quantise -> multiply
+ *     is stream-ordered and can be captured in a HIP graph.
+ *   - Arguments are checked on the host before any HIP call; on an error
+ *     nothing is enqueued and the status says why. FP4_ERR_HIP means the
+ *     launch itself failed. A fault inside a kernel surfaces at the
+ *     caller's next synchronisation, as usual for HIP.
+ *   - Alignment: x, W, packed and scales must be 16-byte aligned (canonical
+ *     packed input of fp4_retile: 8-byte; fp4_quantize's canonical packed
+ *     output: 8-byte); y and gscale 4-byte aligned.
+ *   - Size limits: 1 <= N <= 2^28, 16 <= K <= 2^24, 1 <= M <= 2^24.
+ *   - Calls are thread-safe (no global mutable state).
+ */
+#ifndef FP4_H
+#define FP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define FP4_API __attribute__((visibility("default")))
+#else
+#define FP4_API
+#endif
+
+typedef enum {
+    FP4_OK = 0,
+    FP4_ERR_NULL = -1,        /* a required pointer is NULL */
+    FP4_ERR_SHAPE = -2,       /* a size is out of range or K % 16 != 0 */
+    FP4_ERR_ALIGN = -3,       /* a pointer is not aligned as required */
+    FP4_ERR_LAYOUT = -4,      /* unknown layout tag */
+    FP4_ERR_HIP = -5,         /* the HIP runtime rejected a launch */
+    FP4_ERR_UNSUPPORTED = -6  /* valid request this build cannot serve */
+} fp4_status;
+
+typedef enum { FP4_LAYOUT_ROWMAJOR = 0, FP4_LAYOUT_TILED = 1 } fp4_layout;
+
+/* Human-readable text for a status code (static storage, never NULL). */
+FP4_API const char *fp4_status_string(int status);
+
+/* Bytes of the packed and scale arrays for an N x K weight in `layout`.
+ * ROWMAJOR: N*K/2 and N*K/16. TILED: G*C*4096 and G*C*512 (see above).
+ * Host-only; enqueues nothing. */
+FP4_API int fp4_layout_bytes(int64_t N, int64_t K, int layout, size_t *packed_bytes, size_t *scale_bytes);
+
+/* Quantise a bf16 weight W [N][K] (device) to NVFP4 in `layout`, writing
+ * packed and scales (device, sized by fp4_layout_bytes) and the tensor scale
+ * *gscale (device fp32). The rule, one fp32 IEEE operation per step:
+ *   gscale = amax|W| / 2688 (= 448*6; 0 for an all-zero W);
+ *   per block s = (block_amax / 6) / gscale, scale code = E4M3 nearest-even
+ *   of s, saturating at 448;
+ *   per element code = E2M1 nearest-even of w / (E4M3(code) * gscale),
+ *   saturating at 6, sign from the sign bit (-0 for small negatives);
+ *   a block whose scale code is 0 gets element codes 0.
+ * The bytes are unique under this rule. W must hold finite values. Padding
+ * positions of the tiled layout are written as 0. Uses *gscale as scratch
+ * while it runs. (Load-time step of the engine tour's Part one: shrinking
+ * every weight once, on the GPU.) */
+FP4_API int fp4_quantize(const void *W_bf16, int64_t N, int64_t K, int layout, void *packed, void *scales,
+                 float *gscale, void *stream);
+
+/* Re-tile canonical (ROWMAJOR) packed/scales into the TILED layout. A pure
+ * byte permutation plus zero padding; inputs and outputs must not overlap.
+ * (The README's load-time weight transformation, cached across starts.) */
+FP4_API int fp4_retile(const void *packed_rm, const void *scales_rm, int64_t N, int64_t K, void *packed_tiled,
+               void *scales_tiled, void *stream);
+
+/* y[M][N] = x[M][K] * dequant(W)^T for TILED weights, fp32 accumulation,
+ * y overwritten (fp32, ldy = N). The decode-step matrix-vector product
+ * (M = 1) and its small-M form, where several rows (concurrent streams,
+ * or tokens being verified by speculative decoding) share one pass over
+ * the weights (page "1. The big picture", the batching and speculative
+ * decoding bullets of "The most important number in this book").
+ * Any M >= 1 is accepted. */
+FP4_API int fp4_gemv(float *y, const void *x_bf16, const void *packed, const void *scales, const float *gscale,
+             int64_t M, int64_t N, int64_t K, void *stream);
+
+/* One projection of a fused launch: TILED weights with N rows and their own
+ * tensor scale, writing y[m*ldy + n] (fp32, device) for n < N. */
+typedef struct {
+    const void *packed;
+    const void *scales;
+    const float *gscale;
+    int64_t N;
+    float *y;
+    int64_t ldy;
+} fp4_proj;
+
+#define FP4_MAX_PROJ 8
+
+/* Several projections that read the same x [M][K] (e.g. Q, K and V, or the
+ * gate and up halves of an MLP) in ONE kernel launch: results equal
+ * separate fp4_gemv calls. 1 <= nproj <= FP4_MAX_PROJ; `projs` is host
+ * memory read before the call returns; ldy >= N for each. Cuts the number
+ * of launches per token (page "imp" README: replaying one recorded launch
+ * sequence instead of re-issuing hundreds of launches per token). */
+FP4_API int fp4_gemv_multi(const fp4_proj *projs, int nproj, const void *x_bf16, int64_t M, int64_t K,
+                   void *stream);
+
+/* The same product for prefill-sized M on the matrix cores: weight tiles
+ * are dequantised exactly to bf16 (E2M1 x E4M3 fits bf16) in LDS and fed
+ * to bf16 MFMA with fp32 accumulation; gscale is applied once in the fp32
+ * epilogue. Prefill is compute-bound: thousands of prompt tokens go
+ * through each layer at once (page "imp" README, the prefill paragraph;
+ * page "1. The big picture", "Two phases with very different costs").
+ * Any M >= 1 is accepted; y [M][N] fp32 overwritten. */
+FP4_API int fp4_gemm_prefill(float *y, const void *x_bf16, const void *packed, const void *scales,
+                     const float *gscale, int64_t M, int64_t N, int64_t K, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4_H */

@@ -1,0 +1,99 @@
+"""The C-ABI library loads, exports every function include/fp4.h declares,
+and rejects bad arguments on the host before any HIP call (no GPU needed:
+none of these calls reaches a launch)."""
+import ctypes
+import re
+
+import pytest
+
+import bit_block_scaled_fp4_amd as fp4
+
+OK, ENULL, ESHAPE, EALIGN, ELAYOUT = 0, -1, -2, -3, -4
+A = 1 << 20          # a fake, 16-byte-aligned address; never dereferenced
+
+
+def declared_functions():
+    src = open(fp4.HEADER_PATH).read()
+    return sorted(set(re.findall(r"FP4_API\s+[\w\s\*]*?\b(fp4_\w+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert names == sorted(["fp4_status_string", "fp4_layout_bytes", "fp4_quantize", "fp4_retile", "fp4_gemv",
+                            "fp4_gemv_multi", "fp4_gemm_prefill"])
+    lib = ctypes.CDLL(fp4.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    lib = fp4.raw()
+    for s in (OK, ENULL, ESHAPE, EALIGN, ELAYOUT, -5, -6, 42):
+        assert isinstance(lib.fp4_status_string(s), bytes) and lib.fp4_status_string(s)
+
+
+def test_layout_bytes():
+    assert fp4.layout_bytes(1024, 1024, "rowmajor") == (1024 * 512, 1024 * 64)
+    assert fp4.layout_bytes(1024, 1024, "tiled") == (128 * 4096, 128 * 512)
+    assert fp4.layout_bytes(11, 1040, "tiled") == (2 * 2 * 4096, 2 * 2 * 512)
+    assert fp4.layout_bytes(151936, 1024, "tiled") == (151936 * 512, 151936 * 64)
+    with pytest.raises(fp4.Fp4Error) as e:
+        fp4.layout_bytes(8, 24)
+    assert e.value.status == ESHAPE
+    with pytest.raises(KeyError):
+        fp4.layout_bytes(8, 32, "columnmajor")
+    pb, sb = ctypes.c_size_t(), ctypes.c_size_t()
+    assert fp4.raw().fp4_layout_bytes(8, 32, 7, ctypes.byref(pb), ctypes.byref(sb)) == ELAYOUT
+    assert fp4.raw().fp4_layout_bytes(8, 32, 0, None, ctypes.byref(sb)) == ENULL
+
+
+def test_gemv_argument_errors():
+    L = fp4.raw()
+    assert L.fp4_gemv(None, A, A, A, A, 1, 8, 32, None) == ENULL
+    assert L.fp4_gemv(A, A, A, A, None, 1, 8, 32, None) == ENULL
+    assert L.fp4_gemv(A, A, A, A, A, 0, 8, 32, None) == ESHAPE
+    assert L.fp4_gemv(A, A, A, A, A, 1, 0, 32, None) == ESHAPE
+    assert L.fp4_gemv(A, A, A, A, A, 1, 8, 24, None) == ESHAPE
+    assert L.fp4_gemv(A, A, A, A, A, 1, 8, 0, None) == ESHAPE
+    assert L.fp4_gemv(A, A, A, A, A, 1, 1 << 29, 32, None) == ESHAPE
+    assert L.fp4_gemv(A, A + 8, A, A, A, 1, 8, 32, None) == EALIGN
+    assert L.fp4_gemv(A, A, A + 4, A, A, 1, 8, 32, None) == EALIGN
+    assert L.fp4_gemv(A + 2, A, A, A, A, 1, 8, 32, None) == EALIGN
+
+
+def test_gemv_multi_argument_errors():
+    L = fp4.raw()
+    P = (fp4._Proj * 9)()
+    for i in range(9):
+        P[i] = fp4._Proj(A, A, A, 8, A, 8)
+    assert L.fp4_gemv_multi(None, 1, A, 1, 32, None) == ENULL
+    assert L.fp4_gemv_multi(P, 0, A, 1, 32, None) == ESHAPE
+    assert L.fp4_gemv_multi(P, 9, A, 1, 32, None) == ESHAPE
+    P[1] = fp4._Proj(A, A, A, 8, A, 4)                 # ldy < N
+    assert L.fp4_gemv_multi(P, 2, A, 1, 32, None) == ESHAPE
+    P[1] = fp4._Proj(A, None, A, 8, A, 8)
+    assert L.fp4_gemv_multi(P, 2, A, 1, 32, None) == ENULL
+    P[1] = fp4._Proj(A, A + 1, A, 8, A, 8)
+    assert L.fp4_gemv_multi(P, 2, A, 1, 32, None) == EALIGN
+
+
+def test_quantize_retile_prefill_argument_errors():
+    L = fp4.raw()
+    assert L.fp4_quantize(None, 8, 32, 1, A, A, A, None) == ENULL
+    assert L.fp4_quantize(A, 8, 30, 1, A, A, A, None) == ESHAPE
+    assert L.fp4_quantize(A, 8, 32, 3, A, A, A, None) == ELAYOUT
+    assert L.fp4_quantize(A + 8, 8, 32, 1, A, A, A, None) == EALIGN
+    assert L.fp4_retile(A, A, 8, 32, None, A, None) == ENULL
+    assert L.fp4_retile(A, A, -1, 32, A, A, None) == ESHAPE
+    assert L.fp4_retile(A + 4, A, 8, 32, A, A, None) == EALIGN
+    assert L.fp4_gemm_prefill(A, A, A, A, None, 4, 8, 32, None) == ENULL
+    assert L.fp4_gemm_prefill(A, A, A, A, A, 0, 8, 32, None) == ESHAPE
+    assert L.fp4_gemm_prefill(A, A + 2, A, A, A, 4, 8, 32, None) == EALIGN
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    W = torch.zeros(8, 32, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fp4.quantize(W, out=fp4.NVFP4Weight(torch.zeros(1, dtype=torch.uint8), torch.zeros(1, dtype=torch.uint8),
+                                            torch.zeros(1), 8, 32))

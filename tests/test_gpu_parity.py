@@ -1,0 +1,306 @@
+"""GPU parity: the HIP path against the CPU oracle on the same seeded inputs.
+
+Quantiser bytes and re-tiled layouts must be bit-exact. Products must satisfy
+|y_gpu - y_ref| <= 2e-3 * sum_k |w_nk * x_k| per output element (y_ref in
+fp64, w the dequantised weight), and exactly equal where every partial sum is
+exact in fp32. Sizes run from single tiles with ragged tails to the full
+workload shapes, all through the C ABI (via the thin binding)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import bf16_to_float32, float32_to_bf16_bits, bf16_tensor
+
+from gpu_common import (THREADS, act_bits, assert_within_tolerance, dev, gpu_u8, oracle_quant, to_gpu_bf16,
+                        weight_bits)
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import bit_block_scaled_fp4_amd as fp4
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def gpu_quant(bits, layout="tiled"):
+    w = fp4.quantize(to_gpu_bf16(bits), layout)
+    torch.cuda.synchronize()
+    return w
+
+
+def check_quant_bytes(bits, what):
+    p, s, g = oracle.quantize(bits)
+    w = gpu_quant(bits, "rowmajor")
+    gp, gsc, gg = gpu_u8(w.packed), gpu_u8(w.scales), w.gscale.item()
+    assert np.float32(gg) == g, (what, gg, g)
+    assert np.array_equal(gsc.reshape(s.shape), s), (what, np.flatnonzero(gsc.reshape(s.shape) != s)[:8])
+    assert np.array_equal(gp.reshape(p.shape), p), (what, np.flatnonzero(gp.reshape(p.shape) != p)[:8])
+    pt, st = oracle.tile(p, s)
+    wt = gpu_quant(bits, "tiled")
+    assert np.array_equal(gpu_u8(wt.packed), pt) and np.array_equal(gpu_u8(wt.scales), st), what
+    assert wt.gscale.item() == gg
+    return p, s, g
+
+
+# ------------------------------------------------------------------- quantiser
+def edge_tensors():
+    rng = np.random.default_rng(11)
+    out = {}
+    from test_oracle_pins import load_worked_example
+    out["worked_example"] = load_worked_example()[0]
+    out["zeros"] = np.zeros((9, 48), np.uint16)
+    out["ragged_11x48"] = bf16_tensor((11, 48), 7, 0.1)
+    out["ragged_13x1040"] = bf16_tensor((13, 1040), 8, 0.02, outlier_p=0.01, outlier_scale=20)
+    out["one_row_16"] = bf16_tensor((1, 16), 9, 3.0)
+    out["tiny"] = float32_to_bf16_bits(rng.normal(0, 1e-30, (16, 64)).astype(np.float32))
+    out["huge"] = float32_to_bf16_bits(rng.normal(0, 1e30, (16, 64)).astype(np.float32))
+    wide = rng.normal(0, 1, (32, 256)) * np.exp(rng.uniform(-20, 5, (32, 256)))
+    out["wide_dynamic_range"] = float32_to_bf16_bits(wide.astype(np.float32))
+    ties = np.array([oracle.e2m1_value(c) for c in range(16)])
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 5.5])
+    v = rng.choice(np.concatenate([ties, mids, -mids]), (24, 128)) * 0.4375   # exact tie points for d = 0.4375
+    v[:, ::16] = 2.625
+    out["ties"] = float32_to_bf16_bits(v.astype(np.float32))
+    neg = -np.abs(rng.normal(0, 1, (8, 64))) * 1e-3
+    neg[:, 0] = 5.0
+    out["small_negatives"] = float32_to_bf16_bits(neg.astype(np.float32))
+    return out
+
+
+@pytest.mark.parametrize("name", list(edge_tensors().keys()))
+def test_quantize_bit_exact_edge_cases(name):
+    print("quantize edge case", name, flush=True)
+    check_quant_bytes(edge_tensors()[name], name)
+
+
+@pytest.mark.parametrize("wl,t", [("gemv_1024", "w"), ("qwen3_0p6b_decode", "L1.q"), ("qwen3_0p6b_decode", "L1.o"),
+                                  ("qwen3_0p6b_decode", "L28.down"), ("dense27b_layer", "gate"),
+                                  ("dense27b_layer", "up"), ("dense27b_layer", "down"), ("lm_head", "w")])
+def test_quantize_bit_exact_workloads(wl, t):
+    print("quantize", wl, t, flush=True)
+    p, s, g = check_quant_bytes(weight_bits(wl, t), "%s/%s" % (wl, t))
+    op, os_, og = oracle_quant(wl, t)
+    assert og == g
+
+
+def test_retile_bit_exact_and_pads_with_zeros():
+    for shape, seed in [((11, 1040), 3), ((24, 3072), 4), ((5, 16), 5), ((300, 2064), 6)]:
+        bits = bf16_tensor(shape, seed, 0.05)
+        w = gpu_quant(bits, "rowmajor")
+        N, K = shape
+        pb, sb = fp4.layout_bytes(N, K, "tiled")
+        out = fp4.NVFP4Weight(torch.full((pb,), 0xAB, dtype=torch.uint8, device=dev()),
+                              torch.full((sb,), 0xCD, dtype=torch.uint8, device=dev()), w.gscale, N, K, fp4.TILED)
+        fp4.retile(w, out)
+        p, s, _ = oracle.quantize(bits)
+        pt, st = oracle.tile(p, s)
+        assert np.array_equal(gpu_u8(out.packed), pt) and np.array_equal(gpu_u8(out.scales), st), shape
+
+
+# ------------------------------------------------------------------- products
+def run_gemv(bits_w, bits_x):
+    w = gpu_quant(bits_w)
+    y = fp4.gemv(to_gpu_bf16(bits_x), w)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+@pytest.mark.parametrize("N,K,M", [(1, 16, 1), (7, 32, 1), (16, 1024, 1), (1000, 1040, 1), (1000, 1040, 2),
+                                   (333, 2064, 3), (17, 3072, 5), (64, 5120, 8), (130, 17408, 4), (40, 8192, 16),
+                                   (257, 1024, 7), (2050, 2048, 1)])
+def test_gemv_small_shapes(N, K, M):
+    print("gemv", N, K, M, flush=True)
+    bw = bf16_tensor((N, K), N * 7 + K, 0.03, outlier_p=0.002, outlier_scale=20.0)
+    bx = bf16_tensor((M, K), 99 + M, 1.0)
+    y = run_gemv(bw, bx)
+    p, s, g = oracle.quantize(bw)
+    yr, l1 = oracle.gemv(bx, p, s, g, threads=THREADS)
+    assert_within_tolerance(y, yr, l1, "gemv %dx%d M=%d" % (N, K, M))
+
+
+def test_gemv_exact_when_every_partial_sum_is_exact():
+    """Every block holds 2.625 (so all scales are 0x7E and gscale = 2^-10) and
+    x is +-2^k: every product and partial sum is exact in fp32, so the GPU
+    result must equal the exact oracle value bit for bit."""
+    rng = np.random.default_rng(21)
+    N, K, M = 48, 2048, 3
+    mags = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6]) * 0.4375
+    W = rng.choice(mags, (N, K)) * rng.choice([-1, 1], (N, K))
+    W[:, ::16] = 2.625
+    bw = float32_to_bf16_bits(W.astype(np.float32))
+    x = (2.0 ** rng.integers(-3, 4, (M, K))) * rng.choice([-1, 1], (M, K))
+    bx = float32_to_bf16_bits(x.astype(np.float32))
+    y = run_gemv(bw, bx)
+    p, s, g = oracle.quantize(bw)
+    assert g == 2.0 ** -10 and np.all(s == 0x7E)
+    yr, _ = oracle.gemv(bx, p, s, g)
+    assert np.array_equal(y.astype(np.float64), yr)
+    w = gpu_quant(bw)
+    yp = fp4.gemm_prefill(to_gpu_bf16(bx), w)
+    torch.cuda.synchronize()
+    assert np.array_equal(yp.cpu().numpy().astype(np.float64), yr)
+
+
+def test_gemv_one_hot_selects_a_column():
+    """x = e_k returns column k of the dequantised weight: pins the nibble
+    order, the block-scale index and the tiled layout on the GPU."""
+    bw = weight_bits("gemv_1024", "w")[:200]
+    p, s, g = oracle.quantize(bw)
+    D = oracle.dequant(p, s, g)
+    w = gpu_quant(bw)
+    ks = [0, 1, 2, 15, 16, 31, 32, 33, 511, 512, 1000, 1023]
+    X = np.zeros((len(ks), 1024), np.float32)
+    for i, k in enumerate(ks):
+        X[i, k] = 1.0
+    y = fp4.gemv(to_gpu_bf16(float32_to_bf16_bits(X)), w)
+    torch.cuda.synchronize()
+    # E2M1*E4M3 is exact in fp32, so the only rounding is the final product
+    # with gscale: the result is the exact dequantised weight rounded to fp32.
+    assert np.array_equal(y.cpu().numpy(), D[:, ks].T.astype(np.float32))
+
+
+def test_gemv_workload_gemv_1024():
+    bw, bx = weight_bits("gemv_1024", "w"), act_bits("gemv_1024", "x")
+    y = run_gemv(bw, bx)
+    p, s, g = oracle_quant("gemv_1024", "w")
+    yr, l1 = oracle.gemv(bx, p, s, g, threads=THREADS)
+    assert_within_tolerance(y, yr, l1, "gemv_1024")
+
+
+def test_gemv_workload_qwen_decode_all_layers():
+    """28 layers x (fused QKV, O, fused gate_up, down) at M=1."""
+    wl = "qwen3_0p6b_decode"
+    for l in range(1, 29):
+        print("layer", l, flush=True)
+        xs = {k: act_bits(wl, "L%d.x%d" % (l, k)) for k in (1024, 2048, 3072)}
+        ws = {t: gpu_quant(weight_bits(wl, "L%d.%s" % (l, t))) for t in ("q", "k", "v", "o", "gate", "up", "down")}
+        x1 = to_gpu_bf16(xs[1024])
+        qkv = torch.empty((1, 4096), dtype=torch.float32, device=dev())
+        fp4.gemv_multi(x1, [ws["q"], ws["k"], ws["v"]], [qkv, qkv[:, 2048:], qkv[:, 3072:]], [4096] * 3)
+        gu = torch.empty((1, 6144), dtype=torch.float32, device=dev())
+        fp4.gemv_multi(x1, [ws["gate"], ws["up"]], [gu, gu[:, 3072:]], [6144] * 2)
+        o = fp4.gemv(to_gpu_bf16(xs[2048]), ws["o"])
+        d = fp4.gemv(to_gpu_bf16(xs[3072]), ws["down"])
+        torch.cuda.synchronize()
+        res = {"q": qkv[:, :2048], "k": qkv[:, 2048:3072], "v": qkv[:, 3072:], "gate": gu[:, :3072],
+               "up": gu[:, 3072:], "o": o, "down": d}
+        xin = {"q": 1024, "k": 1024, "v": 1024, "gate": 1024, "up": 1024, "o": 2048, "down": 3072}
+        for t, yt in res.items():
+            p, s, g = oracle_quant(wl, "L%d.%s" % (l, t))
+            assert gpu_u8(ws[t].gscale)[0] == g
+            yr, l1 = oracle.gemv(xs[xin[t]], p, s, g, threads=THREADS)
+            assert_within_tolerance(yt.cpu().numpy(), yr, l1, "L%d.%s" % (l, t))
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 16])
+def test_gemv_workload_dense27b(M):
+    """gate_up (one fused launch) and down of the 27B-class layer; M=1 is the
+    single-stream decode layer, M in {2,4,8,16} the small-M batch."""
+    wl = "dense27b_layer"
+    print("dense27b M=%d" % M, flush=True)
+    if M == 1:
+        xin, xmid = act_bits(wl, "x_in"), act_bits(wl, "x_mid")
+    else:
+        xin, xmid = act_bits("dense27b_smallm", "x_in_m%d" % M), act_bits("dense27b_smallm", "x_mid_m%d" % M)
+    wg, wu, wd = (gpu_quant(weight_bits(wl, t)) for t in ("gate", "up", "down"))
+    gu = torch.empty((M, 2 * 17408), dtype=torch.float32, device=dev())
+    fp4.gemv_multi(to_gpu_bf16(xin), [wg, wu], [gu, gu[:, 17408:]], [2 * 17408] * 2)
+    yd = fp4.gemv(to_gpu_bf16(xmid), wd)
+    torch.cuda.synchronize()
+    gu = gu.cpu().numpy()
+    for t, yt, xx in (("gate", gu[:, :17408], xin), ("up", gu[:, 17408:], xin), ("down", yd.cpu().numpy(), xmid)):
+        p, s, g = oracle_quant(wl, t)
+        yr, l1 = oracle.gemv(xx, p, s, g, threads=THREADS)
+        assert_within_tolerance(yt, yr, l1, "%s M=%d" % (t, M))
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_gemv_workload_lm_head(M):
+    bw, bx = weight_bits("lm_head", "w"), act_bits("lm_head", "x_m%d" % M)
+    w = gpu_quant(bw)
+    y = fp4.gemv(to_gpu_bf16(bx), w)
+    torch.cuda.synchronize()
+    p, s, g = oracle_quant("lm_head", "w")
+    yr, l1 = oracle.gemv(bx, p, s, g, threads=THREADS)
+    assert_within_tolerance(y.cpu().numpy(), yr, l1, "lm_head M=%d" % M)
+
+
+def test_gemv_multi_equals_oracle_for_each_projection_and_is_deterministic():
+    rng_shapes = [(2048, 1024), (1024, 1024), (1024, 1024), (333, 1024)]
+    ws, bws = [], []
+    for i, (N, K) in enumerate(rng_shapes):
+        b = bf16_tensor((N, K), 500 + i, 0.02)
+        bws.append(b)
+        ws.append(gpu_quant(b))
+    bx = bf16_tensor((3, 1024), 77, 1.0)
+    x = to_gpu_bf16(bx)
+    outs = [torch.empty((3, N), dtype=torch.float32, device=dev()) for N, _ in rng_shapes]
+    fp4.gemv_multi(x, ws, outs)
+    outs2 = [torch.empty_like(o) for o in outs]
+    fp4.gemv_multi(x, ws, outs2)
+    torch.cuda.synchronize()
+    for b, o, o2 in zip(bws, outs, outs2):
+        p, s, g = oracle.quantize(b)
+        yr, l1 = oracle.gemv(bx, p, s, g)
+        assert_within_tolerance(o.cpu().numpy(), yr, l1, "multi")
+        assert torch.equal(o, o2)
+
+
+# --------------------------------------------------------------------- prefill
+@pytest.mark.parametrize("M,N,K", [(1, 8, 16), (37, 300, 1040), (200, 129, 2048), (128, 256, 64), (300, 1000, 5120)])
+def test_prefill_small_shapes(M, N, K):
+    print("prefill", M, N, K, flush=True)
+    bw = bf16_tensor((N, K), M + N + K, 0.02, outlier_p=0.002, outlier_scale=20.0)
+    bx = bf16_tensor((M, K), 3 * M + 1, 1.0)
+    w = gpu_quant(bw)
+    y = fp4.gemm_prefill(to_gpu_bf16(bx), w)
+    torch.cuda.synchronize()
+    p, s, g = oracle.quantize(bw)
+    yr, l1 = oracle.gemv(bx, p, s, g, threads=THREADS)
+    assert_within_tolerance(y.cpu().numpy(), yr, l1, "prefill %d %d %d" % (M, N, K))
+
+
+def test_prefill_full_size_sampled_rows():
+    """M=2048 tokens x gate_up 34816x5120 (two 17408-row tensors in one
+    [2048][34816] output via two calls into column slices is not possible with
+    ldy = N, so each half is its own call). Checked on 8 sampled token rows,
+    all 34816 outputs each."""
+    wl = "prefill"
+    bx = act_bits(wl, "x")
+    x = to_gpu_bf16(bx)
+    rows = [0, 1, 127, 128, 1000, 1500, 2046, 2047]
+    for t in ("gate", "up"):
+        w = gpu_quant(weight_bits("dense27b_layer", t))
+        y = fp4.gemm_prefill(x, w)
+        y2 = fp4.gemm_prefill(x, w)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y2)
+        p, s, g = oracle_quant("dense27b_layer", t)
+        yr, l1 = oracle.gemv(bx[rows], p, s, g, threads=THREADS)
+        assert_within_tolerance(y[rows].cpu().numpy(), yr, l1, "prefill %s" % t)
+
+
+def test_gemv_and_prefill_agree_with_each_other():
+    bw = weight_bits("gemv_1024", "w")
+    w = gpu_quant(bw)
+    bx = bf16_tensor((16, 1024), 4242, 1.0)
+    x = to_gpu_bf16(bx)
+    a, b = fp4.gemv(x, w), fp4.gemm_prefill(x, w)
+    torch.cuda.synchronize()
+    p, s, g = oracle_quant("gemv_1024", "w")
+    yr, l1 = oracle.gemv(bx, p, s, g)
+    assert_within_tolerance(a.cpu().numpy(), yr, l1, "gemv")
+    assert_within_tolerance(b.cpu().numpy(), yr, l1, "prefill")
+
+
+def test_errors_raise_on_gpu():
+    W = torch.zeros((8, 24), dtype=torch.bfloat16, device=dev())
+    with pytest.raises(fp4.Fp4Error):
+        fp4.quantize(W, out=fp4.NVFP4Weight(torch.zeros(64, dtype=torch.uint8, device=dev()),
+                                            torch.zeros(64, dtype=torch.uint8, device=dev()),
+                                            torch.zeros(1, device=dev()), 8, 24))
