@@ -89,6 +89,11 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=1.5, help="wall time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    ap.add_argument("--all", action="store_true",
+                    help="after the main line, print one JSON line per other workload (small-M, LM head, "
+                         "prefill, the 28-layer Qwen3-0.6B-shaped decode sequence, the 1024x1024 GEMV)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run 10 device-to-device copies of MIB MiB (calibrates the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only (the decode path is single-GPU); "
@@ -102,6 +107,15 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "copies": 10}))
+        return
     wl = workload("dense27b_layer")
 
     def gpu_bf16(bits):
@@ -231,6 +245,128 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)
+    if args.all:
+        other_workloads(fp4, copies, x_in, x_mid, timed, graph_of_fn(stream), gpu_bf16, dev)
+
+
+def graph_of_fn(stream):
+    import torch
+
+    def graph_of(fn, n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            fn(0)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(n):
+                    fn(i)
+        torch.cuda.synchronize()
+        return g
+    return graph_of
+
+
+def other_workloads(fp4, copies, x_in0, x_mid0, timed, graph_of, gpu_bf16, dev):
+    """One JSON line per remaining workload, each timed from a HIP graph over
+    rotating weight copies of >= 512 MB where the weights are that large."""
+    import torch
+    from workloads import tensor_bits, x_bits, workload
+
+    def line(d):
+        print(json.dumps(d), flush=True)
+
+    ncp = len(copies)
+    # ---- small-M batched decode on the 27B-class layer
+    sm = workload("dense27b_smallm")
+    for M in (2, 4, 8, 16):
+        xi = gpu_bf16(x_bits(sm.x("x_in_m%d" % M)))
+        xm = gpu_bf16(x_bits(sm.x("x_mid_m%d" % M)))
+        gu = torch.empty((M, 2 * INTER), dtype=torch.float32, device=dev)
+        yd = torch.empty((M, HIDDEN), dtype=torch.float32, device=dev)
+
+        def step(i, xi=xi, xm=xm, gu=gu, yd=yd):
+            w = copies[i % ncp]
+            fp4.gemv_multi(xi, [w["gate"], w["up"]], [gu, gu[:, INTER:]], [2 * INTER, 2 * INTER])
+            fp4.gemv(xm, w["down"], out=yd)
+        g = graph_of(step, ncp)
+        g.replay()
+        t = timed(g.replay, 20) / (20 * ncp)
+        B = weight_bytes(2 * INTER, HIDDEN) + weight_bytes(HIDDEN, INTER)
+        flops = 2.0 * M * (2 * INTER * HIDDEN + HIDDEN * INTER)
+        line({"workload": "27B-class dense decode layer, small-M batch", "M": M, "us_per_layer": round(t * 1e6, 3),
+              "weight_GBps": round(B / t / 1e9, 1), "pct_of_hbm_peak": round(100 * B / t / 1e9 / HBM_PEAK_GBPS, 2),
+              "TFLOPs": round(flops / t / 1e12, 2)})
+    # ---- LM head 151936 x 1024, M = 1 and 8
+    lm = workload("lm_head")
+    base = fp4.quantize(gpu_bf16(tensor_bits(lm.tensor("w"))), "tiled")
+    lcp = [base] + [fp4.NVFP4Weight(base.packed.clone(), base.scales.clone(), base.gscale.clone(), base.N, base.K)
+                    for _ in range(6)]
+    for M in (1, 8):
+        x = gpu_bf16(x_bits(lm.x("x_m%d" % M)))
+        y = torch.empty((M, 151936), dtype=torch.float32, device=dev)
+        g = graph_of(lambda i, x=x, y=y: fp4.gemv(x, lcp[i % len(lcp)], out=y), len(lcp) * 8)
+        g.replay()
+        t = timed(g.replay, 5) / (5 * len(lcp) * 8)
+        B = weight_bytes(151936, 1024)
+        line({"workload": "LM head 151936x1024", "M": M, "us": round(t * 1e6, 3), "weight_GBps": round(B / t / 1e9, 1),
+              "pct_of_hbm_peak": round(100 * B / t / 1e9 / HBM_PEAK_GBPS, 2)})
+    del lcp, base
+    # ---- prefill: 2048 tokens x gate_up 5120 -> 34816 (gate and up launches)
+    xp = gpu_bf16(x_bits(workload("prefill").x("x")))
+    yp = torch.empty((2048, INTER), dtype=torch.float32, device=dev)
+
+    def pf(i):
+        w = copies[i % ncp]
+        fp4.gemm_prefill(xp, w["gate"], out=yp)
+        fp4.gemm_prefill(xp, w["up"], out=yp)
+    g = graph_of(pf, 4)
+    g.replay()
+    t = timed(g.replay, 5) / (5 * 4)
+    flops = 2.0 * 2048 * 2 * INTER * HIDDEN
+    line({"workload": "prefill GEMM, M=2048 tokens x gate_up 5120->34816 (bf16 MFMA)", "us": round(t * 1e6, 2),
+          "TFLOPs": round(flops / t / 1e12, 1), "mfma_bf16_peak_TFLOPs": 2500.0,
+          "frac_of_mfma_peak": round(flops / t / 1e12 / 2500.0, 4)})
+    del yp, xp
+    # ---- Qwen3-0.6B-shaped decode: 28 layers x (QKV fused, O, gate_up fused, down), M = 1
+    wl = workload("qwen3_0p6b_decode")
+    layers = []
+    for l in range(1, 29):
+        ws = {t: fp4.quantize(gpu_bf16(tensor_bits(wl.tensor("L%d.%s" % (l, t)))), "tiled")
+              for t in ("q", "k", "v", "o", "gate", "up", "down")}
+        xs = {k: gpu_bf16(x_bits(wl.x("L%d.x%d" % (l, k)))) for k in (1024, 2048, 3072)}
+        layers.append((ws, xs))
+    sets = [layers] + [[({t: fp4.NVFP4Weight(w.packed.clone(), w.scales.clone(), w.gscale.clone(), w.N, w.K)
+                          for t, w in ws.items()}, xs) for ws, xs in layers] for _ in range(2)]
+    qkv = torch.empty((1, 4096), dtype=torch.float32, device=dev)
+    o = torch.empty((1, 1024), dtype=torch.float32, device=dev)
+    gu = torch.empty((1, 6144), dtype=torch.float32, device=dev)
+    d = torch.empty((1, 1024), dtype=torch.float32, device=dev)
+
+    def token(i):
+        for ws, xs in sets[i % len(sets)]:
+            fp4.gemv_multi(xs[1024], [ws["q"], ws["k"], ws["v"]], [qkv, qkv[:, 2048:], qkv[:, 3072:]], [4096] * 3)
+            fp4.gemv(xs[2048], ws["o"], out=o)
+            fp4.gemv_multi(xs[1024], [ws["gate"], ws["up"]], [gu, gu[:, 3072:]], [6144] * 2)
+            fp4.gemv(xs[3072], ws["down"], out=d)
+    g = graph_of(token, len(sets))
+    g.replay()
+    t = timed(g.replay, 10) / (10 * len(sets) * 28)
+    B = 8847360
+    line({"workload": "Qwen3-0.6B-shaped decode, 28 layers x (QKV fused, O, gate_up fused, down), M=1, one HIP graph",
+          "us_per_decode_layer": round(t * 1e6, 3), "weight_GBps": round(B / t / 1e9, 1),
+          "pct_of_hbm_peak": round(100 * B / t / 1e9 / HBM_PEAK_GBPS, 2), "launches_per_layer": 4})
+    del sets, layers
+    # ---- single 1024 x 1024 GEMV (latency)
+    w0 = workload("gemv_1024")
+    base = fp4.quantize(gpu_bf16(tensor_bits(w0.tensor("w"))), "tiled")
+    cps = [base] + [fp4.NVFP4Weight(base.packed.clone(), base.scales.clone(), base.gscale.clone(), base.N, base.K)
+                    for _ in range(899)]
+    x = gpu_bf16(x_bits(w0.x("x")))
+    y = torch.empty((1, 1024), dtype=torch.float32, device=dev)
+    g = graph_of(lambda i: fp4.gemv(x, cps[i % len(cps)], out=y), len(cps))
+    g.replay()
+    t = timed(g.replay, 3) / (3 * len(cps))
+    line({"workload": "single NVFP4 GEMV 1024x1024, M=1 (900 rotating copies)", "us": round(t * 1e6, 3),
+          "weight_GBps": round(589824 / t / 1e9, 1)})
 
 
 if __name__ == "__main__":

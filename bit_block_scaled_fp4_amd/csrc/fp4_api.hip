@@ -105,7 +105,11 @@ int fp4_gemv_multi(const fp4_proj* projs, int nproj, const void* x_bf16, int64_t
     groups += fp4::groups_of(p.N);
   }
   if (groups > (int64_t(1) << 30)) return FP4_ERR_SHAPE;
-  return hip_status(fp4::launch_gemv(a, static_cast<hipStream_t>(stream)));
+  // Up to four activation rows: the vector-ALU kernel (decode once, two
+  // products per weight and row). From five rows on the weights are decoded
+  // once to bf16 and multiplied on the matrix cores.
+  if (M <= 4) return hip_status(fp4::launch_gemv(a, static_cast<hipStream_t>(stream)));
+  return hip_status(fp4::launch_gemv_mfma(a, static_cast<hipStream_t>(stream)));
 }
 
 int fp4_gemv(float* y, const void* x_bf16, const void* packed, const void* scales, const float* gscale, int64_t M,

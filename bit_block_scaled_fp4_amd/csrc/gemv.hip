@@ -128,13 +128,15 @@ __device__ __forceinline__ uint4 ld16_nt(const uint8_t* p) {
 template <int MT, int R>
 __device__ __forceinline__ void load_frag(Frag<MT, R>& f, const uint8_t* ptile, const uint8_t* stile,
                                           const uint16_t* x, int c, int hl, int m0, int M, int K) {
+  // Scales use ordinary (cached) loads: with 4-row units the two halves of a
+  // lane's 16 scale bytes belong to neighbouring workgroups, and the second
+  // one should find the line in L2 rather than fetch it again.
   if constexpr (R == 8) {
-    const uint4 sv = ld16_nt(stile);
+    const uint4 sv = *reinterpret_cast<const uint4*>(stile);
     f.s[0] = sv.x; f.s[1] = sv.y; f.s[2] = sv.z; f.s[3] = sv.w;
   } else {
-    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-    const u32x2_t sv = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(stile));
-    f.s[0] = sv[0]; f.s[1] = sv[1];
+    const uint2 sv = *reinterpret_cast<const uint2*>(stile);
+    f.s[0] = sv.x; f.s[1] = sv.y;
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) f.w[r] = ld16_nt(ptile + r * 512);
