@@ -86,13 +86,19 @@ def layout_bytes(N: int, K: int, layout="tiled"):
 
 @dataclass
 class NVFP4Weight:
-    """Quantised weight: packed codes, E4M3 block scales and the fp32 tensor scale (device)."""
+    """Quantised weight on the device: packed codes, E4M3 block scales and the
+    fp32 tensor scale. In the tiled layout `packed` holds codes and scales
+    together and `scales` is None."""
     packed: torch.Tensor
-    scales: torch.Tensor
+    scales: Optional[torch.Tensor]
     gscale: torch.Tensor
     N: int
     K: int
     layout: int = TILED
+
+
+def _opt(t: Optional[torch.Tensor], name: str) -> Optional[int]:
+    return None if t is None else _dev(t, name, torch.uint8)
 
 
 def quantize(W: torch.Tensor, layout="tiled", out: Optional[NVFP4Weight] = None) -> NVFP4Weight:
@@ -102,10 +108,10 @@ def quantize(W: torch.Tensor, layout="tiled", out: Optional[NVFP4Weight] = None)
     if out is None:
         pb, sb = layout_bytes(N, K, lay)
         out = NVFP4Weight(torch.empty(pb, dtype=torch.uint8, device=W.device),
-                          torch.empty(sb, dtype=torch.uint8, device=W.device),
+                          torch.empty(sb, dtype=torch.uint8, device=W.device) if lay == ROWMAJOR else None,
                           torch.empty(1, dtype=torch.float32, device=W.device), N, K, lay)
     _check(_lib.fp4_quantize(_dev(W, "W", torch.bfloat16), N, K, lay, _dev(out.packed, "packed", torch.uint8),
-                             _dev(out.scales, "scales", torch.uint8), _dev(out.gscale, "gscale", torch.float32),
+                             _opt(out.scales, "scales"), _dev(out.gscale, "gscale", torch.float32),
                              _stream(W.device)), "fp4_quantize")
     return out
 
@@ -115,13 +121,17 @@ def retile(w: NVFP4Weight, out: Optional[NVFP4Weight] = None) -> NVFP4Weight:
     if w.layout != ROWMAJOR:
         raise ValueError("retile expects a row-major weight")
     if out is None:
-        pb, sb = layout_bytes(w.N, w.K, TILED)
-        out = NVFP4Weight(torch.empty(pb, dtype=torch.uint8, device=w.packed.device),
-                          torch.empty(sb, dtype=torch.uint8, device=w.packed.device), w.gscale, w.N, w.K, TILED)
+        pb, _ = layout_bytes(w.N, w.K, TILED)
+        out = NVFP4Weight(torch.empty(pb, dtype=torch.uint8, device=w.packed.device), None, w.gscale, w.N, w.K, TILED)
     _check(_lib.fp4_retile(_dev(w.packed, "packed", torch.uint8), _dev(w.scales, "scales", torch.uint8), w.N, w.K,
-                           _dev(out.packed, "packed_tiled", torch.uint8), _dev(out.scales, "scales_tiled", torch.uint8),
-                           _stream(w.packed.device)), "fp4_retile")
+                           _dev(out.packed, "packed_tiled", torch.uint8), None, _stream(w.packed.device)),
+           "fp4_retile")
     return out
+
+
+def _tiled(w: NVFP4Weight) -> None:
+    if w.layout != TILED:
+        raise ValueError("the products take tiled weights (quantize(..., 'tiled') or retile())")
 
 
 def _x2d(x: torch.Tensor):
@@ -137,9 +147,9 @@ def gemv(x: torch.Tensor, w: NVFP4Weight, out: Optional[torch.Tensor] = None) ->
         raise ValueError("x has K=%d, weight has K=%d" % (K, w.K))
     if out is None:
         out = torch.empty((M, w.N), dtype=torch.float32, device=x.device)
+    _tiled(w)
     _check(_lib.fp4_gemv(_dev(out, "y", torch.float32), _dev(x, "x", torch.bfloat16), _dev(w.packed, "packed"),
-                         _dev(w.scales, "scales"), _dev(w.gscale, "gscale", torch.float32), M, w.N, K,
-                         _stream(x.device)), "fp4_gemv")
+                         None, _dev(w.gscale, "gscale", torch.float32), M, w.N, K, _stream(x.device)), "fp4_gemv")
     return out
 
 
@@ -160,8 +170,8 @@ def gemv_multi(x: torch.Tensor, weights: Sequence[NVFP4Weight], outs: Sequence[t
         avail = y.untyped_storage().nbytes() // 4 - y.storage_offset()   # fp32 elements from y's data_ptr on
         if avail < (M - 1) * ldy + w.N:
             raise ValueError("outs[%d] is too small for M=%d rows of stride %d" % (i, M, ldy))
-        arr[i] = _Proj(_dev(w.packed, "packed"), _dev(w.scales, "scales"), _dev(w.gscale, "gscale", torch.float32),
-                       w.N, y.data_ptr(), ldy)
+        _tiled(w)
+        arr[i] = _Proj(_dev(w.packed, "packed"), None, _dev(w.gscale, "gscale", torch.float32), w.N, y.data_ptr(), ldy)
     _check(_lib.fp4_gemv_multi(arr, n, _dev(x, "x", torch.bfloat16), M, K, _stream(x.device)), "fp4_gemv_multi")
 
 
@@ -172,10 +182,10 @@ def gemm_prefill(x: torch.Tensor, w: NVFP4Weight, out: Optional[torch.Tensor] = 
         raise ValueError("x has K=%d, weight has K=%d" % (K, w.K))
     if out is None:
         out = torch.empty((M, w.N), dtype=torch.float32, device=x.device)
+    _tiled(w)
     _check(_lib.fp4_gemm_prefill(_dev(out, "y", torch.float32), _dev(x, "x", torch.bfloat16),
-                                 _dev(w.packed, "packed"), _dev(w.scales, "scales"),
-                                 _dev(w.gscale, "gscale", torch.float32), M, w.N, K, _stream(x.device)),
-           "fp4_gemm_prefill")
+                                 _dev(w.packed, "packed"), None, _dev(w.gscale, "gscale", torch.float32), M, w.N, K,
+                                 _stream(x.device)), "fp4_gemm_prefill")
     return out
 
 

@@ -47,8 +47,8 @@ int fp4_layout_bytes(int64_t N, int64_t K, int layout, size_t* packed_bytes, siz
     *scale_bytes = (size_t)(N * K / 16);
   } else if (layout == FP4_LAYOUT_TILED) {
     const int64_t tiles = fp4::groups_of(N) * fp4::chunks_of(K);
-    *packed_bytes = (size_t)(tiles * fp4::kTilePacked);
-    *scale_bytes = (size_t)(tiles * fp4::kTileScale);
+    *packed_bytes = (size_t)(tiles * fp4::kTileBytes);   // codes and scales share each tile
+    *scale_bytes = 0;
   } else {
     return FP4_ERR_LAYOUT;
   }
@@ -57,11 +57,10 @@ int fp4_layout_bytes(int64_t N, int64_t K, int layout, size_t* packed_bytes, siz
 
 int fp4_quantize(const void* W_bf16, int64_t N, int64_t K, int layout, void* packed, void* scales,
                  float* gscale, void* stream) {
-  if (!W_bf16 || !packed || !scales || !gscale) return FP4_ERR_NULL;
-  if (int st = check_nk(N, K)) return st;
   if (layout != FP4_LAYOUT_ROWMAJOR && layout != FP4_LAYOUT_TILED) return FP4_ERR_LAYOUT;
-  if (!aligned(W_bf16, 16) || !aligned(packed, layout == FP4_LAYOUT_TILED ? 16 : 8) || !aligned(gscale, 4) ||
-      (layout == FP4_LAYOUT_TILED && !aligned(scales, 16)))
+  if (!W_bf16 || !packed || !gscale || (layout == FP4_LAYOUT_ROWMAJOR && !scales)) return FP4_ERR_NULL;
+  if (int st = check_nk(N, K)) return st;
+  if (!aligned(W_bf16, 16) || !aligned(packed, layout == FP4_LAYOUT_TILED ? 16 : 8) || !aligned(gscale, 4))
     return FP4_ERR_ALIGN;
   return hip_status(fp4::launch_quantize(static_cast<const uint16_t*>(W_bf16), N, K, layout == FP4_LAYOUT_TILED,
                                          static_cast<uint8_t*>(packed), static_cast<uint8_t*>(scales), gscale,
@@ -70,12 +69,12 @@ int fp4_quantize(const void* W_bf16, int64_t N, int64_t K, int layout, void* pac
 
 int fp4_retile(const void* packed_rm, const void* scales_rm, int64_t N, int64_t K, void* packed_tiled,
                void* scales_tiled, void* stream) {
-  if (!packed_rm || !scales_rm || !packed_tiled || !scales_tiled) return FP4_ERR_NULL;
+  (void)scales_tiled;   // the tiled layout keeps the scales inside `packed_tiled`
+  if (!packed_rm || !scales_rm || !packed_tiled) return FP4_ERR_NULL;
   if (int st = check_nk(N, K)) return st;
-  if (!aligned(packed_rm, 8) || !aligned(packed_tiled, 16) || !aligned(scales_tiled, 16)) return FP4_ERR_ALIGN;
+  if (!aligned(packed_rm, 8) || !aligned(packed_tiled, 16)) return FP4_ERR_ALIGN;
   return hip_status(fp4::launch_retile(static_cast<const uint8_t*>(packed_rm), static_cast<const uint8_t*>(scales_rm),
-                                       N, K, static_cast<uint8_t*>(packed_tiled), static_cast<uint8_t*>(scales_tiled),
-                                       static_cast<hipStream_t>(stream)));
+                                       N, K, static_cast<uint8_t*>(packed_tiled), static_cast<hipStream_t>(stream)));
 }
 
 int fp4_gemv_multi(const fp4_proj* projs, int nproj, const void* x_bf16, int64_t M, int64_t K, void* stream) {
@@ -91,13 +90,11 @@ int fp4_gemv_multi(const fp4_proj* projs, int nproj, const void* x_bf16, int64_t
   int64_t groups = 0;
   for (int i = 0; i < nproj; ++i) {
     const fp4_proj& p = projs[i];
-    if (!p.packed || !p.scales || !p.gscale || !p.y) return FP4_ERR_NULL;
+    if (!p.packed || !p.gscale || !p.y) return FP4_ERR_NULL;
     if (int st = check_nk(p.N, K)) return st;
     if (p.ldy < p.N || M * p.ldy > kMaxElems) return FP4_ERR_SHAPE;
-    if (!aligned(p.packed, 16) || !aligned(p.scales, 16) || !aligned(p.y, 4) || !aligned(p.gscale, 4))
-      return FP4_ERR_ALIGN;
-    a.proj[i].packed = static_cast<const uint8_t*>(p.packed);
-    a.proj[i].scales = static_cast<const uint8_t*>(p.scales);
+    if (!aligned(p.packed, 16) || !aligned(p.y, 4) || !aligned(p.gscale, 4)) return FP4_ERR_ALIGN;
+    a.proj[i].tiles = static_cast<const uint8_t*>(p.packed);
     a.proj[i].gscale = p.gscale;
     a.proj[i].y = p.y;
     a.proj[i].ldy = p.ldy;
@@ -114,21 +111,20 @@ int fp4_gemv_multi(const fp4_proj* projs, int nproj, const void* x_bf16, int64_t
 
 int fp4_gemv(float* y, const void* x_bf16, const void* packed, const void* scales, const float* gscale, int64_t M,
              int64_t N, int64_t K, void* stream) {
-  if (!y || !x_bf16 || !packed || !scales || !gscale) return FP4_ERR_NULL;
-  fp4_proj p{packed, scales, gscale, N, y, N};
+  if (!y || !x_bf16 || !packed || !gscale) return FP4_ERR_NULL;
+  fp4_proj p{packed, scales, gscale, N, y, N};   // scales: unused with the tiled layout
   return fp4_gemv_multi(&p, 1, x_bf16, M, K, stream);
 }
 
 int fp4_gemm_prefill(float* y, const void* x_bf16, const void* packed, const void* scales, const float* gscale,
                      int64_t M, int64_t N, int64_t K, void* stream) {
-  if (!y || !x_bf16 || !packed || !scales || !gscale) return FP4_ERR_NULL;
+  (void)scales;   // the tiled layout keeps the scales inside `packed`
+  if (!y || !x_bf16 || !packed || !gscale) return FP4_ERR_NULL;
   if (int st = check_nk(N, K)) return st;
   if (M < 1 || M > kMaxM || M * N > kMaxElems) return FP4_ERR_SHAPE;
-  if (!aligned(x_bf16, 16) || !aligned(packed, 16) || !aligned(scales, 16) || !aligned(y, 4) || !aligned(gscale, 4))
-    return FP4_ERR_ALIGN;
+  if (!aligned(x_bf16, 16) || !aligned(packed, 16) || !aligned(y, 4) || !aligned(gscale, 4)) return FP4_ERR_ALIGN;
   return hip_status(fp4::launch_prefill(y, static_cast<const uint16_t*>(x_bf16), static_cast<const uint8_t*>(packed),
-                                        static_cast<const uint8_t*>(scales), gscale, M, N, K,
-                                        static_cast<hipStream_t>(stream)));
+                                        gscale, M, N, K, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -79,14 +79,15 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv_mfma(const GemvArgs a) 
   const int q = lane >> 4, n16 = lane & 15;
 
   int p = 0;
-  while (p + 1 < a.nproj && (int)blockIdx.x >= a.proj[p + 1].tile_begin) ++p;
+  while (p + 1 < a.nproj && (int)blockIdx.x >= a.proj[p + 1].wg_begin) ++p;
   const int N = a.proj[p].N;
   const int G = (N + 7) >> 3;
   const int C = a.C, K = a.K, M = a.M;
-  const int row0 = ((int)blockIdx.x - a.proj[p].tile_begin) * 16 * NT;
+  const int row0 = ((int)blockIdx.x - a.proj[p].wg_begin) * 16 * NT;
   const float gs = *a.proj[p].gscale;
 
-  // this lane's weight row in each N-subtile
+  // this lane's weight row in each N-subtile: codes at prow + c*kTileBytes +
+  // 16*piece, the piece's two block scales at srow + c*kTileBytes + 8*piece
   const uint8_t* prow[NT];
   const uint8_t* srow[NT];
   bool rvalid[NT];
@@ -96,8 +97,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv_mfma(const GemvArgs a) 
     const int g = n >> 3;
     rvalid[s] = g < G;
     const int gg = rvalid[s] ? g : 0;
-    prow[s] = a.proj[p].packed + (int64_t)gg * C * kTilePacked + (n & 7) * 512;
-    srow[s] = a.proj[p].scales + (int64_t)gg * C * kTileScale + (n & 7) * 2;
+    const uint8_t* tile0 = a.proj[p].tiles + (int64_t)gg * C * kTileBytes;
+    prow[s] = tile0 + (n & 7) * 512;
+    srow[s] = tile0 + tile_scale_offset(n & 7, 0);
   }
 
   for (int m0 = 0; m0 < M; m0 += 16 * MTL) {
@@ -121,8 +123,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv_mfma(const GemvArgs a) 
           const int piece = 4 * (4 * hb + tt) + q;
 #pragma unroll
           for (int s = 0; s < NT; ++s) {
-            wv[s][tt] = *reinterpret_cast<const uint4*>(prow[s] + (int64_t)c * kTilePacked + piece * 16);
-            sv[s][tt] = *reinterpret_cast<const uint16_t*>(srow[s] + (int64_t)c * kTileScale + piece * 16);
+            wv[s][tt] = *reinterpret_cast<const uint4*>(prow[s] + (int64_t)c * kTileBytes + piece * 16);
+            sv[s][tt] = *reinterpret_cast<const uint16_t*>(srow[s] + (int64_t)c * kTileBytes + piece * 8);
           }
           const int k0 = c * kChunkK + 32 * piece;
           const int kv = K - k0;                     // <= 0, 16 or >= 32 (K % 16 == 0)
@@ -212,10 +214,9 @@ template <int NT, int MTL>
 hipError_t launch_nt(GemvArgs a, hipStream_t st, int split) {
   int64_t wgs = 0;
   for (int i = 0; i < a.nproj; ++i) {
-    a.proj[i].tile_begin = (int32_t)wgs;
+    a.proj[i].wg_begin = (int32_t)wgs;
     wgs += (a.proj[i].N + 16 * NT - 1) / (16 * NT);
   }
-  a.total_tiles = (int32_t)wgs;
   int S = split;
   if (S <= 0) {
     // enough waves to fill the machine, never more waves than chunks

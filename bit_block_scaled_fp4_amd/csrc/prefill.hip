@@ -44,8 +44,7 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 }
 
 __global__ __launch_bounds__(256) void k_prefill(float* __restrict__ y, const uint16_t* __restrict__ x,
-                                                 const uint8_t* __restrict__ packed,
-                                                 const uint8_t* __restrict__ scales,
+                                                 const uint8_t* __restrict__ tiles,
                                                  const float* __restrict__ gscale, int M, int N, int K) {
   __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDA];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDA];
@@ -80,9 +79,9 @@ __global__ __launch_bounds__(256) void k_prefill(float* __restrict__ y, const ui
       const int c = k0 / kChunkK, l = (k0 % kChunkK) / 32 + piece;
       uint32_t out[16];
       if (g < G && k0 + piece * 32 < K) {
-        const int64_t tile = (int64_t)g * C + c;
-        const uint4 w = *reinterpret_cast<const uint4*>(packed + tile * kTilePacked + r * 512 + l * 16);
-        const uint32_t sc = *reinterpret_cast<const uint16_t*>(scales + tile * kTileScale + l * 16 + r * 2);
+        const uint8_t* tile = tiles + ((int64_t)g * C + c) * kTileBytes;
+        const uint4 w = *reinterpret_cast<const uint4*>(tile + r * 512 + l * 16);
+        const uint32_t sc = *reinterpret_cast<const uint16_t*>(tile + tile_scale_offset(r, 2 * l));
         const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)sc, 0);
         const float s1 = __builtin_amdgcn_cvt_f32_fp8((int)sc, 1);
 #pragma unroll
@@ -135,11 +134,11 @@ __global__ __launch_bounds__(256) void k_prefill(float* __restrict__ y, const ui
 
 }  // namespace
 
-hipError_t launch_prefill(float* y, const uint16_t* x, const uint8_t* packed, const uint8_t* scales,
-                          const float* gscale, int64_t M, int64_t N, int64_t K, hipStream_t s) {
+hipError_t launch_prefill(float* y, const uint16_t* x, const uint8_t* tiles, const float* gscale, int64_t M,
+                          int64_t N, int64_t K, hipStream_t s) {
   const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
   if (grid.y > 65535u) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_prefill, grid, dim3(256), 0, s, y, x, packed, scales, gscale, (int)M, (int)N, (int)K);
+  hipLaunchKernelGGL(k_prefill, grid, dim3(256), 0, s, y, x, tiles, gscale, (int)M, (int)N, (int)K);
   return hipGetLastError();
 }
 

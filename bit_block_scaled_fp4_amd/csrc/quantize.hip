@@ -122,11 +122,12 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ W, 
     *reinterpret_cast<uint2*>(packed + n * (K / 2) + b * 8) = make_uint2(lo, hi);
     scales[n * kb + b] = (uint8_t)sc;
   } else {
+    // tiled: codes and scale go into the one tile buffer (`packed`)
     const int64_t g = n / kGroupRows, r = n % kGroupRows;
     const int64_t c = b / 64, l = (b % 64) / 2, j = b % 2;
-    const int64_t tile = g * C + c;
-    *reinterpret_cast<uint2*>(packed + tile * kTilePacked + r * 512 + l * 16 + j * 8) = make_uint2(lo, hi);
-    scales[tile * kTileScale + l * 16 + r * 2 + j] = (uint8_t)sc;
+    uint8_t* tile = packed + (g * C + c) * kTileBytes;
+    *reinterpret_cast<uint2*>(tile + r * 512 + l * 16 + j * 8) = make_uint2(lo, hi);
+    tile[tile_scale_offset((int)r, (int)(b % 64))] = (uint8_t)sc;
   }
 }
 
@@ -135,16 +136,17 @@ __global__ void k_finalize(uint32_t* slot) {
   *reinterpret_cast<float*>(slot) = amax / 2688.0f;   // 0 stays 0
 }
 
-// One thread per 16-byte lane piece of a packed tile; threads of the first
-// G*C*32 also build the lane's 16 scale bytes.
+// One thread per 16-byte lane piece of a tile's codes (rows r, pieces l);
+// the threads with r < 2 also write that row parity's 8 scale bytes of
+// piece l (rows r, r + 2, r + 4, r + 6).
 __global__ __launch_bounds__(256) void k_retile(const uint8_t* __restrict__ packed,
                                                 const uint8_t* __restrict__ scales, int64_t N,
-                                                int64_t K, uint8_t* __restrict__ packed_t,
-                                                uint8_t* __restrict__ scales_t) {
+                                                int64_t K, uint8_t* __restrict__ tiles) {
   const int64_t G = groups_of(N), C = chunks_of(K);
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= G * C * 256) return;
-  const int64_t tile = t / 256, rl = t % 256, r = rl / 32, l = rl % 32;
+  const int64_t tile = t / 256, rl = t % 256;
+  const int r = (int)(rl / 32), l = (int)(rl % 32);
   const int64_t g = tile / C, c = tile % C;
   const int64_t row = g * kGroupRows + r;
   const int64_t rb = K / 2;                 // canonical bytes per row
@@ -155,22 +157,23 @@ __global__ __launch_bounds__(256) void k_retile(const uint8_t* __restrict__ pack
     if (kbyte + 8 <= rb) a = *reinterpret_cast<const uint2*>(src);
     if (kbyte + 16 <= rb) b = *reinterpret_cast<const uint2*>(src + 8);
   }
-  *reinterpret_cast<uint4*>(packed_t + tile * kTilePacked + r * 512 + l * 16) = make_uint4(a.x, a.y, b.x, b.y);
-  if (rl < 32) {
+  uint8_t* dst = tiles + tile * kTileBytes;
+  *reinterpret_cast<uint4*>(dst + r * 512 + l * 16) = make_uint4(a.x, a.y, b.x, b.y);
+  if (r < 2) {
     const int64_t kb = K / 16;
-    uint32_t w[4] = {0, 0, 0, 0};
+    uint32_t w[2] = {0, 0};
 #pragma unroll
-    for (int rr = 0; rr < 8; ++rr) {
-      const int64_t row2 = g * kGroupRows + rr;
+    for (int i = 0; i < 4; ++i) {
+      const int64_t row2 = g * kGroupRows + 2 * i + r;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int64_t blk = c * 64 + rl * 2 + j;
+        const int64_t blk = c * 64 + l * 2 + j;
         const uint32_t v = (row2 < N && blk < kb) ? scales[row2 * kb + blk] : 0u;
-        const int pos = rr * 2 + j;
+        const int pos = i * 2 + j;
         w[pos / 4] |= v << (8 * (pos % 4));
       }
     }
-    *reinterpret_cast<uint4*>(scales_t + tile * kTileScale + rl * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint2*>(dst + tile_scale_offset(r, 2 * l)) = make_uint2(w[0], w[1]);
   }
 }
 
@@ -193,11 +196,10 @@ hipError_t launch_quantize(const uint16_t* W, int64_t N, int64_t K, bool tiled, 
   return hipGetLastError();
 }
 
-hipError_t launch_retile(const uint8_t* packed, const uint8_t* scales, int64_t N, int64_t K,
-                         uint8_t* packed_t, uint8_t* scales_t, hipStream_t s) {
+hipError_t launch_retile(const uint8_t* packed, const uint8_t* scales, int64_t N, int64_t K, uint8_t* tiles,
+                         hipStream_t s) {
   const int64_t n = groups_of(N) * chunks_of(K) * 256;
-  hipLaunchKernelGGL(k_retile, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, packed, scales, N, K,
-                     packed_t, scales_t);
+  hipLaunchKernelGGL(k_retile, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, packed, scales, N, K, tiles);
   return hipGetLastError();
 }
 

@@ -29,16 +29,20 @@
  *   FP4_LAYOUT_ROWMAJOR (canonical): packed [N][K/2] bytes, scales [N][K/16]
  *     bytes, both row-major.
  *   FP4_LAYOUT_TILED (device layout read by fp4_gemv, fp4_gemv_multi and
- *     fp4_gemm_prefill): rows form groups of 8 (G = ceil(N/8)), K forms
- *     chunks of 1024 (C = ceil(K/1024)); tile (g, c) is stored at index
- *     g*C + c. In a packed tile (4096 B) byte r*512 + l*16 + i holds
- *     canonical byte (row 8g+r, byte 512c + 16l + i); in a scale tile (512 B)
- *     byte l*16 + r*2 + j holds the scale of (row 8g+r, block 64c + 2l + j),
- *     for r < 8, l < 32, i < 16, j < 2. Positions outside the tensor hold 0.
- *     One 32-lane group thus reads a row's 1024-element chunk as 32
- *     contiguous 16-byte pieces, two whole 16-element blocks per lane, and
- *     the 16 scales it needs for 8 rows as one 16-byte load.
- *
+ *     fp4_gemm_prefill): ONE buffer, `packed`, holding codes and scales.
+ *     Rows form groups of 8 (G = ceil(N/8)), K forms chunks of 1024
+ *     (C = ceil(K/1024)); tile (g, c) is the 4608 bytes at (g*C + c)*4608:
+ *       byte r*512 + l*16 + i          = canonical packed byte
+ *                                        (row 8g+r, byte 512c + 16l + i),
+ *       byte 4096 + h*256 + l*8 + 2i + j = scale of
+ *                                        (row 8g + 2i + h, block 64c + 2l + j),
+ *     for r < 8, l < 32, i < 16 (codes) or i < 4 (scales), h < 2, j < 2.
+ *     Positions outside the tensor hold 0. A 64-lane wave thus reads rows
+ *     2q and 2q+1 of a tile as one contiguous kilobyte (lane 32h + l gets
+ *     piece l, two whole 16-element blocks, of row 2q + h) and finds the 8
+ *     scale bytes it needs for its four rows at 4096 + 8*lane, so the block
+ *     scales travel in the same stream as the codes. The `scales` arguments
+ *     of the calls below are unused with this layout (pass NULL).
  * Conventions for every call:
  *   - Pointers marked "device" are HIP device memory (e.g. a torch CUDA
  *     tensor's data_ptr()) on the current HIP device; the caller owns every
@@ -51,9 +55,9 @@
  *     nothing is enqueued and the status says why. FP4_ERR_HIP means the
  *     launch itself failed. A fault inside a kernel surfaces at the
  *     caller's next synchronisation, as usual for HIP.
- *   - Alignment: x, W, packed and scales must be 16-byte aligned (canonical
- *     packed input of fp4_retile: 8-byte; fp4_quantize's canonical packed
- *     output: 8-byte); y and gscale 4-byte aligned.
+ *   - Alignment: x, W and tiled buffers must be 16-byte aligned (canonical
+ *     packed data: 8-byte; canonical scales: none); y and gscale 4-byte
+ *     aligned.
  *   - Size limits: 1 <= N <= 2^28, 16 <= K <= 2^24, 1 <= M <= 2^24.
  *   - Calls are thread-safe (no global mutable state).
  */
@@ -89,13 +93,14 @@ typedef enum { FP4_LAYOUT_ROWMAJOR = 0, FP4_LAYOUT_TILED = 1 } fp4_layout;
 FP4_API const char *fp4_status_string(int status);
 
 /* Bytes of the packed and scale arrays for an N x K weight in `layout`.
- * ROWMAJOR: N*K/2 and N*K/16. TILED: G*C*4096 and G*C*512 (see above).
- * Host-only; enqueues nothing. */
+ * ROWMAJOR: N*K/2 and N*K/16. TILED: G*C*4608 and 0 (the scales live in
+ * the tiles, see above). Host-only; enqueues nothing. */
 FP4_API int fp4_layout_bytes(int64_t N, int64_t K, int layout, size_t *packed_bytes, size_t *scale_bytes);
 
 /* Quantise a bf16 weight W [N][K] (device) to NVFP4 in `layout`, writing
- * packed and scales (device, sized by fp4_layout_bytes) and the tensor scale
- * *gscale (device fp32). The rule, one fp32 IEEE operation per step:
+ * packed and scales (device, sized by fp4_layout_bytes; TILED writes codes
+ * and scales into `packed` and ignores `scales`, which may be NULL) and the
+ * tensor scale *gscale (device fp32). The rule, one fp32 IEEE operation per step:
  *   gscale = amax|W| / 2688 (= 448*6; 0 for an all-zero W);
  *   per block s = (block_amax / 6) / gscale, scale code = E4M3 nearest-even
  *   of s, saturating at 448;
@@ -109,8 +114,9 @@ FP4_API int fp4_layout_bytes(int64_t N, int64_t K, int layout, size_t *packed_by
 FP4_API int fp4_quantize(const void *W_bf16, int64_t N, int64_t K, int layout, void *packed, void *scales,
                  float *gscale, void *stream);
 
-/* Re-tile canonical (ROWMAJOR) packed/scales into the TILED layout. A pure
- * byte permutation plus zero padding; inputs and outputs must not overlap.
+/* Re-tile canonical (ROWMAJOR) packed/scales into the TILED layout, written
+ * to `packed_tiled` (scales_tiled is unused and may be NULL). A pure byte
+ * permutation plus zero padding; inputs and outputs must not overlap.
  * (The README's load-time weight transformation, cached across starts.) */
 FP4_API int fp4_retile(const void *packed_rm, const void *scales_rm, int64_t N, int64_t K, void *packed_tiled,
                void *scales_tiled, void *stream);
@@ -121,12 +127,13 @@ FP4_API int fp4_retile(const void *packed_rm, const void *scales_rm, int64_t N, 
  * or tokens being verified by speculative decoding) share one pass over
  * the weights (page "1. The big picture", the batching and speculative
  * decoding bullets of "The most important number in this book").
- * Any M >= 1 is accepted. */
+ * Any M >= 1 is accepted. `packed` holds the tiles; `scales` is unused. */
 FP4_API int fp4_gemv(float *y, const void *x_bf16, const void *packed, const void *scales, const float *gscale,
              int64_t M, int64_t N, int64_t K, void *stream);
 
-/* One projection of a fused launch: TILED weights with N rows and their own
- * tensor scale, writing y[m*ldy + n] (fp32, device) for n < N. */
+/* One projection of a fused launch: TILED weights (`packed`; `scales`
+ * unused) with N rows and their own tensor scale, writing y[m*ldy + n]
+ * (fp32, device) for n < N. */
 typedef struct {
     const void *packed;
     const void *scales;
@@ -153,7 +160,8 @@ FP4_API int fp4_gemv_multi(const fp4_proj *projs, int nproj, const void *x_bf16,
  * epilogue. Prefill is compute-bound: thousands of prompt tokens go
  * through each layer at once (page "imp" README, the prefill paragraph;
  * page "1. The big picture", "Two phases with very different costs").
- * Any M >= 1 is accepted; y [M][N] fp32 overwritten. */
+ * Any M >= 1 is accepted; y [M][N] fp32 overwritten. `packed` holds the
+ * tiles; `scales` is unused. */
 FP4_API int fp4_gemm_prefill(float *y, const void *x_bf16, const void *packed, const void *scales,
                      const float *gscale, int64_t M, int64_t N, int64_t K, void *stream);
 

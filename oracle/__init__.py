@@ -54,7 +54,7 @@ def _L():
         lib.orc_dequant.restype = None
         lib.orc_gemv.argtypes = [P, I64, P, P, ctypes.c_float, I64, I64, P, P, ctypes.c_int]
         lib.orc_gemv.restype = None
-        lib.orc_tile.argtypes = [P, P, I64, I64, P, P]
+        lib.orc_tile.argtypes = [P, P, I64, I64, P]
         lib.orc_tile.restype = None
         lib.orc_e4m3_encode_n.argtypes = [P, I64, P]
         lib.orc_e4m3_encode_n.restype = None
@@ -137,16 +137,16 @@ def gemv(x_bits: np.ndarray, packed: np.ndarray, scales: np.ndarray, gscale, thr
     return (y, l1) if with_l1 else y
 
 
-def tile(packed: np.ndarray, scales: np.ndarray):
-    """Canonical -> the GPU library's tiled layout (flat uint8 arrays)."""
+def tile(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Canonical -> the GPU library's tiled layout (one flat uint8 array of
+    4608-byte tiles holding codes and scales)."""
     packed, pp = _c(packed, np.uint8)
     scales, ps = _c(scales, np.uint8)
     N, K = packed.shape[0], packed.shape[1] * 2
     G, C = (N + 7) // 8, (K + 1023) // 1024
-    pt = np.empty(G * C * 4096, dtype=np.uint8)
-    st = np.empty(G * C * 512, dtype=np.uint8)
-    _L().orc_tile(pp, ps, N, K, pt.ctypes.data, st.ctypes.data)
-    return pt, st
+    t = np.empty(G * C * 4608, dtype=np.uint8)
+    _L().orc_tile(pp, ps, N, K, t.ctypes.data)
+    return t
 
 
 def tolerance_ok(y_gpu: np.ndarray, y_ref: np.ndarray, l1: np.ndarray, rel: float = 2e-3):

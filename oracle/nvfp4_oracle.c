@@ -270,33 +270,33 @@ void orc_gemv(const uint16_t *x, int64_t M, const uint8_t *packed, const uint8_t
 /* The GPU library's tiled layout, written out as plain loops so that the
  * GPU re-tiling can be compared byte for byte. Rows form groups of 8
  * (G = ceil(N/8)); K forms chunks of 1024 (C = ceil(K/1024)); tile (g, c) is
- * stored at index g*C + c.
- *   packed tile, 4096 B: byte r*512 + l*16 + i  =  canonical packed byte
- *       (row 8g+r, byte (1024c + 32l)/2 + i)      r<8, l<32, i<16
- *   scale tile, 512 B:   byte l*16 + r*2 + j    =  canonical scale
- *       (row 8g+r, block 64c + 2l + j)            j<2
+ * the 4608 bytes at (g*C + c)*4608 of one buffer:
+ *   codes, bytes 0..4095:  byte r*512 + l*16 + i          =  canonical packed byte
+ *       (row 8g+r, byte (1024c + 32l)/2 + i)              r<8, l<32, i<16
+ *   scales, bytes 4096..:  byte 4096 + h*256 + l*8 + 2i + j  =  canonical scale
+ *       (row 8g + 2i + h, block 64c + 2l + j)             h<2, i<4, j<2
  * Positions outside the tensor (row >= N or k >= K) hold 0. */
-void orc_tile(const uint8_t *packed, const uint8_t *scales, int64_t N, int64_t K, uint8_t *packed_t,
-              uint8_t *scales_t) {
+void orc_tile(const uint8_t *packed, const uint8_t *scales, int64_t N, int64_t K, uint8_t *tiles) {
     int64_t G = (N + 7) / 8, C = (K + 1023) / 1024;
     for (int64_t g = 0; g < G; ++g)
         for (int64_t c = 0; c < C; ++c) {
-            uint8_t *pt = packed_t + (g * C + c) * 4096;
-            uint8_t *st = scales_t + (g * C + c) * 512;
+            uint8_t *t = tiles + (g * C + c) * 4608;
             for (int r = 0; r < 8; ++r)
                 for (int l = 0; l < 32; ++l) {
                     int64_t row = 8 * g + r;
                     for (int i = 0; i < 16; ++i) {
                         int64_t kb = (1024 * c + 32 * l) / 2 + i;      /* byte index in the row */
-                        pt[r * 512 + l * 16 + i] =
-                            (row < N && kb < K / 2) ? packed[row * (K / 2) + kb] : 0;
-                    }
-                    for (int j = 0; j < 2; ++j) {
-                        int64_t blk = 64 * c + 2 * l + j;
-                        st[l * 16 + r * 2 + j] =
-                            (row < N && blk < K / 16) ? scales[row * (K / 16) + blk] : 0;
+                        t[r * 512 + l * 16 + i] = (row < N && kb < K / 2) ? packed[row * (K / 2) + kb] : 0;
                     }
                 }
+            for (int h = 0; h < 2; ++h)
+                for (int l = 0; l < 32; ++l)
+                    for (int i = 0; i < 4; ++i)
+                        for (int j = 0; j < 2; ++j) {
+                            int64_t row = 8 * g + 2 * i + h, blk = 64 * c + 2 * l + j;
+                            t[4096 + h * 256 + l * 8 + 2 * i + j] =
+                                (row < N && blk < K / 16) ? scales[row * (K / 16) + blk] : 0;
+                        }
         }
 }
 

@@ -34,9 +34,10 @@ def test_status_strings():
 
 def test_layout_bytes():
     assert fp4.layout_bytes(1024, 1024, "rowmajor") == (1024 * 512, 1024 * 64)
-    assert fp4.layout_bytes(1024, 1024, "tiled") == (128 * 4096, 128 * 512)
-    assert fp4.layout_bytes(11, 1040, "tiled") == (2 * 2 * 4096, 2 * 2 * 512)
-    assert fp4.layout_bytes(151936, 1024, "tiled") == (151936 * 512, 151936 * 64)
+    # tiled: 4608-byte tiles of codes and scales together, no separate scale array
+    assert fp4.layout_bytes(1024, 1024, "tiled") == (128 * 4608, 0)
+    assert fp4.layout_bytes(11, 1040, "tiled") == (2 * 2 * 4608, 0)
+    assert fp4.layout_bytes(151936, 1024, "tiled") == (151936 * 576, 0)
     with pytest.raises(fp4.Fp4Error) as e:
         fp4.layout_bytes(8, 24)
     assert e.value.status == ESHAPE
@@ -71,15 +72,16 @@ def test_gemv_multi_argument_errors():
     assert L.fp4_gemv_multi(P, 9, A, 1, 32, None) == ESHAPE
     P[1] = fp4._Proj(A, A, A, 8, A, 4)                 # ldy < N
     assert L.fp4_gemv_multi(P, 2, A, 1, 32, None) == ESHAPE
-    P[1] = fp4._Proj(A, None, A, 8, A, 8)
+    P[1] = fp4._Proj(None, A, A, 8, A, 8)
     assert L.fp4_gemv_multi(P, 2, A, 1, 32, None) == ENULL
-    P[1] = fp4._Proj(A, A + 1, A, 8, A, 8)
+    P[1] = fp4._Proj(A + 1, A, A, 8, A, 8)
     assert L.fp4_gemv_multi(P, 2, A, 1, 32, None) == EALIGN
 
 
 def test_quantize_retile_prefill_argument_errors():
     L = fp4.raw()
     assert L.fp4_quantize(None, 8, 32, 1, A, A, A, None) == ENULL
+    assert L.fp4_quantize(A, 8, 32, 0, A, None, A, None) == ENULL    # row-major needs the scale array
     assert L.fp4_quantize(A, 8, 30, 1, A, A, A, None) == ESHAPE
     assert L.fp4_quantize(A, 8, 32, 3, A, A, A, None) == ELAYOUT
     assert L.fp4_quantize(A + 8, 8, 32, 1, A, A, A, None) == EALIGN

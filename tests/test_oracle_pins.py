@@ -272,18 +272,21 @@ def test_tile_matches_reshape_formulation():
     for N, K in [(16, 2048), (24, 1024), (8, 3072)]:
         p = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
         s = rng.integers(0, 256, (N, K // 16), dtype=np.uint8)
-        pt, st = oracle.tile(p, s)
+        t = oracle.tile(p, s).reshape(-1, 4608)
         G, C = N // 8, K // 1024
-        ref_p = p.reshape(G, 8, C, 32, 16).transpose(0, 2, 1, 3, 4).ravel()
-        ref_s = s.reshape(G, 8, C, 32, 2).transpose(0, 2, 3, 1, 4).ravel()
-        assert np.array_equal(pt, ref_p) and np.array_equal(st, ref_s)
+        # codes: [g][r][c][l][i] -> [g][c][r][l][i]; scales: row r = 2i + h,
+        # [g][i][h][c][l][j] -> [g][c][h][l][i][j]
+        ref_p = p.reshape(G, 8, C, 32, 16).transpose(0, 2, 1, 3, 4).reshape(G * C, 4096)
+        ref_s = s.reshape(G, 4, 2, C, 32, 2).transpose(0, 3, 2, 4, 1, 5).reshape(G * C, 512)
+        assert np.array_equal(t[:, :4096], ref_p) and np.array_equal(t[:, 4096:], ref_s)
 
 
 def test_tile_pads_ragged_shapes_with_zeros():
     N, K = 11, 1024 + 48
     p = np.arange(N * K // 2, dtype=np.int64).astype(np.uint8).reshape(N, K // 2) | 1
     s = np.full((N, K // 16), 0x33, np.uint8)
-    pt, st = oracle.tile(p, s)
-    assert pt.size == 2 * 2 * 4096 and st.size == 2 * 2 * 512
+    t = oracle.tile(p, s).reshape(-1, 4608)
+    assert t.shape == (2 * 2, 4608)
+    pt, st = t[:, :4096].ravel(), t[:, 4096:].ravel()
     assert np.count_nonzero(pt) == N * K // 2 and np.count_nonzero(st) == N * K // 16
     assert np.array_equal(np.sort(pt[pt != 0]), np.sort(p.ravel()))
