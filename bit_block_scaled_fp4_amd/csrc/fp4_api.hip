@@ -106,7 +106,7 @@ int fp4_gemv_multi(const fp4_proj* projs, int nproj, const void* x_bf16, int64_t
   // products per weight and row). From five rows on the weights are decoded
   // once to bf16 and multiplied on the matrix cores.
   if (M <= 4) return hip_status(fp4::launch_gemv(a, static_cast<hipStream_t>(stream)));
-  return hip_status(fp4::launch_gemv_mfma(a, static_cast<hipStream_t>(stream)));
+  return hip_status(fp4::launch_gemv_mma(a, static_cast<hipStream_t>(stream)));
 }
 
 int fp4_gemv(float* y, const void* x_bf16, const void* packed, const void* scales, const float* gscale, int64_t M,

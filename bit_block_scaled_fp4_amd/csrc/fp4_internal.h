@@ -58,10 +58,10 @@ hipError_t launch_retile(const uint8_t* packed, const uint8_t* scales, int64_t N
 // workgroup) and wc (waves per row group) override the automatic geometry
 // (tuning).
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t s, int gw = 0, int wc = 0);
-// Small-M product on bf16 MFMA (M padded to 16 per M-tile; 16 or 32 rows
-// per pass, more rows loop passes). nt: 16-row N-subtiles per wave (1 or 2);
-// split: waves per workgroup (0 = automatic).
-hipError_t launch_gemv_mfma(const GemvArgs& a, hipStream_t s, int nt = 2, int split = 0);
+// Small-M product on bf16 MFMA, split over K chunks (16 activation rows per
+// pass, more rows loop passes). With more than one chunk it uses a
+// per-device workspace that it allocates on first need and keeps.
+hipError_t launch_gemv_mma(const GemvArgs& a, hipStream_t s, int ppw = 0);   // ppw > 0: pairs per workgroup (tuning)
 hipError_t launch_prefill(float* y, const uint16_t* x, const uint8_t* tiles, const float* gscale, int64_t M,
                           int64_t N, int64_t K, hipStream_t s);
 

@@ -4,25 +4,31 @@
 // Several activation rows share one pass over the weights, so the weights
 // are still read once (page "1. The big picture", the batching and
 // speculative-decoding bullets of "The most important number in this
-// book"); the vector-ALU kernel would redo two products per weight for
-// every activation row, which makes it ALU-bound from about four rows on.
-// Here each weight is decoded once to bf16 (E2M1 * E4M3 has at most 6
-// significant bits: exact) and fed to v_mfma_f32_16x16x32_bf16 with the
-// activations (M padded to 16 per M-tile) as the A operand; the tensor
-// scale is applied once in the epilogue.
+// book"). On the vector ALUs every extra row costs another two-term dot
+// product per weight pair, which makes that path ALU-bound from about four
+// rows on; here each weight is decoded once to bf16 (E2M1 * E4M3 has at most
+// 6 significant bits: exact) and multiplied on v_mfma_f32_16x16x32_bf16,
+// with up to 16 activation rows per pass as the A operand.
+//
+// Work split (split-K). Workgroup (b, c) owns K chunk c (1024 elements) and a
+// block of 16-row weight pairs (two 8-row groups). It first copies the 16
+// activation rows of its chunk into LDS (rotated by the row index so that the
+// A-operand reads hit distinct banks); its waves then walk the pairs, each
+// pair needing only weight loads. The partial product of chunk c goes to
+// a workspace [C][pairs][16 n][16 m]; a second kernel adds the C partials
+// of every output in chunk order and applies the tensor scale (one chunk:
+// the first kernel writes y directly). Results are deterministic.
 //
 // Operand layout of v_mfma_f32_16x16x32_bf16 (lane l, q = l / 16):
 //   A: row l % 16, k = 8q .. 8q+7;  B: column l % 16, k = 8q .. 8q+7;
 //   D: column l % 16, rows 4q .. 4q+3.
-// The order of the 32 k inside one MFMA is free as long as A and B agree, so
-// lane (q, n) loads row n's 16-byte piece p = 4t + q of a 1024-element chunk
-// (t = 0..7, 32 elements = two scale blocks) and supplies its elements
-// 8j..8j+7 to the j-th of four MFMAs; the A lane (q, m) loads the matching 32
-// activations x[m][32p .. 32p+31]. One wave covers NT 16-row N-subtiles of
-// one chunk, in two batches of four pieces whose loads are all in flight
-// before the batch's arithmetic; S waves of a workgroup split the chunks of
-// the same rows and add their partial tiles in LDS in a fixed order.
+// The k order inside one MFMA is free as long as A and B agree: lane
+// (q, n) loads the 16-byte piece 4t + q (t = 0..7) of weight row n and feeds
+// its elements 8j .. 8j+7 to MFMA (t, j); the A lane (q, m) reads the
+// matching activations x[m][32(4t + q) + 8j ..]. For a fixed t the wave's
+// loads cover 64 contiguous bytes of each of the 16 rows.
 #include <algorithm>
+#include <mutex>
 
 #include "fp4_internal.h"
 
@@ -32,8 +38,17 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kMaxWaves = 8;
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
+constexpr int kWaves = 4;                 // waves per workgroup
+constexpr int kMRows = 16;                // activation rows per pass (MFMA M)
+constexpr int kPairRows = 16;             // weight rows per pair (MFMA N)
+constexpr int kXBytes = kMRows * kChunkK * 2;   // 32 KB of staged activations
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
+}
 
 __device__ __forceinline__ f32x2_t fp4x2_f32(uint32_t w, int sel) {
   switch (sel) {
@@ -45,199 +60,227 @@ __device__ __forceinline__ f32x2_t fp4x2_f32(uint32_t w, int sel) {
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  // exact: both values have <= 6 significant bits and lie in bf16 range
-  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+  // one v_cvt_pk_bf16_f32; exact: both values have <= 6 significant bits
+  // and lie in bf16 range
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-// Four B operands (8 bf16 each) from one 16-byte piece: e2m1 * block scale.
-__device__ __forceinline__ void decode_piece(bf16x8_t (&b)[4], const uint4& w, float s0, float s1) {
+// 8 elements (word j of a piece) times their block scale, as bf16 operands.
+__device__ __forceinline__ bf16x8_t decode8(uint32_t w, float s) {
+  uint32_t o[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float s = j < 2 ? s0 : s1;
-    const uint32_t wd = word(w, j);
-    uint32_t o[4];
+  for (int i = 0; i < 4; ++i) {
+    const f32x2_t e = fp4x2_f32(w, i);
+    o[i] = pack_bf16(e[0] * s, e[1] * s);
+  }
+  return __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
+struct MmaArgs {
+  const uint16_t* x;   // bf16 [M][K]
+  float* ws;           // [C][npairs][16][16] partials (unused when C == 1)
+  int M, K, C, m0;     // m0: first activation row of this pass
+  int nproj;
+  int npairs;          // pairs over all projections
+  int pairs_per_wg;
+  struct Proj {
+    const uint8_t* tiles;
+    const float* gscale;
+    float* y;
+    int64_t ldy;
+    int32_t N;
+    int32_t pair_begin;
+  } proj[kMaxProj];
+};
+
+// Codes (16-byte piece 4t + q of the lane's row) and the piece's two scale
+// bytes for one pair.
+struct PairFrag {
+  uint4 w[8];
+  uint32_t sc[8];
+};
+
+// grid (ceil(npairs / pairs_per_wg), C); block kWaves waves.
+__global__ __launch_bounds__(64 * kWaves) void k_gemv_mma(const MmaArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t xs[kXBytes];
+  const int lane = threadIdx.x & 63, q = lane >> 4, n16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = blockIdx.y, C = a.C, K = a.K;
+  const int pb = blockIdx.x * a.pairs_per_wg;
+  const int pe = min(pb + a.pairs_per_wg, a.npairs);
+  const int rr = n16 & 7;
+
+  auto proj_of = [&](int pair) {
+    int p = 0;
+    while (p + 1 < a.nproj && pair >= a.proj[p + 1].pair_begin) ++p;
+    return p;
+  };
+  // A pair past the workgroup's range gets a zero-byte resource: its loads
+  // return zeros without touching memory, so every wave runs the same loads.
+  auto load_pair = [&](int pair, PairFrag& f) {
+    const bool v = pair < pe;
+    const int p = proj_of(v ? pair : pb);
+    const int lp = (v ? pair : pb) - a.proj[p].pair_begin;
+    const int G = (a.proj[p].N + 7) >> 3;
+    const int g0 = 2 * lp;
+    // one resource over both tiles of the pair (groups g0, g0 + 1 of chunk c);
+    // a missing second group stays outside the resource and reads as zeros
+    const int bytes = !v ? 0 : (g0 + 1 < G ? (C + 1) * kTileBytes : kTileBytes);
+    const __amdgpu_buffer_rsrc_t r = rsrc(a.proj[p].tiles + ((int64_t)g0 * C + c) * kTileBytes, bytes);
+    const int base = (n16 >> 3) * C * kTileBytes;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x2_t e = fp4x2_f32(wd, i);
-      o[i] = pack_bf16(e[0] * s, e[1] * s);
+    for (int t = 0; t < 8; ++t) {
+      const u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(r, base + rr * 512 + (4 * t + q) * 16, 0, 2);
+      f.w[t] = make_uint4(w[0], w[1], w[2], w[3]);
+      f.sc[t] = __builtin_amdgcn_raw_buffer_load_b16(r, base + tile_scale_offset(rr, 2 * (4 * t + q)), 0, 0);
     }
-    b[j] = __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+  };
+
+  PairFrag cur;
+  load_pair(pb + wave, cur);   // in flight while the activations are staged
+
+  // ---- activations of chunk c, rows m0 .. m0+15, into LDS: row m at 2048m,
+  // 16-byte unit u stored at position (u + m) & 127
+  {
+    const int rows = min(kMRows, a.M - a.m0);
+    for (int t = threadIdx.x; t < kMRows * 128; t += 64 * kWaves) {
+      const int m = t >> 7, u = t & 127;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (m < rows) {
+        const __amdgpu_buffer_rsrc_t rx = rsrc(a.x + (int64_t)(a.m0 + m) * K, K * 2);
+        const u32x4_t r = __builtin_amdgcn_raw_buffer_load_b128(rx, (c * kChunkK + u * 8) * 2, 0, 0);   // past K: 0
+        v = make_uint4(r[0], r[1], r[2], r[3]);
+      }
+      *reinterpret_cast<uint4*>(xs + m * 2048 + ((u + m) & 127) * 16) = v;
+    }
+  }
+  __syncthreads();
+
+  for (int pair = pb + wave; pair < pe; pair += kWaves) {
+    PairFrag nxt;
+    load_pair(pair + kWaves, nxt);   // next pair's loads overlap this pair's arithmetic
+    // two accumulators (even and odd pieces) halve the dependent MFMA chain
+    f32x4_t acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      // one piece at a time: keeps the compiler from hoisting every operand
+      __builtin_amdgcn_sched_barrier(0);
+      const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)cur.sc[t], 0);
+      const float s1 = __builtin_amdgcn_cvt_f32_fp8((int)cur.sc[t], 1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x8_t b = decode8(word(cur.w[t], j), j < 2 ? s0 : s1);
+        const int u = 16 * t + 4 * q + j;
+        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(xs + n16 * 2048 + ((u + n16) & 127) * 16);
+        acc2[t & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b, acc2[t & 1], 0, 0, 0);
+      }
+    }
+    const f32x4_t acc = acc2[0] + acc2[1];
+    // lane (q, n16) holds D[m = 4q + i][n = n16]
+    if (C == 1) {
+      const int p = proj_of(pair);
+      const int n = 16 * (pair - a.proj[p].pair_begin) + n16;
+      const float gs = *a.proj[p].gscale;
+      if (n < a.proj[p].N) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = a.m0 + 4 * q + i;
+          if (m < a.M) a.proj[p].y[(int64_t)m * a.proj[p].ldy + n] = gs * acc[i];
+        }
+      }
+    } else if (a.m0 + 4 * q < a.M) {   // rows past M are never read back
+      float* dst = a.ws + ((int64_t)c * a.npairs + pair) * 256 + n16 * 16 + 4 * q;
+      *reinterpret_cast<f32x4_t*>(dst) = acc;
+    }
+    cur = nxt;
   }
 }
 
-// grid: one workgroup per 16*NT-row tile (over all projections); S waves.
-template <int NT, int MTL>
-__global__ __launch_bounds__(64 * kMaxWaves) void k_gemv_mfma(const GemvArgs a) {
-  extern __shared__ f32x4_t red_dyn[];                 // [S][NT][MTL][64] when S > 1
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int S = blockDim.x >> 6;
-  const int q = lane >> 4, n16 = lane & 15;
-
+// y[m][n] = gscale * sum over chunks (in order) of the partials.
+__global__ __launch_bounds__(256) void k_reduce(const MmaArgs a) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (pair, n16, m16)
+  if (t >= (int64_t)a.npairs * 256) return;
+  const int pair = (int)(t >> 8), n16 = (int)((t >> 4) & 15), m16 = (int)(t & 15);
+  const int m = a.m0 + m16;
+  if (m >= a.M) return;
   int p = 0;
-  while (p + 1 < a.nproj && (int)blockIdx.x >= a.proj[p + 1].wg_begin) ++p;
-  const int N = a.proj[p].N;
-  const int G = (N + 7) >> 3;
-  const int C = a.C, K = a.K, M = a.M;
-  const int row0 = ((int)blockIdx.x - a.proj[p].wg_begin) * 16 * NT;
-  const float gs = *a.proj[p].gscale;
-
-  // this lane's weight row in each N-subtile: codes at prow + c*kTileBytes +
-  // 16*piece, the piece's two block scales at srow + c*kTileBytes + 8*piece
-  const uint8_t* prow[NT];
-  const uint8_t* srow[NT];
-  bool rvalid[NT];
-#pragma unroll
-  for (int s = 0; s < NT; ++s) {
-    const int n = row0 + 16 * s + n16;
-    const int g = n >> 3;
-    rvalid[s] = g < G;
-    const int gg = rvalid[s] ? g : 0;
-    const uint8_t* tile0 = a.proj[p].tiles + (int64_t)gg * C * kTileBytes;
-    prow[s] = tile0 + (n & 7) * 512;
-    srow[s] = tile0 + tile_scale_offset(n & 7, 0);
-  }
-
-  for (int m0 = 0; m0 < M; m0 += 16 * MTL) {
-    f32x4_t acc[NT][MTL];
-#pragma unroll
-    for (int s = 0; s < NT; ++s)
-#pragma unroll
-      for (int mt = 0; mt < MTL; ++mt) acc[s][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    for (int c = wave; c < C; c += S) {
-      const bool full = (c + 1) * kChunkK <= K;
-      // two batches of four pieces; every load of a batch is issued before
-      // any of its arithmetic, so a chunk costs two memory round trips
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        uint4 wv[NT][4];
-        uint32_t sv[NT][4];
-        uint4 xv[MTL][4][4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          const int piece = 4 * (4 * hb + tt) + q;
-#pragma unroll
-          for (int s = 0; s < NT; ++s) {
-            wv[s][tt] = *reinterpret_cast<const uint4*>(prow[s] + (int64_t)c * kTileBytes + piece * 16);
-            sv[s][tt] = *reinterpret_cast<const uint16_t*>(srow[s] + (int64_t)c * kTileBytes + piece * 8);
-          }
-          const int k0 = c * kChunkK + 32 * piece;
-          const int kv = K - k0;                     // <= 0, 16 or >= 32 (K % 16 == 0)
-          const int ka = (full || kv > 0) ? k0 : 0, kb = (full || kv >= 32) ? k0 + 16 : 0;
-#pragma unroll
-          for (int mt = 0; mt < MTL; ++mt) {
-            const int m = m0 + 16 * mt + n16;
-            const int mr = m < M ? m : M - 1;
-            const uint4* xp = reinterpret_cast<const uint4*>(a.x + (int64_t)mr * K + ka);
-            const uint4* xq = reinterpret_cast<const uint4*>(a.x + (int64_t)mr * K + kb);
-            xv[mt][tt][0] = xp[0];
-            xv[mt][tt][1] = xp[1];
-            xv[mt][tt][2] = xq[0];
-            xv[mt][tt][3] = xq[1];
-          }
-        }
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          const int piece = 4 * (4 * hb + tt) + q;
-          const int kv = K - (c * kChunkK + 32 * piece);
-          bf16x8_t xa[MTL][4];
-#pragma unroll
-          for (int mt = 0; mt < MTL; ++mt) {
-            const int m = m0 + 16 * mt + n16;
-            const uint4 z = make_uint4(0, 0, 0, 0);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              uint4 v = xv[mt][tt][j];
-              if (m >= M || (!full && (j < 2 ? kv <= 0 : kv < 32))) v = z;
-              xa[mt][j] = __builtin_bit_cast(bf16x8_t, v);
-            }
-          }
-#pragma unroll
-          for (int s = 0; s < NT; ++s) {
-            const uint4 w = rvalid[s] ? wv[s][tt] : make_uint4(0, 0, 0, 0);
-            const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)sv[s][tt], 0);
-            const float s1 = __builtin_amdgcn_cvt_f32_fp8((int)sv[s][tt], 1);
-            bf16x8_t b[4];
-            decode_piece(b, w, s0, s1);
-#pragma unroll
-            for (int mt = 0; mt < MTL; ++mt)
-#pragma unroll
-              for (int j = 0; j < 4; ++j)
-                acc[s][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[mt][j], b[j], acc[s][mt], 0, 0, 0);
-          }
-        }
-      }
-    }
-
-    // lane (q, n16) holds rows m0 + 16 mt + 4q + i, column row0 + 16 s + n16
-    if (S > 1) {
-#pragma unroll
-      for (int s = 0; s < NT; ++s)
-#pragma unroll
-        for (int mt = 0; mt < MTL; ++mt) red_dyn[((wave * NT + s) * MTL + mt) * 64 + lane] = acc[s][mt];
-      __syncthreads();
-      if (wave == 0) {
-#pragma unroll
-        for (int s = 0; s < NT; ++s)
-#pragma unroll
-          for (int mt = 0; mt < MTL; ++mt) {
-            f32x4_t t = red_dyn[(s * MTL + mt) * 64 + lane];
-            for (int w = 1; w < S; ++w) t += red_dyn[((w * NT + s) * MTL + mt) * 64 + lane];   // wave order
-            acc[s][mt] = t;
-          }
-      }
-    }
-    if (wave == 0) {
-#pragma unroll
-      for (int s = 0; s < NT; ++s) {
-        const int n = row0 + 16 * s + n16;
-        if (n >= N) continue;
-#pragma unroll
-        for (int mt = 0; mt < MTL; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int m = m0 + 16 * mt + 4 * q + i;
-            if (m < M) a.proj[p].y[(int64_t)m * a.proj[p].ldy + n] = gs * acc[s][mt][i];
-          }
-      }
-    }
-    if (S > 1) __syncthreads();
-  }
+  while (p + 1 < a.nproj && pair >= a.proj[p + 1].pair_begin) ++p;
+  const int n = 16 * (pair - a.proj[p].pair_begin) + n16;
+  if (n >= a.proj[p].N) return;
+  float s = 0.0f;
+  for (int c = 0; c < a.C; ++c) s += a.ws[((int64_t)c * a.npairs + pair) * 256 + n16 * 16 + m16];
+  a.proj[p].y[(int64_t)m * a.proj[p].ldy + n] = *a.proj[p].gscale * s;
 }
 
-template <int NT, int MTL>
-hipError_t launch_nt(GemvArgs a, hipStream_t st, int split) {
-  int64_t wgs = 0;
-  for (int i = 0; i < a.nproj; ++i) {
-    a.proj[i].wg_begin = (int32_t)wgs;
-    wgs += (a.proj[i].N + 16 * NT - 1) / (16 * NT);
+// Per-device workspace for the chunk partials, allocated on first need and
+// kept (grown, never freed) for the life of the process.
+constexpr int kMaxDevices = 64;
+std::mutex g_ws_mu;
+float* g_ws[kMaxDevices] = {};
+size_t g_ws_bytes[kMaxDevices] = {};
+
+hipError_t workspace(size_t bytes, float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  if (g_ws_bytes[dev] < bytes) {
+    void* p = nullptr;
+    e = hipMalloc(&p, bytes);
+    if (e != hipSuccess) return e;
+    // the previous buffer may still be read by queued kernels: keep it
+    g_ws[dev] = static_cast<float*>(p);
+    g_ws_bytes[dev] = bytes;
   }
-  int S = split;
-  if (S <= 0) {
-    // enough waves to fill the machine, never more waves than chunks
-    S = (int)std::min<int64_t>(kMaxWaves, std::max<int64_t>(1, (2048 + wgs - 1) / wgs));
-    S = std::min(S, a.C);
-    const int per = (a.C + S - 1) / S;
-    S = (a.C + per - 1) / per;
-  }
-  S = std::max(1, std::min(S, std::min(kMaxWaves, a.C)));
-  const size_t shm = S > 1 ? (size_t)S * NT * MTL * 64 * sizeof(f32x4_t) : 0;
-  hipLaunchKernelGGL((k_gemv_mfma<NT, MTL>), dim3((unsigned)wgs), dim3(64 * S), shm, st, a);
-  return hipGetLastError();
+  *out = g_ws[dev];
+  return hipSuccess;
 }
 
 }  // namespace
 
-hipError_t launch_gemv_mfma(const GemvArgs& a, hipStream_t s, int nt, int split) {
-  // 16 or 32 activation rows per pass (64 would spill); more rows loop passes
-  const bool two = a.M > 16;
-  if (nt == 1) return two ? launch_nt<1, 2>(a, s, split) : launch_nt<1, 1>(a, s, split);
-  return two ? launch_nt<2, 2>(a, s, split) : launch_nt<2, 1>(a, s, split);
+hipError_t launch_gemv_mma(const GemvArgs& g, hipStream_t s, int ppw) {
+  MmaArgs a{};
+  a.x = g.x;
+  a.M = g.M;
+  a.K = g.K;
+  a.C = g.C;
+  a.nproj = g.nproj;
+  int64_t pairs = 0;
+  for (int i = 0; i < g.nproj; ++i) {
+    a.proj[i].tiles = g.proj[i].tiles;
+    a.proj[i].gscale = g.proj[i].gscale;
+    a.proj[i].y = g.proj[i].y;
+    a.proj[i].ldy = g.proj[i].ldy;
+    a.proj[i].N = g.proj[i].N;
+    a.proj[i].pair_begin = (int32_t)pairs;
+    pairs += (g.proj[i].N + kPairRows - 1) / kPairRows;
+  }
+  if (pairs > (int64_t(1) << 26)) return hipErrorInvalidValue;
+  a.npairs = (int)pairs;
+  // pairs per workgroup (sweeps on MI355X): 16 when K has few chunks, 8 for
+  // long K (more workgroups per chunk keep every CU busy)
+  a.pairs_per_wg = ppw > 0 ? ppw : (a.C <= 8 ? 16 : 8);
+  const int64_t wgx = (pairs + a.pairs_per_wg - 1) / a.pairs_per_wg;
+  if (a.C > 1) {
+    const size_t bytes = (size_t)a.C * (size_t)pairs * 256 * sizeof(float);
+    hipError_t e = workspace(bytes, &a.ws);
+    if (e != hipSuccess) return e;
+  }
+  for (int m0 = 0; m0 < g.M; m0 += kMRows) {
+    a.m0 = m0;
+    hipLaunchKernelGGL(k_gemv_mma, dim3((unsigned)wgx, (unsigned)a.C), dim3(64 * kWaves), 0, s, a);
+    if (a.C > 1) {
+      const int64_t n = pairs * 256;
+      hipLaunchKernelGGL(k_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+    }
+  }
+  return hipGetLastError();
 }
 
 }  // namespace fp4

@@ -38,9 +38,10 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  // exact: both values have <= 8 significant bits and lie in bf16 range
-  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+  // one v_cvt_pk_bf16_f32; exact: both values have <= 6 significant bits
+  // and lie in bf16 range
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 __global__ __launch_bounds__(256) void k_prefill(float* __restrict__ y, const uint16_t* __restrict__ x,

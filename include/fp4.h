@@ -46,7 +46,15 @@
  * Conventions for every call:
  *   - Pointers marked "device" are HIP device memory (e.g. a torch CUDA
  *     tensor's data_ptr()) on the current HIP device; the caller owns every
- *     buffer; the library allocates nothing and keeps no state between calls.
+ *     buffer. One exception to "the library allocates nothing": fp4_gemv
+ *     and fp4_gemv_multi with M >= 5 and K > 1024 keep the per-chunk
+ *     partial sums in a per-device workspace (C * ceil(N/16) * 1 KiB, C =
+ *     ceil(K/1024), summed over the projections) that the library
+ *     allocates with hipMalloc on the first call that needs it (or needs
+ *     more) and keeps until the process ends; that first call must not be
+ *     made while the stream is being captured into a graph. Calls on one
+ *     device share the workspace, so such calls on different streams of the
+ *     same device must not overlap in time.
  *   - `stream` is a hipStream_t (NULL = the default stream). Calls only
  *     enqueue work: they never synchronise, and results are ready when the
  *     stream's work is. gscale is a device pointer, so quantise -> multiply
@@ -59,7 +67,8 @@
  *     packed data: 8-byte; canonical scales: none); y and gscale 4-byte
  *     aligned.
  *   - Size limits: 1 <= N <= 2^28, 16 <= K <= 2^24, 1 <= M <= 2^24.
- *   - Calls are thread-safe (no global mutable state).
+ *   - Calls may be made from several host threads; the workspace above is
+ *     guarded by a lock while it is (re)allocated.
  */
 #ifndef FP4_H
 #define FP4_H
