@@ -13,31 +13,36 @@
 // 128 x BN/2 as 4 x NJ v_mfma_f32_32x32x16_bf16 tiles. K advances in steps
 // of 64, each split in four 16-deep MFMA slices.
 //
-// Operands. Activations go global -> registers -> LDS (two 32 KB stages,
-// one barrier per step) -> MFMA operand registers. Weights skip LDS: each
-// wave loads its own columns' packed codes straight from the tiled layout
-// into registers and decodes the slice it is about to use while the MFMAs
-// of the previous slice run. This keeps the LDS traffic (the bound of a
-// bf16 GEMM at this tile size) to the activations alone. The dot product
-// is taken over a permuted K order, the same for both operands: lane half h
-// of slice s covers K offsets 32h + 8s .. 32h + 8s + 7 of the step, so a
-// lane's weight codes for a whole step are one 16-byte piece of one row.
+// Data movement. Every global read is a direct-to-LDS buffer load (16 bytes
+// per lane, no registers, coalesced 128-byte row segments):
+//   - activations: two 32 KB stages, one step each, loaded a step ahead;
+//   - packed weight codes: two stages of BN rows x 128 bytes, a window of
+//     four steps each (one 128-byte piece run of every row of the tiled
+//     layout), loaded during the first steps of the window before;
+//   - block scales: two stages holding the tiled layout's scale bytes of the
+//     same windows.
+// Each wave then reads its MFMA operands from LDS: activations as bf16
+// fragments, weights as one 16-byte code piece per lane per step that it
+// decodes to bf16 slice by slice while the previous slice's MFMAs run.
+// Keeping the weights packed in LDS cuts their LDS traffic fourfold against
+// decoded bf16 tiles. The dot product is taken over a permuted K order, the
+// same for both operands: lane half h of slice s covers K offsets
+// 32h + 8s .. 32h + 8s + 7 of the step, so a lane's weight codes for a step
+// are one 16-byte piece of one row.
 //
-// Pipelining. Activation loads (L2 hits: one XCD shares a slab) are issued
-// at the start of the step before their MFMAs and written into the other
-// LDS stage in its second half; weight loads are issued in the middle of the
-// step before last. The activation rows are
-// 128 bytes, eight 16-byte chunks, chunk j of row r at slot j ^ swz(r), so
-// that operand reads and stores never meet in a bank.
+// LDS rows (activations: 64 bf16; weights: 8 code pieces) are eight 16-byte
+// slots, slot j ^ swz(r) holding chunk j of row r, so reads and the DMA
+// writes never meet in a bank. Each step ends with the wave's DMA wait and
+// one barrier.
 //
 // Order. Workgroups go round-robin over the 8 XCDs; tile t = (XCD, rank)
 // is mapped so that one XCD works through all output tiles of one 256-row
 // activation slab (2.6 MB at K = 5120, kept in that XCD's 4 MB L2) while
 // every XCD streams the weights.
 //
-// Loads use buffer resources: activation rows past M, activation columns
-// past K and weight row groups past N read as zeros without touching memory;
-// stores drop rows past M and columns past N the same way.
+// Bounds: the buffer loads read zeros for activation rows past M, columns
+// past K, weight row groups past N and steps past the end, without touching
+// memory; the epilogue's buffer stores drop rows past M and columns past N.
 #include <algorithm>
 
 #include "fp4_internal.h"
@@ -49,24 +54,50 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
 constexpr int BM = 256, BK = 64;
-constexpr int kStage = BM * BK * 2;      // 32 KB of activations per stage
-constexpr int kSmem = 2 * kStage;
+constexpr int kWin = 4;                  // steps per weight window (256 K = 8 pieces of a row)
+constexpr int kAStage = BM * BK * 2;     // 32 KB of activations per stage
 
-// 16-byte chunk slot of chunk j in row r of a stage: j ^ swz(r). Rows are
-// 128 bytes; swz is a bijection on every 8 consecutive rows, and on the even
-// (odd) rows of every 16, so the operand reads (8 or 16 lanes on 8 or 16
-// consecutive rows) never meet in a bank.
+template <int BN>
+struct Lds {
+  static constexpr int kBStage = BN * 128;        // codes of one window
+  static constexpr int kSStage = BN / 8 * 128;    // scale bytes of one window
+  static constexpr int kA = 0, kB = 2 * kAStage, kS = kB + 2 * kBStage;
+  static constexpr int kBytes = kS + 2 * kSStage;
+};
+
+// Chunk slot of chunk j in row r: j ^ swz(r). swz is a bijection on every 8
+// consecutive rows, and on the even (odd) rows of every 16, so 16-byte reads
+// by 8 or 16 lanes of consecutive rows never meet in a bank.
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
+// Buffer resource as four scalars (base, num_records, raw 32-bit format):
+// num_records bytes are readable, anything past them reads as zero.
+__device__ __forceinline__ i32x4_t rsrc4(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  i32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffff));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = kRsrcWord3;
+  return r;
 }
 
-__device__ __forceinline__ uint4 u4(u32x4_t v) { return make_uint4(v[0], v[1], v[2], v[3]); }
+// Direct-to-LDS load of 16 bytes per lane: lane L's bytes land at
+// lds + 16 L (lds wave-uniform). Written as assembly because the compiler
+// would otherwise wait for it before every LDS access; completion is
+// awaited explicitly with dma_wait before the barrier that publishes it.
+// M0 (reserved, so not listed as clobbered) is written by these statements
+// only: nothing else in this kernel uses it.
+__device__ __forceinline__ void dma16(const i32x4_t& rs, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs),
+               "s"(lds)
+               : "memory");
+}
+__device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ f32x2_t fp4x2_f32(uint32_t w, int sel) {
   switch (sel) {
@@ -88,34 +119,20 @@ __device__ __forceinline__ uint32_t dec2(uint32_t w, int sel, float s) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{e[0] * s, e[1] * s}, bf16x2_t));
 }
 
-// Eight codes (word `slice` of a 16-byte piece) as a bf16x8 MFMA operand.
-// `sc` is the aligned dword holding the piece's two block scales, in bytes
-// 0, 1 (hi false) or 2, 3 (hi true); slices 0, 1 use the first scale, 2, 3
-// the second. Byte selects keep every operation on the loaded dword inside
-// the decode, so none is hoisted next to its load (which would wait there).
-__device__ __forceinline__ bf16x8_t decode8(const uint4& piece, uint32_t sc, bool hi, int slice) {
-  float s;
-  if (slice < 2) {
-    const float lo_s = __builtin_amdgcn_cvt_f32_fp8((int)sc, 0), hi_s = __builtin_amdgcn_cvt_f32_fp8((int)sc, 2);
-    s = hi ? hi_s : lo_s;
-  } else {
-    const float lo_s = __builtin_amdgcn_cvt_f32_fp8((int)sc, 1), hi_s = __builtin_amdgcn_cvt_f32_fp8((int)sc, 3);
-    s = hi ? hi_s : lo_s;
-  }
+// Eight codes (word `slice` of a 16-byte piece) as a bf16x8 MFMA operand;
+// `sc` holds the piece's two block scales (slices 0, 1 use byte 0, slices
+// 2, 3 byte 1).
+__device__ __forceinline__ bf16x8_t decode8(const uint4& piece, uint32_t sc, int slice) {
+  const float s = slice < 2 ? __builtin_amdgcn_cvt_f32_fp8((int)sc, 0) : __builtin_amdgcn_cvt_f32_fp8((int)sc, 1);
   const uint32_t w = word(piece, slice);
   const uint4 o = make_uint4(dec2(w, 0, s), dec2(w, 1, s), dec2(w, 2, s), dec2(w, 3, s));
   return __builtin_bit_cast(bf16x8_t, o);
 }
 
-// This thread's activations of one step: rows ra + 32i (i < 8), chunk ac.
-struct ARegs {
-  uint4 a[8];
-};
 // This lane's weights of one step: piece (lane / 32) of row (lane % 32) of
-// each of the wave's NJ 32-column tiles, and the dword holding the piece's
-// two block scales.
+// each of the wave's NJ 32-column tiles, with the piece's two block scales.
 template <int NJ>
-struct BRegs {
+struct Pieces {
   uint4 w[NJ];
   uint32_t sc[NJ];
 };
@@ -127,17 +144,16 @@ struct Frags {
 
 // Deals the instructions of a scheduling region out around its NMFMA MFMAs:
 // after MFMA i come up to kValuPerMfma VALU operations, then one LDS read
-// (i < NDSR), one LDS write (i < NDSW) and one global load (i < NVMEM).
+// (i < NDSR). A wave issues in order, so an MFMA queued behind a long run of
+// decode arithmetic would leave the matrix core idle.
 constexpr int kValuPerMfma = 5;
-template <int NMFMA, int NDSR, int NDSW, int NVMEM>
+template <int NMFMA, int NDSR>
 __device__ __forceinline__ void interleave() {
 #pragma unroll
   for (int i = 0; i < NMFMA; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
     __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);   // VALU
     if (i < NDSR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    if (i < NDSW) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-    if (i < NVMEM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
   }
 }
 
@@ -146,71 +162,85 @@ __global__ __launch_bounds__(256, 1) void k_prefill(float* __restrict__ y, const
                                                     const uint8_t* __restrict__ tiles,
                                                     const float* __restrict__ gscale, int M, int N, int K,
                                                     int m_tiles, int n_tiles, int per_xcd) {
-  constexpr int NJ = BN / 64;   // 32-column MFMA tiles per wave
+  constexpr int NJ = BN / 64;          // 32-column MFMA tiles per wave
+  constexpr int NG = BN / 8;           // 8-row weight groups per tile
+  constexpr int NBI = NG / 4;          // code DMA instructions per wave per window
+  constexpr int NSW = NG / 8;          // waves issuing one scale DMA per window
+  using L = Lds<BN>;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int id = blockIdx.x;
   const int lin = (id & 7) * per_xcd + (id >> 3);   // XCD-contiguous tile index
   if (lin >= m_tiles * n_tiles) return;
   const int m0 = (lin / n_tiles) * BM, n0 = (lin % n_tiles) * BN;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, lh = lane >> 5;
   const int C = (K + kChunkK - 1) / kChunkK;
   const int G = (N + 7) >> 3;
   const int KT = (K + BK - 1) / BK;
+  const uint32_t sbase = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)smem;
 
-  // activations: thread -> rows ra + 32i (i < 8), 16-byte chunk ac of the step
-  const int ra = tid >> 3, ac = tid & 7;
   const int mrows = min(BM, M - m0);
-  const __amdgpu_buffer_rsrc_t rx = rsrc(x + (int64_t)m0 * K, mrows * K * 2);
-  // weights: lane -> row wn * BN/2 + 32j + l32 of the tile (j < NJ), piece lh
-  const int g0 = n0 >> 3;
-  const int ngroups = min(BN / 8, G - g0);
-  const __amdgpu_buffer_rsrc_t rw = rsrc(tiles + (int64_t)g0 * C * kTileBytes, ngroups * C * kTileBytes);
-  // the scale pair of row r sits at an offset = 2 (mod 4) when (r / 2) is odd
-  const bool sc_hi = (tile_scale_offset(l32 & 7, 0) & 2) != 0;
+  const int ngroups = min(NG, G - (n0 >> 3));
+  const i32x4_t rx = rsrc4(x + (int64_t)m0 * K, (uint32_t)(mrows * K * 2));
+  const i32x4_t rw = rsrc4(tiles + (int64_t)(n0 >> 3) * C * kTileBytes, (uint32_t)(ngroups * C * kTileBytes));
+  const i32x4_t rnull = rsrc4(x, 0);
 
-  // Loads of steps past the end go through an empty resource (zeros, no
-  // memory access), so every load is unconditional and the compiler can count
-  // outstanding loads exactly.
-  const __amdgpu_buffer_rsrc_t rnull = rsrc(x, 0);
-  auto load_a = [&](int kt, ARegs& r) {
+  // DMA lane roles. One instruction fills 8 LDS rows of 128 bytes: lane ->
+  // row (lane / 8) of the 8, slot lane % 8, which holds chunk
+  // (lane % 8) ^ swz(row); for 8-aligned row blocks swz(row) is
+  // (lane / 8) ^ (block & 1).
+  const int dr = lane >> 3, ds = lane & 7;
+  const int achunk0 = ds ^ dr, achunk1 = ds ^ dr ^ 1;   // even / odd 8-row blocks
+  // activations: instruction i of this wave fills rows 64 wave + 8i + dr
+  const uint32_t a_row_off = (uint32_t)((wave * 64 + dr) * K * 2);
+  auto dma_a = [&](int kt) {
     const int k0 = kt * BK;
-    const __amdgpu_buffer_rsrc_t rs = kt < KT ? rx : rnull;
-    // a chunk past K (ragged last step) gets bit 31 set: an offset past the
-    // resource (an arithmetic mask, not a select, which the compiler turns
-    // into branches around the loads)
-    const uint32_t oob = (uint32_t)((K - 1 - k0 - ac * 8) >> 31) << 31;
+    const i32x4_t& rs = kt < KT ? rx : rnull;
+    // a chunk past K (ragged last step) gets bit 31 set: an offset past the resource
+    const uint32_t oob0 = (uint32_t)((K - 1 - k0 - achunk0 * 8) >> 31) << 31;
+    const uint32_t oob1 = (uint32_t)((K - 1 - k0 - achunk1 * 8) >> 31) << 31;
+    const uint32_t lds = sbase + L::kA + (kt & 1) * kAStage + wave * 64 * 128;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      r.a[i] = u4(__builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(((ra + 32 * i) * K + k0 + ac * 8) * 2) | oob, 0, 0));
-  };
-  auto load_b = [&](int kt, BRegs<NJ>& r) {
-    const int k0 = kt * BK;
-    const int c = k0 / kChunkK, p = (k0 % kChunkK) / 32 + lh;
-    const __amdgpu_buffer_rsrc_t rs = kt < KT ? rw : rnull;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int nr = wn * (BN / 2) + j * 32 + l32;
-      const int tb = ((nr >> 3) * C + c) * kTileBytes;
-      r.w[j] = u4(__builtin_amdgcn_raw_buffer_load_b128(rs, tb + (nr & 7) * 512 + p * 16, 0, 0));
-      r.sc[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, (tb + tile_scale_offset(nr & 7, 2 * p)) & ~3, 0, 0);
+    for (int i = 0; i < 8; ++i) {
+      const int ch = (i & 1) ? achunk1 : achunk0;
+      const uint32_t off = (a_row_off + (uint32_t)(i * 8 * K * 2) + (uint32_t)((k0 + ch * 8) * 2)) | ((i & 1) ? oob1 : oob0);
+      dma16(rs, off, lds + i * 1024);
     }
   };
-  // quarter q (< 4) of writing a step's activations into an LDS stage
-  auto store_a = [&](const ARegs& r, int stage, int q) {
-    uint8_t* As = smem + stage * kStage;
+  // weight codes: instruction i of this wave fills group g = NBI wave + i
+  // (rows 8g + dr); window `win` covers pieces 8 (win % 4) .. + 7 of chunk win / 4
+  auto dma_b = [&](int win, int i0, int i1) {
+    const bool live = win * kWin < KT;
+    const i32x4_t& rs = live ? rw : rnull;
+    const int c = win >> 2, p0 = (win & 3) * 8;
+    const uint32_t lds = sbase + L::kB + (win & 1) * L::kBStage;
 #pragma unroll
-    for (int i = 2 * q; i < 2 * q + 2; ++i) {
-      const int row = ra + 32 * i;
-      *reinterpret_cast<uint4*>(As + row * 128 + ((ac ^ swz(row)) * 16)) = r.a[i];
+    for (int i = i0; i < i1; ++i) {
+      const int g = NBI * wave + i;
+      const int piece = ds ^ dr ^ (g & 1);
+      const uint32_t off = (uint32_t)((g * C + c) * kTileBytes + dr * 512 + (p0 + piece) * 16);
+      dma16(rs, off, lds + g * 1024);
     }
   };
-  // slice s: lane half h covers K offsets 32h + 8s .. + 7 of the step, which
-  // is chunk 4h + s of the activation row and word s of the weight piece
+  // scales: wave w < NSW fills groups 8w .. 8w + 7, 128 bytes each: half
+  // (lane / 4) % 2 of the tile's scale area, 64 bytes from piece p0 on
+  auto dma_s = [&](int win) {
+    if (wave >= NSW) return;
+    const bool live = win * kWin < KT;
+    const i32x4_t& rs = live ? rw : rnull;
+    const int c = win >> 2, p0 = (win & 3) * 8;
+    const int g = 8 * wave + dr;
+    const uint32_t off = (uint32_t)((g * C + c) * kTileBytes + kTileCodes + ((lane >> 2) & 1) * 256 + p0 * 8 +
+                                    (lane & 3) * 16);
+    dma16(rs, off, sbase + L::kS + (win & 1) * L::kSStage + wave * 1024);
+  };
+
+  // operand reads
   auto read_a = [&](int stage, int s, Frags<NJ>& f) {
-    const uint8_t* As = smem + stage * kStage;
+    const uint8_t* As = smem + L::kA + stage * kAStage;
     const int lchunk = 4 * lh + s;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -218,9 +248,20 @@ __global__ __launch_bounds__(256, 1) void k_prefill(float* __restrict__ y, const
       f.a[i] = *reinterpret_cast<const bf16x8_t*>(As + r * 128 + ((lchunk ^ swz(r)) * 16));
     }
   };
-  auto decode_b = [&](const BRegs<NJ>& r, int s, Frags<NJ>& f) {
+  auto read_pieces = [&](int kt, Pieces<NJ>& p) {
+    const int win = kt / kWin, q = 2 * (kt % kWin) + lh;   // piece within the window
+    const uint8_t* Bs = smem + L::kB + (win & 1) * L::kBStage;
+    const uint8_t* Ss = smem + L::kS + (win & 1) * L::kSStage;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) f.b[j] = decode8(r.w[j], r.sc[j], sc_hi, s);
+    for (int j = 0; j < NJ; ++j) {
+      const int n = wn * (BN / 2) + j * 32 + l32;
+      p.w[j] = *reinterpret_cast<const uint4*>(Bs + n * 128 + ((q ^ swz(n)) * 16));
+      p.sc[j] = *reinterpret_cast<const uint16_t*>(Ss + (n >> 3) * 128 + (n & 1) * 64 + q * 8 + ((n & 7) >> 1) * 2);
+    }
+  };
+  auto decode_b = [&](const Pieces<NJ>& p, int s, Frags<NJ>& f) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) f.b[j] = decode8(p.w[j], p.sc[j], s);
   };
 
   f32x16_t acc[4][NJ];
@@ -238,78 +279,62 @@ __global__ __launch_bounds__(256, 1) void k_prefill(float* __restrict__ y, const
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
   };
 
-  // Step kt uses LDS stage kt % 2 and weight register set kt % 2. On entry
-  // the weight operands of its slice 0 are decoded (in f0.b). It reads its
-  // slice 0 activation operands and issues the activation loads of step
-  // kt + 1 (one register set; they come from L2), then runs its four slices;
-  // alongside the MFMAs of slice s it reads the activation operands of slice
-  // s + 1 and decodes its weight operands, in slices 2 and 3 writes the step
-  // kt + 1 activations into the other stage, and in slice 3 (its weight set
-  // decoded) loads the weights of step kt + 2 and decodes slice 0 of step
-  // kt + 1. One barrier per step.
-  //
-  // Scheduling: a wave issues in order, so an MFMA queued behind a long run
-  // of decode arithmetic leaves the matrix core idle. Each slice is its own
-  // scheduling region (sched_barrier) whose instructions are dealt out
-  // around the MFMAs (sched_group_barrier): after every MFMA a few VALU
-  // operations and at most one LDS or global memory instruction, which the
-  // 32-cycle MFMA covers.
-  Frags<NJ> f0, f1;
-  ARegs an;
-  auto step = [&](int kt, BRegs<NJ>& b_mine, const BRegs<NJ>& b_next, int stage) {
-    read_a(stage, 0, f0);
-    load_a(kt + 1, an);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(f0);
-    read_a(stage, 1, f1);
-    decode_b(b_mine, 1, f1);
-    interleave<4 * NJ, 4, 0, 0>();
-    __builtin_amdgcn_sched_barrier(0);
-    mma(f1);
-    read_a(stage, 2, f0);
-    decode_b(b_mine, 2, f0);
-    interleave<4 * NJ, 4, 0, 0>();
-    __builtin_amdgcn_sched_barrier(0);
-    mma(f0);
-    read_a(stage, 3, f1);
-    decode_b(b_mine, 3, f1);
-    store_a(an, stage ^ 1, 0);
-    store_a(an, stage ^ 1, 1);
-    interleave<4 * NJ, 4, 4, 0>();
-    __builtin_amdgcn_sched_barrier(0);
-    mma(f1);
-    load_b(kt + 2, b_mine);
-    decode_b(b_next, 0, f0);
-    store_a(an, stage ^ 1, 2);
-    store_a(an, stage ^ 1, 3);
-    interleave<4 * NJ, 0, 4, 2 * NJ>();
-    __syncthreads();
-  };
-
-  // prologue: step 0's activations in stage 0, weights of steps 0 and 1 in
-  // registers
-  BRegs<NJ> b0, b1;
-  load_a(0, an);
-  load_b(0, b0);
-  load_b(1, b1);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) store_a(an, 0, q);
-  decode_b(b0, 0, f0);
+  // prologue: step 0's activations, window 0's codes and scales
+  dma_a(0);
+  dma_b(0, 0, NBI);
+  dma_s(0);
+  dma_wait();
   __syncthreads();
+  Frags<NJ> f0, f1;
+  Pieces<NJ> pc;
+  read_pieces(0, pc);
+  decode_b(pc, 0, f0);
 
-  // past the end the loads give zeros and go into a stage no step reads
-  int kt = 0;
-  for (; kt + 2 <= KT; kt += 2) {
-    step(kt, b0, b1, 0);
-    step(kt + 1, b1, b0, 1);
+  // Step kt (activation stage kt % 2, window kt / 4): it loads the
+  // activations of step kt + 1 and, in the first three steps of a window,
+  // the next window's codes (two halves) and scales; runs its four slices,
+  // alongside each reading the next slice's activation operands and decoding
+  // its weight operands; in its last slice reads the weight pieces of step
+  // kt + 1 (published by an earlier barrier) and decodes their slice 0. The
+  // step ends with the DMA wait and the barrier that publishes its loads.
+  for (int kt = 0; kt < KT; ++kt) {
+    const int sa = kt & 1, sw = kt % kWin, win = kt / kWin;
+    read_a(sa, 0, f0);
+    dma_a(kt + 1);
+    if (sw == 0) dma_b(win + 1, 0, NBI / 2);
+    if (sw == 1) dma_b(win + 1, NBI / 2, NBI);
+    if (sw == 2) dma_s(win + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f0);
+    read_a(sa, 1, f1);
+    decode_b(pc, 1, f1);
+    interleave<4 * NJ, 4>();
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f1);
+    read_a(sa, 2, f0);
+    decode_b(pc, 2, f0);
+    interleave<4 * NJ, 4>();
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f0);
+    read_a(sa, 3, f1);
+    decode_b(pc, 3, f1);
+    interleave<4 * NJ, 4>();
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f1);
+    read_pieces(kt + 1, pc);   // past the end: stale LDS, never used
+    decode_b(pc, 0, f0);
+    interleave<4 * NJ, 2 * NJ>();
+    __builtin_amdgcn_sched_barrier(0);
+    dma_wait();
+    __syncthreads();
   }
-  if (kt < KT) step(kt, b0, b1, 0);   // odd step count: the last step sits in stage 0
 
   // epilogue: lane l of a 32x32 tile holds column l % 32 and rows
   // 8(e/4) + 4(l/32) + e%4 (e < 16). Buffer stores drop rows past M (past
   // the resource) and columns past N (bit 31 set in the offset).
   const float gs = *gscale;
-  const __amdgpu_buffer_rsrc_t ry = rsrc(y + (int64_t)m0 * N, mrows * N * 4);
+  const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(y + (int64_t)m0 * N, (short)0, mrows * N * 4,
+                                                                       kRsrcWord3);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -337,6 +362,16 @@ hipError_t launch_prefill(float* y, const uint16_t* x, const uint8_t* tiles, con
   if ((int64_t)BM * K * 2 >= (int64_t(1) << 31) || (int64_t)BM * N * 4 >= (int64_t(1) << 31) ||
       (int64_t)(256 / 8) * C * kTileBytes >= (int64_t(1) << 31))
     return hipErrorInvalidValue;
+  static bool attr_done = false;   // idempotent; racing first calls set the same values
+  if (!attr_done) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_prefill<128>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       Lds<128>::kBytes);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)k_prefill<256>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              Lds<256>::kBytes);
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
   const int64_t mt = (M + BM - 1) / BM;
   // 256 x 256 tiles do twice the MFMA work per LDS and load byte of 256 x 128
   // tiles; take them unless their last round of workgroups over the 256
@@ -353,11 +388,11 @@ hipError_t launch_prefill(float* y, const uint16_t* x, const uint8_t* tiles, con
   if (total > (int64_t(1) << 30)) return hipErrorInvalidValue;
   const int64_t per_xcd = (total + 7) / 8;
   if (wide)
-    hipLaunchKernelGGL(k_prefill<256>, dim3((unsigned)(8 * per_xcd)), dim3(256), kSmem, s, y, x, tiles, gscale,
-                       (int)M, (int)N, (int)K, (int)mt, (int)nt, (int)per_xcd);
+    hipLaunchKernelGGL(k_prefill<256>, dim3((unsigned)(8 * per_xcd)), dim3(256), Lds<256>::kBytes, s, y, x, tiles,
+                       gscale, (int)M, (int)N, (int)K, (int)mt, (int)nt, (int)per_xcd);
   else
-    hipLaunchKernelGGL(k_prefill<128>, dim3((unsigned)(8 * per_xcd)), dim3(256), kSmem, s, y, x, tiles, gscale,
-                       (int)M, (int)N, (int)K, (int)mt, (int)nt, (int)per_xcd);
+    hipLaunchKernelGGL(k_prefill<128>, dim3((unsigned)(8 * per_xcd)), dim3(256), Lds<128>::kBytes, s, y, x, tiles,
+                       gscale, (int)M, (int)N, (int)K, (int)mt, (int)nt, (int)per_xcd);
   return hipGetLastError();
 }
 
