@@ -236,7 +236,7 @@ def main():
             "down_5120x17408": {"us": round(t_d * 1e6, 3), "weight_GBps": round(B_d / t_d / 1e9, 1),
                                 "pct_of_hbm_peak": round(100 * B_d / t_d / 1e9 / HBM_PEAK_GBPS, 2)},
         },
-        "roofline": {"kernel": "k_gemv (all launches of a step: fused gate_up k_gemv<1,1> + down k_gemv<1,2>)", "bound": "hbm",
+        "roofline": {"kernel": "k_gemv<1> (both launches of a step: fused gate_up 2x17408x5120, down 5120x17408)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": (A_gu + A_d) / 2,

@@ -54,9 +54,9 @@ hipError_t launch_quantize(const uint16_t* W, int64_t N, int64_t K, bool tiled, 
                            uint8_t* scales, float* gscale, hipStream_t s);
 hipError_t launch_retile(const uint8_t* packed, const uint8_t* scales, int64_t N, int64_t K, uint8_t* tiles,
                          hipStream_t s);
-// Vector-ALU product for M <= 4 rows per pass. Positive gw (row groups per
-// workgroup) and wc (waves per row group) override the automatic geometry
-// (tuning).
+// Vector-ALU product for M <= 4 activation rows (larger M: an error; those
+// go to launch_gemv_mma). Positive gw (row groups per workgroup) and wc
+// (waves per row group) override the automatic geometry (tuning).
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t s, int gw = 0, int wc = 0);
 // Small-M product on bf16 MFMA, split over K chunks (16 activation rows per
 // pass, more rows loop passes). With more than one chunk it uses a

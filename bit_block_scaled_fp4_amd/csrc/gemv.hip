@@ -126,15 +126,10 @@ struct Round {
   uint4 x[MT][4];
 };
 
-// grid: workgroups over all projections; block: gw * wc waves.
-// Workgroup size limit: 16 waves, 8 when many activation rows need the
-// registers (the launch bound sets the VGPR budget per wave).
+// grid: workgroups over all projections; block: gw * wc waves (at most 16).
 template <int MT>
-constexpr int max_waves() { return MT > 4 ? 8 : kMaxWaves; }
-
-template <int MT>
-__global__ __launch_bounds__(64 * max_waves<MT>()) void k_gemv(const GemvArgs a) {
-  __shared__ float part[max_waves<MT>()][MT][8];
+__global__ __launch_bounds__(64 * kMaxWaves) void k_gemv(const GemvArgs a) {
+  __shared__ float part[kMaxWaves][MT][8];
   const int lane = threadIdx.x & 63, hl = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
@@ -156,7 +151,7 @@ __global__ __launch_bounds__(64 * max_waves<MT>()) void k_gemv(const GemvArgs a)
       for (int i = 0; i < 4; ++i) acc[mi][i] = 0.0f;
 
     for (int c = wc; c < C; c += Wc) {
-      Round<(MT > 4 ? 1 : MT)> f;
+      Round<MT> f;
       {
         const bool v = gvalid;
         const __amdgpu_buffer_rsrc_t r = rsrc(pd.tiles + (v ? ((int64_t)g * C + c) * kTileBytes : 0), v ? kTileBytes : 0);
@@ -166,50 +161,25 @@ __global__ __launch_bounds__(64 * max_waves<MT>()) void k_gemv(const GemvArgs a)
         f.s = make_uint2(sv[0], sv[1]);
       }
       const int off = (c * kChunkK + hl * 32) * 2;   // past K (ragged last chunk): zeros
-      if constexpr (MT <= 4) {
 #pragma unroll
-        for (int mi = 0; mi < MT; ++mi) {
-          const int row = min(m0 + mi, M - 1);
-          const __amdgpu_buffer_rsrc_t rx = rsrc(a.x + (int64_t)row * K, K * 2);
+      for (int mi = 0; mi < MT; ++mi) {
+        const int row = min(m0 + mi, M - 1);
+        const __amdgpu_buffer_rsrc_t rx = rsrc(a.x + (int64_t)row * K, K * 2);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) f.x[mi][q] = ld16<0>(rx, off + q * 16);
-        }
-        // keep every load of the round ahead of the arithmetic
-        __builtin_amdgcn_sched_barrier(0);
+        for (int q = 0; q < 4; ++q) f.x[mi][q] = ld16<0>(rx, off + q * 16);
+      }
+      // keep every load of the round ahead of the arithmetic
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          // row 2i + h: its two block scales are bytes 2(i&1), 2(i&1)+1 of word i >> 1
-          const uint32_t sw = i < 2 ? f.s.x : f.s.y;
-          const float s0 = e4m3(sw, (i & 1) * 2), s1 = e4m3(sw, (i & 1) * 2 + 1);
-          bf16x2_t d[16];
+      for (int i = 0; i < 4; ++i) {
+        // row 2i + h: its two block scales are bytes 2(i&1), 2(i&1)+1 of word i >> 1
+        const uint32_t sw = i < 2 ? f.s.x : f.s.y;
+        const float s0 = e4m3(sw, (i & 1) * 2), s1 = e4m3(sw, (i & 1) * 2 + 1);
+        bf16x2_t d[16];
 #pragma unroll
-          for (int e = 0; e < 16; ++e) d[e] = fp4x2(word(f.w[i], e >> 2), e & 3);
+        for (int e = 0; e < 16; ++e) d[e] = fp4x2(word(f.w[i], e >> 2), e & 3);
 #pragma unroll
-          for (int mi = 0; mi < MT; ++mi) acc[mi][i] = dot_block2(d, f.x[mi], s0, s1, acc[mi][i]);
-        }
-      } else {
-        // many activation rows: decode the tile once, then stream the rows' activations
-        __builtin_amdgcn_sched_barrier(0);
-        bf16x2_t d[4][16];
-        float s0[4], s1[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t sw = i < 2 ? f.s.x : f.s.y;
-          s0[i] = e4m3(sw, (i & 1) * 2);
-          s1[i] = e4m3(sw, (i & 1) * 2 + 1);
-#pragma unroll
-          for (int e = 0; e < 16; ++e) d[i][e] = fp4x2(word(f.w[i], e >> 2), e & 3);
-        }
-#pragma unroll
-        for (int mi = 0; mi < MT; ++mi) {
-          const int row = min(m0 + mi, M - 1);
-          const __amdgpu_buffer_rsrc_t rx = rsrc(a.x + (int64_t)row * K, K * 2);
-          uint4 xv[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) xv[q] = ld16<0>(rx, off + q * 16);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[mi][i] = dot_block2(d[i], xv, s0[i], s1[i], acc[mi][i]);
-        }
+        for (int mi = 0; mi < MT; ++mi) acc[mi][i] = dot_block2(d, f.x[mi], s0, s1, acc[mi][i]);
       }
     }
 
@@ -256,11 +226,10 @@ __global__ __launch_bounds__(64 * max_waves<MT>()) void k_gemv(const GemvArgs a)
 template <int MT>
 static hipError_t launch_mt(GemvArgs a, hipStream_t s, int gw, int wc) {
   const int rounds = (a.C + kMaxWaves - 1) / kMaxWaves;
-  constexpr int kWaves = max_waves<MT>();
   int w = wc > 0 ? wc : (MT == 1 ? (a.C + rounds - 1) / rounds : (a.C + 2) / 3);
-  a.wc = std::max(1, std::min(w, kWaves));
+  a.wc = std::max(1, std::min(w, kMaxWaves));
   a.gw = gw > 0 ? gw : std::max(1, 4 / a.wc);
-  a.gw = std::max(1, std::min(a.gw, kWaves / a.wc));
+  a.gw = std::max(1, std::min(a.gw, kMaxWaves / a.wc));
   int64_t wgs = 0;
   for (int i = 0; i < a.nproj; ++i) {
     a.proj[i].wg_begin = (int32_t)wgs;
@@ -274,8 +243,7 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t s, int gw, int wc) {
   if (a.M == 1) return launch_mt<1>(a, s, gw, wc);
   if (a.M == 2) return launch_mt<2>(a, s, gw, wc);
   if (a.M <= 4) return launch_mt<4>(a, s, gw, wc);
-  if (a.M <= 8) return launch_mt<8>(a, s, gw, wc);
-  return launch_mt<16>(a, s, gw, wc);
+  return hipErrorInvalidValue;   // more rows go to the matrix-core kernel
 }
 
 }  // namespace fp4
