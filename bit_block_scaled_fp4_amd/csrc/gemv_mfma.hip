@@ -201,20 +201,38 @@ __global__ __launch_bounds__(64 * kWaves) void k_gemv_mma(const MmaArgs a) {
   }
 }
 
-// y[m][n] = gscale * sum over chunks (in order) of the partials.
+// y[m][n] = gscale * sum over chunks (in order) of the partials. A thread
+// owns four rows (m, ..., m + 3) of one output column: one 16-byte partial
+// per chunk, up to 16 chunks loaded together (indices past the last chunk
+// are clamped to it and their values dropped), then added in chunk order.
+// grid: npairs * 16 * ceil(rows / 4) threads, rows = min(16, M - m0).
 __global__ __launch_bounds__(256) void k_reduce(const MmaArgs a) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (pair, n16, m16)
-  if (t >= (int64_t)a.npairs * 256) return;
-  const int pair = (int)(t >> 8), n16 = (int)((t >> 4) & 15), m16 = (int)(t & 15);
-  const int m = a.m0 + m16;
-  if (m >= a.M) return;
+  const int r4 = (min(kMRows, a.M - a.m0) + 3) >> 2;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (pair, n16, m4)
+  if (t >= (int64_t)a.npairs * 16 * r4) return;
+  const int m4 = (int)(t % r4);
+  const int pn = (int)(t / r4), pair = pn >> 4, n16 = pn & 15;
   int p = 0;
   while (p + 1 < a.nproj && pair >= a.proj[p + 1].pair_begin) ++p;
   const int n = 16 * (pair - a.proj[p].pair_begin) + n16;
   if (n >= a.proj[p].N) return;
-  float s = 0.0f;
-  for (int c = 0; c < a.C; ++c) s += a.ws[((int64_t)c * a.npairs + pair) * 256 + n16 * 16 + m16];
-  a.proj[p].y[(int64_t)m * a.proj[p].ldy + n] = *a.proj[p].gscale * s;
+  const float gs = *a.proj[p].gscale;
+  const int64_t cstride = (int64_t)a.npairs * 64;   // in f32x4
+  const f32x4_t* src = reinterpret_cast<const f32x4_t*>(a.ws) + (int64_t)pair * 64 + n16 * 4 + m4;
+  f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < a.C; c0 += 16) {
+    f32x4_t v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = src[(int64_t)min(c0 + i, a.C - 1) * cstride];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (c0 + i < a.C) s += v[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = a.m0 + 4 * m4 + i;
+    if (m < a.M) a.proj[p].y[(int64_t)m * a.proj[p].ldy + n] = gs * s[i];
+  }
 }
 
 // Per-device workspace for the chunk partials, allocated on first need and
@@ -276,7 +294,7 @@ hipError_t launch_gemv_mma(const GemvArgs& g, hipStream_t s, int ppw) {
     a.m0 = m0;
     hipLaunchKernelGGL(k_gemv_mma, dim3((unsigned)wgx, (unsigned)a.C), dim3(64 * kWaves), 0, s, a);
     if (a.C > 1) {
-      const int64_t n = pairs * 256;
+      const int64_t n = pairs * 16 * ((std::min(kMRows, g.M - m0) + 3) / 4);
       hipLaunchKernelGGL(k_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
     }
   }
