@@ -9,7 +9,7 @@
 // result once in the epilogue.
 //
 // Tiling. A 256-thread workgroup computes a 256 (tokens) x BN (outputs)
-// tile, BN = 256 or 128; wave (wm, wn) of the 2 x 2 wave grid owns
+// tile, BN = 128, 192 or 256; wave (wm, wn) of the 2 x 2 wave grid owns
 // 128 x BN/2 as 4 x NJ v_mfma_f32_32x32x16_bf16 tiles. K advances in steps
 // of 64, each split in four 16-deep MFMA slices.
 //
@@ -354,46 +354,57 @@ __global__ __launch_bounds__(256, 1) void k_prefill(float* __restrict__ y, const
 
 }  // namespace
 
+template <int BN>
+static hipError_t launch_bn(float* y, const uint16_t* x, const uint8_t* tiles, const float* gscale, int64_t M, int64_t N,
+                     int64_t K, hipStream_t s) {
+  static bool attr_done = false;   // idempotent; racing first calls set the same value
+  if (!attr_done) {
+    const hipError_t e =
+        hipFuncSetAttribute((const void*)k_prefill<BN>, hipFuncAttributeMaxDynamicSharedMemorySize, Lds<BN>::kBytes);
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
+  const int64_t mt = (M + BM - 1) / BM, nt = (N + BN - 1) / BN;
+  const int64_t total = mt * nt;
+  if (total > (int64_t(1) << 30)) return hipErrorInvalidValue;
+  const int64_t per_xcd = (total + 7) / 8;
+  hipLaunchKernelGGL(k_prefill<BN>, dim3((unsigned)(8 * per_xcd)), dim3(256), Lds<BN>::kBytes, s, y, x, tiles, gscale,
+                     (int)M, (int)N, (int)K, (int)mt, (int)nt, (int)per_xcd);
+  return hipGetLastError();
+}
+
 hipError_t launch_prefill(float* y, const uint16_t* x, const uint8_t* tiles, const float* gscale, int64_t M,
-                          int64_t N, int64_t K, hipStream_t s) {
+                          int64_t N, int64_t K, hipStream_t s, int bn) {
   // buffer offsets are 32-bit: one 256-row slab of activations, of outputs
   // and of weights must each stay below 2 GB
   const int64_t C = chunks_of(K);
   if ((int64_t)BM * K * 2 >= (int64_t(1) << 31) || (int64_t)BM * N * 4 >= (int64_t(1) << 31) ||
       (int64_t)(256 / 8) * C * kTileBytes >= (int64_t(1) << 31))
     return hipErrorInvalidValue;
-  static bool attr_done = false;   // idempotent; racing first calls set the same values
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_prefill<128>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       Lds<128>::kBytes);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)k_prefill<256>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              Lds<256>::kBytes);
-    if (e != hipSuccess) return e;
-    attr_done = true;
+  if (bn <= 0) {
+    // Tile width: the time is about (rounds of workgroups over the 256 CUs)
+    // x (time of one tile). Relative tile times measured on MI355X at
+    // M = 2048, K = 5120: 128 wide 0.66, 192 wide 0.85, 256 wide 1 (wider
+    // tiles do more MFMA work per LDS and load byte); ties go to the wider.
+    const int64_t mt = (M + BM - 1) / BM;
+    const int widths[3] = {256, 192, 128};
+    const int cost[3] = {100, 85, 66};
+    int64_t best = -1;
+    for (int i = 0; i < 3; ++i) {
+      const int64_t rounds = (mt * ((N + widths[i] - 1) / widths[i]) + 255) / 256;
+      const int64_t t = rounds * cost[i];
+      if (best < 0 || t < best) {
+        best = t;
+        bn = widths[i];
+      }
+    }
   }
-  const int64_t mt = (M + BM - 1) / BM;
-  // 256 x 256 tiles do twice the MFMA work per LDS and load byte of 256 x 128
-  // tiles; take them unless their last round of workgroups over the 256
-  // compute units is much emptier (the time is about rounds x tile time)
-  const int64_t nt256 = (N + 255) / 256, nt128 = (N + 127) / 128;
-  const int64_t rounds256 = (mt * nt256 + 255) / 256, rounds128 = (mt * nt128 + 255) / 256;
-#ifdef PREFILL_WIDE_RULE
-  const bool wide = PREFILL_WIDE_RULE;
-#else
-  const bool wide = 20 * rounds256 <= 13 * rounds128;
-#endif
-  const int64_t nt = wide ? nt256 : nt128;
-  const int64_t total = mt * nt;
-  if (total > (int64_t(1) << 30)) return hipErrorInvalidValue;
-  const int64_t per_xcd = (total + 7) / 8;
-  if (wide)
-    hipLaunchKernelGGL(k_prefill<256>, dim3((unsigned)(8 * per_xcd)), dim3(256), Lds<256>::kBytes, s, y, x, tiles,
-                       gscale, (int)M, (int)N, (int)K, (int)mt, (int)nt, (int)per_xcd);
-  else
-    hipLaunchKernelGGL(k_prefill<128>, dim3((unsigned)(8 * per_xcd)), dim3(256), Lds<128>::kBytes, s, y, x, tiles,
-                       gscale, (int)M, (int)N, (int)K, (int)mt, (int)nt, (int)per_xcd);
-  return hipGetLastError();
+  switch (bn) {
+    case 128: return launch_bn<128>(y, x, tiles, gscale, M, N, K, s);
+    case 192: return launch_bn<192>(y, x, tiles, gscale, M, N, K, s);
+    case 256: return launch_bn<256>(y, x, tiles, gscale, M, N, K, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace fp4

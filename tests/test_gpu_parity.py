@@ -251,9 +251,10 @@ def test_gemv_multi_equals_oracle_for_each_projection_and_is_deterministic():
 
 
 # --------------------------------------------------------------------- prefill
-# the last two shapes have enough tiles that the launcher takes 256 x 256 tiles
+# (300, 16452, 80) and (257, 16400, 1040) take 256 x 192 tiles, (300, 32768, 80) takes 256 x 256 tiles
 @pytest.mark.parametrize("M,N,K", [(1, 8, 16), (37, 300, 1040), (200, 129, 2048), (128, 256, 64), (300, 1000, 5120),
-                                   (513, 136, 1984), (64, 64, 80), (300, 16452, 80), (257, 16400, 1040)])
+                                   (513, 136, 1984), (64, 64, 80), (300, 16452, 80), (257, 16400, 1040),
+                                   (300, 32768, 80)])
 def test_prefill_small_shapes(M, N, K):
     print("prefill", M, N, K, flush=True)
     bw = bf16_tensor((N, K), M + N + K, 0.02, outlier_p=0.002, outlier_scale=20.0)
