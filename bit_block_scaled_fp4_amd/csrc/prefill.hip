@@ -44,6 +44,7 @@
 // past K, weight row groups past N and steps past the end, without touching
 // memory; the epilogue's buffer stores drop rows past M and columns past N.
 #include <algorithm>
+#include <atomic>
 
 #include "fp4_internal.h"
 
@@ -357,12 +358,17 @@ __global__ __launch_bounds__(256, 1) void k_prefill(float* __restrict__ y, const
 template <int BN>
 static hipError_t launch_bn(float* y, const uint16_t* x, const uint8_t* tiles, const float* gscale, int64_t M, int64_t N,
                      int64_t K, hipStream_t s) {
-  static bool attr_done = false;   // idempotent; racing first calls set the same value
-  if (!attr_done) {
-    const hipError_t e =
-        hipFuncSetAttribute((const void*)k_prefill<BN>, hipFuncAttributeMaxDynamicSharedMemorySize, Lds<BN>::kBytes);
+  // more than 64 KB of dynamic LDS must be allowed once per kernel and device
+  constexpr int kMaxDevices = 64;
+  static std::atomic<bool> attr_set[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  if (!attr_set[dev].load(std::memory_order_acquire)) {   // racing first calls set the same value
+    e = hipFuncSetAttribute((const void*)k_prefill<BN>, hipFuncAttributeMaxDynamicSharedMemorySize, Lds<BN>::kBytes);
     if (e != hipSuccess) return e;
-    attr_done = true;
+    attr_set[dev].store(true, std::memory_order_release);
   }
   const int64_t mt = (M + BM - 1) / BM, nt = (N + BN - 1) / BN;
   const int64_t total = mt * nt;
