@@ -122,6 +122,11 @@ int fp4_gemm_prefill(float* y, const void* x_bf16, const void* packed, const voi
   if (!y || !x_bf16 || !packed || !gscale) return FP4_ERR_NULL;
   if (int st = check_nk(N, K)) return st;
   if (M < 1 || M > kMaxM || M * N > kMaxElems) return FP4_ERR_SHAPE;
+  // the kernel addresses one 256-row slab of x, of y and of weight tiles
+  // with 32-bit buffer offsets
+  const int64_t slab = int64_t(1) << 31;
+  if (256 * K * 2 >= slab || 256 * N * 4 >= slab || 32 * fp4::chunks_of(K) * fp4::kTileBytes >= slab)
+    return FP4_ERR_SHAPE;
   if (!aligned(x_bf16, 16) || !aligned(packed, 16) || !aligned(y, 4) || !aligned(gscale, 4)) return FP4_ERR_ALIGN;
   return hip_status(fp4::launch_prefill(y, static_cast<const uint16_t*>(x_bf16), static_cast<const uint8_t*>(packed),
                                         gscale, M, N, K, static_cast<hipStream_t>(stream)));

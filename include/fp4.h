@@ -163,14 +163,18 @@ typedef struct {
 FP4_API int fp4_gemv_multi(const fp4_proj *projs, int nproj, const void *x_bf16, int64_t M, int64_t K,
                    void *stream);
 
-/* The same product for prefill-sized M on the matrix cores: weight tiles
- * are dequantised exactly to bf16 (E2M1 x E4M3 fits bf16) in LDS and fed
- * to bf16 MFMA with fp32 accumulation; gscale is applied once in the fp32
- * epilogue. Prefill is compute-bound: thousands of prompt tokens go
+/* The same product for prefill-sized M on the matrix cores: packed weight
+ * codes are staged in LDS, dequantised exactly to bf16 (E2M1 x E4M3 fits
+ * bf16) as MFMA operands and fed to bf16 MFMA with fp32 accumulation;
+ * gscale is applied once in the fp32 epilogue. Prefill is compute-bound: thousands of prompt tokens go
  * through each layer at once (page "imp" README, the prefill paragraph;
  * page "1. The big picture", "Two phases with very different costs").
  * Any M >= 1 is accepted; y [M][N] fp32 overwritten. `packed` holds the
- * tiles; `scales` is unused. */
+ * tiles; `scales` is unused. The first call on a device raises the kernels'
+ * dynamic LDS limit (a launch attribute, no allocation). FP4_ERR_SHAPE also
+ * covers shapes whose 256-row slabs reach 2 GB (256*K*2 or 256*N*4 bytes,
+ * or 32 weight row groups: the kernel uses 32-bit buffer offsets), i.e.
+ * K >= 4194304 or N >= 2097152. */
 FP4_API int fp4_gemm_prefill(float *y, const void *x_bf16, const void *packed, const void *scales,
                      const float *gscale, int64_t M, int64_t N, int64_t K, void *stream);
 

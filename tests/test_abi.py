@@ -91,6 +91,9 @@ def test_quantize_retile_prefill_argument_errors():
     assert L.fp4_gemm_prefill(A, A, A, A, None, 4, 8, 32, None) == ENULL
     assert L.fp4_gemm_prefill(A, A, A, A, A, 0, 8, 32, None) == ESHAPE
     assert L.fp4_gemm_prefill(A, A + 2, A, A, A, 4, 8, 32, None) == EALIGN
+    # 256-row slabs of x (256*K*2 bytes) or y (256*N*4 bytes) reaching 2 GB
+    assert L.fp4_gemm_prefill(A, A, A, A, A, 4, 8, 1 << 22, None) == ESHAPE
+    assert L.fp4_gemm_prefill(A, A, A, A, A, 4, 1 << 21, 32, None) == ESHAPE
 
 
 def test_binding_rejects_cpu_tensors():
