@@ -60,6 +60,9 @@ def _L():
         lib.orc_e4m3_encode_n.restype = None
         lib.orc_e2m1_encode_n.argtypes = [P, I64, P]
         lib.orc_e2m1_encode_n.restype = None
+        for f in (lib.orc_argmax_rows_f64, lib.orc_argmax_rows_f32):
+            f.argtypes = [P, I64, I64, I64, P]
+            f.restype = None
         _lib = lib
     return _lib
 
@@ -156,3 +159,22 @@ def tolerance_ok(y_gpu: np.ndarray, y_ref: np.ndarray, l1: np.ndarray, rel: floa
     with np.errstate(divide="ignore", invalid="ignore"):
         ratio = np.where(bound > 0, err / np.where(bound > 0, bound, 1.0), np.where(err > 0, np.inf, 0.0))
     return bool(np.all(err <= bound)), float(ratio.max() if ratio.size else 0.0)
+
+
+def argmax_rows(y: np.ndarray) -> np.ndarray:
+    """Greedy choice per row of y [M][N] (float32 or float64, decided in that
+    precision): the first index of the largest value, a NaN ranking above
+    every number, -0 equal to +0. Returns int32 [M]."""
+    y = np.atleast_2d(y)
+    if y.dtype == np.float32:
+        y, py = _c(y, np.float32)
+        f = _L().orc_argmax_rows_f32
+    else:
+        y, py = _c(y, np.float64)
+        f = _L().orc_argmax_rows_f64
+    M, N = y.shape
+    if N < 1:
+        raise ValueError("argmax_rows: empty rows")
+    idx = np.empty(M, dtype=np.int32)
+    f(py, M, N, N, idx.ctypes.data)
+    return idx

@@ -43,7 +43,8 @@
  * codes; E4M3 encode against torch's round-to-nearest-even cast; E2M1 encode
  * against brute-force nearest search; quantiser round-trip invariants and a
  * hand-worked example; the product against numpy float64 matmul of the
- * dequantised matrix and exact power-of-two cases.
+ * dequantised matrix and exact power-of-two cases; the greedy choice against
+ * the built-in max and numpy's argmax (ties, NaN, infinities, signed zeros).
  */
 #include <math.h>
 #include <pthread.h>
@@ -307,4 +308,44 @@ void orc_e4m3_encode_n(const float *s, int64_t n, uint8_t *out) {
 
 void orc_e2m1_encode_n(const float *v, int64_t n, uint8_t *out) {
     for (int64_t i = 0; i < n; ++i) out[i] = orc_e2m1_encode(v[i]);
+}
+
+/* --------------------------------------------------------- greedy choice */
+
+/* Greedy decoding takes, for the last position, the vocabulary entry with
+ * the largest logit (page "1. The big picture", steps 4 and 5: the final
+ * vector times the vocabulary matrix gives one score per entry; greedy
+ * decoding always picks the most likely). Per row: the first index whose
+ * value is not below any other; a NaN ranks above every number (the first
+ * NaN wins) and -0 equals +0. */
+static int ranks_above_f64(double a, double b) {
+    if (isnan(b)) return 0;
+    if (isnan(a)) return 1;
+    return a > b;
+}
+
+static int ranks_above_f32(float a, float b) {
+    if (isnan(b)) return 0;
+    if (isnan(a)) return 1;
+    return a > b;
+}
+
+void orc_argmax_rows_f64(const double *y, int64_t M, int64_t N, int64_t ldy, int32_t *idx) {
+    for (int64_t m = 0; m < M; ++m) {
+        const double *row = y + m * ldy;
+        int64_t best = 0;
+        for (int64_t n = 1; n < N; ++n)
+            if (ranks_above_f64(row[n], row[best])) best = n;
+        idx[m] = (int32_t)best;
+    }
+}
+
+void orc_argmax_rows_f32(const float *y, int64_t M, int64_t N, int64_t ldy, int32_t *idx) {
+    for (int64_t m = 0; m < M; ++m) {
+        const float *row = y + m * ldy;
+        int64_t best = 0;
+        for (int64_t n = 1; n < N; ++n)
+            if (ranks_above_f32(row[n], row[best])) best = n;
+        idx[m] = (int32_t)best;
+    }
 }

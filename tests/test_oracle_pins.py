@@ -290,3 +290,42 @@ def test_tile_pads_ragged_shapes_with_zeros():
     pt, st = t[:, :4096].ravel(), t[:, 4096:].ravel()
     assert np.count_nonzero(pt) == N * K // 2 and np.count_nonzero(st) == N * K // 16
     assert np.array_equal(np.sort(pt[pt != 0]), np.sort(p.ravel()))
+
+
+# ------------------------------------------------------------- greedy choice
+# Greedy decoding picks the largest logit of the last position (page "1. The
+# big picture", steps 4 and 5). The oracle's rule: the first index of the
+# largest value, NaN above every number, -0 equal to +0.
+def test_argmax_rows_matches_python_max_with_ties():
+    rng = np.random.default_rng(123)
+    for N in (1, 2, 7, 64, 1000):
+        y = rng.integers(-3, 4, size=(5, N)).astype(np.float32)   # many equal values
+        got = oracle.argmax_rows(y)
+        for m in range(5):
+            row = [float(v) for v in y[m]]
+            # the built-in max returns the first maximal item it meets
+            assert got[m] == max(range(N), key=lambda n: row[n])
+
+
+def test_argmax_rows_matches_numpy_with_nan_inf_and_signed_zero():
+    rng = np.random.default_rng(7)
+    for dt in (np.float64, np.float32):
+        y = rng.standard_normal((6, 300)).astype(dt)
+        y[1, 17] = np.nan
+        y[1, 200] = np.nan            # the first NaN wins
+        y[2, :] = 0.0
+        y[2, 0] = -0.0                # -0 ties with +0: index 0
+        y[3, :] = -np.inf
+        y[3, 9] = -1e30               # the only finite value
+        y[4, 250] = np.inf
+        y[5, :] = y[5, 123]           # a constant row: index 0
+        got = oracle.argmax_rows(y)
+        assert np.array_equal(got, np.argmax(y, axis=1).astype(np.int32))
+        assert got.tolist() == [int(np.argmax(y[0])), 17, 0, 9, 250, 0]
+
+
+def test_argmax_rows_decides_in_the_given_precision():
+    y64 = np.array([[1.0, 1.0 + 2.0 ** -40, 0.5]])
+    assert oracle.argmax_rows(y64).tolist() == [1]
+    # both round to 1.0 in fp32: the first one wins
+    assert oracle.argmax_rows(y64.astype(np.float32)).tolist() == [0]
