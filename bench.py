@@ -309,6 +309,15 @@ def other_workloads(fp4, copies, x_in0, x_mid0, timed, graph_of, gpu_bf16, dev):
         B = weight_bytes(151936, 1024)
         line({"workload": "LM head 151936x1024", "M": M, "us": round(t * 1e6, 3), "weight_GBps": round(B / t / 1e9, 1),
               "pct_of_hbm_peak": round(100 * B / t / 1e9 / HBM_PEAK_GBPS, 2)})
+        # the greedy step: the same product, then the per-row argmax of the logits
+        idx = torch.empty((M,), dtype=torch.int32, device=dev)
+        g = graph_of(lambda i, x=x, y=y, idx=idx: fp4.lm_head_greedy(x, lcp[i % len(lcp)], logits=y, out=idx),
+                     len(lcp) * 8)
+        g.replay()
+        t2 = timed(g.replay, 5) / (5 * len(lcp) * 8)
+        line({"workload": "LM head 151936x1024 + greedy choice (logits, then per-row argmax)", "M": M,
+              "us": round(t2 * 1e6, 3), "argmax_added_us": round((t2 - t) * 1e6, 3),
+              "weight_GBps": round(B / t2 / 1e9, 1), "pct_of_hbm_peak": round(100 * B / t2 / 1e9 / HBM_PEAK_GBPS, 2)})
     del lcp, base
     # ---- prefill: 2048 tokens x gate_up 5120 -> 34816 (gate and up launches)
     xp = gpu_bf16(x_bits(workload("prefill").x("x")))

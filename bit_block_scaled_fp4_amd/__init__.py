@@ -7,7 +7,7 @@ memory and streams. There is no CPU fallback: without the built library the
 import fails, and CPU tensors are rejected.
 
 Names follow the C ABI: quantize, retile, gemv, gemv_multi, gemm_prefill,
-layout_bytes.
+argmax_rows, lm_head_greedy, layout_bytes.
 """
 from __future__ import annotations
 
@@ -46,7 +46,10 @@ _lib.fp4_retile.argtypes = [_P, _P, _I64, _I64, _P, _P, _P]
 _lib.fp4_gemv.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]
 _lib.fp4_gemv_multi.argtypes = [ctypes.POINTER(_Proj), _I, _P, _I64, _I64, _P]
 _lib.fp4_gemm_prefill.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]
-for _f in ("fp4_layout_bytes", "fp4_quantize", "fp4_retile", "fp4_gemv", "fp4_gemv_multi", "fp4_gemm_prefill"):
+_lib.fp4_argmax_rows.argtypes = [_P, _P, _I64, _I64, _I64, _P]
+_lib.fp4_lm_head_greedy.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]
+for _f in ("fp4_layout_bytes", "fp4_quantize", "fp4_retile", "fp4_gemv", "fp4_gemv_multi", "fp4_gemm_prefill",
+           "fp4_argmax_rows", "fp4_lm_head_greedy"):
     getattr(_lib, _f).restype = _I
 
 
@@ -137,7 +140,17 @@ def _tiled(w: NVFP4Weight) -> None:
 def _x2d(x: torch.Tensor):
     if x.dim() == 1:
         x = x.view(1, -1)
+    if x.dim() != 2:
+        raise ValueError("x must be [K] or [M][K]")
     return x, x.shape[0], x.shape[1]
+
+
+def _out(out: Optional[torch.Tensor], shape, dtype, device, name: str) -> torch.Tensor:
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s (got %s)" % (name, tuple(shape), tuple(out.shape)))
+    return out
 
 
 def gemv(x: torch.Tensor, w: NVFP4Weight, out: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -145,8 +158,7 @@ def gemv(x: torch.Tensor, w: NVFP4Weight, out: Optional[torch.Tensor] = None) ->
     x, M, K = _x2d(x)
     if K != w.K:
         raise ValueError("x has K=%d, weight has K=%d" % (K, w.K))
-    if out is None:
-        out = torch.empty((M, w.N), dtype=torch.float32, device=x.device)
+    out = _out(out, (M, w.N), torch.float32, x.device, "out")
     _tiled(w)
     _check(_lib.fp4_gemv(_dev(out, "y", torch.float32), _dev(x, "x", torch.bfloat16), _dev(w.packed, "packed"),
                          None, _dev(w.gscale, "gscale", torch.float32), M, w.N, K, _stream(x.device)), "fp4_gemv")
@@ -180,8 +192,7 @@ def gemm_prefill(x: torch.Tensor, w: NVFP4Weight, out: Optional[torch.Tensor] = 
     x, M, K = _x2d(x)
     if K != w.K:
         raise ValueError("x has K=%d, weight has K=%d" % (K, w.K))
-    if out is None:
-        out = torch.empty((M, w.N), dtype=torch.float32, device=x.device)
+    out = _out(out, (M, w.N), torch.float32, x.device, "out")
     _tiled(w)
     _check(_lib.fp4_gemm_prefill(_dev(out, "y", torch.float32), _dev(x, "x", torch.bfloat16),
                                  _dev(w.packed, "packed"), None, _dev(w.gscale, "gscale", torch.float32), M, w.N, K,
@@ -189,10 +200,41 @@ def gemm_prefill(x: torch.Tensor, w: NVFP4Weight, out: Optional[torch.Tensor] = 
     return out
 
 
+def argmax_rows(y: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp4_argmax_rows: int32 [M], per row of fp32 y [M][N] (or [N]) the first
+    index of the largest value (NaN above every number, -0 equal to +0)."""
+    y2 = y.view(1, -1) if y.dim() == 1 else y
+    if y2.dim() != 2:
+        raise ValueError("y must be [N] or [M][N]")
+    M, N = y2.shape
+    out = _out(out, (M,), torch.int32, y.device, "out")
+    _check(_lib.fp4_argmax_rows(_dev(out, "idx", torch.int32), _dev(y2, "y", torch.float32), M, N, N,
+                                _stream(y.device)), "fp4_argmax_rows")
+    return out
+
+
+def lm_head_greedy(x: torch.Tensor, w: NVFP4Weight, logits: Optional[torch.Tensor] = None,
+                   out: Optional[torch.Tensor] = None):
+    """fp4_lm_head_greedy: (idx int32 [M], logits fp32 [M][N]) with logits =
+    x @ dequant(w)^T and idx the greedy choice of each row."""
+    x, M, K = _x2d(x)
+    if K != w.K:
+        raise ValueError("x has K=%d, weight has K=%d" % (K, w.K))
+    logits = _out(logits, (M, w.N), torch.float32, x.device, "logits")
+    out = _out(out, (M,), torch.int32, x.device, "out")
+    _tiled(w)
+    _check(_lib.fp4_lm_head_greedy(_dev(out, "idx", torch.int32), _dev(logits, "logits", torch.float32),
+                                   _dev(x, "x", torch.bfloat16), _dev(w.packed, "packed"), None,
+                                   _dev(w.gscale, "gscale", torch.float32), M, w.N, K, _stream(x.device)),
+           "fp4_lm_head_greedy")
+    return out, logits
+
+
 def raw():
     """The ctypes handle of libfp4.so (for tests that call the C ABI directly)."""
     return _lib
 
 
-__all__ = ["quantize", "retile", "gemv", "gemv_multi", "gemm_prefill", "layout_bytes", "NVFP4Weight",
+__all__ = ["quantize", "retile", "gemv", "gemv_multi", "gemm_prefill", "argmax_rows", "lm_head_greedy",
+           "layout_bytes", "NVFP4Weight",
            "Fp4Error", "raw", "ROWMAJOR", "TILED", "LIB_PATH", "HEADER_PATH"]

@@ -132,4 +132,24 @@ int fp4_gemm_prefill(float* y, const void* x_bf16, const void* packed, const voi
                                         gscale, M, N, K, static_cast<hipStream_t>(stream)));
 }
 
+int fp4_argmax_rows(int32_t* idx, const float* y, int64_t M, int64_t N, int64_t ldy, void* stream) {
+  if (!idx || !y) return FP4_ERR_NULL;
+  if (M < 1 || M > kMaxM || N < 1 || N > kMaxN || ldy < N || M * ldy > kMaxElems) return FP4_ERR_SHAPE;
+  if (!aligned(y, 4) || !aligned(idx, 4)) return FP4_ERR_ALIGN;
+  return hip_status(fp4::launch_argmax(idx, y, M, N, ldy, static_cast<hipStream_t>(stream)));
+}
+
+int fp4_lm_head_greedy(int32_t* idx, float* logits, const void* x_bf16, const void* packed, const void* scales,
+                       const float* gscale, int64_t M, int64_t N, int64_t K, void* stream) {
+  // every argument is checked before the first launch
+  if (!idx || !logits || !x_bf16 || !packed || !gscale) return FP4_ERR_NULL;
+  if (int st = check_nk(N, K)) return st;
+  if (M < 1 || M > kMaxM || M * N > kMaxElems) return FP4_ERR_SHAPE;
+  if (!aligned(idx, 4) || !aligned(logits, 4) || !aligned(x_bf16, 16) || !aligned(packed, 16) ||
+      !aligned(gscale, 4))
+    return FP4_ERR_ALIGN;
+  if (int st = fp4_gemv(logits, x_bf16, packed, scales, gscale, M, N, K, stream)) return st;
+  return fp4_argmax_rows(idx, logits, M, N, N, stream);
+}
+
 }  // extern "C"

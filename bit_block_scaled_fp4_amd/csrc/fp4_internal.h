@@ -67,4 +67,9 @@ hipError_t launch_gemv_mma(const GemvArgs& a, hipStream_t s, int ppw = 0);   // 
 hipError_t launch_prefill(float* y, const uint16_t* x, const uint8_t* tiles, const float* gscale, int64_t M,
                           int64_t N, int64_t K, hipStream_t s, int bn = 0);
 
+// Greedy choice per row of fp32 y [M][N] (row stride ldy): idx[m] = the first
+// index of the largest value. Rows longer than one workgroup's segment use a
+// per-device workspace allocated on first need and kept.
+hipError_t launch_argmax(int32_t* idx, const float* y, int64_t M, int64_t N, int64_t ldy, hipStream_t s);
+
 }  // namespace fp4

@@ -178,6 +178,30 @@ FP4_API int fp4_gemv_multi(const fp4_proj *projs, int nproj, const void *x_bf16,
 FP4_API int fp4_gemm_prefill(float *y, const void *x_bf16, const void *packed, const void *scales,
                      const float *gscale, int64_t M, int64_t N, int64_t K, void *stream);
 
+/* Greedy next-token choice: idx[m] = the first n with y[m][n] not below any
+ * other element of row m, for fp32 y [M][N] (device, row stride ldy >= N);
+ * a NaN ranks above every number (the first NaN wins) and -0 equals +0.
+ * The last vector of a decode step times the vocabulary matrix gives one
+ * logit per vocabulary entry and greedy decoding picks the most likely
+ * (page "1. The big picture", steps 4 and 5). idx is int32 [M] (device).
+ * Rows longer than 4096 elements are split over several workgroups whose
+ * partial results meet in a per-device workspace (8 bytes per workgroup
+ * plus 128 bytes per row), allocated with hipMalloc on the first call that
+ * needs it (or needs more) and kept until the process ends, under the same
+ * rules as the fp4_gemv workspace above: no graph capture during that first
+ * call, and calls on different streams of one device must not overlap.
+ * The result is deterministic. Limits: 1 <= N <= 2^28, 1 <= M <= 2^24,
+ * M * ldy <= 2^40. */
+FP4_API int fp4_argmax_rows(int32_t *idx, const float *y, int64_t M, int64_t N, int64_t ldy, void *stream);
+
+/* The greedy decode step's last product and choice: logits [M][N] (fp32,
+ * device, overwritten) = fp4_gemv(x, W) for the TILED vocabulary matrix W
+ * [N][K], then idx = fp4_argmax_rows(logits). Two launches on `stream`
+ * (plus fp4_gemv's own); all arguments are checked before the first. */
+FP4_API int fp4_lm_head_greedy(int32_t *idx, float *logits, const void *x_bf16, const void *packed,
+                               const void *scales, const float *gscale, int64_t M, int64_t N, int64_t K,
+                               void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,7 +20,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert names == sorted(["fp4_status_string", "fp4_layout_bytes", "fp4_quantize", "fp4_retile", "fp4_gemv",
-                            "fp4_gemv_multi", "fp4_gemm_prefill"])
+                            "fp4_gemv_multi", "fp4_gemm_prefill", "fp4_argmax_rows", "fp4_lm_head_greedy"])
     lib = ctypes.CDLL(fp4.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -96,9 +96,30 @@ def test_quantize_retile_prefill_argument_errors():
     assert L.fp4_gemm_prefill(A, A, A, A, A, 4, 1 << 21, 32, None) == ESHAPE
 
 
+def test_argmax_and_greedy_argument_errors():
+    L = fp4.raw()
+    assert L.fp4_argmax_rows(None, A, 1, 8, 8, None) == ENULL
+    assert L.fp4_argmax_rows(A, None, 1, 8, 8, None) == ENULL
+    assert L.fp4_argmax_rows(A, A, 0, 8, 8, None) == ESHAPE
+    assert L.fp4_argmax_rows(A, A, 1, 0, 8, None) == ESHAPE
+    assert L.fp4_argmax_rows(A, A, 2, 8, 7, None) == ESHAPE          # row stride below N
+    assert L.fp4_argmax_rows(A, A, 1, 1 << 29, 1 << 29, None) == ESHAPE
+    assert L.fp4_argmax_rows(A + 2, A, 1, 8, 8, None) == EALIGN
+    assert L.fp4_argmax_rows(A, A + 1, 1, 8, 8, None) == EALIGN
+    # the greedy step checks everything before its first launch
+    assert L.fp4_lm_head_greedy(None, A, A, A, None, A, 1, 8, 32, None) == ENULL
+    assert L.fp4_lm_head_greedy(A, None, A, A, None, A, 1, 8, 32, None) == ENULL
+    assert L.fp4_lm_head_greedy(A, A, A, A, None, A, 1, 8, 24, None) == ESHAPE
+    assert L.fp4_lm_head_greedy(A, A, A, A, None, A, 0, 8, 32, None) == ESHAPE
+    assert L.fp4_lm_head_greedy(A + 2, A, A, A, None, A, 1, 8, 32, None) == EALIGN
+    assert L.fp4_lm_head_greedy(A, A, A + 8, A, None, A, 1, 8, 32, None) == EALIGN
+
+
 def test_binding_rejects_cpu_tensors():
     import torch
     W = torch.zeros(8, 32, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU tensor"):
         fp4.quantize(W, out=fp4.NVFP4Weight(torch.zeros(1, dtype=torch.uint8), torch.zeros(1, dtype=torch.uint8),
                                             torch.zeros(1), 8, 32))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fp4.argmax_rows(torch.zeros(4, 8))

@@ -306,3 +306,78 @@ def test_errors_raise_on_gpu():
         fp4.quantize(W, out=fp4.NVFP4Weight(torch.zeros(64, dtype=torch.uint8, device=dev()),
                                             torch.zeros(64, dtype=torch.uint8, device=dev()),
                                             torch.zeros(1, device=dev()), 8, 24))
+
+
+# ------------------------------------------------------------- greedy choice
+def planted_rows(M, N, seed):
+    """fp32 rows with the cases the order rule decides: ties of the maximum,
+    NaNs, signed zeros, infinities, a constant row, an all -inf row."""
+    rng = np.random.default_rng(seed)
+    y = rng.standard_normal((M, N)).astype(np.float32)
+    for m in range(M):
+        kind = m % 7
+        if kind == 1:                                   # the maximum at up to three places
+            y[m, rng.choice(N, size=min(3, N), replace=False)] = y[m].max() + 1.0
+        elif kind == 2:                                 # two NaNs: the first wins
+            a, b = sorted(rng.choice(N, size=2, replace=N < 2))
+            y[m, a] = np.nan
+            y[m, b] = np.float32(-np.nan)
+        elif kind == 3:                                 # only signed zeros: index 0
+            y[m] = np.where(rng.random(N) < 0.5, np.float32(-0.0), np.float32(0.0))
+        elif kind == 4:                                 # +inf twice
+            y[m, rng.choice(N, size=min(2, N), replace=False)] = np.inf
+        elif kind == 5:                                 # a constant row
+            y[m] = np.float32(0.25)
+        elif kind == 6:
+            y[m] = -np.inf
+    return y
+
+
+# segments of 4096 elements per workgroup: one, exactly one, one plus one,
+# several with a ragged tail, the vocabulary size, a long row
+@pytest.mark.parametrize("M,N", [(1, 1), (7, 31), (7, 4096), (7, 4097), (9, 3 * 4096 + 5), (8, 151936),
+                                 (2, 1 << 20)])
+def test_argmax_rows_bit_exact(M, N):
+    y = planted_rows(M, N, seed=M * 1000003 + N)
+    got = fp4.argmax_rows(torch.from_numpy(y).to(dev())).cpu().numpy()
+    assert np.array_equal(got, oracle.argmax_rows(y))
+
+
+def test_argmax_rows_strided_and_repeated():
+    """Row stride above N through the C ABI; repeated launches of different
+    sizes (the per-row counters must come back to zero every time)."""
+    L = fp4.raw()
+    stream = torch.cuda.current_stream().cuda_stream
+    for M, N, ldy in [(3, 10000, 10007), (8, 151936, 151936), (3, 10000, 10007), (40, 9000, 9001), (1, 4097, 4100),
+                      (3, 10000, 10007)]:
+        y = planted_rows(M, ldy, seed=N + ldy + M)
+        y[:, N:] = np.inf                                # past N: must be ignored
+        idx = torch.full((M,), -1, dtype=torch.int32, device=dev())
+        yt = torch.from_numpy(y).to(dev())
+        assert L.fp4_argmax_rows(idx.data_ptr(), yt.data_ptr(), M, N, ldy, stream) == 0
+        assert np.array_equal(idx.cpu().numpy(), oracle.argmax_rows(np.ascontiguousarray(y[:, :N]))), (M, N, ldy)
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_lm_head_greedy_workload(M):
+    """The greedy step on the LM head 151936 x 1024: the logits within the
+    product tolerance; the index bit-exact against the oracle's choice on the
+    same fp32 logits; and against the fp64 logits, a value within the two
+    tolerances of the true maximum (equal to it where the top two are
+    further apart than that)."""
+    bw, bx = weight_bits("lm_head", "w"), act_bits("lm_head", "x_m%d" % M)
+    w = gpu_quant(bw)
+    idx, logits = fp4.lm_head_greedy(to_gpu_bf16(bx), w)
+    torch.cuda.synchronize()
+    idx, lg = idx.cpu().numpy(), logits.cpu().numpy()
+    p, s, g = oracle_quant("lm_head", "w")
+    yr, l1 = oracle.gemv(bx, p, s, g, threads=THREADS)
+    assert_within_tolerance(lg, yr, l1, "lm_head logits M=%d" % M)
+    assert np.array_equal(idx, oracle.argmax_rows(lg))
+    ref = oracle.argmax_rows(yr)
+    for m in range(M):
+        tol = 2e-3 * (l1[m, idx[m]] + l1[m, ref[m]])
+        assert yr[m, idx[m]] >= yr[m, ref[m]] - tol
+        second = np.partition(yr[m], -2)[-2]
+        if yr[m, ref[m]] - second > 2e-3 * 2 * l1[m].max():
+            assert idx[m] == ref[m]
