@@ -50,6 +50,10 @@ def _L():
         lib.orc_e2m1_encode.restype = ctypes.c_uint8
         lib.orc_quantize.argtypes = [P, I64, I64, P, P, P]
         lib.orc_quantize.restype = ctypes.c_int
+        lib.orc_quantize_fp8.argtypes = [P, ctypes.c_float, I64, I64, P, P, P]
+        lib.orc_quantize_fp8.restype = ctypes.c_int
+        lib.orc_quantize_f32.argtypes = [P, I64, I64, P, P, P]
+        lib.orc_quantize_f32.restype = ctypes.c_int
         lib.orc_dequant.argtypes = [P, P, ctypes.c_float, I64, I64, P]
         lib.orc_dequant.restype = None
         lib.orc_gemv.argtypes = [P, I64, P, P, ctypes.c_float, I64, I64, P, P, ctypes.c_int]
@@ -113,6 +117,32 @@ def quantize(W_bits: np.ndarray):
     if rc != 0:
         raise ValueError("orc_quantize: bad shape %r" % (W.shape,))
     return packed, scales, np.float32(g[0])
+
+
+def _quantize_with(fn, W: np.ndarray, ptr, *lead):
+    N, K = W.shape
+    packed = np.empty((N, K // 2), dtype=np.uint8)
+    scales = np.empty((N, K // 16), dtype=np.uint8)
+    g = np.zeros(1, dtype=np.float32)
+    rc = fn(ptr, *lead, N, K, packed.ctypes.data, scales.ctypes.data, g.ctypes.data)
+    if rc != 0:
+        raise ValueError("quantize: bad shape %r" % (W.shape,))
+    return packed, scales, np.float32(g[0])
+
+
+def quantize_fp8(W_codes: np.ndarray, scale) -> tuple:
+    """FP8 E4M3 codes (uint8 [N][K]) with one fp32 dequantisation scale: the
+    element values E4M3(code) * scale (one fp32 rounding) go through the same
+    rule as quantize(). Returns (packed, scales, gscale)."""
+    W, pw = _c(W_codes, np.uint8)
+    L = _L()
+    return _quantize_with(lambda p, *a: L.orc_quantize_fp8(p, float(np.float32(scale)), *a), W, pw)
+
+
+def quantize_f32(W: np.ndarray) -> tuple:
+    """fp32 values [N][K] through the same rule as quantize()."""
+    W, pw = _c(W, np.float32)
+    return _quantize_with(_L().orc_quantize_f32, W, pw)
 
 
 def dequant(packed: np.ndarray, scales: np.ndarray, gscale) -> np.ndarray:

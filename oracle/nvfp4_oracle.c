@@ -26,6 +26,9 @@
  *   scale code = E4M3(s) rounded to nearest-even, saturating at 448;
  *   element code = E2M1(w / (E4M3(code)*gscale)) rounded to nearest-even.
  * Dequantised weight: E2M1(q) * E4M3(sc) * gscale.
+ * Sources: bf16 weights, or a checkpoint released in FP8 (E4M3 codes and one
+ * fp32 dequantisation scale per tensor; element value E4M3(code) * scale,
+ * rounded once to fp32), which the imp README's quantiser also accepts.
  * Product: y[m][n] = sum_k dequant(W)[n][k] * x[m][k], here in fp64.
  *
  * Readings where the definition above leaves a choice (each is listed with
@@ -44,7 +47,10 @@
  * against brute-force nearest search; quantiser round-trip invariants and a
  * hand-worked example; the product against numpy float64 matmul of the
  * dequantised matrix and exact power-of-two cases; the greedy choice against
- * the built-in max and numpy's argmax (ties, NaN, infinities, signed zeros).
+ * the built-in max and numpy's argmax (ties, NaN, infinities, signed zeros);
+ * the FP8 source against the bf16 path (power-of-two scales, exact in bf16)
+ * and against fp32 values rounded by numpy (other scales), with torch's E4M3
+ * decode, and the sign flip under a negated scale.
  */
 #include <math.h>
 #include <pthread.h>
@@ -137,18 +143,41 @@ static float bf16_to_f32(uint16_t h) {
     return f;
 }
 
-/* Quantise W (bf16 bits, [N][K] row-major) into the canonical layout.
+/* Where the values to quantise come from: bf16 bit patterns, FP8 E4M3 codes
+ * times one fp32 dequantisation scale (a checkpoint released in FP8: the
+ * imp README says its quantiser builds NVFP4 weights from BF16 or FP8
+ * releases), or fp32 values as they are. Every kind yields one fp32 value per
+ * element; the quantisation steps below do not depend on the kind. */
+typedef struct {
+    int kind;                 /* 0: bf16, 1: fp8 E4M3 codes * scale, 2: fp32 */
+    const uint16_t *bf16;
+    const uint8_t *fp8;
+    float fp8_scale;
+    const float *f32;
+} src_t;
+
+static float src_value(const src_t *src, int64_t i) {
+    if (src->kind == 0) return bf16_to_f32(src->bf16[i]);
+    if (src->kind == 1) {
+        /* E4M3 decodes exactly to fp32; the product is one rounding */
+        volatile float w = (float)E4M3_TAB[src->fp8[i]] * src->fp8_scale;
+        return w;
+    }
+    return src->f32[i];
+}
+
+/* Quantise the [N][K] row-major values of `src` into the canonical layout.
  * Returns 0, or -1 if K is not a multiple of 16 or a size is negative.
  * Every arithmetic step is one fp32 operation, rounded to nearest-even
  * (this file is compiled with -ffp-contract=off and without fast-math). */
-int orc_quantize(const uint16_t *W, int64_t N, int64_t K, uint8_t *packed, uint8_t *scales,
-                 float *gscale_out) {
+static int quantize_src(const src_t *src, int64_t N, int64_t K, uint8_t *packed, uint8_t *scales,
+                        float *gscale_out) {
     tables();
     if (N < 0 || K < 0 || K % 16 != 0) return -1;
     /* 1. tensor amax (exact) */
     float amax = 0.0f;
     for (int64_t i = 0; i < N * K; ++i) {
-        float a = fabsf(bf16_to_f32(W[i]));
+        float a = fabsf(src_value(src, i));
         if (a > amax) amax = a;
     }
     /* 2. tensor scale */
@@ -162,11 +191,12 @@ int orc_quantize(const uint16_t *W, int64_t N, int64_t K, uint8_t *packed, uint8
     *gscale_out = gscale;
     for (int64_t n = 0; n < N; ++n) {
         for (int64_t b = 0; b < K / 16; ++b) {
-            const uint16_t *wb = W + n * K + b * 16;
+            float wb[16];
+            for (int j = 0; j < 16; ++j) wb[j] = src_value(src, n * K + b * 16 + j);
             /* 3. block amax and scale */
             float bamax = 0.0f;
             for (int j = 0; j < 16; ++j) {
-                float a = fabsf(bf16_to_f32(wb[j]));
+                float a = fabsf(wb[j]);
                 if (a > bamax) bamax = a;
             }
             volatile float t = bamax / 6.0f;
@@ -181,7 +211,7 @@ int orc_quantize(const uint16_t *W, int64_t N, int64_t K, uint8_t *packed, uint8
                     codes[j] = 0;
                 } else {
                     volatile float d = s_dec * gscale;
-                    volatile float v = bf16_to_f32(wb[j]) / d;
+                    volatile float v = wb[j] / d;
                     codes[j] = orc_e2m1_encode(v);
                 }
             }
@@ -191,6 +221,28 @@ int orc_quantize(const uint16_t *W, int64_t N, int64_t K, uint8_t *packed, uint8
         }
     }
     return 0;
+}
+
+/* W: bf16 bits [N][K]. */
+int orc_quantize(const uint16_t *W, int64_t N, int64_t K, uint8_t *packed, uint8_t *scales,
+                 float *gscale_out) {
+    src_t src = {0, W, NULL, 0.0f, NULL};
+    return quantize_src(&src, N, K, packed, scales, gscale_out);
+}
+
+/* W: FP8 E4M3 codes [N][K], element value E4M3(code) * scale (fp32). The
+ * NaN codes 0x7F and 0xFF are outside the domain, like non-finite bf16. */
+int orc_quantize_fp8(const uint8_t *W, float scale, int64_t N, int64_t K, uint8_t *packed, uint8_t *scales,
+                     float *gscale_out) {
+    src_t src = {1, NULL, W, scale, NULL};
+    return quantize_src(&src, N, K, packed, scales, gscale_out);
+}
+
+/* W: fp32 values [N][K] (finite). */
+int orc_quantize_f32(const float *W, int64_t N, int64_t K, uint8_t *packed, uint8_t *scales,
+                     float *gscale_out) {
+    src_t src = {2, NULL, NULL, 0.0f, W};
+    return quantize_src(&src, N, K, packed, scales, gscale_out);
 }
 
 /* Dequantised weights, fp64 [N][K]. */

@@ -329,3 +329,55 @@ def test_argmax_rows_decides_in_the_given_precision():
     assert oracle.argmax_rows(y64).tolist() == [1]
     # both round to 1.0 in fp32: the first one wins
     assert oracle.argmax_rows(y64.astype(np.float32)).tolist() == [0]
+
+
+# ------------------------------------------------------- FP8-sourced weights
+# A checkpoint released in FP8 (imp README: the quantiser builds NVFP4 weights
+# from BF16 or FP8 releases) holds E4M3 codes and a dequantisation scale; the
+# element values E4M3(code) * scale, rounded once to fp32, go through the same
+# quantisation rule. The E4M3 decode below is torch's, not the oracle's.
+def fp8_codes(shape, seed):
+    rng = np.random.default_rng(seed)
+    c = rng.integers(0, 256, size=shape, dtype=np.uint8)
+    c[(c & 0x7F) == 0x7F] = 0x7E          # no NaN codes (outside the domain)
+    c.flat[::97] = 0                       # some zeros
+    c.flat[5::131] = 0x80                  # and negative zeros
+    return c
+
+
+def torch_e4m3_values(codes):
+    return torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+
+
+def test_quantize_fp8_with_power_of_two_scale_equals_bf16_path():
+    codes = fp8_codes((24, 2048 + 64), seed=11)
+    s = np.float32(2.0 ** -5)
+    vals = torch_e4m3_values(codes) * s                 # exact: 4 significant bits, scaled by a power of two
+    bits = float32_to_bf16_bits(vals)
+    assert np.array_equal(bf16_to_float32(bits), vals)  # exactly representable in bf16
+    a, b = oracle.quantize_fp8(codes, s), oracle.quantize(bits)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[2] == b[2]
+
+
+def test_quantize_fp8_rounds_each_product_once_to_fp32():
+    codes = fp8_codes((16, 1024 + 32), seed=12)
+    for s in (np.float32(0.0137), np.float32(3.3e-3), np.float32(1.7e3)):
+        vals = (torch_e4m3_values(codes) * s).astype(np.float32)   # numpy: one fp32 rounding per product
+        a, b = oracle.quantize_fp8(codes, s), oracle.quantize_f32(vals)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[2] == b[2]
+
+
+def test_quantize_fp8_sign_and_zero_scale():
+    codes = fp8_codes((8, 512), seed=13)
+    s = np.float32(0.021)
+    pos, neg = oracle.quantize_fp8(codes, s), oracle.quantize_fp8(codes, -s)
+    # every value changes sign (zeros too: 0 * -s = -0), so every code's sign bit flips
+    assert np.array_equal(neg[0], pos[0] ^ 0x88) and np.array_equal(neg[1], pos[1]) and neg[2] == pos[2]
+    z = oracle.quantize_fp8(codes, np.float32(0.0))
+    assert not z[0].any() and not z[1].any() and z[2] == 0.0
+
+
+def test_quantize_f32_entry_equals_bf16_entry():
+    bits = tensor_bits(workload("gemv_1024").tensor("w"))[:64]
+    a, b = oracle.quantize_f32(bf16_to_float32(bits)), oracle.quantize(bits)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[2] == b[2]
