@@ -364,6 +364,27 @@ def other_workloads(fp4, copies, x_in0, x_mid0, timed, graph_of, gpu_bf16, dev):
           "us_per_decode_layer": round(t * 1e6, 3), "weight_GBps": round(B / t / 1e9, 1),
           "pct_of_hbm_peak": round(100 * B / t / 1e9 / HBM_PEAK_GBPS, 2), "launches_per_layer": 4})
     del sets, layers
+    # ---- load-time quantisation of the 27B down projection (5120 x 17408) from bf16 and from an FP8 release.
+    # The rule needs the tensor amax before any block can be encoded, so the input is read twice; the
+    # algorithmic bytes are 2 input reads + the 9/16 byte per element written.
+    from workloads import fp8_release
+    Nq, Kq = HIDDEN, INTER
+    Wb = gpu_bf16(tensor_bits(workload("dense27b_layer").tensor("down")))
+    codes, sc = fp8_release((Nq, Kq), 32, 0.015, outlier_p=0.001, outlier_scale=20)
+    Wf = torch.from_numpy(codes).to(dev)
+    Sf = torch.tensor([float(sc)], dtype=torch.float32, device=dev)
+    for name, ebytes, q in (("bf16", 2, lambda o: fp4.quantize(Wb, "tiled", out=o)),
+                            ("fp8 E4M3 + tensor scale", 1, lambda o: fp4.quantize_fp8(Wf, Sf, "tiled", out=o))):
+        o = q(None)
+        g = graph_of(lambda i, q=q, o=o: q(o), 4)
+        g.replay()
+        t = timed(g.replay, 5) / (5 * 4)
+        alg = 2 * ebytes * Nq * Kq + weight_bytes(Nq, Kq)
+        line({"workload": "load-time NVFP4 quantisation, 5120x17408 from %s (tiled output)" % name,
+              "us": round(t * 1e6, 2), "input_GBps": round(ebytes * Nq * Kq / t / 1e9, 1),
+              "algorithmic_GBps": round(alg / t / 1e9, 1), "pct_of_hbm_peak": round(100 * alg / t / 1e9 / HBM_PEAK_GBPS, 2)})
+        del o
+    del Wb, Wf
     # ---- single 1024 x 1024 GEMV (latency)
     w0 = workload("gemv_1024")
     base = fp4.quantize(gpu_bf16(tensor_bits(w0.tensor("w"))), "tiled")

@@ -6,7 +6,7 @@ the tensors' device, on torch's current stream. PyTorch supplies device
 memory and streams. There is no CPU fallback: without the built library the
 import fails, and CPU tensors are rejected.
 
-Names follow the C ABI: quantize, retile, gemv, gemv_multi, gemm_prefill,
+Names follow the C ABI: quantize, quantize_fp8, retile, gemv, gemv_multi, gemm_prefill,
 argmax_rows, lm_head_greedy, layout_bytes.
 """
 from __future__ import annotations
@@ -42,13 +42,14 @@ _lib.fp4_status_string.argtypes = [_I]
 _lib.fp4_status_string.restype = ctypes.c_char_p
 _lib.fp4_layout_bytes.argtypes = [_I64, _I64, _I, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
 _lib.fp4_quantize.argtypes = [_P, _I64, _I64, _I, _P, _P, _P, _P]
+_lib.fp4_quantize_fp8.argtypes = [_P, _P, _I64, _I64, _I, _P, _P, _P, _P]
 _lib.fp4_retile.argtypes = [_P, _P, _I64, _I64, _P, _P, _P]
 _lib.fp4_gemv.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]
 _lib.fp4_gemv_multi.argtypes = [ctypes.POINTER(_Proj), _I, _P, _I64, _I64, _P]
 _lib.fp4_gemm_prefill.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]
 _lib.fp4_argmax_rows.argtypes = [_P, _P, _I64, _I64, _I64, _P]
 _lib.fp4_lm_head_greedy.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]
-for _f in ("fp4_layout_bytes", "fp4_quantize", "fp4_retile", "fp4_gemv", "fp4_gemv_multi", "fp4_gemm_prefill",
+for _f in ("fp4_layout_bytes", "fp4_quantize", "fp4_quantize_fp8", "fp4_retile", "fp4_gemv", "fp4_gemv_multi", "fp4_gemm_prefill",
            "fp4_argmax_rows", "fp4_lm_head_greedy"):
     getattr(_lib, _f).restype = _I
 
@@ -116,6 +117,25 @@ def quantize(W: torch.Tensor, layout="tiled", out: Optional[NVFP4Weight] = None)
     _check(_lib.fp4_quantize(_dev(W, "W", torch.bfloat16), N, K, lay, _dev(out.packed, "packed", torch.uint8),
                              _opt(out.scales, "scales"), _dev(out.gscale, "gscale", torch.float32),
                              _stream(W.device)), "fp4_quantize")
+    return out
+
+
+def quantize_fp8(W: torch.Tensor, w_scale: torch.Tensor, layout="tiled",
+                 out: Optional[NVFP4Weight] = None) -> NVFP4Weight:
+    """fp4_quantize_fp8: FP8 E4M3 W [N][K] (torch.float8_e4m3fn or uint8 codes)
+    with its fp32 dequantisation scale (a 1-element GPU tensor) -> NVFP4Weight."""
+    N, K = W.shape
+    if W.dtype == torch.float8_e4m3fn:
+        W = W.view(torch.uint8)
+    lay = _LAYOUTS[layout]
+    if out is None:
+        pb, sb = layout_bytes(N, K, lay)
+        out = NVFP4Weight(torch.empty(pb, dtype=torch.uint8, device=W.device),
+                          torch.empty(sb, dtype=torch.uint8, device=W.device) if lay == ROWMAJOR else None,
+                          torch.empty(1, dtype=torch.float32, device=W.device), N, K, lay)
+    _check(_lib.fp4_quantize_fp8(_dev(W, "W", torch.uint8), _dev(w_scale, "w_scale", torch.float32), N, K, lay,
+                                 _dev(out.packed, "packed", torch.uint8), _opt(out.scales, "scales"),
+                                 _dev(out.gscale, "gscale", torch.float32), _stream(W.device)), "fp4_quantize_fp8")
     return out
 
 
@@ -235,6 +255,6 @@ def raw():
     return _lib
 
 
-__all__ = ["quantize", "retile", "gemv", "gemv_multi", "gemm_prefill", "argmax_rows", "lm_head_greedy",
+__all__ = ["quantize", "quantize_fp8", "retile", "gemv", "gemv_multi", "gemm_prefill", "argmax_rows", "lm_head_greedy",
            "layout_bytes", "NVFP4Weight",
            "Fp4Error", "raw", "ROWMAJOR", "TILED", "LIB_PATH", "HEADER_PATH"]

@@ -67,6 +67,22 @@ int fp4_quantize(const void* W_bf16, int64_t N, int64_t K, int layout, void* pac
                                          static_cast<hipStream_t>(stream)));
 }
 
+int fp4_quantize_fp8(const void* W_fp8, const float* w_scale, int64_t N, int64_t K, int layout, void* packed,
+                     void* scales, float* gscale, void* stream) {
+  if (layout != FP4_LAYOUT_ROWMAJOR && layout != FP4_LAYOUT_TILED) return FP4_ERR_LAYOUT;
+  if (!W_fp8 || !w_scale || !packed || !gscale || (layout == FP4_LAYOUT_ROWMAJOR && !scales)) return FP4_ERR_NULL;
+  if (int st = check_nk(N, K)) return st;
+  if (!aligned(W_fp8, 16) || !aligned(packed, layout == FP4_LAYOUT_TILED ? 16 : 8) || !aligned(gscale, 4) ||
+      !aligned(w_scale, 4))
+    return FP4_ERR_ALIGN;
+  // gscale is scratch while the kernels run and w_scale is read by them
+  if (static_cast<const void*>(w_scale) == static_cast<const void*>(gscale)) return FP4_ERR_UNSUPPORTED;
+  return hip_status(fp4::launch_quantize_fp8(static_cast<const uint8_t*>(W_fp8), w_scale, N, K,
+                                             layout == FP4_LAYOUT_TILED, static_cast<uint8_t*>(packed),
+                                             static_cast<uint8_t*>(scales), gscale,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 int fp4_retile(const void* packed_rm, const void* scales_rm, int64_t N, int64_t K, void* packed_tiled,
                void* scales_tiled, void* stream) {
   (void)scales_tiled;   // the tiled layout keeps the scales inside `packed_tiled`

@@ -52,6 +52,9 @@ struct GemvArgs {
 
 hipError_t launch_quantize(const uint16_t* W, int64_t N, int64_t K, bool tiled, uint8_t* packed,
                            uint8_t* scales, float* gscale, hipStream_t s);
+// The same rule for FP8 E4M3 codes times one fp32 scale (*w_scale, device).
+hipError_t launch_quantize_fp8(const uint8_t* W, const float* w_scale, int64_t N, int64_t K, bool tiled,
+                               uint8_t* packed, uint8_t* scales, float* gscale, hipStream_t s);
 hipError_t launch_retile(const uint8_t* packed, const uint8_t* scales, int64_t N, int64_t K, uint8_t* tiles,
                          hipStream_t s);
 // Vector-ALU product for M <= 4 activation rows (larger M: an error; those

@@ -8,10 +8,16 @@
 // (-fhip-fp32-correctly-rounded-divide-sqrt) and this file is compiled with
 // -ffp-contract=off so that no multiply is fused into an add.
 //
+// Sources: bf16 weights, or a checkpoint released in FP8 (the imp README's
+// quantiser builds NVFP4 weights from BF16 or FP8 releases): OCP E4M3 codes
+// and one fp32 dequantisation scale per tensor, element value
+// E4M3(code) * scale rounded once to fp32. The rule is the same for both.
+//
 // Launch sequence for one tensor, all on the caller's stream:
 //   1. k_amax_init   slot := 0
-//   2. k_amax        slot := max over W of the bf16 magnitude bits (atomic max;
-//                    bf16 magnitudes order like their bit patterns)
+//   2. k_amax        slot := max over W of the magnitude bits (atomic max;
+//                    bf16 and E4M3 magnitudes order like their bit patterns,
+//                    and rounding a product by a scale keeps that order)
 //   3. k_encode      one thread per 16-element block: block scale, codes, pack
 //   4. k_finalize    slot := amax / 2688  (the tensor scale gscale)
 #include "fp4_internal.h"
@@ -53,21 +59,78 @@ __device__ __forceinline__ uint32_t e2m1_code(float v) {
   return c | ((__float_as_uint(v) >> 28) & 8u);
 }
 
-__global__ void k_amax_init(uint32_t* slot) { *slot = 0u; }
-
-__global__ __launch_bounds__(256) void k_amax(const uint4* __restrict__ W, int64_t nvec,
-                                              uint32_t* slot) {
-  uint32_t m = 0;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += stride) {
-    const uint4 v = W[i];
+// The two sources. Each gives the 16 fp32 values of a block and their
+// largest magnitude, and turns the amax slot (largest magnitude bits) into
+// the tensor amax.
+struct SrcBf16 {
+  const uint16_t* W;
+  static constexpr int kPerVec = 8;   // elements per 16-byte load
+  __device__ static uint32_t vec_max(const uint4& v) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m = max(m, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
+    return m;
+  }
+  __device__ float amax(uint32_t slot) const { return bf16_bits_to_float(slot); }
+  __device__ float block(int64_t off, float (&w)[16]) const {
+    const uint4* src = reinterpret_cast<const uint4*>(W + off);
+    const uint4 a = src[0], c = src[1];
+    const uint32_t d[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+    uint32_t bm = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      w[2 * j] = bf16_bits_to_float(d[j] & 0xFFFFu);
+      w[2 * j + 1] = bf16_bits_to_float(d[j] >> 16);
+      bm = max(bm, max(d[j] & 0x7FFFu, (d[j] >> 16) & 0x7FFFu));
+    }
+    return bf16_bits_to_float(bm);
+  }
+};
+
+struct SrcFp8 {
+  const uint8_t* W;
+  const float* scale;   // device fp32, the checkpoint's dequantisation multiplier
+  static constexpr int kPerVec = 16;
+  __device__ static uint32_t vec_max(const uint4& v) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) m = max(m, (w[j] >> (8 * b)) & 0x7Fu);
+    return m;
+  }
+  // |RN(e * s)| = RN(|e| * |s|) grows with |e|: the largest code gives the amax
+  __device__ float amax(uint32_t slot) const {
+    return __fmul_rn(__builtin_amdgcn_cvt_f32_fp8((int)slot, 0), fabsf(*scale));
+  }
+  __device__ float block(int64_t off, float (&w)[16]) const {
+    const uint4 v = *reinterpret_cast<const uint4*>(W + off);
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+    const float s = *scale;
+    float bamax = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      m = max(m, w[j] & 0x7FFFu);
-      m = max(m, (w[j] >> 16) & 0x7FFFu);
+      w[4 * j + 0] = __fmul_rn(__builtin_amdgcn_cvt_f32_fp8((int)d[j], 0), s);
+      w[4 * j + 1] = __fmul_rn(__builtin_amdgcn_cvt_f32_fp8((int)d[j], 1), s);
+      w[4 * j + 2] = __fmul_rn(__builtin_amdgcn_cvt_f32_fp8((int)d[j], 2), s);
+      w[4 * j + 3] = __fmul_rn(__builtin_amdgcn_cvt_f32_fp8((int)d[j], 3), s);
     }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) bamax = fmaxf(bamax, fabsf(w[j]));
+    return bamax;
   }
+};
+
+__global__ void k_amax_init(uint32_t* slot) { *slot = 0u; }
+
+template <class Src>
+__global__ __launch_bounds__(256) void k_amax(const uint4* __restrict__ W, int64_t nvec, uint32_t* slot) {
+  uint32_t m = 0;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += stride)
+    m = max(m, Src::vec_max(W[i]));
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
   if ((threadIdx.x & 63) == 0 && m != 0u) atomicMax(slot, m);
@@ -75,9 +138,9 @@ __global__ __launch_bounds__(256) void k_amax(const uint4* __restrict__ W, int64
 
 // One thread per 16-element block. For the tiled layout the thread space is
 // the padded one (G*8 rows x C*64 blocks) so padding is written as zeros.
-__global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ W, int64_t N, int64_t K,
-                                                int tiled, uint8_t* __restrict__ packed,
-                                                uint8_t* __restrict__ scales,
+template <class Src>
+__global__ __launch_bounds__(256) void k_encode(const Src src, int64_t N, int64_t K, int tiled,
+                                                uint8_t* __restrict__ packed, uint8_t* __restrict__ scales,
                                                 const uint32_t* __restrict__ slot) {
   const int64_t kb = K / 16;                          // blocks per row
   const int64_t C = chunks_of(K);
@@ -88,21 +151,11 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ W, 
   const int64_t n = t / bpr, b = t % bpr;
 
   uint32_t sc = 0, lo = 0, hi = 0;  // scale code, packed bytes 0..3 and 4..7
-  const float amax = bf16_bits_to_float(*slot);
+  const float amax = src.amax(*slot);
   if (n < N && b < kb && amax != 0.0f) {
     const float gscale = amax / 2688.0f;
-    const uint4* src = reinterpret_cast<const uint4*>(W + n * K + b * 16);
-    uint32_t h[16];
-    {
-      const uint4 a = src[0], c = src[1];
-      const uint32_t d[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) { h[2 * j] = d[j] & 0xFFFFu; h[2 * j + 1] = d[j] >> 16; }
-    }
-    uint32_t bm = 0;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) bm = max(bm, h[j] & 0x7FFFu);
-    const float bamax = bf16_bits_to_float(bm);
+    float w[16];
+    const float bamax = src.block(n * K + b * 16, w);
     const float s = (bamax / 6.0f) / gscale;
     sc = e4m3_code(s);
     const float s_dec = __builtin_amdgcn_cvt_f32_fp8((int)sc, 0);   // OCP E4M3 decode
@@ -110,7 +163,7 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ W, 
       const float d = __fmul_rn(s_dec, gscale);
       uint32_t codes[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) codes[j] = e2m1_code(bf16_bits_to_float(h[j]) / d);
+      for (int j = 0; j < 16; ++j) codes[j] = e2m1_code(w[j] / d);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         lo |= (codes[2 * j] | (codes[2 * j + 1] << 4)) << (8 * j);
@@ -131,8 +184,9 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ W, 
   }
 }
 
-__global__ void k_finalize(uint32_t* slot) {
-  const float amax = bf16_bits_to_float(*slot);
+template <class Src>
+__global__ void k_finalize(const Src src, uint32_t* slot) {
+  const float amax = src.amax(*slot);
   *reinterpret_cast<float*>(slot) = amax / 2688.0f;   // 0 stays 0
 }
 
@@ -179,21 +233,33 @@ __global__ __launch_bounds__(256) void k_retile(const uint8_t* __restrict__ pack
 
 }  // namespace
 
-hipError_t launch_quantize(const uint16_t* W, int64_t N, int64_t K, bool tiled, uint8_t* packed,
-                           uint8_t* scales, float* gscale, hipStream_t s) {
+template <class Src>
+static hipError_t launch_quantize_src(const Src& src, const void* W, int64_t N, int64_t K, bool tiled,
+                                      uint8_t* packed, uint8_t* scales, float* gscale, hipStream_t s) {
   uint32_t* slot = reinterpret_cast<uint32_t*>(gscale);
   hipLaunchKernelGGL(k_amax_init, dim3(1), dim3(1), 0, s, slot);
-  const int64_t nvec = N * K / 8;
+  const int64_t nvec = N * K / Src::kPerVec;
   const int64_t want = (nvec + 255) / 256;
   const int grid_amax = (int)(want < 4096 ? want : 4096);
-  hipLaunchKernelGGL(k_amax, dim3(grid_amax), dim3(256), 0, s, reinterpret_cast<const uint4*>(W), nvec, slot);
+  hipLaunchKernelGGL((k_amax<Src>), dim3(grid_amax), dim3(256), 0, s, reinterpret_cast<const uint4*>(W), nvec,
+                     slot);
   const int64_t rows = tiled ? groups_of(N) * kGroupRows : N;
   const int64_t bpr = tiled ? chunks_of(K) * 64 : K / 16;
   const int64_t nthreads = rows * bpr;
-  hipLaunchKernelGGL(k_encode, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0, s, W, N, K,
+  hipLaunchKernelGGL((k_encode<Src>), dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0, s, src, N, K,
                      tiled ? 1 : 0, packed, scales, slot);
-  hipLaunchKernelGGL(k_finalize, dim3(1), dim3(1), 0, s, slot);
+  hipLaunchKernelGGL((k_finalize<Src>), dim3(1), dim3(1), 0, s, src, slot);
   return hipGetLastError();
+}
+
+hipError_t launch_quantize(const uint16_t* W, int64_t N, int64_t K, bool tiled, uint8_t* packed,
+                           uint8_t* scales, float* gscale, hipStream_t s) {
+  return launch_quantize_src(SrcBf16{W}, W, N, K, tiled, packed, scales, gscale, s);
+}
+
+hipError_t launch_quantize_fp8(const uint8_t* W, const float* w_scale, int64_t N, int64_t K, bool tiled,
+                               uint8_t* packed, uint8_t* scales, float* gscale, hipStream_t s) {
+  return launch_quantize_src(SrcFp8{W, w_scale}, W, N, K, tiled, packed, scales, gscale, s);
 }
 
 hipError_t launch_retile(const uint8_t* packed, const uint8_t* scales, int64_t N, int64_t K, uint8_t* tiles,

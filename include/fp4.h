@@ -123,6 +123,19 @@ FP4_API int fp4_layout_bytes(int64_t N, int64_t K, int layout, size_t *packed_by
 FP4_API int fp4_quantize(const void *W_bf16, int64_t N, int64_t K, int layout, void *packed, void *scales,
                  float *gscale, void *stream);
 
+/* The same quantisation for a checkpoint released in FP8 (the imp README:
+ * its quantiser builds NVFP4 weights from BF16 or FP8 releases). W_fp8 is
+ * [N][K] OCP E4M3 ("fn") codes, one byte per element (device, 16-byte
+ * aligned); *w_scale (device fp32) is the tensor's dequantisation scale.
+ * Element values are E4M3(code) * *w_scale, rounded once to fp32; from there
+ * the rule, layouts, outputs and gscale are exactly those of fp4_quantize.
+ * The NaN codes 0x7F and 0xFF are outside the domain (results unspecified),
+ * like non-finite bf16 input; *w_scale must be finite. w_scale must not be
+ * the gscale pointer (FP4_ERR_UNSUPPORTED): gscale is scratch while the
+ * kernels run. */
+FP4_API int fp4_quantize_fp8(const void *W_fp8, const float *w_scale, int64_t N, int64_t K, int layout,
+                             void *packed, void *scales, float *gscale, void *stream);
+
 /* Re-tile canonical (ROWMAJOR) packed/scales into the TILED layout, written
  * to `packed_tiled` (scales_tiled is unused and may be NULL). A pure byte
  * permutation plus zero padding; inputs and outputs must not overlap.

@@ -20,7 +20,8 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert names == sorted(["fp4_status_string", "fp4_layout_bytes", "fp4_quantize", "fp4_retile", "fp4_gemv",
-                            "fp4_gemv_multi", "fp4_gemm_prefill", "fp4_argmax_rows", "fp4_lm_head_greedy"])
+                            "fp4_gemv_multi", "fp4_gemm_prefill", "fp4_argmax_rows", "fp4_lm_head_greedy",
+                            "fp4_quantize_fp8"])
     lib = ctypes.CDLL(fp4.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -113,6 +114,19 @@ def test_argmax_and_greedy_argument_errors():
     assert L.fp4_lm_head_greedy(A, A, A, A, None, A, 0, 8, 32, None) == ESHAPE
     assert L.fp4_lm_head_greedy(A + 2, A, A, A, None, A, 1, 8, 32, None) == EALIGN
     assert L.fp4_lm_head_greedy(A, A, A + 8, A, None, A, 1, 8, 32, None) == EALIGN
+
+
+def test_quantize_fp8_argument_errors():
+    L = fp4.raw()
+    B = A + 4096         # another fake address (the tensor scale must not alias gscale)
+    assert L.fp4_quantize_fp8(None, A, 8, 32, 1, A, None, B, None) == ENULL
+    assert L.fp4_quantize_fp8(A, None, 8, 32, 1, A, None, B, None) == ENULL
+    assert L.fp4_quantize_fp8(A, A, 8, 32, 0, A, None, B, None) == ENULL   # row-major needs the scale array
+    assert L.fp4_quantize_fp8(A, A, 8, 30, 1, A, None, B, None) == ESHAPE
+    assert L.fp4_quantize_fp8(A, A, 8, 32, 2, A, None, B, None) == ELAYOUT
+    assert L.fp4_quantize_fp8(A + 8, A, 8, 32, 1, A, None, B, None) == EALIGN
+    assert L.fp4_quantize_fp8(A, A + 2, 8, 32, 1, A, None, B, None) == EALIGN
+    assert L.fp4_quantize_fp8(A, B, 8, 32, 1, A, None, B, None) == -6      # w_scale is gscale
 
 
 def test_binding_rejects_cpu_tensors():

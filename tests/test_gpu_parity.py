@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle
-from workloads import bf16_to_float32, float32_to_bf16_bits, bf16_tensor
+from workloads import bf16_to_float32, float32_to_bf16_bits, bf16_tensor, fp8_release
 
 from gpu_common import (THREADS, act_bits, assert_within_tolerance, dev, gpu_u8, oracle_quant, to_gpu_bf16,
                         weight_bits)
@@ -85,6 +85,58 @@ def test_quantize_bit_exact_workloads(wl, t):
     p, s, g = check_quant_bytes(weight_bits(wl, t), "%s/%s" % (wl, t))
     op, os_, og = oracle_quant(wl, t)
     assert og == g
+
+
+# ------------------------------------------------------ quantiser, FP8 source
+def check_quant_fp8(codes, scale, what):
+    p, s, g = oracle.quantize_fp8(codes, scale)
+    C = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).to(dev())
+    S = torch.tensor([float(scale)], dtype=torch.float32, device=dev())
+    w = fp4.quantize_fp8(C, S, "rowmajor")
+    torch.cuda.synchronize()
+    gp, gsc, gg = gpu_u8(w.packed), gpu_u8(w.scales), w.gscale.item()
+    assert np.float32(gg) == g, (what, gg, g)
+    assert np.array_equal(gsc.reshape(s.shape), s), (what, np.flatnonzero(gsc.reshape(s.shape) != s)[:8])
+    assert np.array_equal(gp.reshape(p.shape), p), (what, np.flatnonzero(gp.reshape(p.shape) != p)[:8])
+    wt = fp4.quantize_fp8(C.view(torch.float8_e4m3fn), S, "tiled")
+    torch.cuda.synchronize()
+    assert np.array_equal(gpu_u8(wt.packed), oracle.tile(p, s)), what
+    assert wt.gscale.item() == gg
+
+
+def fp8_edge_cases():
+    rng = np.random.default_rng(23)
+    every = np.arange(256, dtype=np.uint8)
+    every = every[(every & 0x7F) != 0x7F]                       # all 254 non-NaN codes
+    out = {
+        "ragged_13x1040": fp8_release((13, 1040), 21, 0.02, outlier_p=0.01, outlier_scale=20),
+        "one_row_16": fp8_release((1, 16), 22, 1.0),
+        "every_code_pow2_scale": (np.resize(rng.permutation(every), (16, 1024)), np.float32(2.0 ** -7)),
+        "every_code_odd_scale": (np.resize(rng.permutation(every), (16, 1024)), np.float32(0.0137)),
+        "negative_scale": (np.resize(every, (8, 512)), np.float32(-0.5)),
+        "zero_scale": (np.resize(every, (8, 512)), np.float32(0.0)),
+        "subnormal_codes_only": ((rng.integers(0, 8, (24, 128)) | (rng.integers(0, 2, (24, 128)) << 7)).astype(np.uint8),
+                                 np.float32(0.3)),
+        "tiny_scale": (np.resize(every, (8, 256)), np.float32(1e-30)),
+        "huge_scale": (np.resize(every, (8, 256)), np.float32(3e35)),
+    }
+    return out
+
+
+@pytest.mark.parametrize("name", list(fp8_edge_cases().keys()))
+def test_quantize_fp8_bit_exact_edge_cases(name):
+    print("quantize fp8 edge case", name, flush=True)
+    codes, scale = fp8_edge_cases()[name]
+    check_quant_fp8(codes, scale, name)
+
+
+@pytest.mark.parametrize("shape,seed", [((1024, 1024), 31), ((5120, 17408), 32)])
+def test_quantize_fp8_bit_exact_workload(shape, seed):
+    """An FP8 release of the 1024 x 1024 and 27B down-projection shapes
+    (N(0, 0.015) weights with 0.1 % outliers x20, like the bf16 workloads)."""
+    print("quantize fp8 workload", shape, flush=True)
+    codes, scale = fp8_release(shape, seed, 0.015, outlier_p=0.001, outlier_scale=20)
+    check_quant_fp8(codes, scale, "fp8 %dx%d" % shape)
 
 
 def test_retile_bit_exact_and_pads_with_zeros():

@@ -135,3 +135,20 @@ def bf16_tensor(shape, seed: int, sigma: float, start: int = 0,
     _native().wl_gen_bf16(out.ctypes.data, n, seed & 0xFFFFFFFFFFFFFFFF, start, float(sigma),
                           float(outlier_p), float(outlier_scale), nt)
     return out.reshape(shape)
+
+
+def fp8_release(shape, seed: int, sigma: float, outlier_p: float = 0.0, outlier_scale: float = 1.0):
+    """A synthetic weight tensor as a checkpoint released in FP8 holds it: the
+    seeded sigma*N(0,1) weights of ``bf16_tensor`` (as fp32), one fp32 scale
+    per tensor that maps the largest magnitude onto E4M3's largest finite
+    value (448), and weight / scale cast to OCP E4M3 ("fn") by torch
+    (nearest-even, clipped to +-448). Returns (codes uint8 ``shape``, scale
+    np.float32)."""
+    import torch
+
+    w = bf16_to_float32(bf16_tensor(shape, seed, sigma, outlier_p=outlier_p, outlier_scale=outlier_scale))
+    amax = float(np.abs(w).max())
+    scale = np.float32(amax / 448.0) if amax > 0 else np.float32(1.0)
+    q = np.clip(w / scale, -448.0, 448.0).astype(np.float32)
+    codes = torch.from_numpy(q).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes, scale
