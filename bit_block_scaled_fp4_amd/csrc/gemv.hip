@@ -29,6 +29,7 @@
 // multiply-add by the E4M3 block scale (decoded by v_cvt_f32_fp8, OCP
 // E4M3). The code conversions are shared by the activation rows of a pass.
 #include <algorithm>
+#include <atomic>
 
 #include "fp4_internal.h"
 
@@ -215,17 +216,51 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv(const GemvArgs a) {
 
 }  // namespace
 
+// Compute units of the current device (cached per device; 0 if unknown).
+static int cu_count() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 // Launch geometry, from sweeps on MI355X (graph-timed, rotating weights):
-// one tile per wave per round, rounds issued one after the other (several
-// tiles in flight per wave measured slower); for one activation row the
-// chunks of a group are spread over up to 16 waves (17 chunks: 9 waves, two
-// rounds), for 2-4 rows over about a third as many waves; short K packs
-// about four waves per workgroup:
-//   M = 1: wc = ceil(C / ceil(C / 16));  M > 1: wc = ceil(C / 3);
-//   gw = max(1, 4 / wc).
+// one tile per wave per round, rounds issued one after the other (a second
+// tile in flight per wave measured no faster). Short K packs about four
+// waves per workgroup.
+//   M > 1: wc = ceil(C / 3).
+//   M = 1, at most 16 chunks: one round (wc = C), unless the launch has at
+//     least 8 row groups per CU, where two rounds (wc = ceil(C / 2)) are
+//     faster (gate_up 34816 x 5120: 17.6 against 18.0-18.7 us).
+//   M = 1, more than 16 chunks: about one workgroup per CU, gw =
+//     ceil(groups / CUs) row groups of about 9 / gw waves each, every wave
+//     streaming its chunks (down 5120 x 17408: 10.9 against 11.8 us with 9
+//     waves per group in two rounds; 8192 x 28672: 22.0 against 27.6 us).
+//     Beyond 9 groups per CU the two-round layout below is used.
+//   Otherwise wc = ceil(C / ceil(C / 16)); gw = max(1, 4 / wc).
 template <int MT>
 static hipError_t launch_mt(GemvArgs a, hipStream_t s, int gw, int wc) {
   const int rounds = (a.C + kMaxWaves - 1) / kMaxWaves;
+  if (MT == 1 && gw <= 0 && wc <= 0) {
+    int64_t groups = 0;
+    for (int i = 0; i < a.nproj; ++i) groups += groups_of(a.proj[i].N);
+    const int ncu = cu_count();
+    if (ncu > 0 && a.C > kMaxWaves) {
+      const int64_t per_cu = (groups + ncu - 1) / ncu;
+      if (per_cu <= 9) {
+        gw = (int)per_cu;
+        wc = std::max(1, 9 / gw);
+      }
+    } else if (ncu > 0 && a.C >= 4 && groups >= 8 * (int64_t)ncu) {
+      wc = (a.C + 1) / 2;
+    }
+  }
   int w = wc > 0 ? wc : (MT == 1 ? (a.C + rounds - 1) / rounds : (a.C + 2) / 3);
   a.wc = std::max(1, std::min(w, kMaxWaves));
   a.gw = gw > 0 ? gw : std::max(1, 4 / a.wc);

@@ -163,7 +163,10 @@ def run_gemv(bits_w, bits_x):
 @pytest.mark.parametrize("N,K,M", [(1, 16, 1), (7, 32, 1), (16, 1024, 1), (1000, 1040, 1), (1000, 1040, 2),
                                    (333, 2064, 3), (17, 3072, 5), (64, 5120, 8), (130, 17408, 4), (40, 8192, 16),
                                    (257, 1024, 7), (2050, 2048, 1), (300, 1040, 5), (97, 2064, 17),
-                                   (520, 3072, 32), (130, 4096, 40), (64, 1024, 64)])
+                                   (520, 3072, 32), (130, 4096, 40), (64, 1024, 64),
+                                   # M = 1 with more than 16 chunks: about one workgroup per CU, every
+                                   # wave streaming several chunks (1 and 2 row groups per workgroup)
+                                   (100, 17424, 1), (3000, 20480, 1)])
 def test_gemv_small_shapes(N, K, M):
     print("gemv", N, K, M, flush=True)
     bw = bf16_tensor((N, K), N * 7 + K, 0.03, outlier_p=0.002, outlier_scale=20.0)
