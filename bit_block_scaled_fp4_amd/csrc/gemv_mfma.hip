@@ -11,10 +11,11 @@
 // with up to 16 activation rows per pass as the A operand.
 //
 // Work split (split-K). Workgroup (b, c) owns K chunk c (1024 elements) and a
-// block of 16-row weight pairs (two 8-row groups). It first copies the 16
-// activation rows of its chunk into LDS (rotated by the row index so that the
-// A-operand reads hit distinct banks); its waves then walk the pairs, each
-// pair needing only weight loads. The partial product of chunk c goes to
+// block of 16-row weight pairs (two 8-row groups). It first copies the
+// activation rows of its chunk into LDS (16, or 8 when the pass has at most
+// 8 rows, so that three workgroups fit on a CU; rotated by the row index so
+// that the A-operand reads hit distinct banks); its waves then walk the
+// pairs, each pair needing only weight loads. The partial product of chunk c goes to
 // a workspace [C][pairs][16 n][16 m]; a second kernel adds the C partials
 // of every output in chunk order and applies the tensor scale (one chunk:
 // the first kernel writes y directly). Results are deterministic.
@@ -23,10 +24,20 @@
 //   A: row l % 16, k = 8q .. 8q+7;  B: column l % 16, k = 8q .. 8q+7;
 //   D: column l % 16, rows 4q .. 4q+3.
 // The k order inside one MFMA is free as long as A and B agree: lane
-// (q, n) loads the 16-byte piece 4t + q (t = 0..7) of weight row n and feeds
+// (q, n) takes the 16-byte piece 4t + q (t = 0..7) of weight row n and feeds
 // its elements 8j .. 8j+7 to MFMA (t, j); the A lane (q, m) reads the
-// matching activations x[m][32(4t + q) + 8j ..]. For a fixed t the wave's
-// loads cover 64 contiguous bytes of each of the 16 rows.
+// matching activations x[m][32(4t + q) + 8j ..].
+//
+// Weight loads. In that operand layout one load instruction would touch 64
+// bytes of each of 16 rows (twice the cache lines of a contiguous kilobyte)
+// and the block scales would take eight 2-byte loads per pair. Instead a wave
+// loads each tile of its pair as the M = 1 kernel does (four contiguous
+// kilobytes, rows 2i and 2i + 1 per load, and the tile's 512 scale bytes at
+// 8 bytes per lane) and moves them through a wave-private LDS region: row r
+// of tile T keeps its 16-byte pieces at slot piece ^ (r + 8T), so the writes
+// (8 lanes of one row) and the operand reads (8 or 16 lanes of consecutive
+// rows, one piece each) both spread over all banks. Only the wave that wrote
+// the region reads it, and a wave's LDS operations complete in order.
 #include <algorithm>
 #include <mutex>
 
@@ -44,7 +55,7 @@ constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9
 constexpr int kWaves = 4;                 // waves per workgroup
 constexpr int kMRows = 16;                // activation rows per pass (MFMA M)
 constexpr int kPairRows = 16;             // weight rows per pair (MFMA N)
-constexpr int kXBytes = kMRows * kChunkK * 2;   // 32 KB of staged activations
+constexpr int kTrBytes = 8192 + 1024;           // per wave: one pair's codes and scales
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
@@ -101,13 +112,16 @@ struct MmaArgs {
 // Codes (16-byte piece 4t + q of the lane's row) and the piece's two scale
 // bytes for one pair.
 struct PairFrag {
-  uint4 w[8];
-  uint32_t sc[8];
+  uint4 w[2][4];   // tile T, load i: row 2i + (lane / 32), piece lane % 32
+  uint2 s[2];      // tile T: the tile's scale bytes at 8 * lane
 };
 
-// grid (ceil(npairs / pairs_per_wg), C); block kWaves waves.
+// grid (ceil(npairs / pairs_per_wg), C); block kWaves waves. XR activation
+// rows are staged (8 when M <= 8: rows 8..15 of the A operand are zero).
+template <int XR>
 __global__ __launch_bounds__(64 * kWaves) void k_gemv_mma(const MmaArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t xs[kXBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t xs[XR * kChunkK * 2];
+  __shared__ __attribute__((aligned(16))) uint8_t tr[kWaves * kTrBytes];
   const int lane = threadIdx.x & 63, q = lane >> 4, n16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = blockIdx.y, C = a.C, K = a.K;
@@ -128,27 +142,41 @@ __global__ __launch_bounds__(64 * kWaves) void k_gemv_mma(const MmaArgs a) {
     const int lp = (v ? pair : pb) - a.proj[p].pair_begin;
     const int G = (a.proj[p].N + 7) >> 3;
     const int g0 = 2 * lp;
-    // one resource over both tiles of the pair (groups g0, g0 + 1 of chunk c);
-    // a missing second group stays outside the resource and reads as zeros
     const int bytes = !v ? 0 : (g0 + 1 < G ? (C + 1) * kTileBytes : kTileBytes);
     const __amdgpu_buffer_rsrc_t r = rsrc(a.proj[p].tiles + ((int64_t)g0 * C + c) * kTileBytes, bytes);
-    const int base = (n16 >> 3) * C * kTileBytes;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(r, base + rr * 512 + (4 * t + q) * 16, 0, 2);
-      f.w[t] = make_uint4(w[0], w[1], w[2], w[3]);
-      f.sc[t] = __builtin_amdgcn_raw_buffer_load_b16(r, base + tile_scale_offset(rr, 2 * (4 * t + q)), 0, 0);
+    for (int T = 0; T < 2; ++T) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(r, T * C * kTileBytes + i * 1024 + lane * 16, 0, 2);
+        f.w[T][i] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+      const auto sv = __builtin_amdgcn_raw_buffer_load_b64(r, T * C * kTileBytes + kTileCodes + lane * 8, 0, 0);
+      f.s[T] = make_uint2(sv[0], sv[1]);
     }
   };
-
+  // wave-private transposition region: codes [T][row][piece ^ (row + 8T)] x 16 B, scales [T][512 B]
+  uint8_t* tw = tr + wave * kTrBytes;
+  auto transpose_in = [&](const PairFrag& f) {
+    const int h = lane >> 5, l = lane & 31;
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 2 * i + h;
+        *reinterpret_cast<uint4*>(tw + T * 4096 + r * 512 + ((l ^ (r + 8 * T)) * 16)) = f.w[T][i];
+      }
+      *reinterpret_cast<uint2*>(tw + 8192 + T * 512 + lane * 8) = f.s[T];
+    }
+  };
   PairFrag cur;
   load_pair(pb + wave, cur);   // in flight while the activations are staged
 
   // ---- activations of chunk c, rows m0 .. m0+15, into LDS: row m at 2048m,
   // 16-byte unit u stored at position (u + m) & 127
   {
-    const int rows = min(kMRows, a.M - a.m0);
-    for (int t = threadIdx.x; t < kMRows * 128; t += 64 * kWaves) {
+    const int rows = min(XR, a.M - a.m0);
+    for (int t = threadIdx.x; t < XR * 128; t += 64 * kWaves) {
       const int m = t >> 7, u = t & 127;
       uint4 v = make_uint4(0, 0, 0, 0);
       if (m < rows) {
@@ -166,17 +194,24 @@ __global__ __launch_bounds__(64 * kWaves) void k_gemv_mma(const MmaArgs a) {
     load_pair(pair + kWaves, nxt);   // next pair's loads overlap this pair's arithmetic
     // two accumulators (even and odd pieces) halve the dependent MFMA chain
     f32x4_t acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    transpose_in(cur);
+    const int T = n16 >> 3;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       // one piece at a time: keeps the compiler from hoisting every operand
       __builtin_amdgcn_sched_barrier(0);
-      const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)cur.sc[t], 0);
-      const float s1 = __builtin_amdgcn_cvt_f32_fp8((int)cur.sc[t], 1);
+      const int P = 4 * t + q;
+      const uint4 wv = *reinterpret_cast<const uint4*>(tw + T * 4096 + rr * 512 + ((P ^ (rr + 8 * T)) * 16));
+      const uint32_t sc = *reinterpret_cast<const uint16_t*>(tw + 8192 + T * 512 + (rr & 1) * 256 + P * 8 + (rr >> 1) * 2);
+      const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)sc, 0);
+      const float s1 = __builtin_amdgcn_cvt_f32_fp8((int)sc, 1);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bf16x8_t b = decode8(word(cur.w[t], j), j < 2 ? s0 : s1);
+        const bf16x8_t b = decode8(word(wv, j), j < 2 ? s0 : s1);
         const int u = 16 * t + 4 * q + j;
-        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(xs + n16 * 2048 + ((u + n16) & 127) * 16);
+        const int xr = XR == kMRows ? n16 : (n16 & (XR - 1));
+        bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(xs + xr * 2048 + ((u + xr) & 127) * 16);
+        if (XR < kMRows && n16 >= XR) av = bf16x8_t{};
         acc2[t & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b, acc2[t & 1], 0, 0, 0);
       }
     }
@@ -292,7 +327,10 @@ hipError_t launch_gemv_mma(const GemvArgs& g, hipStream_t s, int ppw) {
   }
   for (int m0 = 0; m0 < g.M; m0 += kMRows) {
     a.m0 = m0;
-    hipLaunchKernelGGL(k_gemv_mma, dim3((unsigned)wgx, (unsigned)a.C), dim3(64 * kWaves), 0, s, a);
+    if (g.M - m0 <= 8)
+      hipLaunchKernelGGL(k_gemv_mma<8>, dim3((unsigned)wgx, (unsigned)a.C), dim3(64 * kWaves), 0, s, a);
+    else
+      hipLaunchKernelGGL(k_gemv_mma<kMRows>, dim3((unsigned)wgx, (unsigned)a.C), dim3(64 * kWaves), 0, s, a);
     if (a.C > 1) {
       const int64_t n = pairs * 16 * ((std::min(kMRows, g.M - m0) + 3) / 4);
       hipLaunchKernelGGL(k_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
