@@ -47,10 +47,11 @@ _lib.fp4_retile.argtypes = [_P, _P, _I64, _I64, _P, _P, _P]
 _lib.fp4_gemv.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]
 _lib.fp4_gemv_multi.argtypes = [ctypes.POINTER(_Proj), _I, _P, _I64, _I64, _P]
 _lib.fp4_gemm_prefill.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]
+_lib.fp4_gemm_prefill_multi.argtypes = [ctypes.POINTER(_Proj), _I, _P, _I64, _I64, _P]
 _lib.fp4_argmax_rows.argtypes = [_P, _P, _I64, _I64, _I64, _P]
 _lib.fp4_lm_head_greedy.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]
 for _f in ("fp4_layout_bytes", "fp4_quantize", "fp4_quantize_fp8", "fp4_retile", "fp4_gemv", "fp4_gemv_multi", "fp4_gemm_prefill",
-           "fp4_argmax_rows", "fp4_lm_head_greedy"):
+           "fp4_gemm_prefill_multi", "fp4_argmax_rows", "fp4_lm_head_greedy"):
     getattr(_lib, _f).restype = _I
 
 
@@ -185,10 +186,9 @@ def gemv(x: torch.Tensor, w: NVFP4Weight, out: Optional[torch.Tensor] = None) ->
     return out
 
 
-def gemv_multi(x: torch.Tensor, weights: Sequence[NVFP4Weight], outs: Sequence[torch.Tensor],
-               ldys: Optional[Sequence[int]] = None) -> None:
-    """fp4_gemv_multi: one launch computing outs[i][m][n] (row stride ldys[i]) for every weight."""
-    x, M, K = _x2d(x)
+def _projs(M: int, K: int, weights: Sequence[NVFP4Weight], outs: Sequence[torch.Tensor],
+           ldys: Optional[Sequence[int]]):
+    """The fp4_proj array of a fused launch, after checking every output's extent."""
     n = len(weights)
     if not 1 <= n <= MAX_PROJ or len(outs) != n:
         raise ValueError("need 1..%d weights and as many outputs" % MAX_PROJ)
@@ -204,7 +204,25 @@ def gemv_multi(x: torch.Tensor, weights: Sequence[NVFP4Weight], outs: Sequence[t
             raise ValueError("outs[%d] is too small for M=%d rows of stride %d" % (i, M, ldy))
         _tiled(w)
         arr[i] = _Proj(_dev(w.packed, "packed"), None, _dev(w.gscale, "gscale", torch.float32), w.N, y.data_ptr(), ldy)
+    return arr, n
+
+
+def gemv_multi(x: torch.Tensor, weights: Sequence[NVFP4Weight], outs: Sequence[torch.Tensor],
+               ldys: Optional[Sequence[int]] = None) -> None:
+    """fp4_gemv_multi: one launch computing outs[i][m][n] (row stride ldys[i]) for every weight."""
+    x, M, K = _x2d(x)
+    arr, n = _projs(M, K, weights, outs, ldys)
     _check(_lib.fp4_gemv_multi(arr, n, _dev(x, "x", torch.bfloat16), M, K, _stream(x.device)), "fp4_gemv_multi")
+
+
+def gemm_prefill_multi(x: torch.Tensor, weights: Sequence[NVFP4Weight], outs: Sequence[torch.Tensor],
+                       ldys: Optional[Sequence[int]] = None) -> None:
+    """fp4_gemm_prefill_multi: one matrix-core launch computing outs[i][m][n]
+    (row stride ldys[i]) for every weight."""
+    x, M, K = _x2d(x)
+    arr, n = _projs(M, K, weights, outs, ldys)
+    _check(_lib.fp4_gemm_prefill_multi(arr, n, _dev(x, "x", torch.bfloat16), M, K, _stream(x.device)),
+           "fp4_gemm_prefill_multi")
 
 
 def gemm_prefill(x: torch.Tensor, w: NVFP4Weight, out: Optional[torch.Tensor] = None) -> torch.Tensor:

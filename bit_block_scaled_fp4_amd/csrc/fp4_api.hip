@@ -132,20 +132,34 @@ int fp4_gemv(float* y, const void* x_bf16, const void* packed, const void* scale
   return fp4_gemv_multi(&p, 1, x_bf16, M, K, stream);
 }
 
+int fp4_gemm_prefill_multi(const fp4_proj* projs, int nproj, const void* x_bf16, int64_t M, int64_t K,
+                           void* stream) {
+  if (!projs || !x_bf16) return FP4_ERR_NULL;
+  if (nproj < 1 || nproj > FP4_MAX_PROJ || M < 1 || M > kMaxM) return FP4_ERR_SHAPE;
+  if (!aligned(x_bf16, 16)) return FP4_ERR_ALIGN;
+  // the kernel addresses one 256-row slab of x, of each y and of weight
+  // tiles with 32-bit buffer offsets
+  const int64_t slab = int64_t(1) << 31;
+  if (int st = check_nk(8, K)) return st;
+  if (256 * K * 2 >= slab || 32 * fp4::chunks_of(K) * fp4::kTileBytes >= slab) return FP4_ERR_SHAPE;
+  fp4::PrefillProjDesc d[FP4_MAX_PROJ];
+  for (int i = 0; i < nproj; ++i) {
+    const fp4_proj& p = projs[i];
+    if (!p.packed || !p.gscale || !p.y) return FP4_ERR_NULL;
+    if (int st = check_nk(p.N, K)) return st;
+    if (p.ldy < p.N || M * p.ldy > kMaxElems || 256 * p.ldy * 4 >= slab) return FP4_ERR_SHAPE;
+    if (!aligned(p.packed, 16) || !aligned(p.y, 4) || !aligned(p.gscale, 4)) return FP4_ERR_ALIGN;
+    d[i] = {static_cast<const uint8_t*>(p.packed), p.gscale, p.y, p.ldy, p.N};
+  }
+  return hip_status(fp4::launch_prefill(d, nproj, static_cast<const uint16_t*>(x_bf16), M, K,
+                                        static_cast<hipStream_t>(stream)));
+}
+
 int fp4_gemm_prefill(float* y, const void* x_bf16, const void* packed, const void* scales, const float* gscale,
                      int64_t M, int64_t N, int64_t K, void* stream) {
-  (void)scales;   // the tiled layout keeps the scales inside `packed`
   if (!y || !x_bf16 || !packed || !gscale) return FP4_ERR_NULL;
-  if (int st = check_nk(N, K)) return st;
-  if (M < 1 || M > kMaxM || M * N > kMaxElems) return FP4_ERR_SHAPE;
-  // the kernel addresses one 256-row slab of x, of y and of weight tiles
-  // with 32-bit buffer offsets
-  const int64_t slab = int64_t(1) << 31;
-  if (256 * K * 2 >= slab || 256 * N * 4 >= slab || 32 * fp4::chunks_of(K) * fp4::kTileBytes >= slab)
-    return FP4_ERR_SHAPE;
-  if (!aligned(x_bf16, 16) || !aligned(packed, 16) || !aligned(y, 4) || !aligned(gscale, 4)) return FP4_ERR_ALIGN;
-  return hip_status(fp4::launch_prefill(y, static_cast<const uint16_t*>(x_bf16), static_cast<const uint8_t*>(packed),
-                                        gscale, M, N, K, static_cast<hipStream_t>(stream)));
+  fp4_proj p{packed, scales, gscale, N, y, N};   // scales: unused with the tiled layout
+  return fp4_gemm_prefill_multi(&p, 1, x_bf16, M, K, stream);
 }
 
 int fp4_argmax_rows(int32_t* idx, const float* y, int64_t M, int64_t N, int64_t ldy, void* stream) {

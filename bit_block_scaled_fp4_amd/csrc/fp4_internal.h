@@ -65,10 +65,18 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t s, int gw = 0, int wc = 0)
 // pass, more rows loop passes). With more than one chunk it uses a
 // per-device workspace that it allocates on first need and keeps.
 hipError_t launch_gemv_mma(const GemvArgs& a, hipStream_t s, int ppw = 0);   // ppw > 0: pairs per workgroup (tuning)
-// Matrix-core product for prefill-sized M. bn > 0 forces the output tile
-// width (128, 192 or 256; tuning), else it is chosen from the shape.
-hipError_t launch_prefill(float* y, const uint16_t* x, const uint8_t* tiles, const float* gscale, int64_t M,
-                          int64_t N, int64_t K, hipStream_t s, int bn = 0);
+// Matrix-core product for prefill-sized M over 1..kMaxProj weight tensors
+// that read the same x (one launch). bn > 0 forces the output tile width
+// (128, 192 or 256; tuning), else it is chosen from the shapes.
+struct PrefillProjDesc {
+  const uint8_t* tiles;
+  const float* gscale;
+  float* y;
+  int64_t ldy;
+  int64_t N;
+};
+hipError_t launch_prefill(const PrefillProjDesc* projs, int nproj, const uint16_t* x, int64_t M, int64_t K,
+                          hipStream_t s, int bn = 0);
 
 // Greedy choice per row of fp32 y [M][N] (row stride ldy): idx[m] = the first
 // index of the largest value. Rows longer than one workgroup's segment use a

@@ -158,11 +158,26 @@ __device__ __forceinline__ void interleave() {
   }
 }
 
+// One launch covers one or more weight tensors that read the same
+// activations (the gate and up halves of an MLP, or Q, K and V): tile t =
+// (256-row slab, projection, BN-column tile), slab-major, so an XCD's run of
+// tiles stays on one activation slab across all projections.
+struct PrefillProj {
+  const uint8_t* tiles;
+  const float* gscale;
+  float* y;
+  int64_t ldy;
+  int32_t N;
+  int32_t nt_begin;   // first column tile of this projection within a slab
+};
+struct PrefillArgs {
+  const uint16_t* x;
+  int32_t M, K, m_tiles, nt_total, per_xcd, nproj;
+  PrefillProj proj[kMaxProj];
+};
+
 template <int BN>
-__global__ __launch_bounds__(256, 1) void k_prefill(float* __restrict__ y, const uint16_t* __restrict__ x,
-                                                    const uint8_t* __restrict__ tiles,
-                                                    const float* __restrict__ gscale, int M, int N, int K,
-                                                    int m_tiles, int n_tiles, int per_xcd) {
+__global__ __launch_bounds__(256, 1) void k_prefill(const PrefillArgs a) {
   constexpr int NJ = BN / 64;          // 32-column MFMA tiles per wave
   constexpr int NG = BN / 8;           // 8-row weight groups per tile
   constexpr int NBI = NG / 4;          // code DMA instructions per wave per window
@@ -170,9 +185,17 @@ __global__ __launch_bounds__(256, 1) void k_prefill(float* __restrict__ y, const
   using L = Lds<BN>;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int id = blockIdx.x;
-  const int lin = (id & 7) * per_xcd + (id >> 3);   // XCD-contiguous tile index
-  if (lin >= m_tiles * n_tiles) return;
-  const int m0 = (lin / n_tiles) * BM, n0 = (lin % n_tiles) * BN;
+  const int lin = (id & 7) * a.per_xcd + (id >> 3);   // XCD-contiguous tile index
+  if (lin >= a.m_tiles * a.nt_total) return;
+  const int mt = lin / a.nt_total, jn = lin - mt * a.nt_total;
+  int pi = 0;
+  while (pi + 1 < a.nproj && jn >= a.proj[pi + 1].nt_begin) ++pi;
+  const PrefillProj& pj = a.proj[pi];
+  const uint16_t* __restrict__ x = a.x;
+  const uint8_t* __restrict__ tiles = pj.tiles;
+  const int M = a.M, N = pj.N, K = a.K;
+  const int64_t ldy = pj.ldy;
+  const int m0 = mt * BM, n0 = (jn - pj.nt_begin) * BN;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -333,8 +356,9 @@ __global__ __launch_bounds__(256, 1) void k_prefill(float* __restrict__ y, const
   // epilogue: lane l of a 32x32 tile holds column l % 32 and rows
   // 8(e/4) + 4(l/32) + e%4 (e < 16). Buffer stores drop rows past M (past
   // the resource) and columns past N (bit 31 set in the offset).
-  const float gs = *gscale;
-  const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(y + (int64_t)m0 * N, (short)0, mrows * N * 4,
+  const float gs = *pj.gscale;
+  const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(pj.y + (int64_t)m0 * ldy, (short)0,
+                                                                       (int)((int64_t)(mrows - 1) * ldy + N) * 4,
                                                                        kRsrcWord3);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -347,7 +371,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill(float* __restrict__ y, const
       for (int e = 0; e < 16; ++e) {
         const int r = r0 + (e >> 2) * 8 + (e & 3);
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, gs * acc[i][j][e]), ry,
-                                              (uint32_t)((r * N + n) * 4) | oobn, 0, 0);
+                                              (uint32_t)((r * (int)ldy + n) * 4) | oobn, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);   // one tile's values live at a time
     }
@@ -356,8 +380,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill(float* __restrict__ y, const
 }  // namespace
 
 template <int BN>
-static hipError_t launch_bn(float* y, const uint16_t* x, const uint8_t* tiles, const float* gscale, int64_t M, int64_t N,
-                     int64_t K, hipStream_t s) {
+static hipError_t launch_bn(PrefillArgs a, const PrefillProjDesc* projs, hipStream_t s) {
   // more than 64 KB of dynamic LDS must be allowed once per kernel and device
   constexpr int kMaxDevices = 64;
   static std::atomic<bool> attr_set[kMaxDevices];
@@ -370,23 +393,43 @@ static hipError_t launch_bn(float* y, const uint16_t* x, const uint8_t* tiles, c
     if (e != hipSuccess) return e;
     attr_set[dev].store(true, std::memory_order_release);
   }
-  const int64_t mt = (M + BM - 1) / BM, nt = (N + BN - 1) / BN;
+  int64_t nt = 0;
+  for (int i = 0; i < a.nproj; ++i) {
+    a.proj[i].nt_begin = (int32_t)nt;
+    nt += (projs[i].N + BN - 1) / BN;
+  }
+  const int64_t mt = (a.M + BM - 1) / BM;
   const int64_t total = mt * nt;
   if (total > (int64_t(1) << 30)) return hipErrorInvalidValue;
   const int64_t per_xcd = (total + 7) / 8;
-  hipLaunchKernelGGL(k_prefill<BN>, dim3((unsigned)(8 * per_xcd)), dim3(256), Lds<BN>::kBytes, s, y, x, tiles, gscale,
-                     (int)M, (int)N, (int)K, (int)mt, (int)nt, (int)per_xcd);
+  a.m_tiles = (int32_t)mt;
+  a.nt_total = (int32_t)nt;
+  a.per_xcd = (int32_t)per_xcd;
+  hipLaunchKernelGGL(k_prefill<BN>, dim3((unsigned)(8 * per_xcd)), dim3(256), Lds<BN>::kBytes, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_prefill(float* y, const uint16_t* x, const uint8_t* tiles, const float* gscale, int64_t M,
-                          int64_t N, int64_t K, hipStream_t s, int bn) {
+hipError_t launch_prefill(const PrefillProjDesc* projs, int nproj, const uint16_t* x, int64_t M, int64_t K,
+                          hipStream_t s, int bn) {
+  if (nproj < 1 || nproj > kMaxProj) return hipErrorInvalidValue;
   // buffer offsets are 32-bit: one 256-row slab of activations, of outputs
   // and of weights must each stay below 2 GB
   const int64_t C = chunks_of(K);
-  if ((int64_t)BM * K * 2 >= (int64_t(1) << 31) || (int64_t)BM * N * 4 >= (int64_t(1) << 31) ||
-      (int64_t)(256 / 8) * C * kTileBytes >= (int64_t(1) << 31))
+  if ((int64_t)BM * K * 2 >= (int64_t(1) << 31) || (int64_t)(256 / 8) * C * kTileBytes >= (int64_t(1) << 31))
     return hipErrorInvalidValue;
+  PrefillArgs a{};
+  a.x = x;
+  a.M = (int32_t)M;
+  a.K = (int32_t)K;
+  a.nproj = nproj;
+  for (int i = 0; i < nproj; ++i) {
+    if ((int64_t)BM * projs[i].ldy * 4 >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    a.proj[i].tiles = projs[i].tiles;
+    a.proj[i].gscale = projs[i].gscale;
+    a.proj[i].y = projs[i].y;
+    a.proj[i].ldy = projs[i].ldy;
+    a.proj[i].N = (int32_t)projs[i].N;
+  }
   if (bn <= 0) {
     // Tile width: the time is about (rounds of workgroups over the 256 CUs)
     // x (time of one tile). Relative tile times measured on MI355X at
@@ -396,19 +439,21 @@ hipError_t launch_prefill(float* y, const uint16_t* x, const uint8_t* tiles, con
     const int widths[3] = {256, 192, 128};
     const int cost[3] = {100, 85, 66};
     int64_t best = -1;
-    for (int i = 0; i < 3; ++i) {
-      const int64_t rounds = (mt * ((N + widths[i] - 1) / widths[i]) + 255) / 256;
-      const int64_t t = rounds * cost[i];
+    for (int w = 0; w < 3; ++w) {
+      int64_t nt = 0;
+      for (int i = 0; i < nproj; ++i) nt += (projs[i].N + widths[w] - 1) / widths[w];
+      const int64_t rounds = (mt * nt + 255) / 256;
+      const int64_t t = rounds * cost[w];
       if (best < 0 || t < best) {
         best = t;
-        bn = widths[i];
+        bn = widths[w];
       }
     }
   }
   switch (bn) {
-    case 128: return launch_bn<128>(y, x, tiles, gscale, M, N, K, s);
-    case 192: return launch_bn<192>(y, x, tiles, gscale, M, N, K, s);
-    case 256: return launch_bn<256>(y, x, tiles, gscale, M, N, K, s);
+    case 128: return launch_bn<128>(a, projs, s);
+    case 192: return launch_bn<192>(a, projs, s);
+    case 256: return launch_bn<256>(a, projs, s);
     default: return hipErrorInvalidValue;
   }
 }

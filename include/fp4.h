@@ -191,6 +191,18 @@ FP4_API int fp4_gemv_multi(const fp4_proj *projs, int nproj, const void *x_bf16,
 FP4_API int fp4_gemm_prefill(float *y, const void *x_bf16, const void *packed, const void *scales,
                      const float *gscale, int64_t M, int64_t N, int64_t K, void *stream);
 
+/* fp4_gemm_prefill over several projections that read the same x [M][K]
+ * (the gate and up halves of an MLP, or Q, K and V) in ONE launch: results
+ * equal separate fp4_gemm_prefill calls, each y[m*ldy + n] (n < N) written
+ * and nothing else. One launch spreads the output tiles of all projections
+ * over the compute units together, so the last round of tiles is fuller
+ * than it is for each projection alone. 1 <= nproj <= FP4_MAX_PROJ;
+ * `projs` is host memory read before the call returns; ldy >= N, and a
+ * 256-row slab of each y (256*ldy*4 bytes) stays below 2 GB. Other limits
+ * and the first-call attribute are those of fp4_gemm_prefill. */
+FP4_API int fp4_gemm_prefill_multi(const fp4_proj *projs, int nproj, const void *x_bf16, int64_t M, int64_t K,
+                                   void *stream);
+
 /* Greedy next-token choice: idx[m] = the first n with y[m][n] not below any
  * other element of row m, for fp32 y [M][N] (device, row stride ldy >= N);
  * a NaN ranks above every number (the first NaN wins) and -0 equals +0.

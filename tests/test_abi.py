@@ -20,7 +20,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert names == sorted(["fp4_status_string", "fp4_layout_bytes", "fp4_quantize", "fp4_retile", "fp4_gemv",
-                            "fp4_gemv_multi", "fp4_gemm_prefill", "fp4_argmax_rows", "fp4_lm_head_greedy",
+                            "fp4_gemv_multi", "fp4_gemm_prefill", "fp4_gemm_prefill_multi", "fp4_argmax_rows", "fp4_lm_head_greedy",
                             "fp4_quantize_fp8"])
     lib = ctypes.CDLL(fp4.LIB_PATH)
     for n in names:
@@ -95,6 +95,29 @@ def test_quantize_retile_prefill_argument_errors():
     # 256-row slabs of x (256*K*2 bytes) or y (256*N*4 bytes) reaching 2 GB
     assert L.fp4_gemm_prefill(A, A, A, A, A, 4, 8, 1 << 22, None) == ESHAPE
     assert L.fp4_gemm_prefill(A, A, A, A, A, 4, 1 << 21, 32, None) == ESHAPE
+
+
+def test_gemm_prefill_multi_argument_errors():
+    L = fp4.raw()
+    P = (fp4._Proj * 9)()
+    for i in range(9):
+        P[i] = fp4._Proj(A, A, A, 8, A, 8)
+    assert L.fp4_gemm_prefill_multi(None, 1, A, 4, 32, None) == ENULL
+    assert L.fp4_gemm_prefill_multi(P, 1, None, 4, 32, None) == ENULL
+    assert L.fp4_gemm_prefill_multi(P, 0, A, 4, 32, None) == ESHAPE
+    assert L.fp4_gemm_prefill_multi(P, 9, A, 4, 32, None) == ESHAPE
+    assert L.fp4_gemm_prefill_multi(P, 2, A, 0, 32, None) == ESHAPE
+    assert L.fp4_gemm_prefill_multi(P, 2, A, 4, 24, None) == ESHAPE
+    assert L.fp4_gemm_prefill_multi(P, 2, A + 2, 4, 32, None) == EALIGN
+    assert L.fp4_gemm_prefill_multi(P, 2, A, 4, 1 << 22, None) == ESHAPE        # x slab of 2 GB
+    P[1] = fp4._Proj(A, A, A, 8, A, 4)                                          # ldy < N
+    assert L.fp4_gemm_prefill_multi(P, 2, A, 4, 32, None) == ESHAPE
+    P[1] = fp4._Proj(A, A, A, 8, A, 1 << 21)                                    # y slab of 2 GB
+    assert L.fp4_gemm_prefill_multi(P, 2, A, 4, 32, None) == ESHAPE
+    P[1] = fp4._Proj(A, A, None, 8, A, 8)
+    assert L.fp4_gemm_prefill_multi(P, 2, A, 4, 32, None) == ENULL
+    P[1] = fp4._Proj(A, A, A, 8, A + 2, 8)
+    assert L.fp4_gemm_prefill_multi(P, 2, A, 4, 32, None) == EALIGN
 
 
 def test_argmax_and_greedy_argument_errors():

@@ -322,6 +322,33 @@ def test_prefill_small_shapes(M, N, K):
     assert_within_tolerance(y.cpu().numpy(), yr, l1, "prefill %d %d %d" % (M, N, K))
 
 
+@pytest.mark.parametrize("M,K,Ns", [(300, 1040, (300, 8, 1000)), (37, 80, (16452, 16400)), (513, 2048, (129,)),
+                                    (257, 64, (256, 128, 192, 8, 200, 1000, 64, 72))])
+def test_prefill_multi_column_slices(M, K, Ns):
+    """Several projections in one launch, each writing a column slice of one
+    shared [M][ldy] output (ldy = sum of N + 3 guard columns): every slice
+    equals the oracle and the separate fp4_gemm_prefill result bit for bit,
+    and the guard columns are never written."""
+    print("prefill_multi", M, K, Ns, flush=True)
+    bx = bf16_tensor((M, K), 11 * M + K, 1.0)
+    x = to_gpu_bf16(bx)
+    bws = [bf16_tensor((N, K), 900 + 7 * i + N, 0.02, outlier_p=0.002, outlier_scale=20.0) for i, N in enumerate(Ns)]
+    ws = [gpu_quant(b) for b in bws]
+    ldy = sum(Ns) + 3
+    y = torch.full((M, ldy), float("nan"), dtype=torch.float32, device=dev())
+    offs = np.cumsum((0,) + tuple(Ns))
+    fp4.gemm_prefill_multi(x, ws, [y[:, o:] for o in offs[:-1]], [ldy] * len(Ns))
+    sep = [fp4.gemm_prefill(x, w) for w in ws]
+    torch.cuda.synchronize()
+    assert torch.isnan(y[:, offs[-1]:]).all()
+    for i, (b, N) in enumerate(zip(bws, Ns)):
+        part = y[:, offs[i]:offs[i] + N]
+        assert torch.equal(part, sep[i]), "projection %d differs from its own launch" % i
+        p, s, g = oracle.quantize(b)
+        yr, l1 = oracle.gemv(bx, p, s, g, threads=THREADS)
+        assert_within_tolerance(part.cpu().numpy(), yr, l1, "prefill_multi %d" % i)
+
+
 def test_prefill_full_size_sampled_rows():
     """M=2048 tokens x gate_up 34816x5120 (two 17408-row tensors in one
     [2048][34816] output via two calls into column slices is not possible with
@@ -331,15 +358,22 @@ def test_prefill_full_size_sampled_rows():
     bx = act_bits(wl, "x")
     x = to_gpu_bf16(bx)
     rows = [0, 1, 127, 128, 1000, 1500, 2046, 2047]
+    ws, ys = {}, {}
     for t in ("gate", "up"):
-        w = gpu_quant(weight_bits("dense27b_layer", t))
-        y = fp4.gemm_prefill(x, w)
+        w = ws[t] = gpu_quant(weight_bits("dense27b_layer", t))
+        y = ys[t] = fp4.gemm_prefill(x, w)
         y2 = fp4.gemm_prefill(x, w)
         torch.cuda.synchronize()
         assert torch.equal(y, y2)
         p, s, g = oracle_quant("dense27b_layer", t)
         yr, l1 = oracle.gemv(bx[rows], p, s, g, threads=THREADS)
         assert_within_tolerance(y[rows].cpu().numpy(), yr, l1, "prefill %s" % t)
+    # the fused launch the bench times: gate and up into the halves of one [2048][34816] output
+    N = ws["gate"].N
+    yf = torch.empty((2048, 2 * N), dtype=torch.float32, device=dev())
+    fp4.gemm_prefill_multi(x, [ws["gate"], ws["up"]], [yf[:, :N], yf[:, N:]], [2 * N, 2 * N])
+    torch.cuda.synchronize()
+    assert torch.equal(yf[:, :N], ys["gate"]) and torch.equal(yf[:, N:], ys["up"])
 
 
 def test_gemv_and_prefill_agree_with_each_other():
