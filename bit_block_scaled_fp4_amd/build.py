@@ -27,7 +27,7 @@ COMMON = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-fvis
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-fhip-fp32-correctly-rounded-divide-sqrt"]
 PER_FILE = {"quantize.hip": ["-ffp-contract=off"]}
-SOURCES = ["fp4_api.hip", "quantize.hip", "gemv.hip", "gemv_mfma.hip", "prefill.hip", "argmax.hip"]
+SOURCES = ["fp4_api.hip", "quantize.hip", "gemv.hip", "gemv_mfma.hip", "prefill.hip", "argmax.hip", "device.hip"]
 
 
 def _compile(src: str) -> str:

@@ -18,8 +18,6 @@
 // of the row's S workgroups reads the S keys with device-coherent loads,
 // writes the index and puts the counter back to zero. One launch, no
 // cache-wide fences.
-#include <mutex>
-
 #include "fp4_internal.h"
 
 namespace fp4 {
@@ -110,56 +108,6 @@ __global__ __launch_bounds__(kThreads) void k_argmax(const ArgmaxArgs a) {
   }
 }
 
-__global__ __launch_bounds__(256) void k_zero_u32(unsigned* p, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0u;
-}
-
-// Per-device workspace for rows split over several workgroups: the partial
-// keys and the row counters, allocated on first need and kept (grown, never
-// freed: queued kernels may still use an older buffer) for the life of the
-// process. New counters are cleared by a kernel on the caller's stream ahead
-// of the launch that uses them; every launch leaves its counters at zero.
-constexpr int kMaxDevices = 64;
-struct Workspace {
-  uint64_t* keys = nullptr;
-  int64_t nkeys = 0;
-  unsigned* cnt = nullptr;
-  int64_t ncnt = 0;
-};
-std::mutex g_mu;
-Workspace g_ws[kMaxDevices];
-
-hipError_t workspace(int64_t nkeys, int64_t ncnt, hipStream_t s, uint64_t** keys, unsigned** cnt) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  std::lock_guard<std::mutex> lock(g_mu);
-  Workspace& w = g_ws[dev];
-  if (w.nkeys < nkeys) {
-    void* p = nullptr;
-    e = hipMalloc(&p, (size_t)nkeys * sizeof(uint64_t));
-    if (e != hipSuccess) return e;
-    w.keys = static_cast<uint64_t*>(p);
-    w.nkeys = nkeys;
-  }
-  if (w.ncnt < ncnt) {
-    void* p = nullptr;
-    e = hipMalloc(&p, (size_t)ncnt * sizeof(unsigned));
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((ncnt + 255) / 256)), dim3(256), 0, s, static_cast<unsigned*>(p),
-                       ncnt);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    w.cnt = static_cast<unsigned*>(p);
-    w.ncnt = ncnt;
-  }
-  *keys = w.keys;
-  *cnt = w.cnt;
-  return hipSuccess;
-}
-
 }  // namespace
 
 hipError_t launch_argmax(int32_t* idx, const float* y, int64_t M, int64_t N, int64_t ldy, hipStream_t s) {
@@ -173,8 +121,12 @@ hipError_t launch_argmax(int32_t* idx, const float* y, int64_t M, int64_t N, int
   if (wgs > INT32_MAX) return hipErrorInvalidValue;
   if (a.S > 1) {
     // counters on separate lines: the atomics of different rows do not queue on one line
-    hipError_t e = workspace(wgs, M * kCntStride, s, &a.keys, &a.cnt);
+    void *keys = nullptr, *cnt = nullptr;
+    hipError_t e = device_workspace(kWsArgmaxKeys, (size_t)wgs * sizeof(uint64_t), false, s, &keys);
+    if (e == hipSuccess) e = device_workspace(kWsArgmaxCounters, (size_t)M * kCntStride * 4, true, s, &cnt);
     if (e != hipSuccess) return e;
+    a.keys = static_cast<uint64_t*>(keys);
+    a.cnt = static_cast<unsigned*>(cnt);
   }
   hipLaunchKernelGGL(k_argmax, dim3((unsigned)wgs), dim3(kThreads), 0, s, a);
   return hipGetLastError();

@@ -67,7 +67,9 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t s, int gw = 0, int wc = 0)
 hipError_t launch_gemv_mma(const GemvArgs& a, hipStream_t s, int ppw = 0);   // ppw > 0: pairs per workgroup (tuning)
 // Matrix-core product for prefill-sized M over 1..kMaxProj weight tensors
 // that read the same x (one launch). bn > 0 forces the output tile width
-// (128, 192 or 256; tuning), else it is chosen from the shapes.
+// (128, 192 or 256; tuning), else it is chosen from the shapes; splits > 0
+// forces the K split of the last round's tiles (1: none; tuning). A split
+// uses per-device workspaces allocated on first need and kept.
 struct PrefillProjDesc {
   const uint8_t* tiles;
   const float* gscale;
@@ -76,7 +78,15 @@ struct PrefillProjDesc {
   int64_t N;
 };
 hipError_t launch_prefill(const PrefillProjDesc* projs, int nproj, const uint16_t* x, int64_t M, int64_t K,
-                          hipStream_t s, int bn = 0);
+                          hipStream_t s, int bn = 0, int splits = 0);
+
+// Compute units of the current device (cached per device; 0 if unknown).
+int device_cu_count();
+// Per-device workspace `which` of at least `bytes` (allocated on first need,
+// grown, never freed; a new buffer is zeroed on stream s when zero_new).
+enum Workspace { kWsGemvMmaPartials, kWsArgmaxKeys, kWsArgmaxCounters, kWsPrefillPartials, kWsPrefillCounters,
+                 kWsCount };
+hipError_t device_workspace(Workspace which, size_t bytes, bool zero_new, hipStream_t s, void** out);
 
 // Greedy choice per row of fp32 y [M][N] (row stride ldy): idx[m] = the first
 // index of the largest value. Rows longer than one workgroup's segment use a

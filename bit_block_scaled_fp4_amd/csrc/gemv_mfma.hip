@@ -39,7 +39,6 @@
 // rows, one piece each) both spread over all banks. Only the wave that wrote
 // the region reads it, and a wave's LDS operations complete in order.
 #include <algorithm>
-#include <mutex>
 
 #include "fp4_internal.h"
 
@@ -270,31 +269,6 @@ __global__ __launch_bounds__(256) void k_reduce(const MmaArgs a) {
   }
 }
 
-// Per-device workspace for the chunk partials, allocated on first need and
-// kept (grown, never freed) for the life of the process.
-constexpr int kMaxDevices = 64;
-std::mutex g_ws_mu;
-float* g_ws[kMaxDevices] = {};
-size_t g_ws_bytes[kMaxDevices] = {};
-
-hipError_t workspace(size_t bytes, float** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  std::lock_guard<std::mutex> lock(g_ws_mu);
-  if (g_ws_bytes[dev] < bytes) {
-    void* p = nullptr;
-    e = hipMalloc(&p, bytes);
-    if (e != hipSuccess) return e;
-    // the previous buffer may still be read by queued kernels: keep it
-    g_ws[dev] = static_cast<float*>(p);
-    g_ws_bytes[dev] = bytes;
-  }
-  *out = g_ws[dev];
-  return hipSuccess;
-}
-
 }  // namespace
 
 hipError_t launch_gemv_mma(const GemvArgs& g, hipStream_t s, int ppw) {
@@ -322,8 +296,10 @@ hipError_t launch_gemv_mma(const GemvArgs& g, hipStream_t s, int ppw) {
   const int64_t wgx = (pairs + a.pairs_per_wg - 1) / a.pairs_per_wg;
   if (a.C > 1) {
     const size_t bytes = (size_t)a.C * (size_t)pairs * 256 * sizeof(float);
-    hipError_t e = workspace(bytes, &a.ws);
+    void* ws = nullptr;
+    hipError_t e = device_workspace(kWsGemvMmaPartials, bytes, false, s, &ws);
     if (e != hipSuccess) return e;
+    a.ws = static_cast<float*>(ws);
   }
   for (int m0 = 0; m0 < g.M; m0 += kMRows) {
     a.m0 = m0;

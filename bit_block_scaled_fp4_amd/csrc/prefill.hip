@@ -55,6 +55,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
@@ -172,11 +174,23 @@ struct PrefillProj {
 };
 struct PrefillArgs {
   const uint16_t* x;
-  int32_t M, K, m_tiles, nt_total, per_xcd, nproj;
+  float* part;         // split tiles: partial sums, kPartFloats<BN> per piece
+  unsigned* cnt;       // split tiles: arrivals (kCntStride apart), zero between launches
+  int32_t M, K, m_tiles, nt_total, nproj;
+  int32_t dp_tiles;    // tiles computed whole by one workgroup: the first ones
+  int32_t per_xcd;     // of those, per XCD
+  int32_t splits;      // workgroups (K ranges) per remaining tile
   PrefillProj proj[kMaxProj];
 };
-
+constexpr int kMaxSplits = 4;
+constexpr int kCntStride = 32;   // one 128-byte line per counter
 template <int BN>
+constexpr int kPartFloats = BM * BN;
+
+// SPLIT = false: workgroup b takes whole tile b' (XCD-contiguous order) of
+// the first dp_tiles; SPLIT = true: workgroup b takes K range b % S of tile
+// dp_tiles + b / S.
+template <int BN, bool SPLIT>
 __global__ __launch_bounds__(256, 1) void k_prefill(const PrefillArgs a) {
   constexpr int NJ = BN / 64;          // 32-column MFMA tiles per wave
   constexpr int NG = BN / 8;           // 8-row weight groups per tile
@@ -184,9 +198,17 @@ __global__ __launch_bounds__(256, 1) void k_prefill(const PrefillArgs a) {
   constexpr int NSW = NG / 8;          // waves issuing one scale DMA per window
   using L = Lds<BN>;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-  const int id = blockIdx.x;
-  const int lin = (id & 7) * a.per_xcd + (id >> 3);   // XCD-contiguous tile index
-  if (lin >= a.m_tiles * a.nt_total) return;
+  __shared__ int last_piece;
+  const int id = blockIdx.x, S = a.splits;
+  int lin, piece = 0;
+  if (!SPLIT) {
+    lin = (id & 7) * a.per_xcd + (id >> 3);
+    if (lin >= a.dp_tiles) return;
+  } else {
+    lin = a.dp_tiles + id / S;
+    piece = id - (id / S) * S;
+  }
+  constexpr bool split = SPLIT;
   const int mt = lin / a.nt_total, jn = lin - mt * a.nt_total;
   int pi = 0;
   while (pi + 1 < a.nproj && jn >= a.proj[pi + 1].nt_begin) ++pi;
@@ -204,6 +226,11 @@ __global__ __launch_bounds__(256, 1) void k_prefill(const PrefillArgs a) {
   const int C = (K + kChunkK - 1) / kChunkK;
   const int G = (N + 7) >> 3;
   const int KT = (K + BK - 1) / BK;
+  // this workgroup's steps: whole windows, piece p of S taking windows
+  // [p nwin / S, (p + 1) nwin / S)
+  const int nwin = (KT + kWin - 1) / kWin;
+  const int kt0 = split ? piece * nwin / S * kWin : 0;
+  const int kt1 = split ? min(KT, (piece + 1) * nwin / S * kWin) : KT;
   const uint32_t sbase = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)smem;
 
   const int mrows = min(BM, M - m0);
@@ -222,7 +249,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill(const PrefillArgs a) {
   const uint32_t a_row_off = (uint32_t)((wave * 64 + dr) * K * 2);
   auto dma_a = [&](int kt) {
     const int k0 = kt * BK;
-    const i32x4_t& rs = kt < KT ? rx : rnull;
+    const i32x4_t& rs = kt < kt1 ? rx : rnull;
     // a chunk past K (ragged last step) gets bit 31 set: an offset past the resource
     const uint32_t oob0 = (uint32_t)((K - 1 - k0 - achunk0 * 8) >> 31) << 31;
     const uint32_t oob1 = (uint32_t)((K - 1 - k0 - achunk1 * 8) >> 31) << 31;
@@ -237,7 +264,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill(const PrefillArgs a) {
   // weight codes: instruction i of this wave fills group g = NBI wave + i
   // (rows 8g + dr); window `win` covers pieces 8 (win % 4) .. + 7 of chunk win / 4
   auto dma_b = [&](int win, int i0, int i1) {
-    const bool live = win * kWin < KT;
+    const bool live = win * kWin < kt1;
     const i32x4_t& rs = live ? rw : rnull;
     const int c = win >> 2, p0 = (win & 3) * 8;
     const uint32_t lds = sbase + L::kB + (win & 1) * L::kBStage;
@@ -253,7 +280,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill(const PrefillArgs a) {
   // (lane / 4) % 2 of the tile's scale area, 64 bytes from piece p0 on
   auto dma_s = [&](int win) {
     if (wave >= NSW) return;
-    const bool live = win * kWin < KT;
+    const bool live = win * kWin < kt1;
     const i32x4_t& rs = live ? rw : rnull;
     const int c = win >> 2, p0 = (win & 3) * 8;
     const int g = 8 * wave + dr;
@@ -303,15 +330,15 @@ __global__ __launch_bounds__(256, 1) void k_prefill(const PrefillArgs a) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
   };
 
-  // prologue: step 0's activations, window 0's codes and scales
-  dma_a(0);
-  dma_b(0, 0, NBI);
-  dma_s(0);
+  // prologue: step kt0's activations, its window's codes and scales
+  dma_a(kt0);
+  dma_b(kt0 / kWin, 0, NBI);
+  dma_s(kt0 / kWin);
   dma_wait();
   __syncthreads();
   Frags<NJ> f0, f1;
   Pieces<NJ> pc;
-  read_pieces(0, pc);
+  read_pieces(kt0, pc);
   decode_b(pc, 0, f0);
 
   // Step kt (activation stage kt % 2, window kt / 4): it loads the
@@ -321,7 +348,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill(const PrefillArgs a) {
   // its weight operands; in its last slice reads the weight pieces of step
   // kt + 1 (published by an earlier barrier) and decodes their slice 0. The
   // step ends with the DMA wait and the barrier that publishes its loads.
-  for (int kt = 0; kt < KT; ++kt) {
+  for (int kt = kt0; kt < kt1; ++kt) {
     const int sa = kt & 1, sw = kt % kWin, win = kt / kWin;
     read_a(sa, 0, f0);
     dma_a(kt + 1);
@@ -353,6 +380,68 @@ __global__ __launch_bounds__(256, 1) void k_prefill(const PrefillArgs a) {
     __syncthreads();
   }
 
+  if constexpr (SPLIT) {
+    // Every piece stores its partial sums with device-scope stores (sc1:
+    // through to the memory side, so another XCD's L2 cannot serve an old
+    // copy), waits for them, and counts itself in; the last of the tile's S
+    // pieces reads the S partials back with device-scope loads and adds them
+    // in piece order, so the sum does not depend on which piece came last.
+    // Layout per piece: [wave][i][j][e / 4][lane][e % 4].
+    const int st = lin - a.dp_tiles;
+    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+        a.part + (int64_t)st * S * kPartFloats<BN>, (short)0, S * kPartFloats<BN> * 4, kRsrcWord3);
+    constexpr int kSc1 = 16;   // cache-policy bit: device scope
+    auto part_off = [&](int p, int i, int j, int q) {
+      return (uint32_t)(p * kPartFloats<BN> * 4 + ((((wave * 4 + i) * NJ + j) * 4 + q) * 64 + lane) * 16);
+    };
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4_t v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rp, part_off(piece, i, j, q), 0, kSc1);
+        }
+    dma_wait();
+    __syncthreads();
+    if (tid == 0) {
+      const unsigned n = __hip_atomic_fetch_add(a.cnt + (int64_t)st * kCntStride, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+      last_piece = n == (unsigned)(S - 1);
+      // all S pieces are in: back to zero for the next launch
+      if (last_piece) __hip_atomic_store(a.cnt + (int64_t)st * kCntStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!last_piece) return;
+    // y = gscale * (sum of the S partials in piece order), 4 rows of one
+    // column per float4 (rows r0 + 8q .. + 3 of element group q)
+    const float gs = *pj.gscale;
+    const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(pj.y + (int64_t)m0 * ldy, (short)0,
+                                                                         (int)((int64_t)(mrows - 1) * ldy + N) * 4,
+                                                                         kRsrcWord3);
+#pragma unroll 8
+    for (int gq = 0; gq < 16 * NJ; ++gq) {
+      const int i = gq / (4 * NJ), j = (gq >> 2) % NJ, q = gq & 3;
+      f32x4_t t[kMaxSplits];
+#pragma unroll
+      for (int p = 0; p < kMaxSplits; ++p)   // pieces past S: past the resource, zeros without an access
+        t[p] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rp, part_off(p, i, j, q), 0, kSc1));
+      f32x4_t sum = t[0];
+#pragma unroll
+      for (int p = 1; p < kMaxSplits; ++p)
+        if (p < S) sum += t[p];
+      const int n = n0 + wn * (BN / 2) + j * 32 + l32;
+      const uint32_t oobn = (uint32_t)((N - 1 - n) >> 31) << 31;
+      const int r0 = wm * 128 + i * 32 + lh * 4 + q * 8;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, gs * sum[e]), ry,
+                                              (uint32_t)(((r0 + e) * (int)ldy + n) * 4) | oobn, 0, 0);
+    }
+    return;
+  }
+
   // epilogue: lane l of a 32x32 tile holds column l % 32 and rows
   // 8(e/4) + 4(l/32) + e%4 (e < 16). Buffer stores drop rows past M (past
   // the resource) and columns past N (bit 31 set in the offset).
@@ -379,8 +468,17 @@ __global__ __launch_bounds__(256, 1) void k_prefill(const PrefillArgs a) {
 
 }  // namespace
 
+// The last round's tiles: with few of them, splitting each along K into S
+// pieces keeps S times as many compute units busy (bounded by kMaxSplits
+// and by the tile's windows).
+static int auto_splits(int64_t total, int64_t nwin, int ncu) {
+  if (ncu <= 0) return 1;
+  const int64_t tail = total - (total - 1) / ncu * ncu;
+  return (int)std::max<int64_t>(1, std::min<int64_t>({kMaxSplits, ncu / tail, nwin}));
+}
+
 template <int BN>
-static hipError_t launch_bn(PrefillArgs a, const PrefillProjDesc* projs, hipStream_t s) {
+static hipError_t launch_bn(PrefillArgs a, const PrefillProjDesc* projs, int splits, hipStream_t s) {
   // more than 64 KB of dynamic LDS must be allowed once per kernel and device
   constexpr int kMaxDevices = 64;
   static std::atomic<bool> attr_set[kMaxDevices];
@@ -389,7 +487,11 @@ static hipError_t launch_bn(PrefillArgs a, const PrefillProjDesc* projs, hipStre
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   if (!attr_set[dev].load(std::memory_order_acquire)) {   // racing first calls set the same value
-    e = hipFuncSetAttribute((const void*)k_prefill<BN>, hipFuncAttributeMaxDynamicSharedMemorySize, Lds<BN>::kBytes);
+    e = hipFuncSetAttribute((const void*)k_prefill<BN, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            Lds<BN>::kBytes);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)k_prefill<BN, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              Lds<BN>::kBytes);
     if (e != hipSuccess) return e;
     attr_set[dev].store(true, std::memory_order_release);
   }
@@ -401,16 +503,40 @@ static hipError_t launch_bn(PrefillArgs a, const PrefillProjDesc* projs, hipStre
   const int64_t mt = (a.M + BM - 1) / BM;
   const int64_t total = mt * nt;
   if (total > (int64_t(1) << 30)) return hipErrorInvalidValue;
-  const int64_t per_xcd = (total + 7) / 8;
+  const int64_t nwin = ((a.K + BK - 1) / BK + kWin - 1) / kWin;
+  const int S = splits > 0 ? (int)std::min<int64_t>({splits, kMaxSplits, nwin})
+                           : auto_splits(total, nwin, device_cu_count());
+  const int64_t ncu = std::max(1, device_cu_count());
+  const int64_t tail = S > 1 ? total - (total - 1) / ncu * ncu : 0;
+  a.dp_tiles = (int32_t)(total - tail);
+  a.per_xcd = (int32_t)((a.dp_tiles + 7) / 8);
+  a.splits = S;
   a.m_tiles = (int32_t)mt;
   a.nt_total = (int32_t)nt;
-  a.per_xcd = (int32_t)per_xcd;
-  hipLaunchKernelGGL(k_prefill<BN>, dim3((unsigned)(8 * per_xcd)), dim3(256), Lds<BN>::kBytes, s, a);
-  return hipGetLastError();
+  if (tail > 0) {
+    void *part = nullptr, *cnt = nullptr;
+    e = device_workspace(kWsPrefillPartials, (size_t)(tail * S) * kPartFloats<BN> * sizeof(float), false, s, &part);
+    if (e == hipSuccess) e = device_workspace(kWsPrefillCounters, (size_t)tail * kCntStride * 4, true, s, &cnt);
+    if (e != hipSuccess) return e;
+    a.part = static_cast<float*>(part);
+    a.cnt = static_cast<unsigned*>(cnt);
+  }
+  // whole tiles, then the K pieces of the rest (a second launch: the split
+  // epilogue in the same kernel would cost the whole-tile path registers)
+  if (a.dp_tiles > 0) {
+    hipLaunchKernelGGL((k_prefill<BN, false>), dim3((unsigned)(8 * a.per_xcd)), dim3(256), Lds<BN>::kBytes, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (tail > 0) {
+    hipLaunchKernelGGL((k_prefill<BN, true>), dim3((unsigned)(tail * S)), dim3(256), Lds<BN>::kBytes, s, a);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 hipError_t launch_prefill(const PrefillProjDesc* projs, int nproj, const uint16_t* x, int64_t M, int64_t K,
-                          hipStream_t s, int bn) {
+                          hipStream_t s, int bn, int splits) {
   if (nproj < 1 || nproj > kMaxProj) return hipErrorInvalidValue;
   // buffer offsets are 32-bit: one 256-row slab of activations, of outputs
   // and of weights must each stay below 2 GB
@@ -431,19 +557,26 @@ hipError_t launch_prefill(const PrefillProjDesc* projs, int nproj, const uint16_
     a.proj[i].N = (int32_t)projs[i].N;
   }
   if (bn <= 0) {
-    // Tile width: the time is about (rounds of workgroups over the 256 CUs)
-    // x (time of one tile). Relative tile times measured on MI355X at
-    // M = 2048, K = 5120: 128 wide 0.66, 192 wide 0.85, 256 wide 1 (wider
-    // tiles do more MFMA work per LDS and load byte); ties go to the wider.
-    const int64_t mt = (M + BM - 1) / BM;
+    // Tile width (and K split), from a cost model fitted on MI355X at
+    // M = 2048, K = 5120: a full round of workgroups over the compute units
+    // takes the tile time (relative: 128 wide 0.66, 192 wide 0.85, 256 wide
+    // 1; wider tiles do more MFMA work per LDS and load byte); a last round
+    // that is not full takes max(0.7, fill) of it (fewer busy units run at
+    // a higher clock); split S ways along K it takes 1/S of a tile plus 0.3
+    // (the partial sums' exchange). Ties go to the wider tile.
+    const int64_t mt = (M + BM - 1) / BM, nwin = ((K + BK - 1) / BK + kWin - 1) / kWin;
+    const int ncu = std::max(1, device_cu_count());
     const int widths[3] = {256, 192, 128};
     const int cost[3] = {100, 85, 66};
     int64_t best = -1;
     for (int w = 0; w < 3; ++w) {
       int64_t nt = 0;
       for (int i = 0; i < nproj; ++i) nt += (projs[i].N + widths[w] - 1) / widths[w];
-      const int64_t rounds = (mt * nt + 255) / 256;
-      const int64_t t = rounds * cost[w];
+      const int64_t total = mt * nt, full = (total - 1) / ncu, tail = total - full * ncu;
+      const int S = splits > 0 ? (int)std::min<int64_t>({splits, kMaxSplits, nwin}) : auto_splits(total, nwin, ncu);
+      const int64_t last = S > 1 ? cost[w] * 100 / S + cost[w] * 30
+                                 : cost[w] * std::max<int64_t>(70, tail * 100 / ncu);
+      const int64_t t = full * cost[w] * 100 + last;
       if (best < 0 || t < best) {
         best = t;
         bn = widths[w];
@@ -451,9 +584,9 @@ hipError_t launch_prefill(const PrefillProjDesc* projs, int nproj, const uint16_
     }
   }
   switch (bn) {
-    case 128: return launch_bn<128>(a, projs, s);
-    case 192: return launch_bn<192>(a, projs, s);
-    case 256: return launch_bn<256>(a, projs, s);
+    case 128: return launch_bn<128>(a, projs, splits, s);
+    case 192: return launch_bn<192>(a, projs, splits, s);
+    case 256: return launch_bn<256>(a, projs, splits, s);
     default: return hipErrorInvalidValue;
   }
 }

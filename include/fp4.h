@@ -46,7 +46,7 @@
  * Conventions for every call:
  *   - Pointers marked "device" are HIP device memory (e.g. a torch CUDA
  *     tensor's data_ptr()) on the current HIP device; the caller owns every
- *     buffer. One exception to "the library allocates nothing": fp4_gemv
+ *     buffer. Exceptions to "the library allocates nothing": fp4_gemv
  *     and fp4_gemv_multi with M >= 5 and K > 1024 keep the per-chunk
  *     partial sums in a per-device workspace (C * ceil(N/16) * 1 KiB, C =
  *     ceil(K/1024), summed over the projections) that the library
@@ -54,7 +54,9 @@
  *     more) and keeps until the process ends; that first call must not be
  *     made while the stream is being captured into a graph. Calls on one
  *     device share the workspace, so such calls on different streams of the
- *     same device must not overlap in time.
+ *     same device must not overlap in time. fp4_gemm_prefill,
+ *     fp4_gemm_prefill_multi and fp4_argmax_rows keep workspaces of their
+ *     own under the same rules (described at each call).
  *   - `stream` is a hipStream_t (NULL = the default stream). Calls only
  *     enqueue work: they never synchronise, and results are ready when the
  *     stream's work is. gscale is a device pointer, so quantise -> multiply
@@ -67,8 +69,8 @@
  *     packed data: 8-byte; canonical scales: none); y and gscale 4-byte
  *     aligned.
  *   - Size limits: 1 <= N <= 2^28, 16 <= K <= 2^24, 1 <= M <= 2^24.
- *   - Calls may be made from several host threads; the workspace above is
- *     guarded by a lock while it is (re)allocated.
+ *   - Calls may be made from several host threads; the workspaces are
+ *     guarded by a lock while they are (re)allocated.
  */
 #ifndef FP4_H
 #define FP4_H
@@ -184,7 +186,18 @@ FP4_API int fp4_gemv_multi(const fp4_proj *projs, int nproj, const void *x_bf16,
  * page "1. The big picture", "Two phases with very different costs").
  * Any M >= 1 is accepted; y [M][N] fp32 overwritten. `packed` holds the
  * tiles; `scales` is unused. The first call on a device raises the kernels'
- * dynamic LDS limit (a launch attribute, no allocation). FP4_ERR_SHAPE also
+ * dynamic LDS limit (a launch attribute, no allocation). Output tiles are
+ * 256 x 128, 192 or 256; when the last round of tiles over the compute
+ * units would leave most of them idle, those tiles are split into up to 4
+ * K ranges on separate workgroups (a second launch) whose fp32 partial sums
+ * meet in a per-device workspace (1 KiB per tile column, per row of 256,
+ * per K range: at most 64 MiB, plus 128 bytes per split tile), allocated
+ * with hipMalloc on the first call that needs it (or needs more) and kept
+ * until the process ends, under the rules of the fp4_gemv workspace above
+ * (no graph capture during that first call; no overlapping calls on
+ * different streams of one device). The partial sums are added in K order
+ * whichever workgroup finishes last: results are deterministic, but a
+ * split tile may differ from an unsplit one in the last bits. FP4_ERR_SHAPE also
  * covers shapes whose 256-row slabs reach 2 GB (256*K*2 or 256*N*4 bytes,
  * or 32 weight row groups: the kernel uses 32-bit buffer offsets), i.e.
  * K >= 4194304 or N >= 2097152. */
@@ -192,14 +205,16 @@ FP4_API int fp4_gemm_prefill(float *y, const void *x_bf16, const void *packed, c
                      const float *gscale, int64_t M, int64_t N, int64_t K, void *stream);
 
 /* fp4_gemm_prefill over several projections that read the same x [M][K]
- * (the gate and up halves of an MLP, or Q, K and V) in ONE launch: results
- * equal separate fp4_gemm_prefill calls, each y[m*ldy + n] (n < N) written
- * and nothing else. One launch spreads the output tiles of all projections
- * over the compute units together, so the last round of tiles is fuller
- * than it is for each projection alone. 1 <= nproj <= FP4_MAX_PROJ;
+ * (the gate and up halves of an MLP, or Q, K and V) in one pass over the
+ * compute units: each y[m*ldy + n] (n < N) is written and nothing else,
+ * with the results of separate fp4_gemm_prefill calls up to the rounding of
+ * split tiles. The output tiles of all projections are spread over the
+ * compute units together, so the last round of tiles is fuller than it is
+ * for each projection alone. 1 <= nproj <= FP4_MAX_PROJ;
  * `projs` is host memory read before the call returns; ldy >= N, and a
- * 256-row slab of each y (256*ldy*4 bytes) stays below 2 GB. Other limits
- * and the first-call attribute are those of fp4_gemm_prefill. */
+ * 256-row slab of each y (256*ldy*4 bytes) stays below 2 GB. Other limits,
+ * the first-call attribute and the workspace are those of
+ * fp4_gemm_prefill. */
 FP4_API int fp4_gemm_prefill_multi(const fp4_proj *projs, int nproj, const void *x_bf16, int64_t M, int64_t K,
                                    void *stream);
 

@@ -327,8 +327,10 @@ def test_prefill_small_shapes(M, N, K):
 def test_prefill_multi_column_slices(M, K, Ns):
     """Several projections in one launch, each writing a column slice of one
     shared [M][ldy] output (ldy = sum of N + 3 guard columns): every slice
-    equals the oracle and the separate fp4_gemm_prefill result bit for bit,
-    and the guard columns are never written."""
+    is within the tolerance of the oracle, as is the separate
+    fp4_gemm_prefill result, a second launch repeats the first bit for bit,
+    and the guard columns are never written. (Fused and separate launches
+    may split different tiles along K, so they agree to rounding only.)"""
     print("prefill_multi", M, K, Ns, flush=True)
     bx = bf16_tensor((M, K), 11 * M + K, 1.0)
     x = to_gpu_bf16(bx)
@@ -338,15 +340,18 @@ def test_prefill_multi_column_slices(M, K, Ns):
     y = torch.full((M, ldy), float("nan"), dtype=torch.float32, device=dev())
     offs = np.cumsum((0,) + tuple(Ns))
     fp4.gemm_prefill_multi(x, ws, [y[:, o:] for o in offs[:-1]], [ldy] * len(Ns))
+    y2 = torch.full_like(y, float("nan"))
+    fp4.gemm_prefill_multi(x, ws, [y2[:, o:] for o in offs[:-1]], [ldy] * len(Ns))
     sep = [fp4.gemm_prefill(x, w) for w in ws]
     torch.cuda.synchronize()
     assert torch.isnan(y[:, offs[-1]:]).all()
+    assert torch.equal(y[:, :offs[-1]], y2[:, :offs[-1]])
     for i, (b, N) in enumerate(zip(bws, Ns)):
         part = y[:, offs[i]:offs[i] + N]
-        assert torch.equal(part, sep[i]), "projection %d differs from its own launch" % i
         p, s, g = oracle.quantize(b)
         yr, l1 = oracle.gemv(bx, p, s, g, threads=THREADS)
         assert_within_tolerance(part.cpu().numpy(), yr, l1, "prefill_multi %d" % i)
+        assert_within_tolerance(sep[i].cpu().numpy(), yr, l1, "prefill separate %d" % i)
 
 
 def test_prefill_full_size_sampled_rows():
@@ -368,12 +373,21 @@ def test_prefill_full_size_sampled_rows():
         p, s, g = oracle_quant("dense27b_layer", t)
         yr, l1 = oracle.gemv(bx[rows], p, s, g, threads=THREADS)
         assert_within_tolerance(y[rows].cpu().numpy(), yr, l1, "prefill %s" % t)
-    # the fused launch the bench times: gate and up into the halves of one [2048][34816] output
+    # the fused launch the bench times: gate and up into the halves of one
+    # [2048][34816] output; its last round of tiles is split along K
     N = ws["gate"].N
     yf = torch.empty((2048, 2 * N), dtype=torch.float32, device=dev())
-    fp4.gemm_prefill_multi(x, [ws["gate"], ws["up"]], [yf[:, :N], yf[:, N:]], [2 * N, 2 * N])
+    yf2 = torch.empty_like(yf)
+    for out in (yf, yf2):
+        fp4.gemm_prefill_multi(x, [ws["gate"], ws["up"]], [out[:, :N], out[:, N:]], [2 * N, 2 * N])
     torch.cuda.synchronize()
-    assert torch.equal(yf[:, :N], ys["gate"]) and torch.equal(yf[:, N:], ys["up"])
+    assert torch.equal(yf, yf2)
+    # the split tiles are the last ones: token slab 7 (rows 1792..2047), the last 64 x 256 columns of up
+    rows_f = rows + [1792, 1900]
+    for h, t in enumerate(("gate", "up")):
+        p, s, g = oracle_quant("dense27b_layer", t)
+        yr, l1 = oracle.gemv(bx[rows_f], p, s, g, threads=THREADS)
+        assert_within_tolerance(yf[rows_f, h * N:(h + 1) * N].cpu().numpy(), yr, l1, "prefill fused %s" % t)
 
 
 def test_gemv_and_prefill_agree_with_each_other():
