@@ -40,6 +40,8 @@
 // the region reads it, and a wave's LDS operations complete in order.
 #include <algorithm>
 
+#include <atomic>
+
 #include "fp4_internal.h"
 
 namespace fp4 {
@@ -269,6 +271,45 @@ __global__ __launch_bounds__(256) void k_reduce(const MmaArgs a) {
   }
 }
 
+// Workgroups of k_gemv_mma<XR> resident per CU (LDS-bound: 3 for XR = 8,
+// 2 for XR = 16 on MI355X), cached per device; 0 if unknown.
+template <int XR>
+int resident_per_cu() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_gemv_mma<XR>, 64 * kWaves, 0) != hipSuccess) return 0;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// Pairs per workgroup. The four waves of a workgroup take its pairs in
+// turn, so a workgroup lasts about ceil(ppw / 4) pair steps, and the grid
+// runs in ceil(workgroups / slots) rounds (slots: workgroups resident on the
+// whole device). The choice minimises rounds x steps over ppw = 4 .. 32,
+// ties to the larger ppw. Sweeps on MI355X (graph-timed, rotating weights)
+// agree within run-to-run noise: e.g. M = 16, gate_up 34816 x 5120 24 pairs
+// (34.0 us against 37-38 with 16), down 5120 x 17408 12 (22.9 against 25.8
+// with 8), LM head 151936 x 1024 20 (27.4 against 35 with 16).
+int pick_pairs_per_wg(int64_t pairs, int C, int64_t slots) {
+  if (slots <= 0) return C <= 8 ? 16 : 8;
+  int best = 16;
+  int64_t best_cost = -1;
+  for (int p = 4; p <= 32; p += 4) {
+    const int64_t wgs = (pairs + p - 1) / p * C;
+    const int64_t cost = (wgs + slots - 1) / slots * (p / 4);
+    if (best_cost < 0 || cost <= best_cost) {
+      best_cost = cost;
+      best = p;
+    }
+  }
+  return best;
+}
+
 }  // namespace
 
 hipError_t launch_gemv_mma(const GemvArgs& g, hipStream_t s, int ppw) {
@@ -290,10 +331,6 @@ hipError_t launch_gemv_mma(const GemvArgs& g, hipStream_t s, int ppw) {
   }
   if (pairs > (int64_t(1) << 26)) return hipErrorInvalidValue;
   a.npairs = (int)pairs;
-  // pairs per workgroup (sweeps on MI355X): 16 when K has few chunks, 8 for
-  // long K (more workgroups per chunk keep every CU busy)
-  a.pairs_per_wg = ppw > 0 ? ppw : (a.C <= 8 ? 16 : 8);
-  const int64_t wgx = (pairs + a.pairs_per_wg - 1) / a.pairs_per_wg;
   if (a.C > 1) {
     const size_t bytes = (size_t)a.C * (size_t)pairs * 256 * sizeof(float);
     void* ws = nullptr;
@@ -301,9 +338,13 @@ hipError_t launch_gemv_mma(const GemvArgs& g, hipStream_t s, int ppw) {
     if (e != hipSuccess) return e;
     a.ws = static_cast<float*>(ws);
   }
+  const int64_t ncu = device_cu_count();
   for (int m0 = 0; m0 < g.M; m0 += kMRows) {
     a.m0 = m0;
-    if (g.M - m0 <= 8)
+    const bool eight = g.M - m0 <= 8;
+    a.pairs_per_wg = ppw > 0 ? ppw : pick_pairs_per_wg(pairs, a.C, ncu * (eight ? resident_per_cu<8>() : resident_per_cu<kMRows>()));
+    const int64_t wgx = (pairs + a.pairs_per_wg - 1) / a.pairs_per_wg;
+    if (eight)
       hipLaunchKernelGGL(k_gemv_mma<8>, dim3((unsigned)wgx, (unsigned)a.C), dim3(64 * kWaves), 0, s, a);
     else
       hipLaunchKernelGGL(k_gemv_mma<kMRows>, dim3((unsigned)wgx, (unsigned)a.C), dim3(64 * kWaves), 0, s, a);
