@@ -9,9 +9,11 @@
 // result once in the epilogue.
 //
 // Tiling. A 256-thread workgroup computes a 256 (tokens) x BN (outputs)
-// tile, BN = 128, 192 or 256; wave (wm, wn) of the 2 x 2 wave grid owns
-// 128 x BN/2 as 4 x NJ v_mfma_f32_32x32x16_bf16 tiles. K advances in steps
-// of 64, each split in four 16-deep MFMA slices.
+// tile, BN = 128, 192 or 256. For BN = 128 and 256 the four waves split the
+// columns (1 x 4 grid: each wave owns all 256 rows x BN/4 columns as 8 x NJ
+// v_mfma_f32_32x32x16_bf16 tiles, so each decoded weight operand feeds 8
+// MFMAs); for BN = 192 they form a 2 x 2 grid (128 x 96 each, 4 x 3 tiles).
+// K advances in steps of 64, each split in four 16-deep MFMA slices.
 //
 // Data movement. Every global read is a direct-to-LDS buffer load (16 bytes
 // per lane, no registers, coalesced 128-byte row segments):
@@ -140,9 +142,9 @@ struct Pieces {
   uint32_t sc[NJ];
 };
 // MFMA operands of one slice.
-template <int NJ>
+template <int MI, int NJ>
 struct Frags {
-  bf16x8_t a[4], b[NJ];
+  bf16x8_t a[MI], b[NJ];
 };
 
 // Deals the instructions of a scheduling region out around its NMFMA MFMAs:
@@ -192,7 +194,12 @@ constexpr int kPartFloats = BM * BN;
 // dp_tiles + b / S.
 template <int BN, bool SPLIT>
 __global__ __launch_bounds__(256, 1) void k_prefill(const PrefillArgs a) {
-  constexpr int NJ = BN / 64;          // 32-column MFMA tiles per wave
+  // wave grid: WM x WN waves, each owning 256 / WM rows (MI 32-row MFMA
+  // tiles) x BN / WN columns (NJ 32-column tiles); 1 x 4 where BN / 4 is a
+  // multiple of 32, so each decoded weight operand feeds 8 MFMAs
+  constexpr int WM = BN % 128 == 0 ? 1 : 2, WN = 4 / WM;
+  constexpr int MI = 8 / WM;
+  constexpr int NJ = BN / (32 * WN);   // 32-column MFMA tiles per wave
   constexpr int NG = BN / 8;           // 8-row weight groups per tile
   constexpr int NBI = NG / 4;          // code DMA instructions per wave per window
   constexpr int NSW = NG / 8;          // waves issuing one scale DMA per window
@@ -221,7 +228,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill(const PrefillArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int l32 = lane & 31, lh = lane >> 5;
   const int C = (K + kChunkK - 1) / kChunkK;
   const int G = (N + 7) >> 3;
@@ -290,12 +297,12 @@ __global__ __launch_bounds__(256, 1) void k_prefill(const PrefillArgs a) {
   };
 
   // operand reads
-  auto read_a = [&](int stage, int s, Frags<NJ>& f) {
+  auto read_a = [&](int stage, int s, Frags<MI, NJ>& f) {
     const uint8_t* As = smem + L::kA + stage * kAStage;
     const int lchunk = 4 * lh + s;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wm * 128 + i * 32 + l32;
+    for (int i = 0; i < MI; ++i) {
+      const int r = wm * (BM / WM) + i * 32 + l32;
       f.a[i] = *reinterpret_cast<const bf16x8_t*>(As + r * 128 + ((lchunk ^ swz(r)) * 16));
     }
   };
@@ -305,26 +312,26 @@ __global__ __launch_bounds__(256, 1) void k_prefill(const PrefillArgs a) {
     const uint8_t* Ss = smem + L::kS + (win & 1) * L::kSStage;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const int n = wn * (BN / 2) + j * 32 + l32;
+      const int n = wn * (BN / WN) + j * 32 + l32;
       p.w[j] = *reinterpret_cast<const uint4*>(Bs + n * 128 + ((q ^ swz(n)) * 16));
       p.sc[j] = *reinterpret_cast<const uint16_t*>(Ss + (n >> 3) * 128 + (n & 1) * 64 + q * 8 + ((n & 7) >> 1) * 2);
     }
   };
-  auto decode_b = [&](const Pieces<NJ>& p, int s, Frags<NJ>& f) {
+  auto decode_b = [&](const Pieces<NJ>& p, int s, Frags<MI, NJ>& f) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j) f.b[j] = decode8(p.w[j], p.sc[j], s);
   };
 
-  f32x16_t acc[4][NJ];
+  f32x16_t acc[MI][NJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-  auto mma = [&](const Frags<NJ>& f) {
+  auto mma = [&](const Frags<MI, NJ>& f) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
@@ -336,7 +343,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill(const PrefillArgs a) {
   dma_s(kt0 / kWin);
   dma_wait();
   __syncthreads();
-  Frags<NJ> f0, f1;
+  Frags<MI, NJ> f0, f1;
   Pieces<NJ> pc;
   read_pieces(kt0, pc);
   decode_b(pc, 0, f0);
@@ -359,22 +366,22 @@ __global__ __launch_bounds__(256, 1) void k_prefill(const PrefillArgs a) {
     mma(f0);
     read_a(sa, 1, f1);
     decode_b(pc, 1, f1);
-    interleave<4 * NJ, 4>();
+    interleave<MI * NJ, MI>();
     __builtin_amdgcn_sched_barrier(0);
     mma(f1);
     read_a(sa, 2, f0);
     decode_b(pc, 2, f0);
-    interleave<4 * NJ, 4>();
+    interleave<MI * NJ, MI>();
     __builtin_amdgcn_sched_barrier(0);
     mma(f0);
     read_a(sa, 3, f1);
     decode_b(pc, 3, f1);
-    interleave<4 * NJ, 4>();
+    interleave<MI * NJ, MI>();
     __builtin_amdgcn_sched_barrier(0);
     mma(f1);
     read_pieces(kt + 1, pc);   // past the end: stale LDS, never used
     decode_b(pc, 0, f0);
-    interleave<4 * NJ, 2 * NJ>();
+    interleave<MI * NJ, 2 * NJ>();
     __builtin_amdgcn_sched_barrier(0);
     dma_wait();
     __syncthreads();
@@ -392,10 +399,10 @@ __global__ __launch_bounds__(256, 1) void k_prefill(const PrefillArgs a) {
         a.part + (int64_t)st * S * kPartFloats<BN>, (short)0, S * kPartFloats<BN> * 4, kRsrcWord3);
     constexpr int kSc1 = 16;   // cache-policy bit: device scope
     auto part_off = [&](int p, int i, int j, int q) {
-      return (uint32_t)(p * kPartFloats<BN> * 4 + ((((wave * 4 + i) * NJ + j) * 4 + q) * 64 + lane) * 16);
+      return (uint32_t)(p * kPartFloats<BN> * 4 + ((((wave * MI + i) * NJ + j) * 4 + q) * 64 + lane) * 16);
     };
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -421,7 +428,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill(const PrefillArgs a) {
                                                                          (int)((int64_t)(mrows - 1) * ldy + N) * 4,
                                                                          kRsrcWord3);
 #pragma unroll 8
-    for (int gq = 0; gq < 16 * NJ; ++gq) {
+    for (int gq = 0; gq < 4 * MI * NJ; ++gq) {
       const int i = gq / (4 * NJ), j = (gq >> 2) % NJ, q = gq & 3;
       f32x4_t t[kMaxSplits];
 #pragma unroll
@@ -431,9 +438,9 @@ __global__ __launch_bounds__(256, 1) void k_prefill(const PrefillArgs a) {
 #pragma unroll
       for (int p = 1; p < kMaxSplits; ++p)
         if (p < S) sum += t[p];
-      const int n = n0 + wn * (BN / 2) + j * 32 + l32;
+      const int n = n0 + wn * (BN / WN) + j * 32 + l32;
       const uint32_t oobn = (uint32_t)((N - 1 - n) >> 31) << 31;
-      const int r0 = wm * 128 + i * 32 + lh * 4 + q * 8;
+      const int r0 = wm * (BM / WM) + i * 32 + lh * 4 + q * 8;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, gs * sum[e]), ry,
@@ -450,12 +457,12 @@ __global__ __launch_bounds__(256, 1) void k_prefill(const PrefillArgs a) {
                                                                        (int)((int64_t)(mrows - 1) * ldy + N) * 4,
                                                                        kRsrcWord3);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const int n = n0 + wn * (BN / 2) + j * 32 + l32;
+      const int n = n0 + wn * (BN / WN) + j * 32 + l32;
       const uint32_t oobn = (uint32_t)((N - 1 - n) >> 31) << 31;
-      const int r0 = wm * 128 + i * 32 + lh * 4;
+      const int r0 = wm * (BM / WM) + i * 32 + lh * 4;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int r = r0 + (e >> 2) * 8 + (e & 3);
