@@ -346,7 +346,18 @@ def other_workloads(fp4, copies, x_in0, x_mid0, timed, graph_of, gpu_bf16, dev):
     line({"workload": "prefill GEMM, M=2048 tokens x gate_up 5120->34816 (bf16 MFMA, one fused launch)",
           "us": round(t * 1e6, 2), "TFLOPs": round(flops / t / 1e12, 1), "mfma_bf16_peak_TFLOPs": 2500.0,
           "frac_of_mfma_peak": round(flops / t / 1e12 / 2500.0, 4)})
-    del yp, yf, xp
+    del yp, yf
+    # reference only (not this library): the same product as a dense bf16 GEMM in the vendor library
+    # (torch.matmul -> hipBLASLt), bf16 weights (4x the bytes of NVFP4), no decode, bf16 and fp32 output
+    wd = [torch.randn(2 * INTER, HIDDEN, device=dev, dtype=torch.bfloat16) for _ in range(4)]
+    for name, fn in (("bf16 out", lambda i: torch.matmul(xp, wd[i % 4].t())),
+                     ("fp32 out", lambda i: torch.mm(xp, wd[i % 4].t(), out_dtype=torch.float32))):
+        for i in range(8):
+            fn(i)
+        tr = timed(lambda c=[0]: (fn(c[0]), c.__setitem__(0, c[0] + 1)), 20) / 20
+        line({"workload": "reference: dense bf16 GEMM of the same prefill shape in hipBLASLt (torch.matmul), "
+                          "bf16 weights, " + name, "us": round(tr * 1e6, 2), "TFLOPs": round(flops / tr / 1e12, 1)})
+    del wd, xp
     # ---- Qwen3-0.6B-shaped decode: 28 layers x (QKV fused, O, gate_up fused, down), M = 1
     wl = workload("qwen3_0p6b_decode")
     layers = []
