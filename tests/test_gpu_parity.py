@@ -354,6 +354,27 @@ def test_prefill_multi_column_slices(M, K, Ns):
         assert_within_tolerance(sep[i].cpu().numpy(), yr, l1, "prefill separate %d" % i)
 
 
+# Shapes whose last round of tiles is split along K after a full round of
+# whole tiles (two launches): 300 x 32776 x 1040 takes 342 tiles of 256 x 192
+# (the last 86, in token rows 256..299, in 2 K ranges); 513 x 32648 x 1040
+# takes 384 tiles of 256 x 256 (the last 128, token row 512, in 2 K ranges).
+@pytest.mark.parametrize("M,N,K,rows", [(300, 32776, 1040, [0, 1, 100, 255, 256, 257, 280, 299]),
+                                        (513, 32648, 1040, [0, 255, 256, 300, 511, 512])])
+def test_prefill_whole_and_split_tiles(M, N, K, rows):
+    print("prefill whole+split", M, N, K, flush=True)
+    bw = bf16_tensor((N, K), 7 * N + K, 0.02, outlier_p=0.002, outlier_scale=20.0)
+    bx = bf16_tensor((M, K), 5 * M + 3, 1.0)
+    w = gpu_quant(bw)
+    x = to_gpu_bf16(bx)
+    y = fp4.gemm_prefill(x, w)
+    y2 = fp4.gemm_prefill(x, w)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    p, s, g = oracle.quantize(bw)
+    yr, l1 = oracle.gemv(bx[rows], p, s, g, threads=THREADS)
+    assert_within_tolerance(y[rows].cpu().numpy(), yr, l1, "prefill whole+split %d %d %d" % (M, N, K))
+
+
 def test_prefill_full_size_sampled_rows():
     """M=2048 tokens x gate_up 34816x5120 (two 17408-row tensors in one
     [2048][34816] output via two calls into column slices is not possible with
