@@ -177,6 +177,28 @@ def test_gemv_small_shapes(N, K, M):
     assert_within_tolerance(y, yr, l1, "gemv %dx%d M=%d" % (N, K, M))
 
 
+@pytest.mark.parametrize("N,K,Ms", [(16, 1 << 20, (1, 5)), ((1 << 21) - 8, 16, (1, 3))])
+def test_extreme_shapes(N, K, Ms):
+    """Near the size limits: K = 2^20 (1024 chunks per row group: 4.7 MB of
+    tiles per group, one workgroup streaming them) and N = 2^21 - 8 rows
+    (262143 row groups; the prefill's 256-row output slab just under 2 GB).
+    Quantisation bit-exact; the decode product and the prefill product
+    within the tolerance."""
+    print("extreme", N, K, Ms, flush=True)
+    bw = bf16_tensor((N, K), 4 * N + K, 0.02, outlier_p=0.002, outlier_scale=20.0)
+    p, s, g = check_quant_bytes(bw, "extreme %dx%d" % (N, K))
+    w = gpu_quant(bw)
+    for M in Ms:
+        bx = bf16_tensor((M, K), 17 + M, 1.0)
+        x = to_gpu_bf16(bx)
+        yg = fp4.gemv(x, w)
+        yp = fp4.gemm_prefill(x, w)
+        torch.cuda.synchronize()
+        yr, l1 = oracle.gemv(bx, p, s, g, threads=THREADS)
+        assert_within_tolerance(yg.cpu().numpy(), yr, l1, "extreme gemv %dx%d M=%d" % (N, K, M))
+        assert_within_tolerance(yp.cpu().numpy(), yr, l1, "extreme prefill %dx%d M=%d" % (N, K, M))
+
+
 def test_gemv_exact_when_every_partial_sum_is_exact():
     """Every block holds 2.625 (so all scales are 0x7E and gscale = 2^-10) and
     x is +-2^k: every product and partial sum is exact in fp32, so the GPU
