@@ -527,3 +527,55 @@ def test_lm_head_greedy_workload(M):
         second = np.partition(yr[m], -2)[-2]
         if yr[m, ref[m]] - second > 2e-3 * 2 * l1[m].max():
             assert idx[m] == ref[m]
+
+
+# ------------------------------------------------------------- graph replay
+def test_graph_replays_match_eager_results():
+    """The calls the bench replays from HIP graphs — the fused M = 1 product,
+    the M = 8 matrix-core product with its K-chunk reduce, the fused prefill
+    product with a K-split tail, and the greedy step (multi-segment argmax) —
+    captured once, replayed four times with eager work and synchronisations
+    between the replays; every replay equals the eager results bit for bit
+    (all these kernels are deterministic)."""
+    torch.manual_seed(0)
+    ws = {name: gpu_quant(bf16_tensor(shape, 600 + i, 0.02, outlier_p=0.002, outlier_scale=20.0))
+          for i, (name, shape) in enumerate([("g", (2048, 2048)), ("u", (2048, 2048)), ("d", (1000, 3072)),
+                                              ("p1", (300, 1040)), ("p2", (1000, 1040)), ("lm", (20000, 1024))])}
+    x1 = to_gpu_bf16(bf16_tensor((1, 2048), 71, 1.0))
+    x8 = to_gpu_bf16(bf16_tensor((8, 3072), 72, 1.0))
+    xp = to_gpu_bf16(bf16_tensor((300, 1040), 73, 1.0))
+    xl = to_gpu_bf16(bf16_tensor((1, 1024), 74, 1.0))
+    outs = {"gu": torch.empty((1, 4096), dtype=torch.float32, device=dev()),
+            "d8": torch.empty((8, 1000), dtype=torch.float32, device=dev()),
+            "pf": torch.empty((300, 1300), dtype=torch.float32, device=dev()),
+            "lg": torch.empty((1, 20000), dtype=torch.float32, device=dev()),
+            "ix": torch.empty((1,), dtype=torch.int32, device=dev())}
+
+    def step(o):
+        fp4.gemv_multi(x1, [ws["g"], ws["u"]], [o["gu"][:, :2048], o["gu"][:, 2048:]], [4096, 4096])
+        fp4.gemv(x8, ws["d"], out=o["d8"])
+        fp4.gemm_prefill_multi(xp, [ws["p1"], ws["p2"]], [o["pf"][:, :300], o["pf"][:, 300:]], [1300, 1300])
+        fp4.lm_head_greedy(xl, ws["lm"], logits=o["lg"], out=o["ix"])
+
+    step(outs)                              # eager (also allocates the workspaces before capture)
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in outs.items()}
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            step(outs)
+    torch.cuda.synchronize()
+    scratch = {k: torch.empty_like(v) for k, v in outs.items()}
+    for rep in range(4):
+        for v in outs.values():
+            v.fill_(float("nan") if v.dtype == torch.float32 else -1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in outs:
+            assert torch.equal(outs[k], ref[k]), (rep, k)
+        step(scratch)                        # eager work between the replays
+        torch.cuda.synchronize()
+        for k in outs:
+            assert torch.equal(scratch[k], ref[k]), (rep, k, "eager")
