@@ -33,12 +33,18 @@ def build(force: bool = True) -> str:
     return _SO
 
 
+# Test hook: the planted-mistake tests point this at a deliberately broken
+# build of the same source, to show that the pins catch each mistake.
+_OVERRIDE_ENV = "ORACLE_LIBRARY_OVERRIDE"
+
+
 def _L():
     global _lib
     if _lib is None:
-        if not os.path.exists(_SO):
+        path = os.environ.get(_OVERRIDE_ENV) or _SO
+        if path == _SO and not os.path.exists(_SO):
             build()
-        lib = ctypes.CDLL(_SO)
+        lib = ctypes.CDLL(path)
         P, I64 = ctypes.c_void_p, ctypes.c_int64
         lib.orc_e2m1_value.argtypes = [ctypes.c_int]
         lib.orc_e2m1_value.restype = ctypes.c_double

@@ -1,0 +1,65 @@
+"""The pins catch plausible mistakes in the oracle. Each case plants one
+mistake in a copy of the oracle's C source (a dropped term, a wrong sign or
+index, a swapped operand or nibble, a wrong constant or rounding rule),
+builds it, and runs the pin suite against that build in a subprocess: at
+least one pin must fail. The unmodified source, built the same way, must
+pass them all (so a failure is the planted mistake's doing)."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PINS = os.path.join(ROOT, "tests", "test_oracle_pins.py")
+
+MUTANTS = [
+    ("product drops the block scale", "y += s * inner;", "y += inner;"),
+    ("product subtracts", "inner += e * xv;", "inner -= e * xv;"),
+    ("product reads activation row 0 for every row", "const uint16_t *xm = j->x + m * K;",
+     "const uint16_t *xm = j->x;"),
+    ("product decodes the odd k from the low nibble",
+     "double e = E2M1_TAB[(k % 2 == 0) ? (byte & 15) : (byte >> 4)];",
+     "double e = E2M1_TAB[(k % 2 == 0) ? (byte >> 4) : (byte & 15)];"),
+    ("product forgets the tensor scale", "j->y[m * j->N + n] = j->gscale * y;", "j->y[m * j->N + n] = y;"),
+    ("tolerance scale drops the tensor scale", "l1 += fabs(e * s * j->gscale * xv);", "l1 += fabs(e * s * xv);"),
+    ("packing puts the even k in the high nibble", "(codes[2 * j] | (codes[2 * j + 1] << 4))",
+     "(codes[2 * j + 1] | (codes[2 * j] << 4))"),
+    ("tensor scale divides by 448 instead of 448 * 6", "amax / 2688.0f", "amax / 448.0f"),
+    ("block scale divides by 4 instead of 6", "bamax / 6.0f", "bamax / 4.0f"),
+    ("E2M1 ties go up", "if (a == mid) { code = (i % 2 == 0) ? i : i + 1; break; }",
+     "if (a == mid) { code = i + 1; break; }"),
+    ("E2M1 sign from v < 0 (negative zero loses its sign)", "(uint8_t)(code | (signbit(v) ? 8 : 0))",
+     "(uint8_t)(code | (v < 0 ? 8 : 0))"),
+    ("E4M3 ties go up", "c = (lo % 2 == 0) ? lo : lo + 1;", "c = lo + 1;"),
+    ("E4M3 saturates to the NaN code", "        c = 0x7E;", "        c = 0x7F;"),
+    ("greedy choice takes the last of equal maxima", "    return a > b;\n}", "    return a >= b;\n}"),
+    ("greedy choice ranks NaN below numbers", "    if (isnan(a)) return 1;", "    if (isnan(a)) return 0;"),
+]
+
+
+def _run_pins(src_text, tmp_path, tag):
+    c = tmp_path / ("%s.c" % tag)
+    so = tmp_path / ("lib%s.so" % tag)
+    c.write_text(src_text)
+    subprocess.check_call(["gcc", *oracle.CFLAGS, str(c), "-o", str(so), "-lm"])
+    env = dict(os.environ)
+    env[oracle._OVERRIDE_ENV] = str(so)
+    r = subprocess.run([sys.executable, "-m", "pytest", PINS, "-x", "-q", "-p", "no:cacheprovider", "-m", "not gpu"],
+                       env=env, cwd=ROOT, capture_output=True, text=True, timeout=600)
+    return r
+
+
+def test_unmodified_oracle_passes_the_pins(tmp_path):
+    r = _run_pins(open(oracle._SRC).read(), tmp_path, "control")
+    assert r.returncode == 0, r.stdout[-2000:]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_a_pin_catches_the_planted_mistake(name, old, new, tmp_path):
+    src = open(oracle._SRC).read()
+    assert old in src, "mutation point not found: " + name
+    r = _run_pins(src.replace(old, new), tmp_path, "mutant")
+    assert r.returncode != 0, "no pin failed for: " + name
