@@ -37,6 +37,14 @@ MUTANTS = [
     ("E4M3 saturates to the NaN code", "        c = 0x7E;", "        c = 0x7F;"),
     ("greedy choice takes the last of equal maxima", "    return a > b;\n}", "    return a >= b;\n}"),
     ("greedy choice ranks NaN below numbers", "    if (isnan(a)) return 1;", "    if (isnan(a)) return 0;"),
+    ("FP8 source divides by its scale", "(float)E4M3_TAB[src->fp8[i]] * src->fp8_scale;",
+     "(float)E4M3_TAB[src->fp8[i]] / src->fp8_scale;"),
+    ("bf16 bits shifted into the wrong place", "uint32_t u = (uint32_t)h << 16;", "uint32_t u = (uint32_t)h << 15;"),
+    ("dequantiser decodes the nibbles swapped", "int q = (k % 2 == 0) ? (byte & 15) : (byte >> 4);",
+     "int q = (k % 2 == 0) ? (byte >> 4) : (byte & 15);"),
+    ("dequantiser forgets the tensor scale",
+     "out[n * K + k] = E2M1_TAB[q] * E4M3_TAB[scales[n * (K / 16) + k / 16]] * (double)gscale;",
+     "out[n * K + k] = E2M1_TAB[q] * E4M3_TAB[scales[n * (K / 16) + k / 16]];"),
 ]
 
 
