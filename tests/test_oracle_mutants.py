@@ -4,6 +4,7 @@ index, a swapped operand or nibble, a wrong constant or rounding rule),
 builds it, and runs the pin suite against that build in a subprocess: at
 least one pin must fail. The unmodified source, built the same way, must
 pass them all (so a failure is the planted mistake's doing)."""
+import concurrent.futures
 import os
 import subprocess
 import sys
@@ -48,26 +49,40 @@ MUTANTS = [
 ]
 
 
-def _run_pins(src_text, tmp_path, tag):
-    c = tmp_path / ("%s.c" % tag)
-    so = tmp_path / ("lib%s.so" % tag)
-    c.write_text(src_text)
-    subprocess.check_call(["gcc", *oracle.CFLAGS, str(c), "-o", str(so), "-lm"])
+def _run_pins(src_text, workdir, tag):
+    c = os.path.join(workdir, "%s.c" % tag)
+    so = os.path.join(workdir, "lib%s.so" % tag)
+    with open(c, "w") as f:
+        f.write(src_text)
+    subprocess.check_call(["gcc", *oracle.CFLAGS, c, "-o", so, "-lm"])
     env = dict(os.environ)
-    env[oracle._OVERRIDE_ENV] = str(so)
+    env[oracle._OVERRIDE_ENV] = so
     r = subprocess.run([sys.executable, "-m", "pytest", PINS, "-x", "-q", "-p", "no:cacheprovider", "-m", "not gpu"],
                        env=env, cwd=ROOT, capture_output=True, text=True, timeout=600)
-    return r
+    return r.returncode, r.stdout[-2000:]
 
 
-def test_unmodified_oracle_passes_the_pins(tmp_path):
-    r = _run_pins(open(oracle._SRC).read(), tmp_path, "control")
-    assert r.returncode == 0, r.stdout[-2000:]
+@pytest.fixture(scope="module")
+def pin_runs(tmp_path_factory):
+    """The control and every mutant, built and run against the pins, a few at a time."""
+    workdir = str(tmp_path_factory.mktemp("oracle_mutants"))
+    src = open(oracle._SRC).read()
+    jobs = {"control": src}
+    for i, (name, old, new) in enumerate(MUTANTS):
+        jobs[name] = src.replace(old, new) if old in src else None
+    with concurrent.futures.ThreadPoolExecutor(max_workers=6) as ex:
+        futs = {name: ex.submit(_run_pins, text, workdir, "m%d" % i)
+                for i, (name, text) in enumerate(jobs.items()) if text is not None}
+        return {name: f.result() for name, f in futs.items()}
+
+
+def test_unmodified_oracle_passes_the_pins(pin_runs):
+    code, out = pin_runs["control"]
+    assert code == 0, out
 
 
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
-def test_a_pin_catches_the_planted_mistake(name, old, new, tmp_path):
-    src = open(oracle._SRC).read()
-    assert old in src, "mutation point not found: " + name
-    r = _run_pins(src.replace(old, new), tmp_path, "mutant")
-    assert r.returncode != 0, "no pin failed for: " + name
+def test_a_pin_catches_the_planted_mistake(name, old, new, pin_runs):
+    assert old in open(oracle._SRC).read(), "mutation point not found: " + name
+    code, _ = pin_runs[name]
+    assert code != 0, "no pin failed for: " + name
