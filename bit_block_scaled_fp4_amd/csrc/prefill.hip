@@ -42,6 +42,13 @@
 // activation slab (2.6 MB at K = 5120, kept in that XCD's 4 MB L2) while
 // every XCD streams the weights.
 //
+// Last round. When the last round of tiles over the compute units would
+// leave most of them idle, those tiles run in a second launch, each split
+// into S <= 4 ranges of whole windows along K on separate workgroups; the
+// pieces exchange fp32 partial sums through a per-device workspace and the
+// last piece of a tile adds them in piece order (so the result does not
+// depend on which piece finishes last) and writes y.
+//
 // Bounds: the buffer loads read zeros for activation rows past M, columns
 // past K, weight row groups past N and steps past the end, without touching
 // memory; the epilogue's buffer stores drop rows past M and columns past N.
