@@ -327,6 +327,30 @@ def test_gemv_multi_equals_oracle_for_each_projection_and_is_deterministic():
         assert torch.equal(o, o2)
 
 
+@pytest.mark.parametrize("M", [5, 9])
+def test_gemv_multi_matrix_core_ragged_projections(M):
+    """Several projections of unequal, ragged row counts (333, 16, 1000 rows;
+    K = 3008: three chunks, so the split-K reduce runs) in one launch on the
+    matrix-core path (M >= 5; M = 9 stages 16 activation rows, M = 5 eight),
+    each equal to the oracle within the tolerance and repeatable bit for bit."""
+    print("gemv_multi mfma", M, flush=True)
+    Ns, K = (333, 16, 1000), 3008
+    bws = [bf16_tensor((N, K), 800 + N, 0.02, outlier_p=0.002, outlier_scale=20.0) for N in Ns]
+    ws = [gpu_quant(b) for b in bws]
+    bx = bf16_tensor((M, K), 900 + M, 1.0)
+    x = to_gpu_bf16(bx)
+    outs = [torch.empty((M, N), dtype=torch.float32, device=dev()) for N in Ns]
+    outs2 = [torch.empty_like(o) for o in outs]
+    fp4.gemv_multi(x, ws, outs)
+    fp4.gemv_multi(x, ws, outs2)
+    torch.cuda.synchronize()
+    for b, o, o2 in zip(bws, outs, outs2):
+        p, s, g = oracle.quantize(b)
+        yr, l1 = oracle.gemv(bx, p, s, g, threads=THREADS)
+        assert_within_tolerance(o.cpu().numpy(), yr, l1, "multi mfma M=%d" % M)
+        assert torch.equal(o, o2)
+
+
 # --------------------------------------------------------------------- prefill
 # (300, 16452, 80) and (257, 16400, 1040) take 256 x 192 tiles, (300, 32768, 80) takes 256 x 256 tiles
 @pytest.mark.parametrize("M,N,K", [(1, 8, 16), (37, 300, 1040), (200, 129, 2048), (128, 256, 64), (300, 1000, 5120),
