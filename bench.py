@@ -96,7 +96,7 @@ def main():
                     help="only run 10 device-to-device copies of MIB MiB (calibrates the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only (the decode path is single-GPU); "
+        print("bench.py measures one GPU only (the decode path is single-GPU); "
               "--gpus %d is not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
