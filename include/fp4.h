@@ -95,7 +95,7 @@ typedef enum {
     FP4_ERR_ALIGN = -3,       /* a pointer is not aligned as required */
     FP4_ERR_LAYOUT = -4,      /* unknown layout tag */
     FP4_ERR_HIP = -5,         /* the HIP runtime rejected a launch */
-    FP4_ERR_UNSUPPORTED = -6  /* valid request this build cannot serve */
+    FP4_ERR_UNSUPPORTED = -6  /* valid request the library cannot serve */
 } fp4_status;
 
 typedef enum { FP4_LAYOUT_ROWMAJOR = 0, FP4_LAYOUT_TILED = 1 } fp4_layout;
