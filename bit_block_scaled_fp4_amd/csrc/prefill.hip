@@ -158,7 +158,7 @@ struct Frags {
 // after MFMA i come up to kValuPerMfma VALU operations, then one LDS read
 // (i < NDSR). A wave issues in order, so an MFMA queued behind a long run of
 // decode arithmetic would leave the matrix core idle.
-constexpr int kValuPerMfma = 5;
+constexpr int kValuPerMfma = 3;   // swept 2..8 on MI355X: 3 best (1-2 % over 5)
 template <int NMFMA, int NDSR>
 __device__ __forceinline__ void interleave() {
 #pragma unroll
