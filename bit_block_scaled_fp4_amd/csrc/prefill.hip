@@ -261,7 +261,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill(const PrefillArgs a) {
   const int achunk0 = ds ^ dr, achunk1 = ds ^ dr ^ 1;   // even / odd 8-row blocks
   // activations: instruction i of this wave fills rows 64 wave + 8i + dr
   const uint32_t a_row_off = (uint32_t)((wave * 64 + dr) * K * 2);
-  auto dma_a = [&](int kt) {
+  auto dma_a = [&](int kt, int i0, int i1) {
     const int k0 = kt * BK;
     const i32x4_t& rs = kt < kt1 ? rx : rnull;
     // a chunk past K (ragged last step) gets bit 31 set: an offset past the resource
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill(const PrefillArgs a) {
     const uint32_t oob1 = (uint32_t)((K - 1 - k0 - achunk1 * 8) >> 31) << 31;
     const uint32_t lds = sbase + L::kA + (kt & 1) * kAStage + wave * 64 * 128;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = i0; i < i1; ++i) {
       const int ch = (i & 1) ? achunk1 : achunk0;
       const uint32_t off = (a_row_off + (uint32_t)(i * 8 * K * 2) + (uint32_t)((k0 + ch * 8) * 2)) | ((i & 1) ? oob1 : oob0);
       dma16(rs, off, lds + i * 1024);
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill(const PrefillArgs a) {
   };
 
   // prologue: step kt0's activations, its window's codes and scales
-  dma_a(kt0);
+  dma_a(kt0, 0, 8);
   dma_b(kt0 / kWin, 0, NBI);
   dma_s(kt0 / kWin);
   dma_wait();
@@ -356,8 +356,10 @@ __global__ __launch_bounds__(256, 1) void k_prefill(const PrefillArgs a) {
   decode_b(pc, 0, f0);
 
   // Step kt (activation stage kt % 2, window kt / 4): it loads the
-  // activations of step kt + 1 and, in the first three steps of a window,
-  // the next window's codes (two halves) and scales; runs its four slices,
+  // activations of step kt + 1 (two of the eight loads in each slice: the
+  // stage was last read a step ago, before the last barrier) and, in the
+  // first three steps of a window, the next window's codes (two halves,
+  // issued at the step's start) and scales; runs its four slices,
   // alongside each reading the next slice's activation operands and decoding
   // its weight operands; in its last slice reads the weight pieces of step
   // kt + 1 (published by an earlier barrier) and decodes their slice 0. The
@@ -365,23 +367,26 @@ __global__ __launch_bounds__(256, 1) void k_prefill(const PrefillArgs a) {
   for (int kt = kt0; kt < kt1; ++kt) {
     const int sa = kt & 1, sw = kt % kWin, win = kt / kWin;
     read_a(sa, 0, f0);
-    dma_a(kt + 1);
+    dma_a(kt + 1, 0, 2);
     if (sw == 0) dma_b(win + 1, 0, NBI / 2);
     if (sw == 1) dma_b(win + 1, NBI / 2, NBI);
     if (sw == 2) dma_s(win + 1);
     __builtin_amdgcn_sched_barrier(0);
     mma(f0);
     read_a(sa, 1, f1);
+    dma_a(kt + 1, 2, 4);
     decode_b(pc, 1, f1);
     interleave<MI * NJ, MI>();
     __builtin_amdgcn_sched_barrier(0);
     mma(f1);
     read_a(sa, 2, f0);
+    dma_a(kt + 1, 4, 6);
     decode_b(pc, 2, f0);
     interleave<MI * NJ, MI>();
     __builtin_amdgcn_sched_barrier(0);
     mma(f0);
     read_a(sa, 3, f1);
+    dma_a(kt + 1, 6, 8);
     decode_b(pc, 3, f1);
     interleave<MI * NJ, MI>();
     __builtin_amdgcn_sched_barrier(0);
