@@ -160,3 +160,25 @@ def test_binding_rejects_cpu_tensors():
                                             torch.zeros(1), 8, 32))
     with pytest.raises(ValueError, match="GPU tensor"):
         fp4.argmax_rows(torch.zeros(4, 8))
+
+
+def test_binding_checks_fused_calls_before_any_gpu_work():
+    """gemv_multi and gemm_prefill_multi reject mismatched K, a wrong number
+    of outputs and more than FP4_MAX_PROJ projections in the binding, before
+    any HIP call (CPU tensors suffice to reach these checks)."""
+    import torch
+    w = fp4.NVFP4Weight(torch.zeros(1, dtype=torch.uint8), None, torch.zeros(1), 8, 32)
+    w64 = fp4.NVFP4Weight(torch.zeros(1, dtype=torch.uint8), None, torch.zeros(1), 8, 64)
+    x = torch.zeros(2, 32, dtype=torch.bfloat16)
+    y = torch.zeros(2, 8)
+    for call in (fp4.gemv_multi, fp4.gemm_prefill_multi):
+        with pytest.raises(ValueError, match="has K=64"):
+            call(x, [w64, w], [y, y])
+        with pytest.raises(ValueError, match="as many outputs"):
+            call(x, [w, w], [y])
+        with pytest.raises(ValueError, match="as many outputs"):
+            call(x, [w] * (fp4.MAX_PROJ + 1), [y] * (fp4.MAX_PROJ + 1))
+        with pytest.raises(ValueError, match="GPU tensor"):
+            call(x, [w], [y])
+    with pytest.raises(ValueError, match=r"\[K\] or \[M\]\[K\]"):
+        fp4.gemm_prefill_multi(torch.zeros(2, 2, 32, dtype=torch.bfloat16), [w], [y])
