@@ -26,7 +26,11 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-fvisibility=hidden",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-fhip-fp32-correctly-rounded-divide-sqrt"]
-PER_FILE = {"quantize.hip": ["-ffp-contract=off"]}
+# gemv_mfma.hip: MFMA results in VGPRs (the 8-row kernel adds every MFMA
+# result into fp32 accumulators on the vector ALUs; AGPR results would cost a
+# v_accvgpr_read per value).
+PER_FILE = {"quantize.hip": ["-ffp-contract=off"],
+            "gemv_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 SOURCES = ["fp4_api.hip", "quantize.hip", "gemv.hip", "gemv_mfma.hip", "prefill.hip", "argmax.hip", "device.hip"]
 
 

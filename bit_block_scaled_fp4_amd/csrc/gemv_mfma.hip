@@ -6,38 +6,45 @@
 // speculative-decoding bullets of "The most important number in this
 // book"). On the vector ALUs every extra row costs another two-term dot
 // product per weight pair, which makes that path ALU-bound from about four
-// rows on; here each weight is decoded once to bf16 (E2M1 * E4M3 has at most
-// 6 significant bits: exact) and multiplied on v_mfma_f32_16x16x32_bf16,
-// with up to 16 activation rows per pass as the A operand.
+// rows on; here the weights are decoded once to exact bf16 and multiplied on
+// v_mfma_f32_16x16x32_bf16 with the activation rows as the A operand.
 //
 // Work split (split-K). Workgroup (b, c) owns K chunk c (1024 elements) and a
 // block of 16-row weight pairs (two 8-row groups). It first copies the
-// activation rows of its chunk into LDS (16, or 8 when the pass has at most
-// 8 rows, so that three workgroups fit on a CU; rotated by the row index so
-// that the A-operand reads hit distinct banks); its waves then walk the
-// pairs, each pair needing only weight loads. The partial product of chunk c goes to
-// a workspace [C][pairs][16 n][16 m]; a second kernel adds the C partials
-// of every output in chunk order and applies the tensor scale (one chunk:
-// the first kernel writes y directly). Results are deterministic.
+// activation rows of its chunk into LDS; its waves then walk the pairs, each
+// pair needing only weight loads. The partial product of chunk c goes to a
+// workspace [C][pairs][16 n][16 m]; a second kernel adds the C partials of
+// every output in chunk order and applies the tensor scale (one chunk: the
+// first kernel writes y directly). Results are deterministic.
 //
 // Operand layout of v_mfma_f32_16x16x32_bf16 (lane l, q = l / 16):
 //   A: row l % 16, k = 8q .. 8q+7;  B: column l % 16, k = 8q .. 8q+7;
 //   D: column l % 16, rows 4q .. 4q+3.
-// The k order inside one MFMA is free as long as A and B agree: lane
-// (q, n) takes the 16-byte piece 4t + q (t = 0..7) of weight row n and feeds
-// its elements 8j .. 8j+7 to MFMA (t, j); the A lane (q, m) reads the
-// matching activations x[m][32(4t + q) + 8j ..].
+// The k order inside one MFMA is free as long as A and B agree.
 //
-// Weight loads. In that operand layout one load instruction would touch 64
+// Two kernels, by the rows of a pass:
+// - k_gemv_mma8 (at most 8 rows): the 16 A rows are (activation row m,
+//   block parity b), A[(m, b)][k] = x[m][k] where k lies in a block of parity
+//   b, else 0. One MFMA then covers one 32-element piece (two blocks) of 16
+//   weight rows and returns the two blocks' sums separately, so the E4M3
+//   block scale (which has a mantissa) multiplies the fp32 result once per
+//   block: the codes convert straight to unscaled bf16
+//   (v_cvt_scalef32_pk_bf16_fp4 at scale 1, two per instruction). About 300
+//   vector instructions per pair instead of about 670 for the scaled decode.
+// - k_gemv_mma16 (9 to 16 rows): A rows are the 16 activation rows and each
+//   weight is decoded with its block scale to exact bf16 (E2M1 * E4M3 has at
+//   most 6 significant bits) before the MFMA; splitting blocks there would
+//   double the MFMAs, which measured slower.
+//
+// Weight loads. In the operand layout one load instruction would touch 64
 // bytes of each of 16 rows (twice the cache lines of a contiguous kilobyte)
-// and the block scales would take eight 2-byte loads per pair. Instead a wave
+// and the block scales would take many 2-byte loads per pair. Instead a wave
 // loads each tile of its pair as the M = 1 kernel does (four contiguous
 // kilobytes, rows 2i and 2i + 1 per load, and the tile's 512 scale bytes at
-// 8 bytes per lane) and moves them through a wave-private LDS region: row r
-// of tile T keeps its 16-byte pieces at slot piece ^ (r + 8T), so the writes
-// (8 lanes of one row) and the operand reads (8 or 16 lanes of consecutive
-// rows, one piece each) both spread over all banks. Only the wave that wrote
-// the region reads it, and a wave's LDS operations complete in order.
+// 8 bytes per lane) and moves them through a wave-private LDS region into the
+// operand layout, with XOR swizzles that keep the writes and the reads free
+// of bank conflicts. Only the wave that wrote the region reads it, and a
+// wave's LDS operations complete in order.
 #include <algorithm>
 
 #include <atomic>
@@ -56,7 +63,7 @@ constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9
 constexpr int kWaves = 4;                 // waves per workgroup
 constexpr int kMRows = 16;                // activation rows per pass (MFMA M)
 constexpr int kPairRows = 16;             // weight rows per pair (MFMA N)
-constexpr int kTrBytes = 8192 + 1024;           // per wave: one pair's codes and scales
+constexpr int kTrBytes = 8192 + 1024;    // per wave: one pair's codes and scales
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
@@ -93,6 +100,26 @@ __device__ __forceinline__ bf16x8_t decode8(uint32_t w, float s) {
   return __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
 }
 
+// Two E2M1 codes (byte sel of w) to two exact bf16, unscaled.
+__device__ __forceinline__ uint32_t fp4x2_bf16(uint32_t w, int sel) {
+  switch (sel) {
+    case 0: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0));
+    case 1: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1));
+    case 2: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2));
+    default: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3));
+  }
+}
+
+// E4M3 byte sel of w to fp32 (exact).
+__device__ __forceinline__ float fp8_f32(uint32_t w, int sel) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_f32_fp8((int)w, 0);
+    case 1: return __builtin_amdgcn_cvt_f32_fp8((int)w, 1);
+    case 2: return __builtin_amdgcn_cvt_f32_fp8((int)w, 2);
+    default: return __builtin_amdgcn_cvt_f32_fp8((int)w, 3);
+  }
+}
+
 struct MmaArgs {
   const uint16_t* x;   // bf16 [M][K]
   float* ws;           // [C][npairs][16][16] partials (unused when C == 1)
@@ -110,18 +137,177 @@ struct MmaArgs {
   } proj[kMaxProj];
 };
 
-// Codes (16-byte piece 4t + q of the lane's row) and the piece's two scale
-// bytes for one pair.
+// One pair's codes and scale bytes, as loaded: tile T, load i holds piece
+// lane % 32 of row 2i + lane / 32; s[T] the tile's scale bytes at 8 * lane.
 struct PairFrag {
-  uint4 w[2][4];   // tile T, load i: row 2i + (lane / 32), piece lane % 32
-  uint2 s[2];      // tile T: the tile's scale bytes at 8 * lane
+  uint4 w[2][4];
+  uint2 s[2];
 };
 
-// grid (ceil(npairs / pairs_per_wg), C); block kWaves waves. XR activation
-// rows are staged (8 when M <= 8: rows 8..15 of the A operand are zero).
-template <int XR>
-__global__ __launch_bounds__(64 * kWaves) void k_gemv_mma(const MmaArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t xs[XR * kChunkK * 2];
+__device__ __forceinline__ int proj_of(const MmaArgs& a, int pair) {
+  int p = 0;
+  while (p + 1 < a.nproj && pair >= a.proj[p + 1].pair_begin) ++p;
+  return p;
+}
+
+// Loads pair `pair` of chunk c. A pair past the workgroup's range [pb, pe)
+// gets a zero-byte resource: its loads return zeros without touching memory,
+// so every wave runs the same loads.
+__device__ __forceinline__ void load_pair(const MmaArgs& a, int pair, int pb, int pe, int c, int lane, PairFrag& f) {
+  const int C = a.C;
+  const bool v = pair < pe;
+  const int p = proj_of(a, v ? pair : pb);
+  const int lp = (v ? pair : pb) - a.proj[p].pair_begin;
+  const int G = (a.proj[p].N + 7) >> 3;
+  const int g0 = 2 * lp;
+  const int bytes = !v ? 0 : (g0 + 1 < G ? (C + 1) * kTileBytes : kTileBytes);
+  const __amdgpu_buffer_rsrc_t r = rsrc(a.proj[p].tiles + ((int64_t)g0 * C + c) * kTileBytes, bytes);
+#pragma unroll
+  for (int T = 0; T < 2; ++T) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(r, T * C * kTileBytes + i * 1024 + lane * 16, 0, 2);
+      f.w[T][i] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    const auto sv = __builtin_amdgcn_raw_buffer_load_b64(r, T * C * kTileBytes + kTileCodes + lane * 8, 0, 0);
+    f.s[T] = make_uint2(sv[0], sv[1]);
+  }
+}
+
+constexpr int kXsRow8 = 2048 + 16;   // k_gemv_mma8: staged activation row, padded for conflict-free A reads
+constexpr int kZeroWin = 256;        // k_gemv_mma8: zeros read by the A lanes of the other block parity
+
+// At most 8 activation rows (m0 .. m0+7) per launch; grid
+// (ceil(npairs / pairs_per_wg), C), block kWaves waves.
+__global__ __launch_bounds__(64 * kWaves) void k_gemv_mma8(const MmaArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t xs[8 * kXsRow8 + kZeroWin];
+  __shared__ __attribute__((aligned(16))) uint8_t tr[kWaves * kTrBytes];
+  const int lane = threadIdx.x & 63, q = lane >> 4, n16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = blockIdx.y, C = a.C, K = a.K;
+  const int pb = blockIdx.x * a.pairs_per_wg;
+  const int pe = min(pb + a.pairs_per_wg, a.npairs);
+
+  // Wave-private region in the operand layout. Pair row n (0..15: tile n / 8,
+  // row n % 8) keeps its 512 code bytes at 512 n, word w of piece p at dword
+  // ((w ^ a_n) << 5) + (((p >> 2) ^ c_n) << 2) + (p & 3), a_n = (n >> 3) ^
+  // (n & 1), c_n = n & 7: word w of four consecutive pieces is one 16-byte
+  // read, the writes (one row per half-wave) and the reads (16 rows per 16
+  // lanes) spread over all banks. Its 64 scale bytes sit at 8192 + 64 n, the
+  // scale of block 2p + b in 16-byte group (2b + (p >> 4)) ^ s_n at byte
+  // p & 15, s_n = ((n >> 1) ^ (n >> 3)) & 3.
+  uint8_t* tw = tr + wave * kTrBytes;
+  const int h = lane >> 5, l = lane & 31;
+  const int wr_code = h * 512 + (h << 7) + (((l >> 2) ^ h) << 4) + ((l & 3) << 2);
+  const int wr_scale = 8192 + h * 64 + l;
+  auto transpose_in = [&](const PairFrag& f) {
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {   // row n = 8T + 2i + h, piece l
+        const uint32_t wv[4] = {f.w[T][i].x, f.w[T][i].y, f.w[T][i].z, f.w[T][i].w};
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          *reinterpret_cast<uint32_t*>(tw + ((wr_code ^ (((w ^ T) << 7) | ((2 * i) << 4))) + (8 * T + 2 * i) * 512)) = wv[w];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {   // scale of row n, block 2l + j: byte 2i + j
+          const int byte = 2 * i + j;
+          const uint32_t word = byte < 4 ? f.s[T].x : f.s[T].y;
+          tw[(wr_scale ^ (((2 * j) ^ ((i ^ T) & 3)) << 4)) + (8 * T + 2 * i) * 64] = (uint8_t)(word >> (8 * (byte & 3)));
+        }
+      }
+    }
+  };
+  // Lane (q, n) reads word q of the pieces of row n (elements 8q .. 8q+7 of
+  // each, block parity q / 2) and the 32 scales of that parity.
+  const int an = (n16 >> 3) ^ (n16 & 1), cn = n16 & 7, sn = ((n16 >> 1) ^ (n16 >> 3)) & 3;
+  const int beta = q >> 1;
+  const int rd_code = n16 * 512 + ((q ^ an) << 7) + (cn << 4);
+  const int rd_scale0 = 8192 + n16 * 64 + (((2 * beta) ^ sn) << 4);
+  const int rd_scale1 = 8192 + n16 * 64 + (((2 * beta + 1) ^ sn) << 4);
+  // A lane (q, r) feeds MFMA row r = (activation row r % 8, parity r / 8): the
+  // activations if its k range has that parity, else zeros.
+  const bool a_valid = (n16 >> 3) == beta;
+  const int a_base = a_valid ? (n16 & 7) * kXsRow8 + 16 * q : 8 * kXsRow8;
+  const int a_step = a_valid ? 256 : 0;
+
+  PairFrag cur;
+  load_pair(a, pb + wave, pb, pe, c, lane, cur);   // in flight while the activations are staged
+
+  // activations of chunk c, rows m0 .. m0+7: row m at kXsRow8 * m, 16-byte
+  // unit u (elements 8u .. 8u+7) at 16u; then the zero window
+  {
+    const int rows = min(8, a.M - a.m0);
+    for (int t = threadIdx.x; t < 8 * 128; t += 64 * kWaves) {
+      const int m = t >> 7, u = t & 127;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (m < rows) {
+        const __amdgpu_buffer_rsrc_t rx = rsrc(a.x + (int64_t)(a.m0 + m) * K, K * 2);
+        const u32x4_t r = __builtin_amdgcn_raw_buffer_load_b128(rx, (c * kChunkK + u * 8) * 2, 0, 0);   // past K: 0
+        v = make_uint4(r[0], r[1], r[2], r[3]);
+      }
+      *reinterpret_cast<uint4*>(xs + m * kXsRow8 + u * 16) = v;
+    }
+    if (threadIdx.x < kZeroWin / 16) *reinterpret_cast<uint4*>(xs + 8 * kXsRow8 + threadIdx.x * 16) = make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();
+
+  for (int pair = pb + wave; pair < pe; pair += kWaves) {
+    PairFrag nxt;
+    load_pair(a, pair + kWaves, pb, pe, c, lane, nxt);   // next pair's loads overlap this pair's arithmetic
+    transpose_in(cur);
+    const uint4 sv0 = *reinterpret_cast<const uint4*>(tw + rd_scale0);
+    const uint4 sv1 = *reinterpret_cast<const uint4*>(tw + rd_scale1);
+    const uint32_t sw[8] = {sv0.x, sv0.y, sv0.z, sv0.w, sv1.x, sv1.y, sv1.z, sv1.w};   // byte p: piece p
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      __builtin_amdgcn_sched_barrier(0);
+      const uint4 cw = *reinterpret_cast<const uint4*>(tw + (rd_code ^ (g << 4)));
+      const uint32_t cws[4] = {cw.x, cw.y, cw.z, cw.w};
+      const int ab = a_base + g * a_step;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {   // piece p = 4g + j
+        uint32_t o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = fp4x2_bf16(cws[j], e);
+        const bf16x8_t b = __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(xs + ab + 64 * j);
+        const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        const float sc = fp8_f32(sw[g], j);   // scale of block 2p + q / 2
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(sc, d[i], acc[i]);
+      }
+    }
+    // lane (q, n) holds parity q / 2 of rows 4 (q % 2) + i; the lane 32 apart
+    // holds the other parity of the same rows
+    f32x4_t tot;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tot[i] = acc[i] + __shfl_xor(acc[i], 32);
+    if (q < 2) {   // rows 4q .. 4q+3
+      if (C == 1) {
+        const int p = proj_of(a, pair);
+        const int n = 16 * (pair - a.proj[p].pair_begin) + n16;
+        const float gs = *a.proj[p].gscale;
+        if (n < a.proj[p].N) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int m = a.m0 + 4 * q + i;
+            if (m < a.M) a.proj[p].y[(int64_t)m * a.proj[p].ldy + n] = gs * tot[i];
+          }
+        }
+      } else if (a.m0 + 4 * q < a.M) {   // rows past M are never read back
+        float* dst = a.ws + ((int64_t)c * a.npairs + pair) * 256 + n16 * 16 + 4 * q;
+        *reinterpret_cast<f32x4_t*>(dst) = tot;
+      }
+    }
+    cur = nxt;
+  }
+}
+
+// 9 to 16 activation rows (m0 .. m0+15) per launch; grid and block as above.
+__global__ __launch_bounds__(64 * kWaves) void k_gemv_mma16(const MmaArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t xs[kMRows * kChunkK * 2];
   __shared__ __attribute__((aligned(16))) uint8_t tr[kWaves * kTrBytes];
   const int lane = threadIdx.x & 63, q = lane >> 4, n16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -130,33 +316,12 @@ __global__ __launch_bounds__(64 * kWaves) void k_gemv_mma(const MmaArgs a) {
   const int pe = min(pb + a.pairs_per_wg, a.npairs);
   const int rr = n16 & 7;
 
-  auto proj_of = [&](int pair) {
-    int p = 0;
-    while (p + 1 < a.nproj && pair >= a.proj[p + 1].pair_begin) ++p;
-    return p;
-  };
-  // A pair past the workgroup's range gets a zero-byte resource: its loads
-  // return zeros without touching memory, so every wave runs the same loads.
-  auto load_pair = [&](int pair, PairFrag& f) {
-    const bool v = pair < pe;
-    const int p = proj_of(v ? pair : pb);
-    const int lp = (v ? pair : pb) - a.proj[p].pair_begin;
-    const int G = (a.proj[p].N + 7) >> 3;
-    const int g0 = 2 * lp;
-    const int bytes = !v ? 0 : (g0 + 1 < G ? (C + 1) * kTileBytes : kTileBytes);
-    const __amdgpu_buffer_rsrc_t r = rsrc(a.proj[p].tiles + ((int64_t)g0 * C + c) * kTileBytes, bytes);
-#pragma unroll
-    for (int T = 0; T < 2; ++T) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(r, T * C * kTileBytes + i * 1024 + lane * 16, 0, 2);
-        f.w[T][i] = make_uint4(w[0], w[1], w[2], w[3]);
-      }
-      const auto sv = __builtin_amdgcn_raw_buffer_load_b64(r, T * C * kTileBytes + kTileCodes + lane * 8, 0, 0);
-      f.s[T] = make_uint2(sv[0], sv[1]);
-    }
-  };
-  // wave-private transposition region: codes [T][row][piece ^ (row + 8T)] x 16 B, scales [T][512 B]
+  // Lane (q, n) takes the 16-byte piece 4t + q (t = 0..7) of weight row n and
+  // feeds its elements 8j .. 8j+7 to MFMA (t, j); the A lane (q, m) reads the
+  // matching activations x[m][32(4t + q) + 8j ..]. Wave-private region: codes
+  // [T][row][piece ^ (row + 8T)] x 16 B (the writes, 8 lanes of one row, and
+  // the reads, 16 lanes of consecutive rows, spread over all banks), then the
+  // two tiles' 512 scale bytes as loaded.
   uint8_t* tw = tr + wave * kTrBytes;
   auto transpose_in = [&](const PairFrag& f) {
     const int h = lane >> 5, l = lane & 31;
@@ -171,13 +336,13 @@ __global__ __launch_bounds__(64 * kWaves) void k_gemv_mma(const MmaArgs a) {
     }
   };
   PairFrag cur;
-  load_pair(pb + wave, cur);   // in flight while the activations are staged
+  load_pair(a, pb + wave, pb, pe, c, lane, cur);   // in flight while the activations are staged
 
-  // ---- activations of chunk c, rows m0 .. m0+15, into LDS: row m at 2048m,
-  // 16-byte unit u stored at position (u + m) & 127
+  // activations of chunk c, rows m0 .. m0+15: row m at 2048m, 16-byte unit u
+  // stored at position (u + m) & 127
   {
-    const int rows = min(XR, a.M - a.m0);
-    for (int t = threadIdx.x; t < XR * 128; t += 64 * kWaves) {
+    const int rows = min(kMRows, a.M - a.m0);
+    for (int t = threadIdx.x; t < kMRows * 128; t += 64 * kWaves) {
       const int m = t >> 7, u = t & 127;
       uint4 v = make_uint4(0, 0, 0, 0);
       if (m < rows) {
@@ -192,7 +357,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_gemv_mma(const MmaArgs a) {
 
   for (int pair = pb + wave; pair < pe; pair += kWaves) {
     PairFrag nxt;
-    load_pair(pair + kWaves, nxt);   // next pair's loads overlap this pair's arithmetic
+    load_pair(a, pair + kWaves, pb, pe, c, lane, nxt);   // next pair's loads overlap this pair's arithmetic
     // two accumulators (even and odd pieces) halve the dependent MFMA chain
     f32x4_t acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     transpose_in(cur);
@@ -210,16 +375,14 @@ __global__ __launch_bounds__(64 * kWaves) void k_gemv_mma(const MmaArgs a) {
       for (int j = 0; j < 4; ++j) {
         const bf16x8_t b = decode8(word(wv, j), j < 2 ? s0 : s1);
         const int u = 16 * t + 4 * q + j;
-        const int xr = XR == kMRows ? n16 : (n16 & (XR - 1));
-        bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(xs + xr * 2048 + ((u + xr) & 127) * 16);
-        if (XR < kMRows && n16 >= XR) av = bf16x8_t{};
+        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(xs + n16 * 2048 + ((u + n16) & 127) * 16);
         acc2[t & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b, acc2[t & 1], 0, 0, 0);
       }
     }
     const f32x4_t acc = acc2[0] + acc2[1];
     // lane (q, n16) holds D[m = 4q + i][n = n16]
     if (C == 1) {
-      const int p = proj_of(pair);
+      const int p = proj_of(a, pair);
       const int n = 16 * (pair - a.proj[p].pair_begin) + n16;
       const float gs = *a.proj[p].gscale;
       if (n < a.proj[p].N) {
@@ -271,9 +434,9 @@ __global__ __launch_bounds__(256) void k_reduce(const MmaArgs a) {
   }
 }
 
-// Workgroups of k_gemv_mma<XR> resident per CU (LDS-bound: 3 for XR = 8,
-// 2 for XR = 16 on MI355X), cached per device; 0 if unknown.
-template <int XR>
+// Workgroups of the kernel resident per CU (LDS-bound: 3 for k_gemv_mma8,
+// 2 for k_gemv_mma16 on MI355X), cached per device; 0 if unknown.
+template <bool EIGHT>
 int resident_per_cu() {
   constexpr int kMaxDevices = 64;
   static std::atomic<int> cached[kMaxDevices];
@@ -281,7 +444,7 @@ int resident_per_cu() {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
   int n = cached[dev].load(std::memory_order_relaxed);
   if (n == 0) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_gemv_mma<XR>, 64 * kWaves, 0) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, EIGHT ? k_gemv_mma8 : k_gemv_mma16, 64 * kWaves, 0) != hipSuccess) return 0;
     cached[dev].store(n, std::memory_order_relaxed);
   }
   return n;
@@ -342,12 +505,12 @@ hipError_t launch_gemv_mma(const GemvArgs& g, hipStream_t s, int ppw) {
   for (int m0 = 0; m0 < g.M; m0 += kMRows) {
     a.m0 = m0;
     const bool eight = g.M - m0 <= 8;
-    a.pairs_per_wg = ppw > 0 ? ppw : pick_pairs_per_wg(pairs, a.C, ncu * (eight ? resident_per_cu<8>() : resident_per_cu<kMRows>()));
+    a.pairs_per_wg = ppw > 0 ? ppw : pick_pairs_per_wg(pairs, a.C, ncu * (eight ? resident_per_cu<true>() : resident_per_cu<false>()));
     const int64_t wgx = (pairs + a.pairs_per_wg - 1) / a.pairs_per_wg;
     if (eight)
-      hipLaunchKernelGGL(k_gemv_mma<8>, dim3((unsigned)wgx, (unsigned)a.C), dim3(64 * kWaves), 0, s, a);
+      hipLaunchKernelGGL(k_gemv_mma8, dim3((unsigned)wgx, (unsigned)a.C), dim3(64 * kWaves), 0, s, a);
     else
-      hipLaunchKernelGGL(k_gemv_mma<kMRows>, dim3((unsigned)wgx, (unsigned)a.C), dim3(64 * kWaves), 0, s, a);
+      hipLaunchKernelGGL(k_gemv_mma16, dim3((unsigned)wgx, (unsigned)a.C), dim3(64 * kWaves), 0, s, a);
     if (a.C > 1) {
       const int64_t n = pairs * 16 * ((std::min(kMRows, g.M - m0) + 3) / 4);
       hipLaunchKernelGGL(k_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
