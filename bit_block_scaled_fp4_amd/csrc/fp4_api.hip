@@ -93,6 +93,12 @@ int fp4_retile(const void* packed_rm, const void* scales_rm, int64_t N, int64_t 
                                        N, K, static_cast<uint8_t*>(packed_tiled), static_cast<hipStream_t>(stream)));
 }
 
+// Whether 3 or 4 activation rows go to the matrix cores: at least 32 MiB
+// of weights in at most 8 K chunks.
+static bool gemv_mma_pays(int64_t groups, int64_t chunks) {
+  return chunks <= 8 && groups * chunks * fp4::kTileBytes >= (int64_t(32) << 20);
+}
+
 int fp4_gemv_multi(const fp4_proj* projs, int nproj, const void* x_bf16, int64_t M, int64_t K, void* stream) {
   if (!projs || !x_bf16) return FP4_ERR_NULL;
   if (nproj < 1 || nproj > FP4_MAX_PROJ || M < 1 || M > kMaxM) return FP4_ERR_SHAPE;
@@ -118,10 +124,15 @@ int fp4_gemv_multi(const fp4_proj* projs, int nproj, const void* x_bf16, int64_t
     groups += fp4::groups_of(p.N);
   }
   if (groups > (int64_t(1) << 30)) return FP4_ERR_SHAPE;
-  // Up to four activation rows: the vector-ALU kernel (decode once, two
-  // products per weight and row). From five rows on the weights are decoded
-  // once to bf16 and multiplied on the matrix cores.
-  if (M <= 4) return hip_status(fp4::launch_gemv(a, static_cast<hipStream_t>(stream)));
+  // Few activation rows: the vector-ALU kernel (decode once, two products per
+  // weight and row, no second launch). From five rows on, and from three on
+  // large launches with few K chunks, the matrix cores: their 8-row kernel
+  // costs about the same at 3 to 8 rows, and their split over K chunks adds
+  // a reduce launch that a large launch with few chunks amortises. MI355X, 4
+  // rows: fused gate_up 2 x 17408 x 5120 28.2 against 30.7 us, LM head
+  // 151936 x 1024 24.3 against 29.8 us; down 5120 x 17408 (17 chunks) 22.8
+  // against 21.3 us, so it stays on the vector ALUs.
+  if (M <= 4 && !(M >= 3 && gemv_mma_pays(groups, a.C))) return hip_status(fp4::launch_gemv(a, static_cast<hipStream_t>(stream)));
   return hip_status(fp4::launch_gemv_mma(a, static_cast<hipStream_t>(stream)));
 }
 

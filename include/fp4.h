@@ -47,7 +47,9 @@
  *   - Pointers marked "device" are HIP device memory (e.g. a torch CUDA
  *     tensor's data_ptr()) on the current HIP device; the caller owns every
  *     buffer. Exceptions to "the library allocates nothing": fp4_gemv
- *     and fp4_gemv_multi with M >= 5 and K > 1024 keep the per-chunk
+ *     and fp4_gemv_multi on the matrix-core path (M >= 5; M = 3 or 4 when
+ *     the call reads at least 32 MiB of weights and K <= 8192) with
+ *     K > 1024 keep the per-chunk
  *     partial sums in a per-device workspace (C * ceil(N/16) * 1 KiB, C =
  *     ceil(K/1024), summed over the projections) that the library
  *     allocates with hipMalloc on the first call that needs it (or needs

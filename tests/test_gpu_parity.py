@@ -306,6 +306,20 @@ def test_gemv_workload_lm_head(M):
     assert_within_tolerance(y.cpu().numpy(), yr, l1, "lm_head M=%d" % M)
 
 
+@pytest.mark.parametrize("M", [3, 4])
+def test_gemv_lm_head_three_and_four_rows(M):
+    """3 or 4 rows on a call of at least 32 MiB with at most 8 K chunks go to
+    the matrix cores (the LM head: one chunk, 87 MB); the rows are the first
+    M of the LM head's 8-row activations."""
+    bw, bx = weight_bits("lm_head", "w"), act_bits("lm_head", "x_m8")[:M]
+    w = gpu_quant(bw)
+    y = fp4.gemv(to_gpu_bf16(bx), w)
+    torch.cuda.synchronize()
+    p, s, g = oracle_quant("lm_head", "w")
+    yr, l1 = oracle.gemv(bx, p, s, g, threads=THREADS)
+    assert_within_tolerance(y.cpu().numpy(), yr, l1, "lm_head M=%d" % M)
+
+
 def test_gemv_multi_equals_oracle_for_each_projection_and_is_deterministic():
     rng_shapes = [(2048, 1024), (1024, 1024), (1024, 1024), (333, 1024)]
     ws, bws = [], []
