@@ -199,12 +199,15 @@ def test_extreme_shapes(N, K, Ms):
         assert_within_tolerance(yp.cpu().numpy(), yr, l1, "extreme prefill %dx%d M=%d" % (N, K, M))
 
 
-def test_gemv_exact_when_every_partial_sum_is_exact():
+@pytest.mark.parametrize("M", [3, 6, 12])
+def test_gemv_exact_when_every_partial_sum_is_exact(M):
     """Every block holds 2.625 (so all scales are 0x7E and gscale = 2^-10) and
-    x is +-2^k: every product and partial sum is exact in fp32, so the GPU
-    result must equal the exact oracle value bit for bit."""
+    x is +-2^k: every product and partial sum, in any order, is exact in fp32
+    (multiples of 2^-4 below 2^17, times 448), so the GPU result must equal
+    the exact oracle value bit for bit. M = 3: vector ALUs; 6: the block-split
+    matrix-core kernel; 12: the 16-row one (both with the K-chunk reduce)."""
     rng = np.random.default_rng(21)
-    N, K, M = 48, 2048, 3
+    N, K = 48, 2048
     mags = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6]) * 0.4375
     W = rng.choice(mags, (N, K)) * rng.choice([-1, 1], (N, K))
     W[:, ::16] = 2.625
@@ -220,6 +223,25 @@ def test_gemv_exact_when_every_partial_sum_is_exact():
     yp = fp4.gemm_prefill(to_gpu_bf16(bx), w)
     torch.cuda.synchronize()
     assert np.array_equal(yp.cpu().numpy().astype(np.float64), yr)
+
+
+@pytest.mark.parametrize("M", [3, 5, 8, 12])
+def test_gemv_block_scales_alternate_by_parity(M):
+    """Even 16-element blocks are 1000 times smaller than odd ones, with the
+    ratio varied per row, so a block scale applied to the other block of its
+    piece (the matrix-core kernels handle the two blocks of a 32-element
+    piece in different rows or lanes) moves y far outside the tolerance."""
+    rng = np.random.default_rng(23 + M)
+    N, K = 40, 3072
+    W = rng.normal(0, 1, (N, K))
+    parity = (np.arange(K) // 16) % 2
+    W *= np.where(parity == 0, 1e-3, 1.0)[None, :] * rng.uniform(0.5, 2.0, (N, 1))
+    bw = float32_to_bf16_bits(W.astype(np.float32))
+    bx = float32_to_bf16_bits(rng.normal(0, 1, (M, K)).astype(np.float32))
+    y = run_gemv(bw, bx)
+    p, s, g = oracle.quantize(bw)
+    yr, l1 = oracle.gemv(bx, p, s, g)
+    assert_within_tolerance(y, yr, l1, "alternating block scales M=%d" % M)
 
 
 def test_gemv_one_hot_selects_a_column():
