@@ -197,6 +197,10 @@ __global__ __launch_bounds__(64 * kWaves) void k_gemv_mma8(const MmaArgs a) {
   // scale of block 2p + b in 16-byte group (2b + (p >> 4)) ^ s_n at byte
   // p & 15, s_n = ((n >> 1) ^ (n >> 3)) & 3.
   uint8_t* tw = tr + wave * kTrBytes;
+  // Write addresses with the fields that depend on (T, i, w) left at zero:
+  // a write XORs (w ^ T) into bits 7..8 (the word field, a_n = T ^ h) and 2i
+  // into bits 4..6 (the piece-group field, c_n = 2i + h), then adds the row
+  // base 512 (8T + 2i); likewise for the scales (s_n = (i ^ T) & 3).
   const int h = lane >> 5, l = lane & 31;
   const int wr_code = h * 512 + (h << 7) + (((l >> 2) ^ h) << 4) + ((l & 3) << 2);
   const int wr_scale = 8192 + h * 64 + l;
