@@ -7,7 +7,9 @@ memory and streams. There is no CPU fallback: without the built library the
 import fails, and CPU tensors are rejected.
 
 Names follow the C ABI: quantize, quantize_fp8, retile, gemv, gemv_multi, gemm_prefill,
-argmax_rows, lm_head_greedy, layout_bytes.
+gemm_prefill_multi, argmax_rows, lm_head_greedy, layout_bytes, workspace_bytes. The
+products take an optional `workspace` (a zero-filled uint8 GPU tensor, see
+new_workspace), which selects the C ABI's *_ws forms.
 """
 from __future__ import annotations
 
@@ -24,6 +26,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "fp4.h")
 
 ROWMAJOR, TILED = 0, 1
 MAX_PROJ = 8
+OP_GEMV, OP_GEMM_PREFILL, OP_ARGMAX_ROWS, OP_LM_HEAD_GREEDY = 0, 1, 2, 3
 _LAYOUTS = {"rowmajor": ROWMAJOR, "tiled": TILED, ROWMAJOR: ROWMAJOR, TILED: TILED}
 
 if not os.path.exists(LIB_PATH):
@@ -44,14 +47,21 @@ _lib.fp4_layout_bytes.argtypes = [_I64, _I64, _I, ctypes.POINTER(ctypes.c_size_t
 _lib.fp4_quantize.argtypes = [_P, _I64, _I64, _I, _P, _P, _P, _P]
 _lib.fp4_quantize_fp8.argtypes = [_P, _P, _I64, _I64, _I, _P, _P, _P, _P]
 _lib.fp4_retile.argtypes = [_P, _P, _I64, _I64, _P, _P, _P]
+_SZ = ctypes.c_size_t
 _lib.fp4_gemv.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]
+_lib.fp4_gemv_ws.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P]
 _lib.fp4_gemv_multi.argtypes = [ctypes.POINTER(_Proj), _I, _P, _I64, _I64, _P]
+_lib.fp4_gemv_multi_ws.argtypes = [ctypes.POINTER(_Proj), _I, _P, _I64, _I64, _P, _SZ, _P]
 _lib.fp4_gemm_prefill.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]
+_lib.fp4_gemm_prefill_ws.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P]
 _lib.fp4_gemm_prefill_multi.argtypes = [ctypes.POINTER(_Proj), _I, _P, _I64, _I64, _P]
-_lib.fp4_argmax_rows.argtypes = [_P, _P, _I64, _I64, _I64, _P]
-_lib.fp4_lm_head_greedy.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]
-for _f in ("fp4_layout_bytes", "fp4_quantize", "fp4_quantize_fp8", "fp4_retile", "fp4_gemv", "fp4_gemv_multi", "fp4_gemm_prefill",
-           "fp4_gemm_prefill_multi", "fp4_argmax_rows", "fp4_lm_head_greedy"):
+_lib.fp4_gemm_prefill_multi_ws.argtypes = [ctypes.POINTER(_Proj), _I, _P, _I64, _I64, _P, _SZ, _P]
+_lib.fp4_argmax_rows.argtypes = [_P, _P, _I64, _I64, _I64, _P, _SZ, _P]
+_lib.fp4_lm_head_greedy.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P]
+_lib.fp4_workspace_bytes.argtypes = [_I, _I64, _I64, ctypes.POINTER(_I64), _I, ctypes.POINTER(_SZ)]
+for _f in ("fp4_layout_bytes", "fp4_quantize", "fp4_quantize_fp8", "fp4_retile", "fp4_gemv", "fp4_gemv_ws",
+           "fp4_gemv_multi", "fp4_gemv_multi_ws", "fp4_gemm_prefill", "fp4_gemm_prefill_ws", "fp4_gemm_prefill_multi",
+           "fp4_gemm_prefill_multi_ws", "fp4_argmax_rows", "fp4_lm_head_greedy", "fp4_workspace_bytes"):
     getattr(_lib, _f).restype = _I
 
 
@@ -87,6 +97,30 @@ def layout_bytes(N: int, K: int, layout="tiled"):
     pb, sb = ctypes.c_size_t(), ctypes.c_size_t()
     _check(_lib.fp4_layout_bytes(N, K, _LAYOUTS[layout], ctypes.byref(pb), ctypes.byref(sb)), "fp4_layout_bytes")
     return pb.value, sb.value
+
+
+def workspace_bytes(op: int, M: int, K: int, Ns: Sequence[int]) -> int:
+    """fp4_workspace_bytes: workspace bytes a call of `op` (OP_GEMV,
+    OP_GEMM_PREFILL, OP_ARGMAX_ROWS, OP_LM_HEAD_GREEDY) needs on the current
+    device for M rows, K inputs and projections of Ns[i] outputs."""
+    n = len(Ns)
+    arr = (_I64 * max(1, n))(*Ns)
+    out = ctypes.c_size_t()
+    _check(_lib.fp4_workspace_bytes(int(op), M, K, arr, n, ctypes.byref(out)), "fp4_workspace_bytes")
+    return out.value
+
+
+def new_workspace(nbytes: int, device=None) -> torch.Tensor:
+    """A zero-filled uint8 GPU tensor to pass as `workspace` (at least 1 byte;
+    torch's allocator aligns it to 512 bytes). Allocate it once and reuse it
+    for calls that run one after another."""
+    return torch.zeros(max(1, int(nbytes)), dtype=torch.uint8, device=device or torch.device("cuda"))
+
+
+def _ws(ws: Optional[torch.Tensor]):
+    if ws is None:
+        return None, 0
+    return _dev(ws, "workspace", torch.uint8), ws.numel()
 
 
 @dataclass
@@ -174,15 +208,21 @@ def _out(out: Optional[torch.Tensor], shape, dtype, device, name: str) -> torch.
     return out
 
 
-def gemv(x: torch.Tensor, w: NVFP4Weight, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """fp4_gemv: y[M][N] = x[M][K] @ dequant(w)^T (fp32), x bf16, w tiled."""
+def gemv(x: torch.Tensor, w: NVFP4Weight, out: Optional[torch.Tensor] = None,
+         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp4_gemv (fp4_gemv_ws with a workspace): y[M][N] = x[M][K] @ dequant(w)^T
+    (fp32), x bf16, w tiled."""
     x, M, K = _x2d(x)
     if K != w.K:
         raise ValueError("x has K=%d, weight has K=%d" % (K, w.K))
     out = _out(out, (M, w.N), torch.float32, x.device, "out")
     _tiled(w)
-    _check(_lib.fp4_gemv(_dev(out, "y", torch.float32), _dev(x, "x", torch.bfloat16), _dev(w.packed, "packed"),
-                         None, _dev(w.gscale, "gscale", torch.float32), M, w.N, K, _stream(x.device)), "fp4_gemv")
+    args = (_dev(out, "y", torch.float32), _dev(x, "x", torch.bfloat16), _dev(w.packed, "packed"), None,
+            _dev(w.gscale, "gscale", torch.float32), M, w.N, K)
+    if workspace is None:
+        _check(_lib.fp4_gemv(*args, _stream(x.device)), "fp4_gemv")
+    else:
+        _check(_lib.fp4_gemv_ws(*args, *_ws(workspace), _stream(x.device)), "fp4_gemv_ws")
     return out
 
 
@@ -208,37 +248,52 @@ def _projs(M: int, K: int, weights: Sequence[NVFP4Weight], outs: Sequence[torch.
 
 
 def gemv_multi(x: torch.Tensor, weights: Sequence[NVFP4Weight], outs: Sequence[torch.Tensor],
-               ldys: Optional[Sequence[int]] = None) -> None:
-    """fp4_gemv_multi: one launch computing outs[i][m][n] (row stride ldys[i]) for every weight."""
+               ldys: Optional[Sequence[int]] = None, workspace: Optional[torch.Tensor] = None) -> None:
+    """fp4_gemv_multi (fp4_gemv_multi_ws with a workspace): one launch computing
+    outs[i][m][n] (row stride ldys[i]) for every weight."""
     x, M, K = _x2d(x)
     arr, n = _projs(M, K, weights, outs, ldys)
-    _check(_lib.fp4_gemv_multi(arr, n, _dev(x, "x", torch.bfloat16), M, K, _stream(x.device)), "fp4_gemv_multi")
+    if workspace is None:
+        _check(_lib.fp4_gemv_multi(arr, n, _dev(x, "x", torch.bfloat16), M, K, _stream(x.device)), "fp4_gemv_multi")
+    else:
+        _check(_lib.fp4_gemv_multi_ws(arr, n, _dev(x, "x", torch.bfloat16), M, K, *_ws(workspace), _stream(x.device)),
+               "fp4_gemv_multi_ws")
 
 
 def gemm_prefill_multi(x: torch.Tensor, weights: Sequence[NVFP4Weight], outs: Sequence[torch.Tensor],
-                       ldys: Optional[Sequence[int]] = None) -> None:
-    """fp4_gemm_prefill_multi: one matrix-core launch computing outs[i][m][n]
-    (row stride ldys[i]) for every weight."""
+                       ldys: Optional[Sequence[int]] = None, workspace: Optional[torch.Tensor] = None) -> None:
+    """fp4_gemm_prefill_multi (fp4_gemm_prefill_multi_ws with a workspace): one
+    matrix-core launch computing outs[i][m][n] (row stride ldys[i]) for every weight."""
     x, M, K = _x2d(x)
     arr, n = _projs(M, K, weights, outs, ldys)
-    _check(_lib.fp4_gemm_prefill_multi(arr, n, _dev(x, "x", torch.bfloat16), M, K, _stream(x.device)),
-           "fp4_gemm_prefill_multi")
+    if workspace is None:
+        _check(_lib.fp4_gemm_prefill_multi(arr, n, _dev(x, "x", torch.bfloat16), M, K, _stream(x.device)),
+               "fp4_gemm_prefill_multi")
+    else:
+        _check(_lib.fp4_gemm_prefill_multi_ws(arr, n, _dev(x, "x", torch.bfloat16), M, K, *_ws(workspace),
+                                              _stream(x.device)), "fp4_gemm_prefill_multi_ws")
 
 
-def gemm_prefill(x: torch.Tensor, w: NVFP4Weight, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """fp4_gemm_prefill: the same product on bf16 MFMA for prefill-sized M."""
+def gemm_prefill(x: torch.Tensor, w: NVFP4Weight, out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp4_gemm_prefill (fp4_gemm_prefill_ws with a workspace): the same product
+    on bf16 MFMA for prefill-sized M."""
     x, M, K = _x2d(x)
     if K != w.K:
         raise ValueError("x has K=%d, weight has K=%d" % (K, w.K))
     out = _out(out, (M, w.N), torch.float32, x.device, "out")
     _tiled(w)
-    _check(_lib.fp4_gemm_prefill(_dev(out, "y", torch.float32), _dev(x, "x", torch.bfloat16),
-                                 _dev(w.packed, "packed"), None, _dev(w.gscale, "gscale", torch.float32), M, w.N, K,
-                                 _stream(x.device)), "fp4_gemm_prefill")
+    args = (_dev(out, "y", torch.float32), _dev(x, "x", torch.bfloat16), _dev(w.packed, "packed"), None,
+            _dev(w.gscale, "gscale", torch.float32), M, w.N, K)
+    if workspace is None:
+        _check(_lib.fp4_gemm_prefill(*args, _stream(x.device)), "fp4_gemm_prefill")
+    else:
+        _check(_lib.fp4_gemm_prefill_ws(*args, *_ws(workspace), _stream(x.device)), "fp4_gemm_prefill_ws")
     return out
 
 
-def argmax_rows(y: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+def argmax_rows(y: torch.Tensor, out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """fp4_argmax_rows: int32 [M], per row of fp32 y [M][N] (or [N]) the first
     index of the largest value (NaN above every number, -0 equal to +0)."""
     y2 = y.view(1, -1) if y.dim() == 1 else y
@@ -247,12 +302,12 @@ def argmax_rows(y: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Te
     M, N = y2.shape
     out = _out(out, (M,), torch.int32, y.device, "out")
     _check(_lib.fp4_argmax_rows(_dev(out, "idx", torch.int32), _dev(y2, "y", torch.float32), M, N, N,
-                                _stream(y.device)), "fp4_argmax_rows")
+                                *_ws(workspace), _stream(y.device)), "fp4_argmax_rows")
     return out
 
 
 def lm_head_greedy(x: torch.Tensor, w: NVFP4Weight, logits: Optional[torch.Tensor] = None,
-                   out: Optional[torch.Tensor] = None):
+                   out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
     """fp4_lm_head_greedy: (idx int32 [M], logits fp32 [M][N]) with logits =
     x @ dequant(w)^T and idx the greedy choice of each row."""
     x, M, K = _x2d(x)
@@ -263,8 +318,8 @@ def lm_head_greedy(x: torch.Tensor, w: NVFP4Weight, logits: Optional[torch.Tenso
     _tiled(w)
     _check(_lib.fp4_lm_head_greedy(_dev(out, "idx", torch.int32), _dev(logits, "logits", torch.float32),
                                    _dev(x, "x", torch.bfloat16), _dev(w.packed, "packed"), None,
-                                   _dev(w.gscale, "gscale", torch.float32), M, w.N, K, _stream(x.device)),
-           "fp4_lm_head_greedy")
+                                   _dev(w.gscale, "gscale", torch.float32), M, w.N, K, *_ws(workspace),
+                                   _stream(x.device)), "fp4_lm_head_greedy")
     return out, logits
 
 
@@ -273,6 +328,7 @@ def raw():
     return _lib
 
 
-__all__ = ["quantize", "quantize_fp8", "retile", "gemv", "gemv_multi", "gemm_prefill", "argmax_rows", "lm_head_greedy",
-           "layout_bytes", "NVFP4Weight",
+__all__ = ["quantize", "quantize_fp8", "retile", "gemv", "gemv_multi", "gemm_prefill", "gemm_prefill_multi",
+           "argmax_rows", "lm_head_greedy", "layout_bytes", "workspace_bytes", "new_workspace", "NVFP4Weight",
+           "OP_GEMV", "OP_GEMM_PREFILL", "OP_ARGMAX_ROWS", "OP_LM_HEAD_GREEDY",
            "Fp4Error", "raw", "ROWMAJOR", "TILED", "LIB_PATH", "HEADER_PATH"]

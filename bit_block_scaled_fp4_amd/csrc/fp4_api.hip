@@ -2,6 +2,7 @@
 // checks on the host, then kernel launches on the caller's stream.
 #include "../../include/fp4.h"
 
+#include <algorithm>
 #include <cstdint>
 
 #include "fp4_internal.h"
@@ -35,6 +36,7 @@ const char* fp4_status_string(int status) {
     case FP4_ERR_LAYOUT: return "unknown layout tag";
     case FP4_ERR_HIP: return "HIP launch failed";
     case FP4_ERR_UNSUPPORTED: return "unsupported request";
+    case FP4_ERR_WORKSPACE: return "workspace smaller than fp4_workspace_bytes reports";
     default: return "unknown status";
   }
 }
@@ -99,11 +101,26 @@ static bool gemv_mma_pays(int64_t groups, int64_t chunks) {
   return chunks <= 8 && groups * chunks * fp4::kTileBytes >= (int64_t(32) << 20);
 }
 
-int fp4_gemv_multi(const fp4_proj* projs, int nproj, const void* x_bf16, int64_t M, int64_t K, void* stream) {
+// Few activation rows: the vector-ALU kernel (decode once, two products per
+// weight and row, no second launch). From five rows on, and from three on
+// large launches with few K chunks, the matrix cores: their 8-row kernel
+// costs about the same at 3 to 8 rows, and their split over K chunks adds a
+// second launch that a large launch with few chunks amortises. MI355X, 4
+// rows: fused gate_up 2 x 17408 x 5120 28.2 against 30.7 us, LM head
+// 151936 x 1024 24.3 against 29.8 us; down 5120 x 17408 (17 chunks) 22.8
+// against 21.3 us, so it stays on the vector ALUs.
+static bool gemv_on_valu(const fp4::GemvArgs& a) {
+  int64_t groups = 0;
+  for (int i = 0; i < a.nproj; ++i) groups += fp4::groups_of(a.proj[i].N);
+  return a.M <= 4 && !(a.M >= 3 && gemv_mma_pays(groups, a.C));
+}
+
+// Checks the projections of a fused product and fills `a`.
+static int gemv_args(const fp4_proj* projs, int nproj, const void* x_bf16, int64_t M, int64_t K, fp4::GemvArgs& a) {
   if (!projs || !x_bf16) return FP4_ERR_NULL;
   if (nproj < 1 || nproj > FP4_MAX_PROJ || M < 1 || M > kMaxM) return FP4_ERR_SHAPE;
   if (!aligned(x_bf16, 16)) return FP4_ERR_ALIGN;
-  fp4::GemvArgs a{};
+  a = fp4::GemvArgs{};
   a.x = static_cast<const uint16_t*>(x_bf16);
   a.M = (int32_t)M;
   a.K = (int32_t)K;
@@ -124,27 +141,57 @@ int fp4_gemv_multi(const fp4_proj* projs, int nproj, const void* x_bf16, int64_t
     groups += fp4::groups_of(p.N);
   }
   if (groups > (int64_t(1) << 30)) return FP4_ERR_SHAPE;
-  // Few activation rows: the vector-ALU kernel (decode once, two products per
-  // weight and row, no second launch). From five rows on, and from three on
-  // large launches with few K chunks, the matrix cores: their 8-row kernel
-  // costs about the same at 3 to 8 rows, and their split over K chunks adds
-  // a reduce launch that a large launch with few chunks amortises. MI355X, 4
-  // rows: fused gate_up 2 x 17408 x 5120 28.2 against 30.7 us, LM head
-  // 151936 x 1024 24.3 against 29.8 us; down 5120 x 17408 (17 chunks) 22.8
-  // against 21.3 us, so it stays on the vector ALUs.
-  if (M <= 4 && !(M >= 3 && gemv_mma_pays(groups, a.C))) return hip_status(fp4::launch_gemv(a, static_cast<hipStream_t>(stream)));
-  return hip_status(fp4::launch_gemv_mma(a, static_cast<hipStream_t>(stream)));
+  return FP4_OK;
+}
+
+// Workspace bytes a product with these arguments uses (0: none).
+static size_t gemv_ws_need(const fp4::GemvArgs& a) { return gemv_on_valu(a) ? 0 : fp4::gemv_mma_ws_bytes(a); }
+
+// A caller's workspace: NULL means none; otherwise 256-byte aligned and at
+// least `need` bytes.
+static int take_ws(void* workspace, size_t bytes, size_t need, fp4::Workspace& ws) {
+  ws = fp4::Workspace{};
+  if (!workspace) return FP4_OK;
+  if (!aligned(workspace, 256)) return FP4_ERR_ALIGN;
+  if (bytes < need) return FP4_ERR_WORKSPACE;
+  ws.p = static_cast<uint8_t*>(workspace);
+  ws.bytes = bytes;
+  return FP4_OK;
+}
+
+static int gemv_run(const fp4::GemvArgs& a, const fp4::Workspace& ws, hipStream_t s) {
+  if (gemv_on_valu(a)) return hip_status(fp4::launch_gemv(a, s));
+  return hip_status(fp4::launch_gemv_mma(a, ws, s));
+}
+
+int fp4_gemv_multi_ws(const fp4_proj* projs, int nproj, const void* x_bf16, int64_t M, int64_t K, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  fp4::GemvArgs a;
+  if (int st = gemv_args(projs, nproj, x_bf16, M, K, a)) return st;
+  fp4::Workspace ws;
+  if (int st = take_ws(workspace, workspace_bytes, gemv_ws_need(a), ws)) return st;
+  return gemv_run(a, ws, static_cast<hipStream_t>(stream));
+}
+
+int fp4_gemv_multi(const fp4_proj* projs, int nproj, const void* x_bf16, int64_t M, int64_t K, void* stream) {
+  return fp4_gemv_multi_ws(projs, nproj, x_bf16, M, K, nullptr, 0, stream);
+}
+
+int fp4_gemv_ws(float* y, const void* x_bf16, const void* packed, const void* scales, const float* gscale, int64_t M,
+                int64_t N, int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!y || !x_bf16 || !packed || !gscale) return FP4_ERR_NULL;
+  fp4_proj p{packed, scales, gscale, N, y, N};   // scales: unused with the tiled layout
+  return fp4_gemv_multi_ws(&p, 1, x_bf16, M, K, workspace, workspace_bytes, stream);
 }
 
 int fp4_gemv(float* y, const void* x_bf16, const void* packed, const void* scales, const float* gscale, int64_t M,
              int64_t N, int64_t K, void* stream) {
-  if (!y || !x_bf16 || !packed || !gscale) return FP4_ERR_NULL;
-  fp4_proj p{packed, scales, gscale, N, y, N};   // scales: unused with the tiled layout
-  return fp4_gemv_multi(&p, 1, x_bf16, M, K, stream);
+  return fp4_gemv_ws(y, x_bf16, packed, scales, gscale, M, N, K, nullptr, 0, stream);
 }
 
-int fp4_gemm_prefill_multi(const fp4_proj* projs, int nproj, const void* x_bf16, int64_t M, int64_t K,
-                           void* stream) {
+// Checks the projections of a fused prefill product and fills `d`.
+static int prefill_args(const fp4_proj* projs, int nproj, const void* x_bf16, int64_t M, int64_t K,
+                        fp4::PrefillProjDesc (&d)[FP4_MAX_PROJ]) {
   if (!projs || !x_bf16) return FP4_ERR_NULL;
   if (nproj < 1 || nproj > FP4_MAX_PROJ || M < 1 || M > kMaxM) return FP4_ERR_SHAPE;
   if (!aligned(x_bf16, 16)) return FP4_ERR_ALIGN;
@@ -153,7 +200,6 @@ int fp4_gemm_prefill_multi(const fp4_proj* projs, int nproj, const void* x_bf16,
   const int64_t slab = int64_t(1) << 31;
   if (int st = check_nk(8, K)) return st;
   if (256 * K * 2 >= slab || 32 * fp4::chunks_of(K) * fp4::kTileBytes >= slab) return FP4_ERR_SHAPE;
-  fp4::PrefillProjDesc d[FP4_MAX_PROJ];
   for (int i = 0; i < nproj; ++i) {
     const fp4_proj& p = projs[i];
     if (!p.packed || !p.gscale || !p.y) return FP4_ERR_NULL;
@@ -162,35 +208,141 @@ int fp4_gemm_prefill_multi(const fp4_proj* projs, int nproj, const void* x_bf16,
     if (!aligned(p.packed, 16) || !aligned(p.y, 4) || !aligned(p.gscale, 4)) return FP4_ERR_ALIGN;
     d[i] = {static_cast<const uint8_t*>(p.packed), p.gscale, p.y, p.ldy, p.N};
   }
-  return hip_status(fp4::launch_prefill(d, nproj, static_cast<const uint16_t*>(x_bf16), M, K,
+  return FP4_OK;
+}
+
+int fp4_gemm_prefill_multi_ws(const fp4_proj* projs, int nproj, const void* x_bf16, int64_t M, int64_t K,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  fp4::PrefillProjDesc d[FP4_MAX_PROJ];
+  if (int st = prefill_args(projs, nproj, x_bf16, M, K, d)) return st;
+  fp4::Workspace ws;
+  const size_t need = workspace ? fp4::prefill_ws_bytes(d, nproj, M, K) : 0;
+  if (int st = take_ws(workspace, workspace_bytes, need, ws)) return st;
+  return hip_status(fp4::launch_prefill(d, nproj, static_cast<const uint16_t*>(x_bf16), M, K, ws,
                                         static_cast<hipStream_t>(stream)));
+}
+
+int fp4_gemm_prefill_multi(const fp4_proj* projs, int nproj, const void* x_bf16, int64_t M, int64_t K,
+                           void* stream) {
+  return fp4_gemm_prefill_multi_ws(projs, nproj, x_bf16, M, K, nullptr, 0, stream);
+}
+
+int fp4_gemm_prefill_ws(float* y, const void* x_bf16, const void* packed, const void* scales, const float* gscale,
+                        int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!y || !x_bf16 || !packed || !gscale) return FP4_ERR_NULL;
+  fp4_proj p{packed, scales, gscale, N, y, N};   // scales: unused with the tiled layout
+  return fp4_gemm_prefill_multi_ws(&p, 1, x_bf16, M, K, workspace, workspace_bytes, stream);
 }
 
 int fp4_gemm_prefill(float* y, const void* x_bf16, const void* packed, const void* scales, const float* gscale,
                      int64_t M, int64_t N, int64_t K, void* stream) {
-  if (!y || !x_bf16 || !packed || !gscale) return FP4_ERR_NULL;
-  fp4_proj p{packed, scales, gscale, N, y, N};   // scales: unused with the tiled layout
-  return fp4_gemm_prefill_multi(&p, 1, x_bf16, M, K, stream);
+  return fp4_gemm_prefill_ws(y, x_bf16, packed, scales, gscale, M, N, K, nullptr, 0, stream);
 }
 
-int fp4_argmax_rows(int32_t* idx, const float* y, int64_t M, int64_t N, int64_t ldy, void* stream) {
+static int argmax_check(const int32_t* idx, const float* y, int64_t M, int64_t N, int64_t ldy) {
   if (!idx || !y) return FP4_ERR_NULL;
   if (M < 1 || M > kMaxM || N < 1 || N > kMaxN || ldy < N || M * ldy > kMaxElems) return FP4_ERR_SHAPE;
   if (!aligned(y, 4) || !aligned(idx, 4)) return FP4_ERR_ALIGN;
-  return hip_status(fp4::launch_argmax(idx, y, M, N, ldy, static_cast<hipStream_t>(stream)));
+  return FP4_OK;
 }
 
-int fp4_lm_head_greedy(int32_t* idx, float* logits, const void* x_bf16, const void* packed, const void* scales,
-                       const float* gscale, int64_t M, int64_t N, int64_t K, void* stream) {
-  // every argument is checked before the first launch
+int fp4_argmax_rows(int32_t* idx, const float* y, int64_t M, int64_t N, int64_t ldy, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (int st = argmax_check(idx, y, M, N, ldy)) return st;
+  fp4::Workspace ws;
+  if (int st = take_ws(workspace, workspace_bytes, fp4::argmax_ws_bytes(M, N), ws)) return st;
+  return hip_status(fp4::launch_argmax(idx, y, M, N, ldy, ws, static_cast<hipStream_t>(stream)));
+}
+
+// The greedy step's plan: the product launch itself ends with the choice
+// (one launch) when a workspace is given and the product is a single launch
+// whose every workgroup covers all rows (vector ALUs, or the matrix cores
+// with one K chunk and at most 16 rows); otherwise the product, then
+// fp4_argmax_rows' kernel.
+static bool greedy_fused(const fp4::GemvArgs& a) {
+  if (a.M > 16) return false;
+  return gemv_on_valu(a) || a.C == 1;
+}
+
+static size_t greedy_ws_need(const fp4::GemvArgs& a, int64_t N) {
+  if (greedy_fused(a)) {
+    const int64_t S = gemv_on_valu(a) ? fp4::gemv_workgroups(a) : fp4::gemv_mma_workgroups(a);
+    return fp4::greedy_ws_bytes(a.M, S);
+  }
+  return std::max(gemv_ws_need(a), fp4::argmax_ws_bytes(a.M, N));
+}
+
+static int greedy_args(int32_t* idx, float* logits, const void* x_bf16, const void* packed, const float* gscale,
+                       int64_t M, int64_t N, int64_t K, fp4::GemvArgs& a) {
   if (!idx || !logits || !x_bf16 || !packed || !gscale) return FP4_ERR_NULL;
   if (int st = check_nk(N, K)) return st;
   if (M < 1 || M > kMaxM || M * N > kMaxElems) return FP4_ERR_SHAPE;
   if (!aligned(idx, 4) || !aligned(logits, 4) || !aligned(x_bf16, 16) || !aligned(packed, 16) ||
       !aligned(gscale, 4))
     return FP4_ERR_ALIGN;
-  if (int st = fp4_gemv(logits, x_bf16, packed, scales, gscale, M, N, K, stream)) return st;
-  return fp4_argmax_rows(idx, logits, M, N, N, stream);
+  fp4_proj p{packed, nullptr, gscale, N, logits, N};
+  return gemv_args(&p, 1, x_bf16, M, K, a);
+}
+
+int fp4_lm_head_greedy(int32_t* idx, float* logits, const void* x_bf16, const void* packed, const void* scales,
+                       const float* gscale, int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  (void)scales;   // unused with the tiled layout
+  // every argument is checked before the first launch
+  fp4::GemvArgs a;
+  if (int st = greedy_args(idx, logits, x_bf16, packed, gscale, M, N, K, a)) return st;
+  fp4::Workspace ws;
+  if (int st = take_ws(workspace, workspace_bytes, workspace ? greedy_ws_need(a, N) : 0, ws)) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (ws.valid() && greedy_fused(a)) {
+    a.greedy.idx = idx;
+    a.greedy.keys = reinterpret_cast<uint64_t*>(ws.scratch());
+    a.greedy.cnt = ws.counter(0);
+    return gemv_run(a, ws, s);
+  }
+  if (int st = gemv_run(a, ws, s)) return st;
+  return hip_status(fp4::launch_argmax(idx, logits, M, N, N, ws, s));
+}
+
+int fp4_workspace_bytes(int op, int64_t M, int64_t K, const int64_t* Ns, int nproj, size_t* bytes) {
+  if (!bytes || !Ns) return FP4_ERR_NULL;
+  if (nproj < 1 || nproj > FP4_MAX_PROJ || M < 1 || M > kMaxM) return FP4_ERR_SHAPE;
+  *bytes = 0;
+  // the planners read only shapes: stand-in pointers, never dereferenced
+  static const uint8_t stand_in[16] __attribute__((aligned(16))) = {};
+  void* const sp = const_cast<uint8_t*>(stand_in);
+  fp4_proj p[FP4_MAX_PROJ];
+  for (int i = 0; i < nproj; ++i) p[i] = fp4_proj{sp, nullptr, static_cast<float*>(sp), Ns[i], static_cast<float*>(sp), Ns[i]};
+  switch (op) {
+    case FP4_OP_GEMV: {
+      fp4::GemvArgs a;
+      if (int st = gemv_args(p, nproj, sp, M, K, a)) return st;
+      *bytes = gemv_ws_need(a);
+      return FP4_OK;
+    }
+    case FP4_OP_GEMM_PREFILL: {
+      fp4::PrefillProjDesc d[FP4_MAX_PROJ];
+      if (int st = prefill_args(p, nproj, sp, M, K, d)) return st;
+      *bytes = fp4::prefill_ws_bytes(d, nproj, M, K);
+      return FP4_OK;
+    }
+    case FP4_OP_ARGMAX_ROWS: {
+      if (nproj != 1) return FP4_ERR_SHAPE;
+      if (Ns[0] < 1 || Ns[0] > kMaxN || M * Ns[0] > kMaxElems) return FP4_ERR_SHAPE;
+      *bytes = fp4::argmax_ws_bytes(M, Ns[0]);
+      return FP4_OK;
+    }
+    case FP4_OP_LM_HEAD_GREEDY: {
+      if (nproj != 1) return FP4_ERR_SHAPE;
+      fp4::GemvArgs a;
+      int32_t* const ip = static_cast<int32_t*>(sp);
+      if (int st = greedy_args(ip, static_cast<float*>(sp), sp, sp, static_cast<float*>(sp), M, Ns[0], K, a)) return st;
+      *bytes = greedy_ws_need(a, Ns[0]);
+      return FP4_OK;
+    }
+    default:
+      return FP4_ERR_UNSUPPORTED;
+  }
 }
 
 }  // extern "C"

@@ -30,6 +30,36 @@ __host__ __device__ inline int tile_scale_offset(int r, int b) {
   return kTileCodes + (r & 1) * 256 + (b >> 1) * 8 + (r >> 1) * 2 + (b & 1);
 }
 
+// Caller-owned scratch memory (include/fp4.h, "Workspaces"). The first
+// kWsHeaderBytes hold counters, one per 128-byte line, that are zero before
+// a call and that every kernel using them puts back to zero; the bytes after
+// the header are scratch that a call overwrites freely.
+constexpr size_t kWsHeaderBytes = 65536;
+constexpr int kWsCounterWords = 32;                          // u32 words per counter line
+constexpr int kWsCounters = (int)(kWsHeaderBytes / 128);     // 512
+struct Workspace {
+  uint8_t* p = nullptr;
+  size_t bytes = 0;
+  bool valid() const { return p != nullptr; }
+  unsigned* counter(int i) const { return reinterpret_cast<unsigned*>(p) + (size_t)i * kWsCounterWords; }
+  uint8_t* scratch() const { return p + kWsHeaderBytes; }
+};
+
+// Greedy choice folded into a product launch whose every workgroup covers
+// all M activation rows (include/fp4.h, fp4_lm_head_greedy). Each workgroup
+// stores its largest (value, index) key per row in keys[m * S + wg]; the
+// arrivals are counted on eight first-level counters (workgroup % 8, one
+// per XCD's share of the grid) and one second-level counter; the last
+// workgroup to arrive reads the S keys of every row and writes idx.
+struct GreedyArgs {
+  int32_t* idx = nullptr;   // [M] (nullptr: no greedy epilogue)
+  uint64_t* keys = nullptr; // [M][S]
+  unsigned* cnt = nullptr;  // 9 counters, kWsCounterWords apart: 8 first-level, then the second-level one
+  int32_t S = 0;            // workgroups of the launch
+};
+// Workspace bytes of a greedy epilogue over S workgroups and M rows.
+inline size_t greedy_ws_bytes(int64_t M, int64_t S) { return kWsHeaderBytes + (size_t)(M * S) * 8; }
+
 struct ProjDesc {
   const uint8_t* tiles;
   const float* gscale;
@@ -48,6 +78,7 @@ struct GemvArgs {
   int32_t wc;         // waves per row group (set by the launcher)
   int32_t gw;         // row groups per workgroup (set by the launcher)
   ProjDesc proj[kMaxProj];
+  GreedyArgs greedy;  // optional epilogue (one projection, M <= 16)
 };
 
 hipError_t launch_quantize(const uint16_t* W, int64_t N, int64_t K, bool tiled, uint8_t* packed,
@@ -61,10 +92,18 @@ hipError_t launch_retile(const uint8_t* packed, const uint8_t* scales, int64_t N
 // go to launch_gemv_mma). Positive gw (row groups per workgroup) and wc
 // (waves per row group) override the automatic geometry (tuning).
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t s, int gw = 0, int wc = 0);
+// Workgroups launch_gemv would launch for `a` (geometry as chosen there).
+int64_t gemv_workgroups(const GemvArgs& a);
 // Small-M product on bf16 MFMA, split over K chunks (16 activation rows per
-// pass, more rows loop passes). With more than one chunk it uses a
-// per-device workspace that it allocates on first need and keeps.
-hipError_t launch_gemv_mma(const GemvArgs& a, hipStream_t s, int ppw = 0);   // ppw > 0: pairs per workgroup (tuning)
+// pass, more rows loop passes). With more than one chunk the chunk partial
+// sums meet in the workspace (`ws` valid: a second kernel adds them in chunk
+// order) or are added atomically into y after a fill kernel zeroes it (no
+// workspace; the summation order then varies between calls).
+hipError_t launch_gemv_mma(const GemvArgs& a, const Workspace& ws, hipStream_t s, int ppw = 0);   // ppw > 0: pairs per workgroup (tuning)
+// Workspace bytes launch_gemv_mma needs for `a` with a workspace (0 when it uses none).
+size_t gemv_mma_ws_bytes(const GemvArgs& a);
+// Workgroups of the (single) pass of launch_gemv_mma for M <= 16 rows.
+int64_t gemv_mma_workgroups(const GemvArgs& a);
 // Matrix-core product for prefill-sized M over 1..kMaxProj weight tensors
 // that read the same x (one launch). bn > 0 forces the output tile width
 // (128, 192 or 256; tuning), else it is chosen from the shapes; splits > 0
@@ -77,20 +116,22 @@ struct PrefillProjDesc {
   int64_t ldy;
   int64_t N;
 };
+// Without a workspace the last round's tiles are never split.
 hipError_t launch_prefill(const PrefillProjDesc* projs, int nproj, const uint16_t* x, int64_t M, int64_t K,
-                          hipStream_t s, int bn = 0, int splits = 0);
+                          const Workspace& ws, hipStream_t s, int bn = 0, int splits = 0);
+// Workspace bytes a split of the last round's tiles needs (upper bound over
+// tile widths and splits; 0 when no split can happen).
+size_t prefill_ws_bytes(const PrefillProjDesc* projs, int nproj, int64_t M, int64_t K);
 
 // Compute units of the current device (cached per device; 0 if unknown).
 int device_cu_count();
-// Per-device workspace `which` of at least `bytes` (allocated on first need,
-// grown, never freed; a new buffer is zeroed on stream s when zero_new).
-enum Workspace { kWsGemvMmaPartials, kWsArgmaxKeys, kWsArgmaxCounters, kWsPrefillPartials, kWsPrefillCounters,
-                 kWsCount };
-hipError_t device_workspace(Workspace which, size_t bytes, bool zero_new, hipStream_t s, void** out);
 
 // Greedy choice per row of fp32 y [M][N] (row stride ldy): idx[m] = the first
-// index of the largest value. Rows longer than one workgroup's segment use a
-// per-device workspace allocated on first need and kept.
-hipError_t launch_argmax(int32_t* idx, const float* y, int64_t M, int64_t N, int64_t ldy, hipStream_t s);
+// index of the largest value. With a workspace, rows longer than one
+// workgroup's segment are split over workgroups whose keys meet there;
+// without one, one workgroup reads each whole row.
+hipError_t launch_argmax(int32_t* idx, const float* y, int64_t M, int64_t N, int64_t ldy, const Workspace& ws,
+                         hipStream_t s);
+size_t argmax_ws_bytes(int64_t M, int64_t N);
 
 }  // namespace fp4

@@ -29,9 +29,9 @@
 // multiply-add by the E4M3 block scale (decoded by v_cvt_f32_fp8, OCP
 // E4M3). The code conversions are shared by the activation rows of a pass.
 #include <algorithm>
-#include <atomic>
 
 #include "fp4_internal.h"
+#include "greedy.h"
 
 namespace fp4 {
 namespace {
@@ -128,9 +128,17 @@ struct Round {
 };
 
 // grid: workgroups over all projections; block: gw * wc waves (at most 16).
-template <int MT>
+// GREEDY (one projection, M <= MT): the launch ends with the greedy choice
+// over each row of y (greedy.h); a separate instantiation, so the plain
+// product keeps its registers.
+template <int MT, bool GREEDY>
 __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv(const GemvArgs a) {
   __shared__ float part[kMaxWaves][MT][8];
+  __shared__ uint64_t red[GREEDY ? kMaxWaves * MT : 1];
+  __shared__ int flag;
+  uint64_t keys[MT];
+#pragma unroll
+  for (int mi = 0; mi < MT; ++mi) keys[mi] = 0;
   const int lane = threadIdx.x & 63, hl = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
@@ -193,7 +201,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv(const GemvArgs a) {
 #pragma unroll
       for (int mi = 0; mi < MT; ++mi) {
         const float t = reduce4(acc[mi], hl);
-        if (holder && gvalid && n < N && m0 + mi < M) pd.y[(int64_t)(m0 + mi) * pd.ldy + n] = gs * t;
+        if (holder && gvalid && n < N && m0 + mi < M) {
+          const float v = gs * t;
+          pd.y[(int64_t)(m0 + mi) * pd.ldy + n] = v;
+          if (GREEDY) keys[mi] = umax64(keys[mi], greedy_key(v, n));
+        }
       }
     } else {
 #pragma unroll
@@ -207,28 +219,23 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv(const GemvArgs a) {
         float s = 0.0f;
         for (int w = 0; w < Wc; ++w) s += part[gg * Wc + w][mi][r];   // chunk order
         const int n = 8 * (((int)blockIdx.x - pd.wg_begin) * Gw + gg) + r;
-        if (n < N && m0 + mi < M) pd.y[(int64_t)(m0 + mi) * pd.ldy + n] = gs * s;
+        if (n < N && m0 + mi < M) {
+          const float v = gs * s;
+          pd.y[(int64_t)(m0 + mi) * pd.ldy + n] = v;
+          if (GREEDY) {
+#pragma unroll
+            for (int j = 0; j < MT; ++j)
+              if (j == mi) keys[j] = umax64(keys[j], greedy_key(v, n));
+          }
+        }
       }
       __syncthreads();
     }
   }
+  if (GREEDY) greedy_finish<MT>(a.greedy, keys, M, red, &flag);
 }
 
 }  // namespace
-
-// Compute units of the current device (cached per device; 0 if unknown).
-static int cu_count() {
-  constexpr int kMaxDevices = 64;
-  static std::atomic<int> cached[kMaxDevices];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
-  int n = cached[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cached[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
 
 // Launch geometry, from sweeps on MI355X (graph-timed, rotating weights):
 // one tile per wave per round, rounds issued one after the other (a second
@@ -247,13 +254,14 @@ static int cu_count() {
 //   Row groups per workgroup never exceed groups / CUs (small launches keep
 //   every CU busy: Qwen3-0.6B-shaped QKV 4096 x 1024 at M = 1 3.15 against
 //   3.44 us with four groups per workgroup; M = 2 3.51 against 3.94 us).
+// Fills a.wc, a.gw and the projections' wg_begin; returns the workgroups.
 template <int MT>
-static hipError_t launch_mt(GemvArgs a, hipStream_t s, int gw, int wc) {
+static int64_t plan_mt(GemvArgs& a, int gw, int wc) {
   const int rounds = (a.C + kMaxWaves - 1) / kMaxWaves;
+  int64_t groups = 0;
+  for (int i = 0; i < a.nproj; ++i) groups += groups_of(a.proj[i].N);
+  const int ncu = device_cu_count();
   if (MT == 1 && gw <= 0 && wc <= 0) {
-    int64_t groups = 0;
-    for (int i = 0; i < a.nproj; ++i) groups += groups_of(a.proj[i].N);
-    const int ncu = cu_count();
     if (ncu > 0 && a.C > kMaxWaves) {
       const int64_t per_cu = (groups + ncu - 1) / ncu;
       if (per_cu <= 9) {
@@ -269,21 +277,34 @@ static hipError_t launch_mt(GemvArgs a, hipStream_t s, int gw, int wc) {
   if (gw <= 0) {
     // about four waves per workgroup, but never so many row groups per
     // workgroup that the launch has fewer workgroups than CUs
-    int64_t groups = 0;
-    for (int i = 0; i < a.nproj; ++i) groups += groups_of(a.proj[i].N);
-    const int ncu = cu_count();
     gw = std::max(1, 4 / a.wc);
     if (ncu > 0) gw = (int)std::max<int64_t>(1, std::min<int64_t>(gw, groups / ncu));
   }
-  a.gw = gw;
-  a.gw = std::max(1, std::min(a.gw, kMaxWaves / a.wc));
+  a.gw = std::max(1, std::min(gw, kMaxWaves / a.wc));
   int64_t wgs = 0;
   for (int i = 0; i < a.nproj; ++i) {
     a.proj[i].wg_begin = (int32_t)wgs;
     wgs += (groups_of(a.proj[i].N) + a.gw - 1) / a.gw;
   }
-  hipLaunchKernelGGL((k_gemv<MT>), dim3((unsigned)wgs), dim3(64 * a.gw * a.wc), 0, s, a);
+  return wgs;
+}
+
+template <int MT>
+static hipError_t launch_mt(GemvArgs a, hipStream_t s, int gw, int wc) {
+  const int64_t wgs = plan_mt<MT>(a, gw, wc);
+  a.greedy.S = (int32_t)wgs;
+  if (a.greedy.idx)
+    hipLaunchKernelGGL((k_gemv<MT, true>), dim3((unsigned)wgs), dim3(64 * a.gw * a.wc), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_gemv<MT, false>), dim3((unsigned)wgs), dim3(64 * a.gw * a.wc), 0, s, a);
   return hipGetLastError();
+}
+
+int64_t gemv_workgroups(const GemvArgs& a) {
+  GemvArgs b = a;
+  if (a.M == 1) return plan_mt<1>(b, 0, 0);
+  if (a.M == 2) return plan_mt<2>(b, 0, 0);
+  return plan_mt<4>(b, 0, 0);
 }
 
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t s, int gw, int wc) {

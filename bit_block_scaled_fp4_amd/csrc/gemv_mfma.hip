@@ -12,10 +12,14 @@
 // Work split (split-K). Workgroup (b, c) owns K chunk c (1024 elements) and a
 // block of 16-row weight pairs (two 8-row groups). It first copies the
 // activation rows of its chunk into LDS; its waves then walk the pairs, each
-// pair needing only weight loads. The partial product of chunk c goes to a
-// workspace [C][pairs][16 n][16 m]; a second kernel adds the C partials of
-// every output in chunk order and applies the tensor scale (one chunk: the
-// first kernel writes y directly). Results are deterministic.
+// pair needing only weight loads. With one chunk the kernel writes y
+// directly. Otherwise the chunk partials meet in one of two ways:
+//   - in the caller's workspace [C][pairs][16 n][16 m], and a second kernel
+//     adds the C partials of every output in chunk order and applies the
+//     tensor scale (deterministic);
+//   - without a workspace, a fill kernel first zeroes y and every workgroup
+//     adds its scaled partials into y with fp32 atomics (the order of the
+//     chunk sums, and so the last bits of y, can vary between calls).
 //
 // Operand layout of v_mfma_f32_16x16x32_bf16 (lane l, q = l / 16):
 //   A: row l % 16, k = 8q .. 8q+7;  B: column l % 16, k = 8q .. 8q+7;
@@ -50,6 +54,7 @@
 #include <atomic>
 
 #include "fp4_internal.h"
+#include "greedy.h"
 
 namespace fp4 {
 namespace {
@@ -122,7 +127,7 @@ __device__ __forceinline__ float fp8_f32(uint32_t w, int sel) {
 
 struct MmaArgs {
   const uint16_t* x;   // bf16 [M][K]
-  float* ws;           // [C][npairs][16][16] partials (unused when C == 1)
+  float* ws;           // [C][npairs][16][16] partials (C > 1; nullptr: atomic adds into y)
   int M, K, C, m0;     // m0: first activation row of this pass
   int nproj;
   int npairs;          // pairs over all projections
@@ -135,7 +140,58 @@ struct MmaArgs {
     int32_t N;
     int32_t pair_begin;
   } proj[kMaxProj];
+  GreedyArgs greedy;   // C == 1, one projection, M <= rows of the kernel
 };
+
+__device__ __forceinline__ int proj_of(const struct MmaArgs& a, int pair);
+
+// Epilogue of one pair: lane (q, n16) holds rows m0 + 4q + i (i < 4) of
+// output column n16 of the pair in v[i]. C == 1: y = gscale * v (and the
+// lane's greedy keys); with a workspace: the unscaled chunk partial; else
+// gscale * v added into y.
+template <bool GREEDY>
+__device__ __forceinline__ void pair_out(const MmaArgs& a, int pair, int c, int q, int n16, const f32x4_t& v,
+                                         uint64_t (&kk)[4]) {
+  if (a.C == 1 || !a.ws) {
+    const int p = proj_of(a, pair);
+    const int n = 16 * (pair - a.proj[p].pair_begin) + n16;
+    const float gs = *a.proj[p].gscale;
+    if (n < a.proj[p].N) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = a.m0 + 4 * q + i;
+        if (m < a.M) {
+          float* dst = a.proj[p].y + (int64_t)m * a.proj[p].ldy + n;
+          const float val = gs * v[i];
+          if (a.C == 1) {
+            *dst = val;
+            if (GREEDY) kk[i] = umax64(kk[i], greedy_key(val, n));
+          } else {
+            __hip_atomic_fetch_add(dst, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+      }
+    }
+  } else if (a.m0 + 4 * q < a.M) {   // rows past M are never read back
+    float* dst = a.ws + ((int64_t)c * a.npairs + pair) * 256 + n16 * 16 + 4 * q;
+    *reinterpret_cast<f32x4_t*>(dst) = v;
+  }
+}
+
+// Greedy epilogue of a launch (a.greedy.idx set): lane (q, n16) holds keys of
+// rows 4q + i in kk[i]. The reduction scratch reuses the activation staging
+// area `xs` (at least 16 * NR * 8 bytes) once every wave is past its last
+// pair.
+template <int NR>
+__device__ __forceinline__ void mma_greedy(const MmaArgs& a, int q, const uint64_t (&kk)[4], uint8_t* xs,
+                                           int* flag) {
+  __syncthreads();
+  uint64_t* red = reinterpret_cast<uint64_t*>(xs);
+  uint64_t k[NR];
+#pragma unroll
+  for (int j = 0; j < NR; ++j) k[j] = (j >> 2) == q ? kk[j & 3] : 0;
+  greedy_finish<NR>(a.greedy, k, a.M, red, flag);
+}
 
 // One pair's codes and scale bytes, as loaded: tile T, load i holds piece
 // lane % 32 of row 2i + lane / 32; s[T] the tile's scale bytes at 8 * lane.
@@ -178,13 +234,17 @@ constexpr int kXsRow8 = 2048 + 16;   // k_gemv_mma8: staged activation row, padd
 constexpr int kZeroWin = 256;        // k_gemv_mma8: zeros read by the A lanes of the other block parity
 
 // At most 8 activation rows (m0 .. m0+7) per launch; grid
-// (ceil(npairs / pairs_per_wg), C), block kWaves waves.
+// (ceil(npairs / pairs_per_wg), C), block kWaves waves. GREEDY: the greedy
+// epilogue (C == 1, a.greedy set).
+template <bool GREEDY>
 __global__ __launch_bounds__(64 * kWaves) void k_gemv_mma8(const MmaArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t xs[8 * kXsRow8 + kZeroWin];
   __shared__ __attribute__((aligned(16))) uint8_t tr[kWaves * kTrBytes];
+  __shared__ int flag;
+  uint64_t kk[4] = {0, 0, 0, 0};
   const int lane = threadIdx.x & 63, q = lane >> 4, n16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c = blockIdx.y, C = a.C, K = a.K;
+  const int c = blockIdx.y, K = a.K;
   const int pb = blockIdx.x * a.pairs_per_wg;
   const int pe = min(pb + a.pairs_per_wg, a.npairs);
 
@@ -288,34 +348,22 @@ __global__ __launch_bounds__(64 * kWaves) void k_gemv_mma8(const MmaArgs a) {
     f32x4_t tot;
 #pragma unroll
     for (int i = 0; i < 4; ++i) tot[i] = acc[i] + __shfl_xor(acc[i], 32);
-    if (q < 2) {   // rows 4q .. 4q+3
-      if (C == 1) {
-        const int p = proj_of(a, pair);
-        const int n = 16 * (pair - a.proj[p].pair_begin) + n16;
-        const float gs = *a.proj[p].gscale;
-        if (n < a.proj[p].N) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int m = a.m0 + 4 * q + i;
-            if (m < a.M) a.proj[p].y[(int64_t)m * a.proj[p].ldy + n] = gs * tot[i];
-          }
-        }
-      } else if (a.m0 + 4 * q < a.M) {   // rows past M are never read back
-        float* dst = a.ws + ((int64_t)c * a.npairs + pair) * 256 + n16 * 16 + 4 * q;
-        *reinterpret_cast<f32x4_t*>(dst) = tot;
-      }
-    }
+    if (q < 2) pair_out<GREEDY>(a, pair, c, q, n16, tot, kk);   // rows 4q .. 4q+3
     cur = nxt;
   }
+  if (GREEDY) mma_greedy<8>(a, q, kk, xs, &flag);
 }
 
 // 9 to 16 activation rows (m0 .. m0+15) per launch; grid and block as above.
+template <bool GREEDY>
 __global__ __launch_bounds__(64 * kWaves) void k_gemv_mma16(const MmaArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t xs[kMRows * kChunkK * 2];
   __shared__ __attribute__((aligned(16))) uint8_t tr[kWaves * kTrBytes];
+  __shared__ int flag;
+  uint64_t kk[4] = {0, 0, 0, 0};
   const int lane = threadIdx.x & 63, q = lane >> 4, n16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c = blockIdx.y, C = a.C, K = a.K;
+  const int c = blockIdx.y, K = a.K;
   const int pb = blockIdx.x * a.pairs_per_wg;
   const int pe = min(pb + a.pairs_per_wg, a.npairs);
   const int rr = n16 & 7;
@@ -385,23 +433,10 @@ __global__ __launch_bounds__(64 * kWaves) void k_gemv_mma16(const MmaArgs a) {
     }
     const f32x4_t acc = acc2[0] + acc2[1];
     // lane (q, n16) holds D[m = 4q + i][n = n16]
-    if (C == 1) {
-      const int p = proj_of(a, pair);
-      const int n = 16 * (pair - a.proj[p].pair_begin) + n16;
-      const float gs = *a.proj[p].gscale;
-      if (n < a.proj[p].N) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = a.m0 + 4 * q + i;
-          if (m < a.M) a.proj[p].y[(int64_t)m * a.proj[p].ldy + n] = gs * acc[i];
-        }
-      }
-    } else if (a.m0 + 4 * q < a.M) {   // rows past M are never read back
-      float* dst = a.ws + ((int64_t)c * a.npairs + pair) * 256 + n16 * 16 + 4 * q;
-      *reinterpret_cast<f32x4_t*>(dst) = acc;
-    }
+    pair_out<GREEDY>(a, pair, c, q, n16, acc, kk);
     cur = nxt;
   }
+  if (GREEDY) mma_greedy<16>(a, q, kk, xs, &flag);
 }
 
 // y[m][n] = gscale * sum over chunks (in order) of the partials. A thread
@@ -448,7 +483,7 @@ int resident_per_cu() {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
   int n = cached[dev].load(std::memory_order_relaxed);
   if (n == 0) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, EIGHT ? k_gemv_mma8 : k_gemv_mma16, 64 * kWaves, 0) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, EIGHT ? k_gemv_mma8<false> : k_gemv_mma16<false>, 64 * kWaves, 0) != hipSuccess) return 0;
     cached[dev].store(n, std::memory_order_relaxed);
   }
   return n;
@@ -477,9 +512,18 @@ int pick_pairs_per_wg(int64_t pairs, int C, int64_t slots) {
   return best;
 }
 
-}  // namespace
+// y[m][n] = 0 for rows m0 .. m0 + rows - 1 of every projection (before the
+// atomic adds of a multi-chunk pass without a workspace). grid.y: projection.
+__global__ __launch_bounds__(256) void k_zero_rows(const MmaArgs a, int rows) {
+  const auto& pj = a.proj[blockIdx.y];
+  const int64_t n_all = (int64_t)rows * pj.N;
+  for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < n_all; t += (int64_t)gridDim.x * 256) {
+    const int64_t m = t / pj.N, n = t - m * pj.N;
+    pj.y[(a.m0 + m) * pj.ldy + n] = 0.0f;
+  }
+}
 
-hipError_t launch_gemv_mma(const GemvArgs& g, hipStream_t s, int ppw) {
+MmaArgs mma_args(const GemvArgs& g) {
   MmaArgs a{};
   a.x = g.x;
   a.M = g.M;
@@ -496,31 +540,68 @@ hipError_t launch_gemv_mma(const GemvArgs& g, hipStream_t s, int ppw) {
     a.proj[i].pair_begin = (int32_t)pairs;
     pairs += (g.proj[i].N + kPairRows - 1) / kPairRows;
   }
-  if (pairs > (int64_t(1) << 26)) return hipErrorInvalidValue;
-  a.npairs = (int)pairs;
-  if (a.C > 1) {
-    const size_t bytes = (size_t)a.C * (size_t)pairs * 256 * sizeof(float);
-    void* ws = nullptr;
-    hipError_t e = device_workspace(kWsGemvMmaPartials, bytes, false, s, &ws);
-    if (e != hipSuccess) return e;
-    a.ws = static_cast<float*>(ws);
-  }
+  a.npairs = pairs > (int64_t(1) << 26) ? -1 : (int)pairs;
+  a.greedy = g.greedy;
+  return a;
+}
+
+int pairs_per_wg_for(const MmaArgs& a, bool eight) {
   const int64_t ncu = device_cu_count();
+  return pick_pairs_per_wg(a.npairs, a.C, ncu * (eight ? resident_per_cu<true>() : resident_per_cu<false>()));
+}
+
+}  // namespace
+
+size_t gemv_mma_ws_bytes(const GemvArgs& g) {
+  if (g.C <= 1) return 0;
+  const MmaArgs a = mma_args(g);
+  if (a.npairs < 0) return 0;
+  return kWsHeaderBytes + (size_t)a.C * (size_t)a.npairs * 256 * sizeof(float);
+}
+
+int64_t gemv_mma_workgroups(const GemvArgs& g) {
+  const MmaArgs a = mma_args(g);
+  if (a.npairs < 0) return 0;
+  const int ppw = pairs_per_wg_for(a, g.M <= 8);
+  return (a.npairs + ppw - 1) / ppw;
+}
+
+hipError_t launch_gemv_mma(const GemvArgs& g, const Workspace& ws, hipStream_t s, int ppw) {
+  MmaArgs a = mma_args(g);
+  if (a.npairs < 0) return hipErrorInvalidValue;
+  const int64_t pairs = a.npairs;
+  const bool use_ws = a.C > 1 && ws.valid();
+  if (use_ws) a.ws = reinterpret_cast<float*>(ws.scratch());
   for (int m0 = 0; m0 < g.M; m0 += kMRows) {
     a.m0 = m0;
     const bool eight = g.M - m0 <= 8;
-    a.pairs_per_wg = ppw > 0 ? ppw : pick_pairs_per_wg(pairs, a.C, ncu * (eight ? resident_per_cu<true>() : resident_per_cu<false>()));
+    a.pairs_per_wg = ppw > 0 ? ppw : pairs_per_wg_for(a, eight);
     const int64_t wgx = (pairs + a.pairs_per_wg - 1) / a.pairs_per_wg;
-    if (eight)
-      hipLaunchKernelGGL(k_gemv_mma8, dim3((unsigned)wgx, (unsigned)a.C), dim3(64 * kWaves), 0, s, a);
+    a.greedy.S = (int32_t)wgx;
+    const int rows = std::min(kMRows, g.M - m0);
+    if (a.C > 1 && !use_ws) {
+      int64_t most = 0;
+      for (int i = 0; i < a.nproj; ++i) most = std::max<int64_t>(most, (int64_t)rows * a.proj[i].N);
+      const int64_t blocks = std::min<int64_t>((most + 255) / 256, 4096);
+      hipLaunchKernelGGL(k_zero_rows, dim3((unsigned)blocks, (unsigned)a.nproj), dim3(256), 0, s, a, rows);
+    }
+    const dim3 grid((unsigned)wgx, (unsigned)a.C), block(64 * kWaves);
+    if (eight && a.greedy.idx)
+      hipLaunchKernelGGL(k_gemv_mma8<true>, grid, block, 0, s, a);
+    else if (eight)
+      hipLaunchKernelGGL(k_gemv_mma8<false>, grid, block, 0, s, a);
+    else if (a.greedy.idx)
+      hipLaunchKernelGGL(k_gemv_mma16<true>, grid, block, 0, s, a);
     else
-      hipLaunchKernelGGL(k_gemv_mma16, dim3((unsigned)wgx, (unsigned)a.C), dim3(64 * kWaves), 0, s, a);
-    if (a.C > 1) {
-      const int64_t n = pairs * 16 * ((std::min(kMRows, g.M - m0) + 3) / 4);
+      hipLaunchKernelGGL(k_gemv_mma16<false>, grid, block, 0, s, a);
+    if (use_ws) {
+      const int64_t n = pairs * 16 * ((rows + 3) / 4);
       hipLaunchKernelGGL(k_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
     }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace fp4

@@ -1,0 +1,112 @@
+// Greedy next-token choice, device side: the order of (value, index) keys
+// and the combine of per-workgroup results through a caller's workspace.
+//
+// The last vector of a decode step times the vocabulary matrix gives one
+// logit per vocabulary entry; greedy decoding takes the most likely (page
+// "1. The big picture", steps 4 and 5). Here: the first index of the largest
+// value, a NaN ranking above every number, -0 equal to +0.
+//
+// Each value becomes a 64-bit key: the high word maps the fp32 value onto
+// unsigned integers in the same order (every NaN as one value above +inf,
+// -0 folded onto +0), the low word is the complement of the index, so of two
+// equal values the smaller index has the larger key. Every key is nonzero
+// (the smallest high word, that of -inf, is 0x007FFFFF), so 0 can stand for
+// "no element". The answer is the largest key; max is associative and
+// commutative, so the result does not depend on how the work is split or in
+// which order workgroups finish.
+#pragma once
+
+#include "fp4_internal.h"
+
+namespace fp4 {
+
+__device__ __forceinline__ uint64_t greedy_key(float v, int n) {
+  uint32_t u = __float_as_uint(v);
+  if ((u & 0x7fffffffu) > 0x7f800000u)
+    u = 0x7fc00000u;   // every NaN ranks as the largest value
+  else if ((u & 0x7fffffffu) == 0)
+    u = 0u;            // -0 equals +0
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)o << 32) | (uint64_t)(0xffffffffu - (uint32_t)n);
+}
+
+__device__ __forceinline__ int32_t greedy_index(uint64_t key) { return (int32_t)(0xffffffffu - (uint32_t)key); }
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ uint64_t wave_max64(uint64_t k) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) k = umax64(k, __shfl_xor(k, d));
+  return k;
+}
+
+// Largest key over the workgroup, valid in thread 0. `red` is LDS of at
+// least blockDim.x / 64 entries; every thread of the workgroup must call.
+__device__ __forceinline__ uint64_t block_max64(uint64_t k, uint64_t* red) {
+  const int nw = blockDim.x >> 6;
+  k = wave_max64(k);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = k;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    for (int w = 1; w < nw; ++w) k = umax64(k, red[w]);
+  return k;
+}
+
+// End of a product launch with the greedy epilogue (GreedyArgs). Called by
+// every thread of the workgroup, in uniform control flow, after the
+// workgroup's outputs are written; k[m] is the thread's largest key of row m
+// (0 where it wrote none), m < M <= NR. `red` is LDS of 16 * NR entries.
+//
+// The workgroup's keys are stored with device-coherent stores, which
+// complete before the workgroup counts itself in. Of the workgroups with
+// index % 8 == j, the last to arrive on counter j puts it back to zero and
+// counts the group in on the second-level counter; the last group's last
+// workgroup puts that one back to zero and reads every key with
+// device-coherent loads. Arrivals on one counter line serialise, so spreading
+// them over eight lines keeps each queue short.
+template <int NR>
+__device__ void greedy_finish(const GreedyArgs& g, const uint64_t (&k)[NR], int M, uint64_t* red, int* flag) {
+  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6, lane = threadIdx.x & 63;
+  const int wg = blockIdx.x, S = g.S;
+#pragma unroll
+  for (int m = 0; m < NR; ++m) {
+    const uint64_t v = wave_max64(k[m]);
+    if (lane == 0) red[wave * NR + m] = v;
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < M) {
+    uint64_t v = 0;
+    for (int w = 0; w < nw; ++w) v = umax64(v, red[w * NR + threadIdx.x]);
+    __hip_atomic_store(g.keys + (int64_t)threadIdx.x * S + wg, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the key is visible device-wide
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int j = wg & 7;
+    const unsigned nj = (unsigned)((S - j + 7) >> 3);   // workgroups with index % 8 == j
+    unsigned* c1 = g.cnt + j * kWsCounterWords;
+    int last = 0;
+    if (__hip_atomic_fetch_add(c1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nj - 1) {
+      __hip_atomic_store(c1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // all nj arrivals are in
+      unsigned* c2 = g.cnt + 8 * kWsCounterWords;
+      const unsigned groups = (unsigned)(S < 8 ? S : 8);
+      if (__hip_atomic_fetch_add(c2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == groups - 1) {
+        __hip_atomic_store(c2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = 1;
+      }
+    }
+    *flag = last;
+  }
+  __syncthreads();
+  if (!*flag) return;
+  for (int m = 0; m < M; ++m) {
+    uint64_t v = 0;
+    for (int t = (int)threadIdx.x; t < S; t += (int)blockDim.x)
+      v = umax64(v, __hip_atomic_load(g.keys + (int64_t)m * S + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    v = block_max64(v, red);
+    if (threadIdx.x == 0) g.idx[m] = greedy_index(v);
+  }
+}
+
+}  // namespace fp4

@@ -45,9 +45,10 @@
 // Last round. When the last round of tiles over the compute units would
 // leave most of them idle, those tiles run in a second launch, each split
 // into S <= 4 ranges of whole windows along K on separate workgroups; the
-// pieces exchange fp32 partial sums through a per-device workspace and the
-// last piece of a tile adds them in piece order (so the result does not
-// depend on which piece finishes last) and writes y.
+// pieces exchange fp32 partial sums through the caller's workspace (its
+// header holds one arrival counter per split tile) and the last piece of a
+// tile adds them in piece order (so the result does not depend on which
+// piece finishes last) and writes y. Without a workspace nothing is split.
 //
 // Bounds: the buffer loads read zeros for activation rows past M, columns
 // past K, weight row groups past N and steps past the end, without touching
@@ -184,7 +185,7 @@ struct PrefillProj {
 struct PrefillArgs {
   const uint16_t* x;
   float* part;         // split tiles: partial sums, kPartFloats<BN> per piece
-  unsigned* cnt;       // split tiles: arrivals (kCntStride apart), zero between launches
+  unsigned* cnt;       // split tiles: arrivals (kCntStride apart, the workspace header), zero between launches
   int32_t M, K, m_tiles, nt_total, nproj;
   int32_t dp_tiles;    // tiles computed whole by one workgroup: the first ones
   int32_t per_xcd;     // of those, per XCD
@@ -192,7 +193,7 @@ struct PrefillArgs {
   PrefillProj proj[kMaxProj];
 };
 constexpr int kMaxSplits = 4;
-constexpr int kCntStride = 32;   // one 128-byte line per counter
+constexpr int kCntStride = kWsCounterWords;   // one 128-byte line per counter
 template <int BN>
 constexpr int kPartFloats = BM * BN;
 
@@ -496,8 +497,67 @@ static int auto_splits(int64_t total, int64_t nwin, int ncu) {
   return (int)std::max<int64_t>(1, std::min<int64_t>({kMaxSplits, ncu / tail, nwin}));
 }
 
+// What launch_prefill runs: the tile width, the K split S of the last
+// round's tiles and how many tiles that round holds (0: none split).
+struct PrefillPlan {
+  int bn = 0;
+  int S = 1;
+  int64_t tail = 0;
+};
+
+static int64_t tiles_of(const PrefillProjDesc* projs, int nproj, int64_t M, int bn) {
+  int64_t nt = 0;
+  for (int i = 0; i < nproj; ++i) nt += (projs[i].N + bn - 1) / bn;
+  return (M + BM - 1) / BM * nt;
+}
+
+static int splits_of(int64_t total, int64_t nwin, int ncu, int splits, bool allow) {
+  if (!allow) return 1;
+  return splits > 0 ? (int)std::min<int64_t>({splits, kMaxSplits, nwin}) : auto_splits(total, nwin, ncu);
+}
+
+static PrefillPlan plan_prefill(const PrefillProjDesc* projs, int nproj, int64_t M, int64_t K, int bn, int splits,
+                                bool allow_split) {
+  PrefillPlan pl;
+  const int64_t nwin = ((K + BK - 1) / BK + kWin - 1) / kWin;
+  const int ncu = std::max(1, device_cu_count());
+  if (bn <= 0) {
+    // Tile width (and K split), from a cost model fitted on MI355X at
+    // M = 2048, K = 5120: a full round of workgroups over the compute units
+    // takes the tile time (relative: 128 wide 0.66, 192 wide 0.85, 256 wide
+    // 1; wider tiles do more MFMA work per LDS and load byte); a last round
+    // that is not full takes max(0.7, fill) of it (fewer busy units run at
+    // a higher clock); split S ways along K it takes 1/S of a tile plus 0.3
+    // (the partial sums' exchange). Ties go to the wider tile.
+    const int widths[3] = {256, 192, 128};
+    const int cost[3] = {100, 85, 66};
+    int64_t best = -1;
+    for (int w = 0; w < 3; ++w) {
+      const int64_t total = tiles_of(projs, nproj, M, widths[w]), full = (total - 1) / ncu, tail = total - full * ncu;
+      const int S = splits_of(total, nwin, ncu, splits, allow_split);
+      const int64_t last = S > 1 ? cost[w] * 100 / S + cost[w] * 30
+                                 : cost[w] * std::max<int64_t>(70, tail * 100 / ncu);
+      const int64_t t = full * cost[w] * 100 + last;
+      if (best < 0 || t < best) {
+        best = t;
+        bn = widths[w];
+      }
+    }
+  }
+  pl.bn = bn;
+  const int64_t total = tiles_of(projs, nproj, M, bn);
+  pl.S = splits_of(total, nwin, ncu, splits, allow_split);
+  pl.tail = pl.S > 1 ? total - (total - 1) / ncu * ncu : 0;
+  if (pl.tail > kWsCounters) {   // one header counter per split tile
+    pl.S = 1;
+    pl.tail = 0;
+  }
+  return pl;
+}
+
 template <int BN>
-static hipError_t launch_bn(PrefillArgs a, const PrefillProjDesc* projs, int splits, hipStream_t s) {
+static hipError_t launch_bn(PrefillArgs a, const PrefillProjDesc* projs, const PrefillPlan& pl, const Workspace& ws,
+                            hipStream_t s) {
   // more than 64 KB of dynamic LDS must be allowed once per kernel and device
   constexpr int kMaxDevices = 64;
   static std::atomic<bool> attr_set[kMaxDevices];
@@ -522,23 +582,15 @@ static hipError_t launch_bn(PrefillArgs a, const PrefillProjDesc* projs, int spl
   const int64_t mt = (a.M + BM - 1) / BM;
   const int64_t total = mt * nt;
   if (total > (int64_t(1) << 30)) return hipErrorInvalidValue;
-  const int64_t nwin = ((a.K + BK - 1) / BK + kWin - 1) / kWin;
-  const int S = splits > 0 ? (int)std::min<int64_t>({splits, kMaxSplits, nwin})
-                           : auto_splits(total, nwin, device_cu_count());
-  const int64_t ncu = std::max(1, device_cu_count());
-  const int64_t tail = S > 1 ? total - (total - 1) / ncu * ncu : 0;
+  const int64_t tail = pl.tail;
   a.dp_tiles = (int32_t)(total - tail);
   a.per_xcd = (int32_t)((a.dp_tiles + 7) / 8);
-  a.splits = S;
+  a.splits = pl.S;
   a.m_tiles = (int32_t)mt;
   a.nt_total = (int32_t)nt;
   if (tail > 0) {
-    void *part = nullptr, *cnt = nullptr;
-    e = device_workspace(kWsPrefillPartials, (size_t)(tail * S) * kPartFloats<BN> * sizeof(float), false, s, &part);
-    if (e == hipSuccess) e = device_workspace(kWsPrefillCounters, (size_t)tail * kCntStride * 4, true, s, &cnt);
-    if (e != hipSuccess) return e;
-    a.part = static_cast<float*>(part);
-    a.cnt = static_cast<unsigned*>(cnt);
+    a.part = reinterpret_cast<float*>(ws.scratch());
+    a.cnt = ws.counter(0);
   }
   // whole tiles, then the K pieces of the rest (a second launch: the split
   // epilogue in the same kernel would cost the whole-tile path registers)
@@ -548,14 +600,20 @@ static hipError_t launch_bn(PrefillArgs a, const PrefillProjDesc* projs, int spl
     if (e != hipSuccess) return e;
   }
   if (tail > 0) {
-    hipLaunchKernelGGL((k_prefill<BN, true>), dim3((unsigned)(tail * S)), dim3(256), Lds<BN>::kBytes, s, a);
+    hipLaunchKernelGGL((k_prefill<BN, true>), dim3((unsigned)(tail * pl.S)), dim3(256), Lds<BN>::kBytes, s, a);
     e = hipGetLastError();
   }
   return e;
 }
 
+size_t prefill_ws_bytes(const PrefillProjDesc* projs, int nproj, int64_t M, int64_t K) {
+  const PrefillPlan pl = plan_prefill(projs, nproj, M, K, 0, 0, true);
+  if (pl.tail == 0) return 0;
+  return kWsHeaderBytes + (size_t)(pl.tail * pl.S) * (size_t)(BM * pl.bn) * sizeof(float);
+}
+
 hipError_t launch_prefill(const PrefillProjDesc* projs, int nproj, const uint16_t* x, int64_t M, int64_t K,
-                          hipStream_t s, int bn, int splits) {
+                          const Workspace& ws, hipStream_t s, int bn, int splits) {
   if (nproj < 1 || nproj > kMaxProj) return hipErrorInvalidValue;
   // buffer offsets are 32-bit: one 256-row slab of activations, of outputs
   // and of weights must each stay below 2 GB
@@ -575,37 +633,16 @@ hipError_t launch_prefill(const PrefillProjDesc* projs, int nproj, const uint16_
     a.proj[i].ldy = projs[i].ldy;
     a.proj[i].N = (int32_t)projs[i].N;
   }
-  if (bn <= 0) {
-    // Tile width (and K split), from a cost model fitted on MI355X at
-    // M = 2048, K = 5120: a full round of workgroups over the compute units
-    // takes the tile time (relative: 128 wide 0.66, 192 wide 0.85, 256 wide
-    // 1; wider tiles do more MFMA work per LDS and load byte); a last round
-    // that is not full takes max(0.7, fill) of it (fewer busy units run at
-    // a higher clock); split S ways along K it takes 1/S of a tile plus 0.3
-    // (the partial sums' exchange). Ties go to the wider tile.
-    const int64_t mt = (M + BM - 1) / BM, nwin = ((K + BK - 1) / BK + kWin - 1) / kWin;
-    const int ncu = std::max(1, device_cu_count());
-    const int widths[3] = {256, 192, 128};
-    const int cost[3] = {100, 85, 66};
-    int64_t best = -1;
-    for (int w = 0; w < 3; ++w) {
-      int64_t nt = 0;
-      for (int i = 0; i < nproj; ++i) nt += (projs[i].N + widths[w] - 1) / widths[w];
-      const int64_t total = mt * nt, full = (total - 1) / ncu, tail = total - full * ncu;
-      const int S = splits > 0 ? (int)std::min<int64_t>({splits, kMaxSplits, nwin}) : auto_splits(total, nwin, ncu);
-      const int64_t last = S > 1 ? cost[w] * 100 / S + cost[w] * 30
-                                 : cost[w] * std::max<int64_t>(70, tail * 100 / ncu);
-      const int64_t t = full * cost[w] * 100 + last;
-      if (best < 0 || t < best) {
-        best = t;
-        bn = widths[w];
-      }
-    }
+  PrefillPlan pl = plan_prefill(projs, nproj, M, K, bn, splits, ws.valid());
+  if (pl.tail > 0 &&
+      ws.bytes < kWsHeaderBytes + (size_t)(pl.tail * pl.S) * (size_t)(BM * pl.bn) * sizeof(float)) {
+    pl.S = 1;   // the workspace is too small for this split (tuning calls only: the API checks the size)
+    pl.tail = 0;
   }
-  switch (bn) {
-    case 128: return launch_bn<128>(a, projs, splits, s);
-    case 192: return launch_bn<192>(a, projs, splits, s);
-    case 256: return launch_bn<256>(a, projs, splits, s);
+  switch (pl.bn) {
+    case 128: return launch_bn<128>(a, projs, pl, ws, s);
+    case 192: return launch_bn<192>(a, projs, pl, ws, s);
+    case 256: return launch_bn<256>(a, projs, pl, ws, s);
     default: return hipErrorInvalidValue;
   }
 }

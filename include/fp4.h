@@ -46,19 +46,22 @@
  * Conventions for every call:
  *   - Pointers marked "device" are HIP device memory (e.g. a torch CUDA
  *     tensor's data_ptr()) on the current HIP device; the caller owns every
- *     buffer. Exceptions to "the library allocates nothing": fp4_gemv
- *     and fp4_gemv_multi on the matrix-core path (M >= 5; M = 3 or 4 when
- *     the call reads at least 32 MiB of weights and K <= 8192) with
- *     K > 1024 keep the per-chunk
- *     partial sums in a per-device workspace (C * ceil(N/16) * 1 KiB, C =
- *     ceil(K/1024), summed over the projections) that the library
- *     allocates with hipMalloc on the first call that needs it (or needs
- *     more) and keeps until the process ends; that first call must not be
- *     made while the stream is being captured into a graph. Calls on one
- *     device share the workspace, so such calls on different streams of the
- *     same device must not overlap in time. fp4_gemm_prefill,
- *     fp4_gemm_prefill_multi and fp4_argmax_rows keep workspaces of their
- *     own under the same rules (described at each call).
+ *     buffer. The library allocates nothing and keeps no state between
+ *     calls (it caches each device's compute-unit count, a device property).
+ *   - Workspaces. Some products split work over workgroups whose partial
+ *     results meet in scratch memory. That memory is a caller-owned device
+ *     buffer, the workspace, passed to the *_ws forms and to the greedy
+ *     calls; fp4_workspace_bytes gives the size a call needs. A workspace is
+ *     256-byte aligned and filled with zeros once before its first use (e.g.
+ *     hipMemset after allocating it). Its first 64 KiB are counters that
+ *     every call leaves at zero when its kernels complete; the bytes after
+ *     them are scratch that a call overwrites. One workspace can therefore
+ *     serve any sequence of calls that run one after another (one stream, or
+ *     a graph replayed on one stream); calls that may run at the same time
+ *     need separate workspaces. A NULL workspace selects paths that need
+ *     none (documented at each call), so the calls without a workspace
+ *     argument never touch memory other than their arguments, and calls on
+ *     different streams never share memory unless their arguments do.
  *   - `stream` is a hipStream_t (NULL = the default stream). Calls only
  *     enqueue work: they never synchronise, and results are ready when the
  *     stream's work is. gscale is a device pointer, so quantise -> multiply
@@ -71,8 +74,7 @@
  *     packed data: 8-byte; canonical scales: none); y and gscale 4-byte
  *     aligned.
  *   - Size limits: 1 <= N <= 2^28, 16 <= K <= 2^24, 1 <= M <= 2^24.
- *   - Calls may be made from several host threads; the workspaces are
- *     guarded by a lock while they are (re)allocated.
+ *   - Calls may be made from several host threads at once.
  */
 #ifndef FP4_H
 #define FP4_H
@@ -97,7 +99,8 @@ typedef enum {
     FP4_ERR_ALIGN = -3,       /* a pointer is not aligned as required */
     FP4_ERR_LAYOUT = -4,      /* unknown layout tag */
     FP4_ERR_HIP = -5,         /* the HIP runtime rejected a launch */
-    FP4_ERR_UNSUPPORTED = -6  /* valid request the library cannot serve */
+    FP4_ERR_UNSUPPORTED = -6, /* valid request the library cannot serve */
+    FP4_ERR_WORKSPACE = -7    /* workspace smaller than fp4_workspace_bytes reports */
 } fp4_status;
 
 typedef enum { FP4_LAYOUT_ROWMAJOR = 0, FP4_LAYOUT_TILED = 1 } fp4_layout;
@@ -153,9 +156,22 @@ FP4_API int fp4_retile(const void *packed_rm, const void *scales_rm, int64_t N, 
  * or tokens being verified by speculative decoding) share one pass over
  * the weights (page "1. The big picture", the batching and speculative
  * decoding bullets of "The most important number in this book").
- * Any M >= 1 is accepted. `packed` holds the tiles; `scales` is unused. */
+ * Any M >= 1 is accepted. `packed` holds the tiles; `scales` is unused.
+ * Up to 4 rows (and 3-4 rows on large launches with few K chunks aside)
+ * run on the vector ALUs, more on the matrix cores in passes of 16 rows.
+ * The matrix-core path splits K into chunks of 1024 over workgroups; with
+ * more than one chunk this call (no workspace) first zeroes y with a fill
+ * kernel and adds the chunk sums into y with fp32 atomics, so the last
+ * bits of y can differ between calls. fp4_gemv_ws adds them in chunk order
+ * through a workspace instead (deterministic). */
 FP4_API int fp4_gemv(float *y, const void *x_bf16, const void *packed, const void *scales, const float *gscale,
              int64_t M, int64_t N, int64_t K, void *stream);
+
+/* fp4_gemv with a workspace (see Conventions; NULL = fp4_gemv). A chunked
+ * matrix-core product keeps the chunk partial sums in the workspace and a
+ * second kernel adds them in chunk order: results are deterministic. */
+FP4_API int fp4_gemv_ws(float *y, const void *x_bf16, const void *packed, const void *scales, const float *gscale,
+                        int64_t M, int64_t N, int64_t K, void *workspace, size_t workspace_bytes, void *stream);
 
 /* One projection of a fused launch: TILED weights (`packed`; `scales`
  * unused) with N rows and their own tensor scale, writing y[m*ldy + n]
@@ -180,6 +196,10 @@ typedef struct {
 FP4_API int fp4_gemv_multi(const fp4_proj *projs, int nproj, const void *x_bf16, int64_t M, int64_t K,
                    void *stream);
 
+/* fp4_gemv_multi with a workspace, as fp4_gemv_ws. */
+FP4_API int fp4_gemv_multi_ws(const fp4_proj *projs, int nproj, const void *x_bf16, int64_t M, int64_t K,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
 /* The same product for prefill-sized M on the matrix cores: packed weight
  * codes are staged in LDS, dequantised exactly to bf16 (E2M1 x E4M3 fits
  * bf16) as MFMA operands and fed to bf16 MFMA with fp32 accumulation;
@@ -189,22 +209,22 @@ FP4_API int fp4_gemv_multi(const fp4_proj *projs, int nproj, const void *x_bf16,
  * Any M >= 1 is accepted; y [M][N] fp32 overwritten. `packed` holds the
  * tiles; `scales` is unused. The first call on a device raises the kernels'
  * dynamic LDS limit (a launch attribute, no allocation). Output tiles are
- * 256 x 128, 192 or 256; when the last round of tiles over the compute
- * units would leave most of them idle, those tiles are split into up to 4
- * K ranges on separate workgroups (a second launch) whose fp32 partial sums
- * meet in a per-device workspace (1 KiB per tile column, per row of 256,
- * per K range: at most 64 MiB, plus 128 bytes per split tile), allocated
- * with hipMalloc on the first call that needs it (or needs more) and kept
- * until the process ends, under the rules of the fp4_gemv workspace above
- * (no graph capture during that first call; no overlapping calls on
- * different streams of one device). The partial sums are added in K order
- * whichever workgroup finishes last: results are deterministic, but a
- * split tile may differ from an unsplit one in the last bits. FP4_ERR_SHAPE also
- * covers shapes whose 256-row slabs reach 2 GB (256*K*2 or 256*N*4 bytes,
- * or 32 weight row groups: the kernel uses 32-bit buffer offsets), i.e.
- * K >= 4194304 or N >= 2097152. */
+ * 256 x 128, 192 or 256. FP4_ERR_SHAPE also covers shapes whose 256-row
+ * slabs reach 2 GB (256*K*2 or 256*N*4 bytes, or 32 weight row groups: the
+ * kernel uses 32-bit buffer offsets), i.e. K >= 4194304 or N >= 2097152. */
 FP4_API int fp4_gemm_prefill(float *y, const void *x_bf16, const void *packed, const void *scales,
                      const float *gscale, int64_t M, int64_t N, int64_t K, void *stream);
+
+/* fp4_gemm_prefill with a workspace (see Conventions; NULL =
+ * fp4_gemm_prefill). When the last round of tiles over the compute units
+ * would leave most of them idle, those tiles are split into up to 4 K
+ * ranges on separate workgroups (a second launch) whose fp32 partial sums
+ * meet in the workspace; the last piece of a tile adds them in K order,
+ * whichever finishes last. Results are deterministic, but a split tile may
+ * differ from an unsplit one in the last bits. */
+FP4_API int fp4_gemm_prefill_ws(float *y, const void *x_bf16, const void *packed, const void *scales,
+                                const float *gscale, int64_t M, int64_t N, int64_t K, void *workspace,
+                                size_t workspace_bytes, void *stream);
 
 /* fp4_gemm_prefill over several projections that read the same x [M][K]
  * (the gate and up halves of an MLP, or Q, K and V) in one pass over the
@@ -214,11 +234,14 @@ FP4_API int fp4_gemm_prefill(float *y, const void *x_bf16, const void *packed, c
  * compute units together, so the last round of tiles is fuller than it is
  * for each projection alone. 1 <= nproj <= FP4_MAX_PROJ;
  * `projs` is host memory read before the call returns; ldy >= N, and a
- * 256-row slab of each y (256*ldy*4 bytes) stays below 2 GB. Other limits,
- * the first-call attribute and the workspace are those of
- * fp4_gemm_prefill. */
+ * 256-row slab of each y (256*ldy*4 bytes) stays below 2 GB. Other limits
+ * and the first-call attribute are those of fp4_gemm_prefill. */
 FP4_API int fp4_gemm_prefill_multi(const fp4_proj *projs, int nproj, const void *x_bf16, int64_t M, int64_t K,
                                    void *stream);
+
+/* fp4_gemm_prefill_multi with a workspace, as fp4_gemm_prefill_ws. */
+FP4_API int fp4_gemm_prefill_multi_ws(const fp4_proj *projs, int nproj, const void *x_bf16, int64_t M, int64_t K,
+                                      void *workspace, size_t workspace_bytes, void *stream);
 
 /* Greedy next-token choice: idx[m] = the first n with y[m][n] not below any
  * other element of row m, for fp32 y [M][N] (device, row stride ldy >= N);
@@ -226,23 +249,44 @@ FP4_API int fp4_gemm_prefill_multi(const fp4_proj *projs, int nproj, const void 
  * The last vector of a decode step times the vocabulary matrix gives one
  * logit per vocabulary entry and greedy decoding picks the most likely
  * (page "1. The big picture", steps 4 and 5). idx is int32 [M] (device).
- * Rows longer than 4096 elements are split over several workgroups whose
- * partial results meet in a per-device workspace (8 bytes per workgroup
- * plus 128 bytes per row), allocated with hipMalloc on the first call that
- * needs it (or needs more) and kept until the process ends, under the same
- * rules as the fp4_gemv workspace above: no graph capture during that first
- * call, and calls on different streams of one device must not overlap.
- * The result is deterministic. Limits: 1 <= N <= 2^28, 1 <= M <= 2^24,
- * M * ldy <= 2^40. */
-FP4_API int fp4_argmax_rows(int32_t *idx, const float *y, int64_t M, int64_t N, int64_t ldy, void *stream);
+ * With a workspace (see Conventions), rows longer than 4096 elements are
+ * split over several workgroups whose partial results meet there; with
+ * NULL, one workgroup reads each whole row (slower on long rows). The
+ * result is deterministic either way. Limits: 1 <= N <= 2^28,
+ * 1 <= M <= 2^24, M * ldy <= 2^40. */
+FP4_API int fp4_argmax_rows(int32_t *idx, const float *y, int64_t M, int64_t N, int64_t ldy, void *workspace,
+                            size_t workspace_bytes, void *stream);
 
 /* The greedy decode step's last product and choice: logits [M][N] (fp32,
  * device, overwritten) = fp4_gemv(x, W) for the TILED vocabulary matrix W
- * [N][K], then idx = fp4_argmax_rows(logits). Two launches on `stream`
- * (plus fp4_gemv's own); all arguments are checked before the first. */
+ * [N][K], and idx [M] (int32, device) = the greedy choice of each row of
+ * the logits, as fp4_argmax_rows takes it. With a workspace, and when the
+ * product is one launch whose workgroups each cover all M rows (M <= 4,
+ * or M <= 16 with K <= 1024), the choice is that launch's epilogue: every
+ * workgroup leaves its largest (value, index) per row in the workspace and
+ * the last one to finish picks the index (one launch in all). Otherwise
+ * the product, then fp4_argmax_rows with the same workspace. All arguments
+ * are checked before the first launch. */
 FP4_API int fp4_lm_head_greedy(int32_t *idx, float *logits, const void *x_bf16, const void *packed,
                                const void *scales, const float *gscale, int64_t M, int64_t N, int64_t K,
-                               void *stream);
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/* Which call a workspace size is asked for. */
+typedef enum {
+    FP4_OP_GEMV = 0,           /* fp4_gemv_ws, fp4_gemv_multi_ws */
+    FP4_OP_GEMM_PREFILL = 1,   /* fp4_gemm_prefill_ws, fp4_gemm_prefill_multi_ws */
+    FP4_OP_ARGMAX_ROWS = 2,    /* fp4_argmax_rows (K unused, Ns[0] = N) */
+    FP4_OP_LM_HEAD_GREEDY = 3  /* fp4_lm_head_greedy (Ns[0] = N) */
+} fp4_op;
+
+/* *bytes = the workspace bytes a call of `op` with M activation rows, K
+ * input features and nproj projections of Ns[i] output features needs on
+ * the current device (0: the call uses none, any workspace or NULL will
+ * do). Host only; enqueues nothing. The size depends on the launch plan,
+ * which reads the device's compute-unit count. Returns FP4_ERR_SHAPE for
+ * arguments the call itself would reject, FP4_ERR_UNSUPPORTED for an
+ * unknown op. */
+FP4_API int fp4_workspace_bytes(int op, int64_t M, int64_t K, const int64_t *Ns, int nproj, size_t *bytes);
 
 #ifdef __cplusplus
 }

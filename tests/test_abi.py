@@ -8,28 +8,34 @@ import pytest
 
 import bit_block_scaled_fp4_amd as fp4
 
-OK, ENULL, ESHAPE, EALIGN, ELAYOUT = 0, -1, -2, -3, -4
+OK, ENULL, ESHAPE, EALIGN, ELAYOUT, EWS = 0, -1, -2, -3, -4, -7
 A = 1 << 20          # a fake, 16-byte-aligned address; never dereferenced
 
 
-def declared_functions():
-    src = open(fp4.HEADER_PATH).read()
-    return sorted(set(re.findall(r"FP4_API\s+[\w\s\*]*?\b(fp4_\w+)\s*\(", src)))
+def declared_functions(path=None):
+    src = open(path or fp4.HEADER_PATH).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(?:int|void|size_t|const char)\s*\*?\s*(fp4_\w+)\s*\(", src)))
 
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert names == sorted(["fp4_status_string", "fp4_layout_bytes", "fp4_quantize", "fp4_retile", "fp4_gemv",
-                            "fp4_gemv_multi", "fp4_gemm_prefill", "fp4_gemm_prefill_multi", "fp4_argmax_rows", "fp4_lm_head_greedy",
-                            "fp4_quantize_fp8"])
+                            "fp4_gemv_ws", "fp4_gemv_multi", "fp4_gemv_multi_ws", "fp4_gemm_prefill",
+                            "fp4_gemm_prefill_ws", "fp4_gemm_prefill_multi", "fp4_gemm_prefill_multi_ws",
+                            "fp4_argmax_rows", "fp4_lm_head_greedy", "fp4_quantize_fp8", "fp4_workspace_bytes"])
     lib = ctypes.CDLL(fp4.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
+    import os
+    for h in sorted(os.listdir(os.path.dirname(fp4.HEADER_PATH))):   # every header under include/
+        for n in declared_functions(os.path.join(os.path.dirname(fp4.HEADER_PATH), h)):
+            assert hasattr(lib, n), (h, n)
 
 
 def test_status_strings():
     lib = fp4.raw()
-    for s in (OK, ENULL, ESHAPE, EALIGN, ELAYOUT, -5, -6, 42):
+    for s in (OK, ENULL, ESHAPE, EALIGN, ELAYOUT, -5, -6, -7, 42):
         assert isinstance(lib.fp4_status_string(s), bytes) and lib.fp4_status_string(s)
 
 
@@ -122,21 +128,54 @@ def test_gemm_prefill_multi_argument_errors():
 
 def test_argmax_and_greedy_argument_errors():
     L = fp4.raw()
-    assert L.fp4_argmax_rows(None, A, 1, 8, 8, None) == ENULL
-    assert L.fp4_argmax_rows(A, None, 1, 8, 8, None) == ENULL
-    assert L.fp4_argmax_rows(A, A, 0, 8, 8, None) == ESHAPE
-    assert L.fp4_argmax_rows(A, A, 1, 0, 8, None) == ESHAPE
-    assert L.fp4_argmax_rows(A, A, 2, 8, 7, None) == ESHAPE          # row stride below N
-    assert L.fp4_argmax_rows(A, A, 1, 1 << 29, 1 << 29, None) == ESHAPE
-    assert L.fp4_argmax_rows(A + 2, A, 1, 8, 8, None) == EALIGN
-    assert L.fp4_argmax_rows(A, A + 1, 1, 8, 8, None) == EALIGN
+    assert L.fp4_argmax_rows(None, A, 1, 8, 8, None, 0, None) == ENULL
+    assert L.fp4_argmax_rows(A, None, 1, 8, 8, None, 0, None) == ENULL
+    assert L.fp4_argmax_rows(A, A, 0, 8, 8, None, 0, None) == ESHAPE
+    assert L.fp4_argmax_rows(A, A, 1, 0, 8, None, 0, None) == ESHAPE
+    assert L.fp4_argmax_rows(A, A, 2, 8, 7, None, 0, None) == ESHAPE          # row stride below N
+    assert L.fp4_argmax_rows(A, A, 1, 1 << 29, 1 << 29, None, 0, None) == ESHAPE
+    assert L.fp4_argmax_rows(A + 2, A, 1, 8, 8, None, 0, None) == EALIGN
+    assert L.fp4_argmax_rows(A, A + 1, 1, 8, 8, None, 0, None) == EALIGN
+    # a workspace: 256-byte aligned, at least what fp4_workspace_bytes reports
+    need = fp4.workspace_bytes(fp4.OP_ARGMAX_ROWS, 2, 0, [10000])
+    assert need > 65536
+    assert L.fp4_argmax_rows(A, A, 2, 10000, 10000, A + 16, need, None) == EALIGN
+    assert L.fp4_argmax_rows(A, A, 2, 10000, 10000, A, need - 1, None) == EWS
     # the greedy step checks everything before its first launch
-    assert L.fp4_lm_head_greedy(None, A, A, A, None, A, 1, 8, 32, None) == ENULL
-    assert L.fp4_lm_head_greedy(A, None, A, A, None, A, 1, 8, 32, None) == ENULL
-    assert L.fp4_lm_head_greedy(A, A, A, A, None, A, 1, 8, 24, None) == ESHAPE
-    assert L.fp4_lm_head_greedy(A, A, A, A, None, A, 0, 8, 32, None) == ESHAPE
-    assert L.fp4_lm_head_greedy(A + 2, A, A, A, None, A, 1, 8, 32, None) == EALIGN
-    assert L.fp4_lm_head_greedy(A, A, A + 8, A, None, A, 1, 8, 32, None) == EALIGN
+    assert L.fp4_lm_head_greedy(None, A, A, A, None, A, 1, 8, 32, None, 0, None) == ENULL
+    assert L.fp4_lm_head_greedy(A, None, A, A, None, A, 1, 8, 32, None, 0, None) == ENULL
+    assert L.fp4_lm_head_greedy(A, A, A, A, None, A, 1, 8, 24, None, 0, None) == ESHAPE
+    assert L.fp4_lm_head_greedy(A, A, A, A, None, A, 0, 8, 32, None, 0, None) == ESHAPE
+    assert L.fp4_lm_head_greedy(A + 2, A, A, A, None, A, 1, 8, 32, None, 0, None) == EALIGN
+    assert L.fp4_lm_head_greedy(A, A, A + 8, A, None, A, 1, 8, 32, None, 0, None) == EALIGN
+    need = fp4.workspace_bytes(fp4.OP_LM_HEAD_GREEDY, 1, 1024, [151936])
+    assert L.fp4_lm_head_greedy(A, A, A, A, None, A, 1, 151936, 1024, A, need - 8, None) == EWS
+
+
+def test_workspace_bytes_query():
+    """Sizes of the caller-owned workspaces: nothing for calls without
+    scratch, the 64 KiB counter header plus the partial sums or keys
+    otherwise; bad queries are rejected."""
+    H = 65536
+    assert fp4.workspace_bytes(fp4.OP_GEMV, 1, 17408, [5120]) == 0             # M = 1: vector ALUs, no split
+    assert fp4.workspace_bytes(fp4.OP_GEMV, 8, 1024, [151936]) == 0            # one K chunk: no partials
+    # M = 8 on 17 chunks: C * pairs * 16 * 16 fp32 partial sums
+    assert fp4.workspace_bytes(fp4.OP_GEMV, 8, 17408, [5120]) == H + 17 * 320 * 1024
+    assert fp4.workspace_bytes(fp4.OP_GEMV, 8, 5120, [17408, 17408]) == H + 5 * 2176 * 1024
+    assert fp4.workspace_bytes(fp4.OP_ARGMAX_ROWS, 3, 0, [4096]) == 0          # one segment per row
+    assert fp4.workspace_bytes(fp4.OP_ARGMAX_ROWS, 3, 0, [4097]) == H + 3 * 2 * 8
+    assert fp4.workspace_bytes(fp4.OP_ARGMAX_ROWS, 600, 0, [8192]) == H + 512 * 2 * 8   # 512 rows per launch
+    assert fp4.workspace_bytes(fp4.OP_LM_HEAD_GREEDY, 1, 1024, [151936]) > H
+    for bad in ((fp4.OP_GEMV, 0, 32, [8]), (fp4.OP_GEMV, 1, 24, [8]), (fp4.OP_ARGMAX_ROWS, 1, 0, [8, 8]),
+                (fp4.OP_LM_HEAD_GREEDY, 1, 32, [0])):
+        with pytest.raises(fp4.Fp4Error) as e:
+            fp4.workspace_bytes(*bad)
+        assert e.value.status == ESHAPE, bad
+    with pytest.raises(fp4.Fp4Error) as e:
+        fp4.workspace_bytes(9, 1, 32, [8])
+    assert e.value.status == -6
+    out = ctypes.c_size_t()
+    assert fp4.raw().fp4_workspace_bytes(0, 1, 32, None, 1, ctypes.byref(out)) == ENULL
 
 
 def test_quantize_fp8_argument_errors():

@@ -363,28 +363,59 @@ def test_gemv_multi_equals_oracle_for_each_projection_and_is_deterministic():
         assert torch.equal(o, o2)
 
 
+def ws_for(op, M, K, Ns):
+    return fp4.new_workspace(fp4.workspace_bytes(op, M, K, Ns), dev())
+
+
 @pytest.mark.parametrize("M", [5, 9])
 def test_gemv_multi_matrix_core_ragged_projections(M):
     """Several projections of unequal, ragged row counts (333, 16, 1000 rows;
-    K = 3008: three chunks, so the split-K reduce runs) in one launch on the
+    K = 3008: three chunks, so the K split runs) in one launch on the
     matrix-core path (M >= 5; M = 9 stages 16 activation rows, M = 5 eight),
-    each equal to the oracle within the tolerance and repeatable bit for bit."""
+    each equal to the oracle within the tolerance: with a workspace (chunk
+    partials added in order by a second kernel: repeatable bit for bit) and
+    without (y zeroed, then atomic adds; outputs start as NaN)."""
     print("gemv_multi mfma", M, flush=True)
     Ns, K = (333, 16, 1000), 3008
     bws = [bf16_tensor((N, K), 800 + N, 0.02, outlier_p=0.002, outlier_scale=20.0) for N in Ns]
     ws = [gpu_quant(b) for b in bws]
     bx = bf16_tensor((M, K), 900 + M, 1.0)
     x = to_gpu_bf16(bx)
+    work = ws_for(fp4.OP_GEMV, M, K, Ns)
+    assert work.numel() > 65536
     outs = [torch.empty((M, N), dtype=torch.float32, device=dev()) for N in Ns]
     outs2 = [torch.empty_like(o) for o in outs]
-    fp4.gemv_multi(x, ws, outs)
-    fp4.gemv_multi(x, ws, outs2)
+    outs_na = [torch.full_like(o, float("nan")) for o in outs]
+    fp4.gemv_multi(x, ws, outs, workspace=work)
+    fp4.gemv_multi(x, ws, outs2, workspace=work)
+    fp4.gemv_multi(x, ws, outs_na)
     torch.cuda.synchronize()
-    for b, o, o2 in zip(bws, outs, outs2):
+    assert torch.count_nonzero(work[:65536]) == 0        # the counter header stays zero
+    for b, o, o2, on in zip(bws, outs, outs2, outs_na):
         p, s, g = oracle.quantize(b)
         yr, l1 = oracle.gemv(bx, p, s, g, threads=THREADS)
-        assert_within_tolerance(o.cpu().numpy(), yr, l1, "multi mfma M=%d" % M)
+        assert_within_tolerance(o.cpu().numpy(), yr, l1, "multi mfma ws M=%d" % M)
+        assert_within_tolerance(on.cpu().numpy(), yr, l1, "multi mfma atomic M=%d" % M)
         assert torch.equal(o, o2)
+
+
+def test_workspace_too_small_is_an_error():
+    """A workspace smaller than fp4_workspace_bytes reports is rejected before
+    any launch; one that is large enough but not 256-byte aligned too."""
+    N, K, M = 1000, 3008, 8
+    w = gpu_quant(bf16_tensor((N, K), 5, 0.02))
+    x = to_gpu_bf16(bf16_tensor((M, K), 6, 1.0))
+    need = fp4.workspace_bytes(fp4.OP_GEMV, M, K, [N])
+    small = fp4.new_workspace(need - 1, dev())
+    with pytest.raises(fp4.Fp4Error) as e:
+        fp4.gemv(x, w, workspace=small)
+    assert e.value.status == -7
+    big = fp4.new_workspace(need + 512, dev())
+    L = fp4.raw()
+    y = torch.empty((M, N), dtype=torch.float32, device=dev())
+    st = L.fp4_gemv_ws(y.data_ptr(), x.data_ptr(), w.packed.data_ptr(), None, w.gscale.data_ptr(), M, N, K,
+                       big.data_ptr() + 16, need, torch.cuda.current_stream().cuda_stream)
+    assert st == -3
 
 
 # --------------------------------------------------------------------- prefill
@@ -448,13 +479,18 @@ def test_prefill_whole_and_split_tiles(M, N, K, rows):
     bx = bf16_tensor((M, K), 5 * M + 3, 1.0)
     w = gpu_quant(bw)
     x = to_gpu_bf16(bx)
-    y = fp4.gemm_prefill(x, w)
-    y2 = fp4.gemm_prefill(x, w)
+    work = ws_for(fp4.OP_GEMM_PREFILL, M, K, [N])
+    assert work.numel() > 65536                          # the last round is split
+    y = fp4.gemm_prefill(x, w, workspace=work)
+    y2 = fp4.gemm_prefill(x, w, workspace=work)
+    y3 = fp4.gemm_prefill(x, w)                          # no workspace: nothing split
     torch.cuda.synchronize()
     assert torch.equal(y, y2)
+    assert torch.count_nonzero(work[:65536]) == 0
     p, s, g = oracle.quantize(bw)
     yr, l1 = oracle.gemv(bx[rows], p, s, g, threads=THREADS)
     assert_within_tolerance(y[rows].cpu().numpy(), yr, l1, "prefill whole+split %d %d %d" % (M, N, K))
+    assert_within_tolerance(y3[rows].cpu().numpy(), yr, l1, "prefill unsplit %d %d %d" % (M, N, K))
 
 
 def test_prefill_full_size_sampled_rows():
@@ -481,8 +517,9 @@ def test_prefill_full_size_sampled_rows():
     N = ws["gate"].N
     yf = torch.empty((2048, 2 * N), dtype=torch.float32, device=dev())
     yf2 = torch.empty_like(yf)
+    work = ws_for(fp4.OP_GEMM_PREFILL, 2048, 5120, [N, N])
     for out in (yf, yf2):
-        fp4.gemm_prefill_multi(x, [ws["gate"], ws["up"]], [out[:, :N], out[:, N:]], [2 * N, 2 * N])
+        fp4.gemm_prefill_multi(x, [ws["gate"], ws["up"]], [out[:, :N], out[:, N:]], [2 * N, 2 * N], workspace=work)
     torch.cuda.synchronize()
     assert torch.equal(yf, yf2)
     # the split tiles are the last ones: token slab 7 (rows 1792..2047), the last 64 x 256 columns of up
@@ -545,36 +582,55 @@ def planted_rows(M, N, seed):
                                  (2, 1 << 20)])
 def test_argmax_rows_bit_exact(M, N):
     y = planted_rows(M, N, seed=M * 1000003 + N)
-    got = fp4.argmax_rows(torch.from_numpy(y).to(dev())).cpu().numpy()
-    assert np.array_equal(got, oracle.argmax_rows(y))
+    yt = torch.from_numpy(y).to(dev())
+    work = ws_for(fp4.OP_ARGMAX_ROWS, M, 0, [N])
+    got = fp4.argmax_rows(yt, workspace=work).cpu().numpy()
+    got_nows = fp4.argmax_rows(yt).cpu().numpy()
+    ref = oracle.argmax_rows(y)
+    assert np.array_equal(got, ref)
+    assert np.array_equal(got_nows, ref)
 
 
 def test_argmax_rows_strided_and_repeated():
     """Row stride above N through the C ABI; repeated launches of different
-    sizes (the per-row counters must come back to zero every time)."""
+    sizes sharing one workspace (the per-row counters must come back to zero
+    every time), more rows than the workspace header has counters (600: two
+    launches), and the same calls without a workspace."""
     L = fp4.raw()
     stream = torch.cuda.current_stream().cuda_stream
-    for M, N, ldy in [(3, 10000, 10007), (8, 151936, 151936), (3, 10000, 10007), (40, 9000, 9001), (1, 4097, 4100),
-                      (3, 10000, 10007)]:
+    cases = [(3, 10000, 10007), (8, 151936, 151936), (3, 10000, 10007), (40, 9000, 9001), (1, 4097, 4100),
+             (600, 5000, 5003), (3, 10000, 10007)]
+    work = fp4.new_workspace(max(fp4.workspace_bytes(fp4.OP_ARGMAX_ROWS, M, 0, [N]) for M, N, _ in cases), dev())
+    for M, N, ldy in cases:
         y = planted_rows(M, ldy, seed=N + ldy + M)
         y[:, N:] = np.inf                                # past N: must be ignored
-        idx = torch.full((M,), -1, dtype=torch.int32, device=dev())
+        ref = oracle.argmax_rows(np.ascontiguousarray(y[:, :N]))
         yt = torch.from_numpy(y).to(dev())
-        assert L.fp4_argmax_rows(idx.data_ptr(), yt.data_ptr(), M, N, ldy, stream) == 0
-        assert np.array_equal(idx.cpu().numpy(), oracle.argmax_rows(np.ascontiguousarray(y[:, :N]))), (M, N, ldy)
+        for wp, wb in ((work.data_ptr(), work.numel()), (None, 0)):
+            idx = torch.full((M,), -1, dtype=torch.int32, device=dev())
+            assert L.fp4_argmax_rows(idx.data_ptr(), yt.data_ptr(), M, N, ldy, wp, wb, stream) == 0
+            assert np.array_equal(idx.cpu().numpy(), ref), (M, N, ldy, wp is None)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(work[:65536]) == 0
 
 
-@pytest.mark.parametrize("M", [1, 8])
-def test_lm_head_greedy_workload(M):
-    """The greedy step on the LM head 151936 x 1024: the logits within the
-    product tolerance; the index bit-exact against the oracle's choice on the
-    same fp32 logits; and against the fp64 logits, a value within the two
-    tolerances of the true maximum (equal to it where the top two are
-    further apart than that)."""
-    bw, bx = weight_bits("lm_head", "w"), act_bits("lm_head", "x_m%d" % M)
+@pytest.mark.parametrize("M,fused", [(1, True), (8, True), (3, True), (1, False), (8, False)])
+def test_lm_head_greedy_workload(M, fused):
+    """The greedy step on the LM head 151936 x 1024, with a workspace (the
+    choice is the product launch's epilogue) and without (product, then a
+    whole-row argmax): the logits within the product tolerance; the index
+    bit-exact against the oracle's choice on the same fp32 logits; and
+    against the fp64 logits, a value within the two tolerances of the true
+    maximum (equal to it where the top two are further apart than that)."""
+    bw, bx = weight_bits("lm_head", "w"), act_bits("lm_head", "x_m8")[:M]
+    if M in (1, 8):
+        bx = act_bits("lm_head", "x_m%d" % M)
     w = gpu_quant(bw)
-    idx, logits = fp4.lm_head_greedy(to_gpu_bf16(bx), w)
+    work = ws_for(fp4.OP_LM_HEAD_GREEDY, M, 1024, [151936]) if fused else None
+    idx, logits = fp4.lm_head_greedy(to_gpu_bf16(bx), w, workspace=work)
     torch.cuda.synchronize()
+    if fused:
+        assert torch.count_nonzero(work[:65536]) == 0
     idx, lg = idx.cpu().numpy(), logits.cpu().numpy()
     p, s, g = oracle_quant("lm_head", "w")
     yr, l1 = oracle.gemv(bx, p, s, g, threads=THREADS)
@@ -590,43 +646,65 @@ def test_lm_head_greedy_workload(M):
 
 
 # ------------------------------------------------------------- graph replay
-def test_graph_replays_match_eager_results():
-    """The calls the bench replays from HIP graphs — the fused M = 1 product,
-    the M = 8 matrix-core product with its K-chunk reduce, the fused prefill
-    product with a K-split tail, and the greedy step (multi-segment argmax) —
-    captured once, replayed four times with eager work and synchronisations
-    between the replays; every replay equals the eager results bit for bit
-    (all these kernels are deterministic)."""
-    torch.manual_seed(0)
+def _graph_case():
+    """Weights, inputs and outputs of the calls the bench replays from graphs."""
     ws = {name: gpu_quant(bf16_tensor(shape, 600 + i, 0.02, outlier_p=0.002, outlier_scale=20.0))
           for i, (name, shape) in enumerate([("g", (2048, 2048)), ("u", (2048, 2048)), ("d", (1000, 3072)),
                                               ("p1", (300, 1040)), ("p2", (1000, 1040)), ("lm", (20000, 1024))])}
-    x1 = to_gpu_bf16(bf16_tensor((1, 2048), 71, 1.0))
-    x8 = to_gpu_bf16(bf16_tensor((8, 3072), 72, 1.0))
-    xp = to_gpu_bf16(bf16_tensor((300, 1040), 73, 1.0))
-    xl = to_gpu_bf16(bf16_tensor((1, 1024), 74, 1.0))
-    outs = {"gu": torch.empty((1, 4096), dtype=torch.float32, device=dev()),
+    xs = {"x1": to_gpu_bf16(bf16_tensor((1, 2048), 71, 1.0)), "x8": to_gpu_bf16(bf16_tensor((8, 3072), 72, 1.0)),
+          "xp": to_gpu_bf16(bf16_tensor((300, 1040), 73, 1.0)), "xl": to_gpu_bf16(bf16_tensor((1, 1024), 74, 1.0))}
+    return ws, xs
+
+
+def _graph_outs():
+    return {"gu": torch.empty((1, 4096), dtype=torch.float32, device=dev()),
             "d8": torch.empty((8, 1000), dtype=torch.float32, device=dev()),
+            "d8a": torch.empty((8, 1000), dtype=torch.float32, device=dev()),
             "pf": torch.empty((300, 1300), dtype=torch.float32, device=dev()),
             "lg": torch.empty((1, 20000), dtype=torch.float32, device=dev()),
             "ix": torch.empty((1,), dtype=torch.int32, device=dev())}
 
-    def step(o):
-        fp4.gemv_multi(x1, [ws["g"], ws["u"]], [o["gu"][:, :2048], o["gu"][:, 2048:]], [4096, 4096])
-        fp4.gemv(x8, ws["d"], out=o["d8"])
-        fp4.gemm_prefill_multi(xp, [ws["p1"], ws["p2"]], [o["pf"][:, :300], o["pf"][:, 300:]], [1300, 1300])
-        fp4.lm_head_greedy(xl, ws["lm"], logits=o["lg"], out=o["ix"])
 
-    step(outs)                              # eager (also allocates the workspaces before capture)
+def _graph_step(ws, xs, o, work):
+    fp4.gemv_multi(xs["x1"], [ws["g"], ws["u"]], [o["gu"][:, :2048], o["gu"][:, 2048:]], [4096, 4096])
+    fp4.gemv(xs["x8"], ws["d"], out=o["d8"], workspace=work)
+    fp4.gemv(xs["x8"], ws["d"], out=o["d8a"])          # no workspace: fill kernel + atomic adds
+    fp4.gemm_prefill_multi(xs["xp"], [ws["p1"], ws["p2"]], [o["pf"][:, :300], o["pf"][:, 300:]], [1300, 1300],
+                           workspace=work)
+    fp4.lm_head_greedy(xs["xl"], ws["lm"], logits=o["lg"], out=o["ix"], workspace=work)
+
+
+def _graph_work():
+    need = max(fp4.workspace_bytes(fp4.OP_GEMV, 8, 3072, [1000]),
+               fp4.workspace_bytes(fp4.OP_GEMM_PREFILL, 300, 1040, [300, 1000]),
+               fp4.workspace_bytes(fp4.OP_LM_HEAD_GREEDY, 1, 1024, [20000]))
+    return fp4.new_workspace(need, dev())
+
+
+def test_graph_replays_match_eager_results():
+    """The calls the bench replays from HIP graphs — the fused M = 1 product,
+    the M = 8 matrix-core product with its K-chunk reduce (workspace) and
+    with atomic adds (none), the fused prefill product with a K-split tail,
+    and the greedy step folded into the LM-head launch, all sharing one
+    workspace — captured once, replayed four times with eager work and
+    synchronisations between the replays; every replay equals the eager
+    results bit for bit (the atomic-add product: within the tolerance of the
+    eager one, since its summation order is free)."""
+    ws, xs = _graph_case()
+    outs, work = _graph_outs(), _graph_work()
+    _graph_step(ws, xs, outs, work)          # eager
     torch.cuda.synchronize()
     ref = {k: v.clone() for k, v in outs.items()}
     side = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(side):
         with torch.cuda.graph(g, stream=side):
-            step(outs)
+            _graph_step(ws, xs, outs, work)
     torch.cuda.synchronize()
-    scratch = {k: torch.empty_like(v) for k, v in outs.items()}
+    scratch = _graph_outs()
+    bd = bf16_tensor((1000, 3072), 602, 0.02, outlier_p=0.002, outlier_scale=20.0)
+    p, s, gsc = oracle.quantize(bd)
+    yr, l1 = oracle.gemv(bf16_tensor((8, 3072), 72, 1.0), p, s, gsc)
     for rep in range(4):
         for v in outs.values():
             v.fill_(float("nan") if v.dtype == torch.float32 else -1)
@@ -634,8 +712,99 @@ def test_graph_replays_match_eager_results():
         g.replay()
         torch.cuda.synchronize()
         for k in outs:
-            assert torch.equal(outs[k], ref[k]), (rep, k)
-        step(scratch)                        # eager work between the replays
+            if k == "d8a":
+                assert_within_tolerance(outs[k].cpu().numpy(), yr, l1, "atomic replay %d" % rep)
+            else:
+                assert torch.equal(outs[k], ref[k]), (rep, k)
+        _graph_step(ws, xs, scratch, work)   # eager work between the replays
         torch.cuda.synchronize()
         for k in outs:
-            assert torch.equal(scratch[k], ref[k]), (rep, k, "eager")
+            if k != "d8a":
+                assert torch.equal(scratch[k], ref[k]), (rep, k, "eager")
+        assert torch.count_nonzero(work[:65536]) == 0
+
+
+_FIRST_CALLS_UNDER_CAPTURE = r"""
+import sys, torch
+sys.path.insert(0, sys.argv[1]); sys.path.insert(0, sys.argv[1] + "/tests")
+import test_gpu_parity as t
+import bit_block_scaled_fp4_amd as fp4
+t.fp4 = fp4
+ws, xs = t._graph_case()
+outs, work = t._graph_outs(), t._graph_work()
+torch.cuda.synchronize()
+side = torch.cuda.Stream()
+g = torch.cuda.CUDAGraph()
+with torch.cuda.stream(side):
+    with torch.cuda.graph(g, stream=side):     # the process's first product calls
+        t._graph_step(ws, xs, outs, work)
+torch.cuda.synchronize()
+g.replay(); g.replay()
+torch.cuda.synchronize()
+eager = t._graph_outs()
+t._graph_step(ws, xs, eager, work)
+torch.cuda.synchronize()
+for k in outs:
+    if k != "d8a":
+        assert torch.equal(outs[k], eager[k]), k
+print("first calls under capture ok", flush=True)
+"""
+
+
+def test_first_calls_under_graph_capture():
+    """A process whose first product, prefill and greedy calls are made while
+    the stream is captured into a graph (the library allocates nothing and
+    sets up nothing on the stream on a first call); the replays equal eager
+    results. Runs in a fresh process, since this one has made such calls."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", _FIRST_CALLS_UNDER_CAPTURE, root], capture_output=True, text=True,
+                       timeout=240)
+    assert r.returncode == 0 and "capture ok" in r.stdout, r.stdout[-2000:] + r.stderr[-4000:]
+
+
+def test_two_streams_at_once():
+    """The 27B down projection at M = 8 (matrix cores, 17 K chunks) on one
+    stream and the LM-head greedy step (M = 1, choice in the product launch)
+    on another, both default priority, issued back to back three times before
+    one synchronisation: first each with its own workspace, then both without
+    (atomic adds; whole-row argmax). Every result against the oracle: the
+    products within the tolerance, the indices equal to the oracle's choice
+    on the GPU's logits."""
+    print("two streams", flush=True)
+    wd = gpu_quant(weight_bits("dense27b_layer", "down"))
+    wl = gpu_quant(weight_bits("lm_head", "w"))
+    bx8, bxl = act_bits("dense27b_smallm", "x_mid_m8"), act_bits("lm_head", "x_m1")
+    x8, xl = to_gpu_bf16(bx8), to_gpu_bf16(bxl)
+    wa = ws_for(fp4.OP_GEMV, 8, 17408, [5120])
+    wb = ws_for(fp4.OP_LM_HEAD_GREEDY, 1, 1024, [151936])
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    res = []
+    for use_ws in (True, False):
+        ys = [torch.full((8, 5120), float("nan"), device=dev()) for _ in range(3)]
+        lgs = [torch.empty((1, 151936), device=dev()) for _ in range(3)]
+        ixs = [torch.full((1,), -1, dtype=torch.int32, device=dev()) for _ in range(3)]
+        s1.wait_stream(torch.cuda.current_stream())
+        s2.wait_stream(torch.cuda.current_stream())
+        for r in range(3):
+            with torch.cuda.stream(s1):
+                fp4.gemv(x8, wd, out=ys[r], workspace=wa if use_ws else None)
+            with torch.cuda.stream(s2):
+                fp4.lm_head_greedy(xl, wl, logits=lgs[r], out=ixs[r], workspace=wb if use_ws else None)
+        torch.cuda.synchronize()
+        res.append((use_ws, ys, lgs, ixs))
+    pd, sd, gd = oracle_quant("dense27b_layer", "down")
+    yr, l1 = oracle.gemv(bx8, pd, sd, gd, threads=THREADS)
+    pl, sl, gl = oracle_quant("lm_head", "w")
+    yl, ll1 = oracle.gemv(bxl, pl, sl, gl, threads=THREADS)
+    for use_ws, ys, lgs, ixs in res:
+        for r in range(3):
+            assert_within_tolerance(ys[r].cpu().numpy(), yr, l1, "down M=8 ws=%s rep %d" % (use_ws, r))
+            lg = lgs[r].cpu().numpy()
+            assert_within_tolerance(lg, yl, ll1, "lm head ws=%s rep %d" % (use_ws, r))
+            assert np.array_equal(ixs[r].cpu().numpy(), oracle.argmax_rows(lg)), (use_ws, r)
+        if use_ws:
+            assert all(torch.equal(ys[0], y) for y in ys)
+    assert torch.count_nonzero(wa[:65536]) == 0 and torch.count_nonzero(wb[:65536]) == 0
