@@ -171,7 +171,10 @@ class Timer:
 
     def windows(self, g, per, reps=REPS):
         """Replay g once (warm), then `reps` timed replays; microseconds per
-        unit (`per` units per replay) of each."""
+        unit (`per` units per replay) of each. Before each window a spin
+        kernel keeps the stream busy while the host submits the start event
+        and the graph, so the window holds the graph's GPU work and not the
+        host's submission latency."""
         torch = self.torch
         g.replay()
         torch.cuda.synchronize()
@@ -179,6 +182,7 @@ class Timer:
         for _ in range(reps):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             with torch.cuda.stream(self.stream):
+                torch.cuda._sleep(1 << 21)
                 a.record(self.stream)
                 g.replay()
                 b.record(self.stream)

@@ -255,20 +255,18 @@ int fp4_argmax_rows(int32_t* idx, const float* y, int64_t M, int64_t N, int64_t 
 }
 
 // The greedy step's plan: the product launch itself ends with the choice
-// (one launch) when a workspace is given and the product is a single launch
+// (one launch) when a workspace is given, the product is a single launch
 // whose every workgroup covers all rows (vector ALUs, or the matrix cores
-// with one K chunk and at most 16 rows); otherwise the product, then
-// fp4_argmax_rows' kernel.
+// with one K chunk and at most 16 rows) and its workgroups' keys fit in the
+// workspace header; otherwise the product, then fp4_argmax_rows' kernel.
 static bool greedy_fused(const fp4::GemvArgs& a) {
-  if (a.M > 16) return false;
-  return gemv_on_valu(a) || a.C == 1;
+  if (a.M > 16 || !(gemv_on_valu(a) || a.C == 1)) return false;
+  const int64_t S = gemv_on_valu(a) ? fp4::gemv_workgroups(a) : fp4::gemv_mma_workgroups(a);
+  return S > 0 && fp4::greedy_keys_fit(a.M, S);
 }
 
 static size_t greedy_ws_need(const fp4::GemvArgs& a, int64_t N) {
-  if (greedy_fused(a)) {
-    const int64_t S = gemv_on_valu(a) ? fp4::gemv_workgroups(a) : fp4::gemv_mma_workgroups(a);
-    return fp4::greedy_ws_bytes(a.M, S);
-  }
+  if (greedy_fused(a)) return fp4::kWsHeaderBytes;
   return std::max(gemv_ws_need(a), fp4::argmax_ws_bytes(a.M, N));
 }
 
@@ -296,8 +294,7 @@ int fp4_lm_head_greedy(int32_t* idx, float* logits, const void* x_bf16, const vo
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (ws.valid() && greedy_fused(a)) {
     a.greedy.idx = idx;
-    a.greedy.keys = reinterpret_cast<uint64_t*>(ws.scratch());
-    a.greedy.cnt = ws.counter(0);
+    a.greedy.keys = reinterpret_cast<uint64_t*>(ws.p);   // the header: zero between calls
     return gemv_run(a, ws, s);
   }
   if (int st = gemv_run(a, ws, s)) return st;

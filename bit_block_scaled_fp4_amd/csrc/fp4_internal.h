@@ -47,18 +47,16 @@ struct Workspace {
 
 // Greedy choice folded into a product launch whose every workgroup covers
 // all M activation rows (include/fp4.h, fp4_lm_head_greedy). Each workgroup
-// stores its largest (value, index) key per row in keys[m * S + wg]; the
-// arrivals are counted on eight first-level counters (workgroup % 8, one
-// per XCD's share of the grid) and one second-level counter; the last
-// workgroup to arrive reads the S keys of every row and writes idx.
+// stores its largest (value, index) key per row in keys[m * S + wg], part of
+// the workspace header (zero between calls); the workgroup with the last
+// index collects them, writes idx and zeroes them again (greedy.h).
 struct GreedyArgs {
   int32_t* idx = nullptr;   // [M] (nullptr: no greedy epilogue)
-  uint64_t* keys = nullptr; // [M][S]
-  unsigned* cnt = nullptr;  // 9 counters, kWsCounterWords apart: 8 first-level, then the second-level one
+  uint64_t* keys = nullptr; // [M][S], in the workspace header
   int32_t S = 0;            // workgroups of the launch
 };
-// Workspace bytes of a greedy epilogue over S workgroups and M rows.
-inline size_t greedy_ws_bytes(int64_t M, int64_t S) { return kWsHeaderBytes + (size_t)(M * S) * 8; }
+// Whether the M x S keys fit in the workspace header.
+inline bool greedy_keys_fit(int64_t M, int64_t S) { return M * S * 8 <= (int64_t)kWsHeaderBytes; }
 
 struct ProjDesc {
   const uint8_t* tiles;

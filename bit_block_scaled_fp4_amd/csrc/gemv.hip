@@ -235,6 +235,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv(const GemvArgs a) {
   if (GREEDY) greedy_finish<MT>(a.greedy, keys, M, red, &flag);
 }
 
+
 }  // namespace
 
 // Launch geometry, from sweeps on MI355X (graph-timed, rotating weights):

@@ -58,13 +58,17 @@ __device__ __forceinline__ uint64_t block_max64(uint64_t k, uint64_t* red) {
 // workgroup's outputs are written; k[m] is the thread's largest key of row m
 // (0 where it wrote none), m < M <= NR. `red` is LDS of 16 * NR entries.
 //
-// The workgroup's keys are stored with device-coherent stores, which
-// complete before the workgroup counts itself in. Of the workgroups with
-// index % 8 == j, the last to arrive on counter j puts it back to zero and
-// counts the group in on the second-level counter; the last group's last
-// workgroup puts that one back to zero and reads every key with
-// device-coherent loads. Arrivals on one counter line serialise, so spreading
-// them over eight lines keeps each queue short.
+// Every workgroup stores its largest key per row (never 0: each workgroup
+// writes at least one output of every row) into its slot of the zeroed key
+// array and is done: no counters, nothing to wait for. The workgroup with the
+// last index then reads the M x S slots until none is 0, takes each row's
+// largest key, writes idx and zeroes the slots for the next launch. Only that
+// one workgroup waits, after its own work, so the others always find a free
+// slot to run in whatever the dispatch order; the wait is bounded (about a
+// second): a timeout writes idx = -1 and leaves the slots as they are (the
+// workspace must then be zeroed again).
+constexpr int kGreedyMaxPolls = 1 << 18;
+
 template <int NR>
 __device__ void greedy_finish(const GreedyArgs& g, const uint64_t (&k)[NR], int M, uint64_t* red, int* flag) {
   const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6, lane = threadIdx.x & 63;
@@ -79,34 +83,54 @@ __device__ void greedy_finish(const GreedyArgs& g, const uint64_t (&k)[NR], int 
     uint64_t v = 0;
     for (int w = 0; w < nw; ++w) v = umax64(v, red[w * NR + threadIdx.x]);
     __hip_atomic_store(g.keys + (int64_t)threadIdx.x * S + wg, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the key is visible device-wide
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int j = wg & 7;
-    const unsigned nj = (unsigned)((S - j + 7) >> 3);   // workgroups with index % 8 == j
-    unsigned* c1 = g.cnt + j * kWsCounterWords;
-    int last = 0;
-    if (__hip_atomic_fetch_add(c1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nj - 1) {
-      __hip_atomic_store(c1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // all nj arrivals are in
-      unsigned* c2 = g.cnt + 8 * kWsCounterWords;
-      const unsigned groups = (unsigned)(S < 8 ? S : 8);
-      if (__hip_atomic_fetch_add(c2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == groups - 1) {
-        __hip_atomic_store(c2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last = 1;
+  if (wg != S - 1) return;
+  uint64_t acc[NR];
+  int poll = 0;
+  for (;; ++poll) {
+    int missing = 0;
+#pragma unroll
+    for (int m = 0; m < NR; ++m) acc[m] = 0;
+    for (int base = 0; base < S; base += 2 * (int)blockDim.x) {
+      uint64_t v[NR][2];
+#pragma unroll
+      for (int m = 0; m < NR; ++m)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int t = base + u * (int)blockDim.x + (int)threadIdx.x;
+          v[m][u] = (m < M && t < S)
+                        ? __hip_atomic_load(g.keys + (int64_t)m * S + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                        : 1;   // outside the array: counts as present
+        }
+#pragma unroll
+      for (int m = 0; m < NR; ++m) {
+        missing |= (v[m][0] == 0) | (v[m][1] == 0);
+        acc[m] = umax64(acc[m], umax64(v[m][0], v[m][1]));
       }
     }
-    *flag = last;
+    __syncthreads();
+    if (threadIdx.x == 0) *flag = 0;
+    __syncthreads();
+    if (missing) *flag = 1;
+    __syncthreads();
+    if (!*flag || poll == kGreedyMaxPolls) break;
+    __builtin_amdgcn_s_sleep(8);
+  }
+  const bool timed_out = *flag != 0;
+#pragma unroll
+  for (int m = 0; m < NR; ++m) {
+    const uint64_t v = wave_max64(acc[m]);
+    if (lane == 0) red[wave * NR + m] = v;
   }
   __syncthreads();
-  if (!*flag) return;
-  for (int m = 0; m < M; ++m) {
+  if ((int)threadIdx.x < M) {
     uint64_t v = 0;
-    for (int t = (int)threadIdx.x; t < S; t += (int)blockDim.x)
-      v = umax64(v, __hip_atomic_load(g.keys + (int64_t)m * S + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    v = block_max64(v, red);
-    if (threadIdx.x == 0) g.idx[m] = greedy_index(v);
+    for (int w = 0; w < nw; ++w) v = umax64(v, red[w * NR + threadIdx.x]);
+    g.idx[threadIdx.x] = timed_out ? -1 : greedy_index(v);
   }
+  if (timed_out) return;
+  for (int i = (int)threadIdx.x; i < M * S; i += (int)blockDim.x)
+    __hip_atomic_store(g.keys + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace fp4
