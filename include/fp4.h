@@ -271,6 +271,21 @@ FP4_API int fp4_lm_head_greedy(int32_t *idx, float *logits, const void *x_bf16, 
                                const void *scales, const float *gscale, int64_t M, int64_t N, int64_t K,
                                void *workspace, size_t workspace_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * fp4_gemv_multi_ws with the workspace taken from a fixed device array of
+ * FP4_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until the
+ * process ends. Same arguments, results and limits as fp4_gemv_multi
+ * otherwise (deterministic, like fp4_gemv_multi_ws). FP4_ERR_WORKSPACE if
+ * the call needs more scratch than the array holds (fp4_workspace_bytes with
+ * FP4_OP_GEMV tells; e.g. 17 K chunks x 4096 output rows of partial sums).
+ * All calls on one GPU share the array: calls that may overlap in time on
+ * one GPU race and must not be made. The first call on a device looks up
+ * the array's device address (hipGetSymbolAddress); no call allocates. */
+#define FP4_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+FP4_API int fp4_gemv_multi_noalloc(const fp4_proj *projs, int nproj, const void *x_bf16, int64_t M, int64_t K,
+                                   void *stream);
+
 /* Which call a workspace size is asked for. */
 typedef enum {
     FP4_OP_GEMV = 0,           /* fp4_gemv_ws, fp4_gemv_multi_ws */

@@ -23,7 +23,8 @@ def test_every_declared_symbol_is_exported():
     assert names == sorted(["fp4_status_string", "fp4_layout_bytes", "fp4_quantize", "fp4_retile", "fp4_gemv",
                             "fp4_gemv_ws", "fp4_gemv_multi", "fp4_gemv_multi_ws", "fp4_gemm_prefill",
                             "fp4_gemm_prefill_ws", "fp4_gemm_prefill_multi", "fp4_gemm_prefill_multi_ws",
-                            "fp4_argmax_rows", "fp4_lm_head_greedy", "fp4_quantize_fp8", "fp4_workspace_bytes"])
+                            "fp4_argmax_rows", "fp4_lm_head_greedy", "fp4_quantize_fp8", "fp4_workspace_bytes",
+                            "fp4_gemv_multi_noalloc"])
     lib = ctypes.CDLL(fp4.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
