@@ -255,14 +255,17 @@ int fp4_argmax_rows(int32_t* idx, const float* y, int64_t M, int64_t N, int64_t 
 }
 
 // The greedy step's plan: the product launch itself ends with the choice
-// (one launch) when a workspace is given, the product is a single launch
-// whose every workgroup covers all rows (vector ALUs, or the matrix cores
-// with one K chunk and at most 16 rows) and its workgroups' keys fit in the
-// workspace header; otherwise the product, then fp4_argmax_rows' kernel.
+// (one launch) when a workspace is given, the product runs on the vector
+// ALUs (its every workgroup covers all rows) and the workgroups' keys fit in
+// the workspace header; otherwise the product, then fp4_argmax_rows' kernel.
+// On the matrix cores the epilogue measured slower than the second launch
+// (MI355X, LM head 151936 x 1024: M = 3 +7.2 against +5.4 us, M = 8 +8.6
+// against +6.6 us; vector ALUs, M = 1: +4.4 against +5.9 us).
 static bool greedy_fused(const fp4::GemvArgs& a) {
-  if (a.M > 16 || !(gemv_on_valu(a) || a.C == 1)) return false;
-  const int64_t S = gemv_on_valu(a) ? fp4::gemv_workgroups(a) : fp4::gemv_mma_workgroups(a);
-  return S > 0 && fp4::greedy_keys_fit(a.M, S);
+  if (!gemv_on_valu(a)) return false;
+  fp4::GemvArgs b = a;
+  b.greedy.idx = reinterpret_cast<int32_t*>(1);   // plan the launch with the epilogue
+  return fp4::greedy_keys_fit(a.M, fp4::gemv_workgroups(b));
 }
 
 static size_t greedy_ws_need(const fp4::GemvArgs& a, int64_t N) {

@@ -76,7 +76,7 @@ struct GemvArgs {
   int32_t wc;         // waves per row group (set by the launcher)
   int32_t gw;         // row groups per workgroup (set by the launcher)
   ProjDesc proj[kMaxProj];
-  GreedyArgs greedy;  // optional epilogue (one projection, M <= 16)
+  GreedyArgs greedy;  // optional epilogue of the vector-ALU kernel (one projection)
 };
 
 hipError_t launch_quantize(const uint16_t* W, int64_t N, int64_t K, bool tiled, uint8_t* packed,
@@ -100,8 +100,7 @@ int64_t gemv_workgroups(const GemvArgs& a);
 hipError_t launch_gemv_mma(const GemvArgs& a, const Workspace& ws, hipStream_t s, int ppw = 0);   // ppw > 0: pairs per workgroup (tuning)
 // Workspace bytes launch_gemv_mma needs for `a` with a workspace (0 when it uses none).
 size_t gemv_mma_ws_bytes(const GemvArgs& a);
-// Workgroups of the (single) pass of launch_gemv_mma for M <= 16 rows.
-int64_t gemv_mma_workgroups(const GemvArgs& a);
+
 // Matrix-core product for prefill-sized M over 1..kMaxProj weight tensors
 // that read the same x (one launch). bn > 0 forces the output tile width
 // (128, 192 or 256; tuning), else it is chosen from the shapes; splits > 0

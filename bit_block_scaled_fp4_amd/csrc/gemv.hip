@@ -275,6 +275,9 @@ static int64_t plan_mt(GemvArgs& a, int gw, int wc) {
   }
   int w = wc > 0 ? wc : (MT == 1 ? (a.C + rounds - 1) / rounds : (a.C + 2) / 3);
   a.wc = std::max(1, std::min(w, kMaxWaves));
+  // the greedy epilogue's last workgroup reads one key per workgroup and row:
+  // 8 waves per workgroup halve them against the default 4
+  if (gw <= 0 && a.greedy.idx) gw = std::max(1, 8 / a.wc);
   if (gw <= 0) {
     // about four waves per workgroup, but never so many row groups per
     // workgroup that the launch has fewer workgroups than CUs

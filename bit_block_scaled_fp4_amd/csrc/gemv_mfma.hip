@@ -54,7 +54,6 @@
 #include <atomic>
 
 #include "fp4_internal.h"
-#include "greedy.h"
 
 namespace fp4 {
 namespace {
@@ -140,18 +139,14 @@ struct MmaArgs {
     int32_t N;
     int32_t pair_begin;
   } proj[kMaxProj];
-  GreedyArgs greedy;   // C == 1, one projection, M <= rows of the kernel
 };
 
 __device__ __forceinline__ int proj_of(const struct MmaArgs& a, int pair);
 
 // Epilogue of one pair: lane (q, n16) holds rows m0 + 4q + i (i < 4) of
-// output column n16 of the pair in v[i]. C == 1: y = gscale * v (and the
-// lane's greedy keys); with a workspace: the unscaled chunk partial; else
-// gscale * v added into y.
-template <bool GREEDY>
-__device__ __forceinline__ void pair_out(const MmaArgs& a, int pair, int c, int q, int n16, const f32x4_t& v,
-                                         uint64_t (&kk)[4]) {
+// output column n16 of the pair in v[i]. C == 1: y = gscale * v; with a
+// workspace: the unscaled chunk partial; else gscale * v added into y.
+__device__ __forceinline__ void pair_out(const MmaArgs& a, int pair, int c, int q, int n16, const f32x4_t& v) {
   if (a.C == 1 || !a.ws) {
     const int p = proj_of(a, pair);
     const int n = 16 * (pair - a.proj[p].pair_begin) + n16;
@@ -162,13 +157,10 @@ __device__ __forceinline__ void pair_out(const MmaArgs& a, int pair, int c, int 
         const int m = a.m0 + 4 * q + i;
         if (m < a.M) {
           float* dst = a.proj[p].y + (int64_t)m * a.proj[p].ldy + n;
-          const float val = gs * v[i];
-          if (a.C == 1) {
-            *dst = val;
-            if (GREEDY) kk[i] = umax64(kk[i], greedy_key(val, n));
-          } else {
-            __hip_atomic_fetch_add(dst, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
+          if (a.C == 1)
+            *dst = gs * v[i];
+          else
+            __hip_atomic_fetch_add(dst, gs * v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
     }
@@ -176,21 +168,6 @@ __device__ __forceinline__ void pair_out(const MmaArgs& a, int pair, int c, int 
     float* dst = a.ws + ((int64_t)c * a.npairs + pair) * 256 + n16 * 16 + 4 * q;
     *reinterpret_cast<f32x4_t*>(dst) = v;
   }
-}
-
-// Greedy epilogue of a launch (a.greedy.idx set): lane (q, n16) holds keys of
-// rows 4q + i in kk[i]. The reduction scratch reuses the activation staging
-// area `xs` (at least 16 * NR * 8 bytes) once every wave is past its last
-// pair.
-template <int NR>
-__device__ __forceinline__ void mma_greedy(const MmaArgs& a, int q, const uint64_t (&kk)[4], uint8_t* xs,
-                                           int* flag) {
-  __syncthreads();
-  uint64_t* red = reinterpret_cast<uint64_t*>(xs);
-  uint64_t k[NR];
-#pragma unroll
-  for (int j = 0; j < NR; ++j) k[j] = (j >> 2) == q ? kk[j & 3] : 0;
-  greedy_finish<NR>(a.greedy, k, a.M, red, flag);
 }
 
 // One pair's codes and scale bytes, as loaded: tile T, load i holds piece
@@ -234,14 +211,10 @@ constexpr int kXsRow8 = 2048 + 16;   // k_gemv_mma8: staged activation row, padd
 constexpr int kZeroWin = 256;        // k_gemv_mma8: zeros read by the A lanes of the other block parity
 
 // At most 8 activation rows (m0 .. m0+7) per launch; grid
-// (ceil(npairs / pairs_per_wg), C), block kWaves waves. GREEDY: the greedy
-// epilogue (C == 1, a.greedy set).
-template <bool GREEDY>
+// (ceil(npairs / pairs_per_wg), C), block kWaves waves.
 __global__ __launch_bounds__(64 * kWaves) void k_gemv_mma8(const MmaArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t xs[8 * kXsRow8 + kZeroWin];
   __shared__ __attribute__((aligned(16))) uint8_t tr[kWaves * kTrBytes];
-  __shared__ int flag;
-  uint64_t kk[4] = {0, 0, 0, 0};
   const int lane = threadIdx.x & 63, q = lane >> 4, n16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = blockIdx.y, K = a.K;
@@ -348,19 +321,15 @@ __global__ __launch_bounds__(64 * kWaves) void k_gemv_mma8(const MmaArgs a) {
     f32x4_t tot;
 #pragma unroll
     for (int i = 0; i < 4; ++i) tot[i] = acc[i] + __shfl_xor(acc[i], 32);
-    if (q < 2) pair_out<GREEDY>(a, pair, c, q, n16, tot, kk);   // rows 4q .. 4q+3
+    if (q < 2) pair_out(a, pair, c, q, n16, tot);   // rows 4q .. 4q+3
     cur = nxt;
   }
-  if (GREEDY) mma_greedy<8>(a, q, kk, xs, &flag);
 }
 
 // 9 to 16 activation rows (m0 .. m0+15) per launch; grid and block as above.
-template <bool GREEDY>
 __global__ __launch_bounds__(64 * kWaves) void k_gemv_mma16(const MmaArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t xs[kMRows * kChunkK * 2];
   __shared__ __attribute__((aligned(16))) uint8_t tr[kWaves * kTrBytes];
-  __shared__ int flag;
-  uint64_t kk[4] = {0, 0, 0, 0};
   const int lane = threadIdx.x & 63, q = lane >> 4, n16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = blockIdx.y, K = a.K;
@@ -433,10 +402,9 @@ __global__ __launch_bounds__(64 * kWaves) void k_gemv_mma16(const MmaArgs a) {
     }
     const f32x4_t acc = acc2[0] + acc2[1];
     // lane (q, n16) holds D[m = 4q + i][n = n16]
-    pair_out<GREEDY>(a, pair, c, q, n16, acc, kk);
+    pair_out(a, pair, c, q, n16, acc);
     cur = nxt;
   }
-  if (GREEDY) mma_greedy<16>(a, q, kk, xs, &flag);
 }
 
 // y[m][n] = gscale * sum over chunks (in order) of the partials. A thread
@@ -483,7 +451,7 @@ int resident_per_cu() {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
   int n = cached[dev].load(std::memory_order_relaxed);
   if (n == 0) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, EIGHT ? k_gemv_mma8<false> : k_gemv_mma16<false>, 64 * kWaves, 0) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, EIGHT ? k_gemv_mma8 : k_gemv_mma16, 64 * kWaves, 0) != hipSuccess) return 0;
     cached[dev].store(n, std::memory_order_relaxed);
   }
   return n;
@@ -541,7 +509,6 @@ MmaArgs mma_args(const GemvArgs& g) {
     pairs += (g.proj[i].N + kPairRows - 1) / kPairRows;
   }
   a.npairs = pairs > (int64_t(1) << 26) ? -1 : (int)pairs;
-  a.greedy = g.greedy;
   return a;
 }
 
@@ -559,13 +526,6 @@ size_t gemv_mma_ws_bytes(const GemvArgs& g) {
   return kWsHeaderBytes + (size_t)a.C * (size_t)a.npairs * 256 * sizeof(float);
 }
 
-int64_t gemv_mma_workgroups(const GemvArgs& g) {
-  const MmaArgs a = mma_args(g);
-  if (a.npairs < 0) return 0;
-  const int ppw = pairs_per_wg_for(a, g.M <= 8);
-  return (a.npairs + ppw - 1) / ppw;
-}
-
 hipError_t launch_gemv_mma(const GemvArgs& g, const Workspace& ws, hipStream_t s, int ppw) {
   MmaArgs a = mma_args(g);
   if (a.npairs < 0) return hipErrorInvalidValue;
@@ -577,7 +537,6 @@ hipError_t launch_gemv_mma(const GemvArgs& g, const Workspace& ws, hipStream_t s
     const bool eight = g.M - m0 <= 8;
     a.pairs_per_wg = ppw > 0 ? ppw : pairs_per_wg_for(a, eight);
     const int64_t wgx = (pairs + a.pairs_per_wg - 1) / a.pairs_per_wg;
-    a.greedy.S = (int32_t)wgx;
     const int rows = std::min(kMRows, g.M - m0);
     if (a.C > 1 && !use_ws) {
       int64_t most = 0;
@@ -586,14 +545,10 @@ hipError_t launch_gemv_mma(const GemvArgs& g, const Workspace& ws, hipStream_t s
       hipLaunchKernelGGL(k_zero_rows, dim3((unsigned)blocks, (unsigned)a.nproj), dim3(256), 0, s, a, rows);
     }
     const dim3 grid((unsigned)wgx, (unsigned)a.C), block(64 * kWaves);
-    if (eight && a.greedy.idx)
-      hipLaunchKernelGGL(k_gemv_mma8<true>, grid, block, 0, s, a);
-    else if (eight)
-      hipLaunchKernelGGL(k_gemv_mma8<false>, grid, block, 0, s, a);
-    else if (a.greedy.idx)
-      hipLaunchKernelGGL(k_gemv_mma16<true>, grid, block, 0, s, a);
+    if (eight)
+      hipLaunchKernelGGL(k_gemv_mma8, grid, block, 0, s, a);
     else
-      hipLaunchKernelGGL(k_gemv_mma16<false>, grid, block, 0, s, a);
+      hipLaunchKernelGGL(k_gemv_mma16, grid, block, 0, s, a);
     if (use_ws) {
       const int64_t n = pairs * 16 * ((rows + 3) / 4);
       hipLaunchKernelGGL(k_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);

@@ -85,28 +85,33 @@ __device__ void greedy_finish(const GreedyArgs& g, const uint64_t (&k)[NR], int 
     __hip_atomic_store(g.keys + (int64_t)threadIdx.x * S + wg, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (wg != S - 1) return;
+  // J keys per row and thread in one round of loads (NR * J = 16: the
+  // round's loads stay within the product's register budget)
+  constexpr int J = NR >= 16 ? 1 : 16 / NR;
   uint64_t acc[NR];
   int poll = 0;
   for (;; ++poll) {
     int missing = 0;
 #pragma unroll
     for (int m = 0; m < NR; ++m) acc[m] = 0;
-    for (int base = 0; base < S; base += 2 * (int)blockDim.x) {
-      uint64_t v[NR][2];
+    for (int base = 0; base < S; base += J * (int)blockDim.x) {
+      uint64_t v[NR][J];
 #pragma unroll
       for (int m = 0; m < NR; ++m)
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < J; ++u) {
           const int t = base + u * (int)blockDim.x + (int)threadIdx.x;
           v[m][u] = (m < M && t < S)
                         ? __hip_atomic_load(g.keys + (int64_t)m * S + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                         : 1;   // outside the array: counts as present
         }
 #pragma unroll
-      for (int m = 0; m < NR; ++m) {
-        missing |= (v[m][0] == 0) | (v[m][1] == 0);
-        acc[m] = umax64(acc[m], umax64(v[m][0], v[m][1]));
-      }
+      for (int m = 0; m < NR; ++m)
+#pragma unroll
+        for (int u = 0; u < J; ++u) {
+          missing |= v[m][u] == 0;
+          acc[m] = umax64(acc[m], v[m][u]);
+        }
     }
     __syncthreads();
     if (threadIdx.x == 0) *flag = 0;

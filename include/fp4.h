@@ -260,13 +260,16 @@ FP4_API int fp4_argmax_rows(int32_t *idx, const float *y, int64_t M, int64_t N, 
 /* The greedy decode step's last product and choice: logits [M][N] (fp32,
  * device, overwritten) = fp4_gemv(x, W) for the TILED vocabulary matrix W
  * [N][K], and idx [M] (int32, device) = the greedy choice of each row of
- * the logits, as fp4_argmax_rows takes it. With a workspace, and when the
- * product is one launch whose workgroups each cover all M rows (M <= 4,
- * or M <= 16 with K <= 1024), the choice is that launch's epilogue: every
- * workgroup leaves its largest (value, index) per row in the workspace and
- * the last one to finish picks the index (one launch in all). Otherwise
- * the product, then fp4_argmax_rows with the same workspace. All arguments
- * are checked before the first launch. */
+ * the logits, as fp4_argmax_rows takes it. With a workspace, when the
+ * product runs on the vector ALUs (see fp4_gemv: up to 4 rows), the choice
+ * is that launch's epilogue: every workgroup leaves its largest (value,
+ * index) per row in the workspace header and the workgroup with the last
+ * index waits for the others' keys (bounded; idx = -1 if they never came,
+ * after which the workspace must be zeroed again), picks the index and
+ * clears the keys: one launch in all. Otherwise the product, then
+ * fp4_argmax_rows with the same workspace (on the matrix cores that second
+ * launch measured faster than the epilogue). All arguments are checked
+ * before the first launch. */
 FP4_API int fp4_lm_head_greedy(int32_t *idx, float *logits, const void *x_bf16, const void *packed,
                                const void *scales, const float *gscale, int64_t M, int64_t N, int64_t K,
                                void *workspace, size_t workspace_bytes, void *stream);
