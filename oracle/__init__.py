@@ -70,6 +70,14 @@ def _L():
         lib.orc_e4m3_encode_n.restype = None
         lib.orc_e2m1_encode_n.argtypes = [P, I64, P]
         lib.orc_e2m1_encode_n.restype = None
+        lib.orc_gemv_f64.argtypes = [P, I64, P, P, ctypes.c_float, I64, I64, P, P, ctypes.c_int]
+        lib.orc_gemv_f64.restype = None
+        lib.orc_silu.argtypes = [ctypes.c_double]
+        lib.orc_silu.restype = ctypes.c_double
+        lib.orc_swiglu.argtypes = [P, P, I64, P]
+        lib.orc_swiglu.restype = None
+        lib.orc_rmsnorm.argtypes = [P, P, I64, I64, ctypes.c_double, P]
+        lib.orc_rmsnorm.restype = None
         for f in (lib.orc_argmax_rows_f64, lib.orc_argmax_rows_f32):
             f.argtypes = [P, I64, I64, I64, P]
             f.restype = None
@@ -174,6 +182,46 @@ def gemv(x_bits: np.ndarray, packed: np.ndarray, scales: np.ndarray, gscale, thr
     _L().orc_gemv(px, M, pp, ps, float(np.float32(gscale)), N, K, y.ctypes.data,
                   l1.ctypes.data if with_l1 else None, int(threads))
     return (y, l1) if with_l1 else y
+
+
+def gemv_f64(x: np.ndarray, packed: np.ndarray, scales: np.ndarray, gscale, threads: int = 1):
+    """The product for fp64 activations x [M][K] (e.g. RMS-normalised rows):
+    (y [M][N], l1 [M][N]) as gemv()."""
+    x, px = _c(np.atleast_2d(x), np.float64)
+    packed, pp = _c(packed, np.uint8)
+    scales, ps = _c(scales, np.uint8)
+    M, K = x.shape
+    N = packed.shape[0]
+    assert packed.shape[1] * 2 == K and scales.shape == (N, K // 16)
+    y = np.empty((M, N), dtype=np.float64)
+    l1 = np.empty((M, N), dtype=np.float64)
+    _L().orc_gemv_f64(px, M, pp, ps, float(np.float32(gscale)), N, K, y.ctypes.data, l1.ctypes.data, int(threads))
+    return y, l1
+
+
+def silu(z: float) -> float:
+    return _L().orc_silu(float(z))
+
+
+def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """h = silu(g) * u elementwise, fp64 (g: gate product, u: up product)."""
+    g, pg = _c(g, np.float64)
+    u, pu = _c(u, np.float64)
+    assert g.shape == u.shape
+    h = np.empty(g.shape, dtype=np.float64)
+    _L().orc_swiglu(pg, pu, g.size, h.ctypes.data)
+    return h
+
+
+def rmsnorm(x_bits: np.ndarray, gain_bits: np.ndarray, eps: float) -> np.ndarray:
+    """RMS-normalised rows of bf16 x [M][K] times the bf16 gain [K], fp64."""
+    x, px = _c(np.atleast_2d(x_bits), np.uint16)
+    g, pg = _c(gain_bits, np.uint16)
+    M, K = x.shape
+    assert g.shape == (K,)
+    out = np.empty((M, K), dtype=np.float64)
+    _L().orc_rmsnorm(px, pg, M, K, float(eps), out.ctypes.data)
+    return out
 
 
 def tile(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:

@@ -260,7 +260,8 @@ void orc_dequant(const uint8_t *packed, const uint8_t *scales, float gscale, int
 /* --------------------------------------------------------------- product */
 
 typedef struct {
-    const uint16_t *x;
+    const uint16_t *x;        /* bf16 activations, or NULL ... */
+    const double *xd;         /* ... fp64 activations */
     const uint8_t *packed, *scales;
     double gscale;
     int64_t M, N, K, n0, n1;
@@ -274,7 +275,8 @@ static void *gemv_rows(void *arg) {
         const uint8_t *q = j->packed + n * (K / 2);
         const uint8_t *sc = j->scales + n * (K / 16);
         for (int64_t m = 0; m < j->M; ++m) {
-            const uint16_t *xm = j->x + m * K;
+            const uint16_t *xm = j->x ? j->x + m * K : NULL;
+            const double *xdm = j->xd ? j->xd + m * K : NULL;
             double y = 0.0, l1 = 0.0;
             for (int64_t b = 0; b < K / 16; ++b) {
                 double s = E4M3_TAB[sc[b]];
@@ -283,7 +285,7 @@ static void *gemv_rows(void *arg) {
                     int64_t k = b * 16 + i;
                     uint8_t byte = q[k / 2];
                     double e = E2M1_TAB[(k % 2 == 0) ? (byte & 15) : (byte >> 4)];
-                    double xv = (double)bf16_to_f32(xm[k]);
+                    double xv = xm ? (double)bf16_to_f32(xm[k]) : xdm[k];
                     inner += e * xv;
                     l1 += fabs(e * s * j->gscale * xv);
                 }
@@ -300,8 +302,9 @@ static void *gemv_rows(void *arg) {
  * in fp64, and l1[m][n] = sum_k |dequant(W)[n][k] * x[m][k]| (the scale of
  * the error bound). x is bf16 bits [M][K]; packed/scales canonical layout.
  * Rows n are split over `nthreads` threads; each sum runs in k order. */
-void orc_gemv(const uint16_t *x, int64_t M, const uint8_t *packed, const uint8_t *scales,
-              float gscale, int64_t N, int64_t K, double *y, double *l1, int nthreads) {
+static void gemv_any(const uint16_t *x, const double *xd, int64_t M, const uint8_t *packed,
+                     const uint8_t *scales, float gscale, int64_t N, int64_t K, double *y, double *l1,
+                     int nthreads) {
     tables();
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 256) nthreads = 256;
@@ -309,13 +312,59 @@ void orc_gemv(const uint16_t *x, int64_t M, const uint8_t *packed, const uint8_t
     pthread_t th[256];
     gemv_job jobs[256];
     for (int t = 0; t < nthreads; ++t) {
-        gemv_job j = {x, packed, scales, (double)gscale, M, N, K, N * t / nthreads,
+        gemv_job j = {x, xd, packed, scales, (double)gscale, M, N, K, N * t / nthreads,
                       N * (t + 1) / nthreads, y, l1};
         jobs[t] = j;
     }
     for (int t = 1; t < nthreads; ++t) pthread_create(&th[t], 0, gemv_rows, &jobs[t]);
     gemv_rows(&jobs[0]);
     for (int t = 1; t < nthreads; ++t) pthread_join(th[t], 0);
+}
+
+void orc_gemv(const uint16_t *x, int64_t M, const uint8_t *packed, const uint8_t *scales,
+              float gscale, int64_t N, int64_t K, double *y, double *l1, int nthreads) {
+    gemv_any(x, NULL, M, packed, scales, gscale, N, K, y, l1, nthreads);
+}
+
+/* The same product for fp64 activations x [M][K] (a normalised input, kept
+ * exact): y and l1 as orc_gemv. */
+void orc_gemv_f64(const double *x, int64_t M, const uint8_t *packed, const uint8_t *scales,
+                  float gscale, int64_t N, int64_t K, double *y, double *l1, int nthreads) {
+    gemv_any(NULL, x, M, packed, scales, gscale, N, K, y, l1, nthreads);
+}
+
+/* ----------------------------------------------------- fused neighbours */
+
+/* The steps on either side of the product in a decode layer. Each layer
+ * runs attention, then the MLP, each on the residual stream (page "1. The
+ * big picture", step 3), for the Qwen3 family the pages use as their
+ * example. Written out from these readings (the pages give no formulas):
+ *   - the MLP is gated: h = silu(gate(x)) * up(x), then down(h), with
+ *     silu(z) = z * sigmoid(z) = z / (1 + e^-z);
+ *   - attention's Q, K and V products read the RMS-normalised stream:
+ *     x_hat[k] = x[k] / sqrt(mean over k of x[k]^2 + eps) * gain[k].
+ * Both in fp64 here. */
+
+double orc_silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* h[i] = silu(g[i]) * u[i] for n elements (g: the gate product, u: up). */
+void orc_swiglu(const double *g, const double *u, int64_t n, double *h) {
+    for (int64_t i = 0; i < n; ++i) h[i] = orc_silu(g[i]) * u[i];
+}
+
+/* out[m][k] = x[m][k] / sqrt(mean_k x[m][k]^2 + eps) * gain[k]; x [M][K]
+ * and gain [K] are bf16 bits. */
+void orc_rmsnorm(const uint16_t *x, const uint16_t *gain, int64_t M, int64_t K, double eps, double *out) {
+    for (int64_t m = 0; m < M; ++m) {
+        double ss = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double v = (double)bf16_to_f32(x[m * K + k]);
+            ss += v * v;
+        }
+        double r = 1.0 / sqrt(ss / (double)K + eps);
+        for (int64_t k = 0; k < K; ++k)
+            out[m * K + k] = (double)bf16_to_f32(x[m * K + k]) * r * (double)bf16_to_f32(gain[k]);
+    }
 }
 
 /* --------------------------------------------------------- device layout */

@@ -19,8 +19,8 @@ PINS = os.path.join(ROOT, "tests", "test_oracle_pins.py")
 MUTANTS = [
     ("product drops the block scale", "y += s * inner;", "y += inner;"),
     ("product subtracts", "inner += e * xv;", "inner -= e * xv;"),
-    ("product reads activation row 0 for every row", "const uint16_t *xm = j->x + m * K;",
-     "const uint16_t *xm = j->x;"),
+    ("product reads activation row 0 for every row", "const uint16_t *xm = j->x ? j->x + m * K : NULL;",
+     "const uint16_t *xm = j->x ? j->x : NULL;"),
     ("product decodes the odd k from the low nibble",
      "double e = E2M1_TAB[(k % 2 == 0) ? (byte & 15) : (byte >> 4)];",
      "double e = E2M1_TAB[(k % 2 == 0) ? (byte >> 4) : (byte & 15)];"),
@@ -46,6 +46,17 @@ MUTANTS = [
     ("dequantiser forgets the tensor scale",
      "out[n * K + k] = E2M1_TAB[q] * E4M3_TAB[scales[n * (K / 16) + k / 16]] * (double)gscale;",
      "out[n * K + k] = E2M1_TAB[q] * E4M3_TAB[scales[n * (K / 16) + k / 16]];"),
+    ("silu uses e^z instead of e^-z", "return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
+    ("swiglu gates the gate product with silu of up", "h[i] = orc_silu(g[i]) * u[i];",
+     "h[i] = orc_silu(u[i]) * g[i];"),
+    ("rmsnorm sums instead of averaging", "double r = 1.0 / sqrt(ss / (double)K + eps);",
+     "double r = 1.0 / sqrt(ss + eps);"),
+    ("rmsnorm drops eps", "double r = 1.0 / sqrt(ss / (double)K + eps);", "double r = 1.0 / sqrt(ss / (double)K);"),
+    ("rmsnorm forgets the square root", "double r = 1.0 / sqrt(ss / (double)K + eps);",
+     "double r = 1.0 / (ss / (double)K + eps);"),
+    ("rmsnorm drops the gain", "* r * (double)bf16_to_f32(gain[k]);", "* r;"),
+    ("fp64-activation product reads activation row 0", "const double *xdm = j->xd ? j->xd + m * K : NULL;",
+     "const double *xdm = j->xd ? j->xd : NULL;"),
 ]
 
 

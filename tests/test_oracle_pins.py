@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import oracle
-from workloads import bf16_to_float32, float32_to_bf16_bits, tensor_bits, workload, x_bits
+from workloads import bf16_tensor, bf16_to_float32, float32_to_bf16_bits, tensor_bits, workload, x_bits
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -381,3 +381,86 @@ def test_quantize_f32_entry_equals_bf16_entry():
     bits = tensor_bits(workload("gemv_1024").tensor("w"))[:64]
     a, b = oracle.quantize_f32(bf16_to_float32(bits)), oracle.quantize(bits)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[2] == b[2]
+
+
+# ------------------------------------------- fused neighbours: SwiGLU, RMSNorm
+def test_silu_closed_forms_and_identities():
+    """silu(z) = z * sigmoid(z). At z = ln k the sigmoid is exactly k/(k+1);
+    the sigmoid's symmetry gives silu(z) - silu(-z) = z; the minimum of silu
+    is -W0(1/e) (Lambert W), taken at z = -1 - W0(1/e); silu(z) -> z for
+    large z and -> 0 for very negative z."""
+    for k in (2.0, 3.0, 7.0, 0.5, 100.0):
+        z = np.log(k)
+        assert oracle.silu(z) == pytest.approx(z * k / (k + 1), rel=1e-14)
+    zs = np.linspace(-30, 30, 6001)
+    h = oracle.swiglu(zs, np.ones_like(zs))                      # silu itself at u = 1
+    assert np.allclose(h - oracle.swiglu(-zs, np.ones_like(zs)), zs, rtol=1e-14, atol=1e-14)
+    from scipy.special import lambertw
+    w = float(lambertw(np.exp(-1.0)).real)
+    grid = np.linspace(-3.0, 1.0, 400001)
+    v = oracle.swiglu(grid, np.ones_like(grid))
+    assert v.min() == pytest.approx(-w, abs=1e-10)
+    assert grid[v.argmin()] == pytest.approx(-1.0 - w, abs=2e-5)
+    assert oracle.silu(0.0) == 0.0
+    assert oracle.silu(60.0) == pytest.approx(60.0, rel=1e-15)
+    assert 0.0 >= oracle.silu(-60.0) > -1e-23
+
+
+def test_swiglu_gates_the_up_product_with_silu_of_the_gate():
+    """h(g, u) is silu(g) at u = 1 (pinned above), linear in u, zero for a
+    zero gate whatever u is, and not symmetric in its operands."""
+    rng = np.random.default_rng(21)
+    g, u = rng.normal(0, 3, 1000), rng.normal(0, 3, 1000)
+    h = oracle.swiglu(g, u)
+    assert np.allclose(oracle.swiglu(g, 2 * u), 2 * h, rtol=1e-15)
+    assert np.allclose(h, oracle.swiglu(g, np.ones_like(g)) * u, rtol=1e-15)
+    assert np.all(oracle.swiglu(np.zeros_like(u), u) == 0)
+    assert not np.allclose(h, oracle.swiglu(u, g))
+
+
+def test_rmsnorm_properties_and_a_closed_form():
+    """Rows come out with unit mean square (gain 1, eps 0), point the same way
+    as the input, do not change when the row is scaled by a power of two or
+    repeated (a mean, not a sum), and the gain multiplies each column. With
+    eps = 1e-6 a row of +-1 maps to +-1/sqrt(1 + 1e-6); a zero row stays zero."""
+    x = bf16_tensor((6, 96), 31, 1.5)
+    ones = float32_to_bf16_bits(np.ones(96, np.float32))
+    out = oracle.rmsnorm(x, ones, 0.0)
+    assert np.allclose((out ** 2).mean(axis=1), 1.0, rtol=1e-14)
+    xf = bf16_to_float32(x).astype(np.float64)
+    nz = xf != 0
+    ratio = np.where(nz, out / np.where(nz, xf, 1.0), np.nan)
+    for m in range(6):
+        r = ratio[m][nz[m]]
+        assert np.all(r > 0) and np.allclose(r, r[0], rtol=1e-15)
+    assert np.array_equal(oracle.rmsnorm(float32_to_bf16_bits((xf * 4).astype(np.float32)), ones, 0.0), out)
+    twice = np.concatenate([x, x], axis=1)
+    ones2 = float32_to_bf16_bits(np.ones(192, np.float32))
+    assert np.allclose(oracle.rmsnorm(twice, ones2, 0.0)[:, :96], out, rtol=1e-15)
+    gain = bf16_tensor((96,), 32, 1.0)
+    assert np.allclose(oracle.rmsnorm(x, gain, 0.0), out * bf16_to_float32(gain)[None, :], rtol=1e-15)
+    pm = float32_to_bf16_bits(np.array([[1, -1, 1, -1, -1, 1, 1, 1]], np.float32))
+    ones8 = float32_to_bf16_bits(np.ones(8, np.float32))
+    expect = 0.99999950000037499969        # 1 / sqrt(1.000001)
+    assert np.allclose(oracle.rmsnorm(pm, ones8, 1e-6)[0], expect * bf16_to_float32(pm)[0].astype(np.float64),
+                       rtol=1e-15, atol=0)
+    z = np.zeros((2, 32), np.uint16)
+    assert np.all(oracle.rmsnorm(z, float32_to_bf16_bits(np.ones(32, np.float32)), 1e-6) == 0)
+
+
+def test_gemv_f64_equals_bf16_entry_and_numpy():
+    """The fp64-activation product equals the bf16 one on bf16-valued rows
+    (same sums in the same order) and numpy's float64 matmul of the
+    dequantised weights on arbitrary fp64 rows."""
+    rng = np.random.default_rng(33)
+    W = float32_to_bf16_bits(rng.normal(0, 0.05, (40, 1056)).astype(np.float32))
+    p, s, g = oracle.quantize(W)
+    xb = float32_to_bf16_bits(rng.normal(0, 1, (3, 1056)).astype(np.float32))
+    y1, l1 = oracle.gemv(xb, p, s, g)
+    y2, l2 = oracle.gemv_f64(bf16_to_float32(xb).astype(np.float64), p, s, g)
+    assert np.array_equal(y1, y2) and np.array_equal(l1, l2)
+    xd = rng.normal(0, 1, (4, 1056))
+    D = dequant_from_bits(p, s, g)
+    y3, l3 = oracle.gemv_f64(xd, p, s, g)
+    assert np.allclose(y3, xd @ D.T, rtol=1e-12, atol=1e-14 * np.abs(D).sum())
+    assert np.allclose(l3, np.abs(xd) @ np.abs(D).T, rtol=1e-12)
