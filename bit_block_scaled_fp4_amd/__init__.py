@@ -26,7 +26,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "fp4.h")
 
 ROWMAJOR, TILED = 0, 1
 MAX_PROJ = 8
-OP_GEMV, OP_GEMM_PREFILL, OP_ARGMAX_ROWS, OP_LM_HEAD_GREEDY = 0, 1, 2, 3
+OP_GEMV, OP_GEMM_PREFILL, OP_ARGMAX_ROWS, OP_LM_HEAD_GREEDY, OP_GEMV_RMSNORM, OP_GEMV_SWIGLU = 0, 1, 2, 3, 4, 5
 _LAYOUTS = {"rowmajor": ROWMAJOR, "tiled": TILED, ROWMAJOR: ROWMAJOR, TILED: TILED}
 
 if not os.path.exists(LIB_PATH):
@@ -59,9 +59,12 @@ _lib.fp4_gemm_prefill_multi_ws.argtypes = [ctypes.POINTER(_Proj), _I, _P, _I64, 
 _lib.fp4_argmax_rows.argtypes = [_P, _P, _I64, _I64, _I64, _P, _SZ, _P]
 _lib.fp4_lm_head_greedy.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P]
 _lib.fp4_workspace_bytes.argtypes = [_I, _I64, _I64, ctypes.POINTER(_I64), _I, ctypes.POINTER(_SZ)]
+_lib.fp4_gemv_multi_rmsnorm.argtypes = [ctypes.POINTER(_Proj), _I, _P, _P, ctypes.c_float, _I64, _I64, _P, _SZ, _P]
+_lib.fp4_gemv_swiglu.argtypes = [_P, _I64, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P]
 for _f in ("fp4_layout_bytes", "fp4_quantize", "fp4_quantize_fp8", "fp4_retile", "fp4_gemv", "fp4_gemv_ws",
            "fp4_gemv_multi", "fp4_gemv_multi_ws", "fp4_gemm_prefill", "fp4_gemm_prefill_ws", "fp4_gemm_prefill_multi",
-           "fp4_gemm_prefill_multi_ws", "fp4_argmax_rows", "fp4_lm_head_greedy", "fp4_workspace_bytes"):
+           "fp4_gemm_prefill_multi_ws", "fp4_argmax_rows", "fp4_lm_head_greedy", "fp4_workspace_bytes",
+           "fp4_gemv_multi_rmsnorm", "fp4_gemv_swiglu"):
     getattr(_lib, _f).restype = _I
 
 
@@ -260,6 +263,35 @@ def gemv_multi(x: torch.Tensor, weights: Sequence[NVFP4Weight], outs: Sequence[t
                "fp4_gemv_multi_ws")
 
 
+def gemv_multi_rmsnorm(x: torch.Tensor, gain: torch.Tensor, eps: float, weights: Sequence[NVFP4Weight],
+                       outs: Sequence[torch.Tensor], ldys: Optional[Sequence[int]] = None,
+                       workspace: Optional[torch.Tensor] = None) -> None:
+    """fp4_gemv_multi_rmsnorm: outs[i] = RMSNorm(x; gain, eps) @ dequant(weights[i])^T
+    (gain bf16 [K]); needs a workspace beyond 2 rows (workspace_bytes(OP_GEMV_RMSNORM, ...))."""
+    x, M, K = _x2d(x)
+    if gain.numel() != K:
+        raise ValueError("gain must have K=%d elements" % K)
+    arr, n = _projs(M, K, weights, outs, ldys)
+    _check(_lib.fp4_gemv_multi_rmsnorm(arr, n, _dev(x, "x", torch.bfloat16), _dev(gain, "gain", torch.bfloat16),
+                                       float(eps), M, K, *_ws(workspace), _stream(x.device)), "fp4_gemv_multi_rmsnorm")
+
+
+def gemv_swiglu(x: torch.Tensor, gate: NVFP4Weight, up: NVFP4Weight, out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp4_gemv_swiglu: h = bf16(silu(x @ dequant(gate)^T) * (x @ dequant(up)^T)), bf16 [M][N]."""
+    x, M, K = _x2d(x)
+    if gate.K != K or up.K != K or gate.N != up.N:
+        raise ValueError("gate and up must be [N][K] with the K of x")
+    _tiled(gate)
+    _tiled(up)
+    out = _out(out, (M, gate.N), torch.bfloat16, x.device, "out")
+    _check(_lib.fp4_gemv_swiglu(_dev(out, "h", torch.bfloat16), gate.N, _dev(x, "x", torch.bfloat16),
+                                _dev(gate.packed, "gate"), _dev(gate.gscale, "gate gscale", torch.float32),
+                                _dev(up.packed, "up"), _dev(up.gscale, "up gscale", torch.float32), M, gate.N, K,
+                                *_ws(workspace), _stream(x.device)), "fp4_gemv_swiglu")
+    return out
+
+
 def gemm_prefill_multi(x: torch.Tensor, weights: Sequence[NVFP4Weight], outs: Sequence[torch.Tensor],
                        ldys: Optional[Sequence[int]] = None, workspace: Optional[torch.Tensor] = None) -> None:
     """fp4_gemm_prefill_multi (fp4_gemm_prefill_multi_ws with a workspace): one
@@ -329,6 +361,7 @@ def raw():
 
 
 __all__ = ["quantize", "quantize_fp8", "retile", "gemv", "gemv_multi", "gemm_prefill", "gemm_prefill_multi",
-           "argmax_rows", "lm_head_greedy", "layout_bytes", "workspace_bytes", "new_workspace", "NVFP4Weight",
-           "OP_GEMV", "OP_GEMM_PREFILL", "OP_ARGMAX_ROWS", "OP_LM_HEAD_GREEDY",
+           "argmax_rows", "lm_head_greedy", "gemv_multi_rmsnorm", "gemv_swiglu", "layout_bytes", "workspace_bytes",
+           "new_workspace", "NVFP4Weight", "OP_GEMV", "OP_GEMM_PREFILL", "OP_ARGMAX_ROWS", "OP_LM_HEAD_GREEDY",
+           "OP_GEMV_RMSNORM", "OP_GEMV_SWIGLU",
            "Fp4Error", "raw", "ROWMAJOR", "TILED", "LIB_PATH", "HEADER_PATH"]

@@ -144,8 +144,17 @@ static int gemv_args(const fp4_proj* projs, int nproj, const void* x_bf16, int64
   return FP4_OK;
 }
 
+static size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+// Bytes of partial sums a product with these arguments keeps in scratch (0:
+// none; the vector ALUs and one K chunk keep none).
+static size_t gemv_partials(const fp4::GemvArgs& a) { return gemv_on_valu(a) ? 0 : fp4::gemv_mma_partial_bytes(a); }
+
 // Workspace bytes a product with these arguments uses (0: none).
-static size_t gemv_ws_need(const fp4::GemvArgs& a) { return gemv_on_valu(a) ? 0 : fp4::gemv_mma_ws_bytes(a); }
+static size_t gemv_ws_need(const fp4::GemvArgs& a) {
+  const size_t p = gemv_partials(a);
+  return p ? fp4::kWsHeaderBytes + p : 0;
+}
 
 // A caller's workspace: NULL means none; otherwise 256-byte aligned and at
 // least `need` bytes.
@@ -159,10 +168,13 @@ static int take_ws(void* workspace, size_t bytes, size_t need, fp4::Workspace& w
   return FP4_OK;
 }
 
-static int gemv_run(const fp4::GemvArgs& a, const fp4::Workspace& ws, hipStream_t s) {
+// The product; `scratch` (may be null) holds its partial sums.
+static int gemv_run(const fp4::GemvArgs& a, uint8_t* scratch, hipStream_t s) {
   if (gemv_on_valu(a)) return hip_status(fp4::launch_gemv(a, s));
-  return hip_status(fp4::launch_gemv_mma(a, ws, s));
+  return hip_status(fp4::launch_gemv_mma(a, reinterpret_cast<float*>(scratch), s));
 }
+
+static uint8_t* scratch_of(const fp4::Workspace& ws) { return ws.valid() ? ws.scratch() : nullptr; }
 
 int fp4_gemv_multi_ws(const fp4_proj* projs, int nproj, const void* x_bf16, int64_t M, int64_t K, void* workspace,
                       size_t workspace_bytes, void* stream) {
@@ -170,7 +182,7 @@ int fp4_gemv_multi_ws(const fp4_proj* projs, int nproj, const void* x_bf16, int6
   if (int st = gemv_args(projs, nproj, x_bf16, M, K, a)) return st;
   fp4::Workspace ws;
   if (int st = take_ws(workspace, workspace_bytes, gemv_ws_need(a), ws)) return st;
-  return gemv_run(a, ws, static_cast<hipStream_t>(stream));
+  return gemv_run(a, scratch_of(ws), static_cast<hipStream_t>(stream));
 }
 
 int fp4_gemv_multi(const fp4_proj* projs, int nproj, const void* x_bf16, int64_t M, int64_t K, void* stream) {
@@ -263,9 +275,7 @@ int fp4_argmax_rows(int32_t* idx, const float* y, int64_t M, int64_t N, int64_t 
 // against +6.6 us; vector ALUs, M = 1: +4.4 against +5.9 us).
 static bool greedy_fused(const fp4::GemvArgs& a) {
   if (!gemv_on_valu(a)) return false;
-  fp4::GemvArgs b = a;
-  b.greedy.idx = reinterpret_cast<int32_t*>(1);   // plan the launch with the epilogue
-  return fp4::greedy_keys_fit(a.M, fp4::gemv_workgroups(b));
+  return fp4::greedy_keys_fit(a.M, fp4::gemv_workgroups(a));
 }
 
 static size_t greedy_ws_need(const fp4::GemvArgs& a, int64_t N) {
@@ -298,10 +308,93 @@ int fp4_lm_head_greedy(int32_t* idx, float* logits, const void* x_bf16, const vo
   if (ws.valid() && greedy_fused(a)) {
     a.greedy.idx = idx;
     a.greedy.keys = reinterpret_cast<uint64_t*>(ws.p);   // the header: zero between calls
-    return gemv_run(a, ws, s);
+    return gemv_run(a, scratch_of(ws), s);
   }
-  if (int st = gemv_run(a, ws, s)) return st;
+  if (int st = gemv_run(a, scratch_of(ws), s)) return st;
   return hip_status(fp4::launch_argmax(idx, logits, M, N, N, ws, s));
+}
+
+// RMS normalisation before the products: inside the vector-ALU launch for
+// up to 2 rows (3-4 rows would spill there), else a norm kernel writing the
+// normalised rows into the workspace, then the product on them.
+static bool rms_fused(const fp4::GemvArgs& a) { return gemv_on_valu(a) && a.M <= 2; }
+
+static size_t rms_ws_need(const fp4::GemvArgs& a) {
+  if (rms_fused(a)) return 0;
+  return fp4::kWsHeaderBytes + align256((size_t)a.M * (size_t)a.K * 2) + gemv_partials(a);
+}
+
+static int rms_check(const void* gain_bf16, float eps) {
+  if (!gain_bf16) return FP4_ERR_NULL;
+  if (!aligned(gain_bf16, 16)) return FP4_ERR_ALIGN;
+  if (!(eps >= 0.0f && eps <= 3.0e38f)) return FP4_ERR_SHAPE;   // finite, not negative, not NaN
+  return FP4_OK;
+}
+
+int fp4_gemv_multi_rmsnorm(const fp4_proj* projs, int nproj, const void* x_bf16, const void* gain_bf16, float eps,
+                           int64_t M, int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
+  fp4::GemvArgs a;
+  if (int st = gemv_args(projs, nproj, x_bf16, M, K, a)) return st;
+  if (int st = rms_check(gain_bf16, eps)) return st;
+  const size_t need = rms_ws_need(a);
+  fp4::Workspace ws;
+  if (int st = take_ws(workspace, workspace_bytes, need, ws)) return st;
+  if (need > 0 && !ws.valid()) return FP4_ERR_WORKSPACE;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (rms_fused(a)) {
+    a.gain = static_cast<const uint16_t*>(gain_bf16);
+    a.eps = eps;
+    return gemv_run(a, nullptr, s);
+  }
+  uint16_t* xn = reinterpret_cast<uint16_t*>(ws.scratch());
+  if (int st = hip_status(fp4::launch_rmsnorm(a.x, static_cast<const uint16_t*>(gain_bf16), eps, M, K, xn, s))) return st;
+  a.x = xn;
+  return gemv_run(a, ws.scratch() + align256((size_t)M * (size_t)K * 2), s);
+}
+
+// The gated MLP's first half: one vector-ALU launch computing gate and up and
+// writing h when the pair runs there, else the pair's product into fp32
+// buffers in the workspace, then an elementwise kernel.
+static int swiglu_args(void* h_bf16, int64_t ldh, const void* x_bf16, const void* gate_packed, const float* gate_gscale,
+                       const void* up_packed, const float* up_gscale, int64_t M, int64_t N, int64_t K,
+                       fp4::GemvArgs& a) {
+  if (!h_bf16 || !gate_packed || !up_packed || !gate_gscale || !up_gscale) return FP4_ERR_NULL;
+  if (ldh < N || M < 1 || M > kMaxM || M * ldh > kMaxElems) return FP4_ERR_SHAPE;
+  if (!aligned(h_bf16, 2)) return FP4_ERR_ALIGN;
+  static float stand_in __attribute__((aligned(16)));   // validated as y, never written
+  fp4_proj p[2] = {{gate_packed, nullptr, gate_gscale, N, &stand_in, N}, {up_packed, nullptr, up_gscale, N, &stand_in, N}};
+  if (int st = gemv_args(p, 2, x_bf16, M, K, a)) return st;
+  a.h = static_cast<uint16_t*>(h_bf16);
+  a.ldh = ldh;
+  return FP4_OK;
+}
+
+static size_t swiglu_ws_need(const fp4::GemvArgs& a) {
+  if (gemv_on_valu(a)) return 0;
+  const size_t gu = align256((size_t)a.M * (size_t)a.proj[0].N * 4);
+  return fp4::kWsHeaderBytes + 2 * gu + gemv_partials(a);
+}
+
+int fp4_gemv_swiglu(void* h_bf16, int64_t ldh, const void* x_bf16, const void* gate_packed, const float* gate_gscale,
+                    const void* up_packed, const float* up_gscale, int64_t M, int64_t N, int64_t K, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  fp4::GemvArgs a;
+  if (int st = swiglu_args(h_bf16, ldh, x_bf16, gate_packed, gate_gscale, up_packed, up_gscale, M, N, K, a)) return st;
+  const size_t need = swiglu_ws_need(a);
+  fp4::Workspace ws;
+  if (int st = take_ws(workspace, workspace_bytes, need, ws)) return st;
+  if (need > 0 && !ws.valid()) return FP4_ERR_WORKSPACE;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (gemv_on_valu(a)) return hip_status(fp4::launch_gemv_swiglu(a, s));
+  const size_t gu = align256((size_t)M * (size_t)N * 4);
+  float* g = reinterpret_cast<float*>(ws.scratch());
+  float* u = reinterpret_cast<float*>(ws.scratch() + gu);
+  a.proj[0].y = g;
+  a.proj[1].y = u;
+  a.proj[0].ldy = a.proj[1].ldy = N;
+  a.h = nullptr;
+  if (int st = gemv_run(a, ws.scratch() + 2 * gu, s)) return st;
+  return hip_status(fp4::launch_swiglu(g, u, M, N, static_cast<uint16_t*>(h_bf16), ldh, s));
 }
 
 int fp4_workspace_bytes(int op, int64_t M, int64_t K, const int64_t* Ns, int nproj, size_t* bytes) {
@@ -330,6 +423,20 @@ int fp4_workspace_bytes(int op, int64_t M, int64_t K, const int64_t* Ns, int npr
       if (nproj != 1) return FP4_ERR_SHAPE;
       if (Ns[0] < 1 || Ns[0] > kMaxN || M * Ns[0] > kMaxElems) return FP4_ERR_SHAPE;
       *bytes = fp4::argmax_ws_bytes(M, Ns[0]);
+      return FP4_OK;
+    }
+    case FP4_OP_GEMV_RMSNORM: {
+      fp4::GemvArgs a;
+      if (int st = gemv_args(p, nproj, sp, M, K, a)) return st;
+      *bytes = rms_ws_need(a);
+      return FP4_OK;
+    }
+    case FP4_OP_GEMV_SWIGLU: {
+      if (nproj != 1) return FP4_ERR_SHAPE;
+      fp4::GemvArgs a;
+      if (int st = swiglu_args(sp, Ns[0], sp, sp, static_cast<float*>(sp), sp, static_cast<float*>(sp), M, Ns[0], K, a))
+        return st;
+      *bytes = swiglu_ws_need(a);
       return FP4_OK;
     }
     case FP4_OP_LM_HEAD_GREEDY: {

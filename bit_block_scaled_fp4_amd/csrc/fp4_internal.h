@@ -77,6 +77,14 @@ struct GemvArgs {
   int32_t gw;         // row groups per workgroup (set by the launcher)
   ProjDesc proj[kMaxProj];
   GreedyArgs greedy;  // optional epilogue of the vector-ALU kernel (one projection)
+  // optional SwiGLU epilogue of the vector-ALU kernel (projections 0 = gate
+  // and 1 = up, equal N): h[m][n] = bf16(silu(gate) * up), bf16 [M][ldh]
+  uint16_t* h;
+  int64_t ldh;
+  // optional RMSNorm prologue of the vector-ALU kernel: every product reads
+  // bf16(x[m][k] / sqrt(mean_k x[m][k]^2 + eps) * gain[k]) instead of x
+  const uint16_t* gain;
+  float eps;
 };
 
 hipError_t launch_quantize(const uint16_t* W, int64_t N, int64_t K, bool tiled, uint8_t* packed,
@@ -92,14 +100,24 @@ hipError_t launch_retile(const uint8_t* packed, const uint8_t* scales, int64_t N
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t s, int gw = 0, int wc = 0);
 // Workgroups launch_gemv would launch for `a` (geometry as chosen there).
 int64_t gemv_workgroups(const GemvArgs& a);
+// The SwiGLU launch of the vector-ALU kernel (a.h set, two projections).
+hipError_t launch_gemv_swiglu(const GemvArgs& a, hipStream_t s);
+// Fallbacks for the matrix-core rows (neighbours.hip): RMS-normalised rows
+// out = bf16(x * rsqrt(mean(x^2) + eps) * gain), bf16 [M][K]; and
+// h = bf16(silu(g) * u) from fp32 g, u [M][N] (row stride N) into h [M][ldh].
+hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* gain, float eps, int64_t M, int64_t K, uint16_t* out,
+                          hipStream_t s);
+hipError_t launch_swiglu(const float* g, const float* u, int64_t M, int64_t N, uint16_t* h, int64_t ldh,
+                         hipStream_t s);
 // Small-M product on bf16 MFMA, split over K chunks (16 activation rows per
 // pass, more rows loop passes). With more than one chunk the chunk partial
-// sums meet in the workspace (`ws` valid: a second kernel adds them in chunk
-// order) or are added atomically into y after a fill kernel zeroes it (no
-// workspace; the summation order then varies between calls).
-hipError_t launch_gemv_mma(const GemvArgs& a, const Workspace& ws, hipStream_t s, int ppw = 0);   // ppw > 0: pairs per workgroup (tuning)
-// Workspace bytes launch_gemv_mma needs for `a` with a workspace (0 when it uses none).
-size_t gemv_mma_ws_bytes(const GemvArgs& a);
+// sums meet in `partials` (gemv_mma_partial_bytes of scratch: a second
+// kernel adds them in chunk order) or, when it is null, are added
+// atomically into y after a fill kernel zeroes it (the summation order then
+// varies between calls).
+hipError_t launch_gemv_mma(const GemvArgs& a, float* partials, hipStream_t s, int ppw = 0);   // ppw > 0: pairs per workgroup (tuning)
+// Bytes of partial sums launch_gemv_mma keeps for `a` (0 when it keeps none).
+size_t gemv_mma_partial_bytes(const GemvArgs& a);
 
 // Matrix-core product for prefill-sized M over 1..kMaxProj weight tensors
 // that read the same x (one launch). bn > 0 forces the output tile width

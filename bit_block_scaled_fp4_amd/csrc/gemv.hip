@@ -127,32 +127,109 @@ struct Round {
   uint4 x[MT][4];
 };
 
+// What the kernel does around the products.
+enum Mode { kPlain = 0, kGreedy = 1, kSwiglu = 2, kRms = 3 };
+
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);   // NaN stays NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// 8 bf16 activations times r and the 8 matching bf16 gains, rounded back to
+// bf16 (two fp32 multiplies, one rounding to nearest even per element).
+__device__ __forceinline__ uint4 norm8(const uint4& x, const uint4& g, float r) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t xw = word(x, i), gw = word(g, i);
+    const float x0 = __uint_as_float(xw << 16), x1 = __uint_as_float(xw & 0xffff0000u);
+    const float g0 = __uint_as_float(gw << 16), g1 = __uint_as_float(gw & 0xffff0000u);
+    const f32x2_t v = {x0 * r * g0, x1 * r * g1};
+    o[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// 1 / sqrt(mean_k x[row][k]^2 + eps) for the rows m0 .. m0 + MT - 1 (< M), in
+// fp32, computed by the whole workgroup into rinv[]; `tmp` is LDS of
+// kMaxWaves * MT floats.
+template <int MT>
+__device__ __forceinline__ void row_rms(const GemvArgs& a, int m0, float* rinv, float* tmp) {
+  const int K = a.K, M = a.M;
+  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6, lane = threadIdx.x & 63;
+  float ss[MT];
+#pragma unroll
+  for (int mi = 0; mi < MT; ++mi) {
+    ss[mi] = 0.0f;
+    const int row = min(m0 + mi, M - 1);
+    const __amdgpu_buffer_rsrc_t rx = rsrc(a.x + (int64_t)row * K, K * 2);
+    for (int u = threadIdx.x; u < K / 8; u += blockDim.x) {
+      const uint4 v = ld16<0>(rx, u * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w = word(v, i);
+        const float f0 = __uint_as_float(w << 16), f1 = __uint_as_float(w & 0xffff0000u);
+        ss[mi] = fmaf(f0, f0, ss[mi]);
+        ss[mi] = fmaf(f1, f1, ss[mi]);
+      }
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) ss[mi] += __shfl_xor(ss[mi], d);
+    if (lane == 0) tmp[wave * MT + mi] = ss[mi];
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < MT) {
+    float t = 0.0f;
+    for (int w = 0; w < nw; ++w) t += tmp[w * MT + threadIdx.x];
+    rinv[threadIdx.x] = 1.0f / sqrtf(t / (float)K + a.eps);
+  }
+  __syncthreads();
+}
+
 // grid: workgroups over all projections; block: gw * wc waves (at most 16).
-// GREEDY (one projection, M <= MT): the launch ends with the greedy choice
-// over each row of y (greedy.h); a separate instantiation, so the plain
-// product keeps its registers.
-template <int MT, bool GREEDY>
+// MODE kGreedy (one projection, M <= MT): the launch ends with the greedy
+// choice over each row of y (greedy.h). kSwiglu (projections gate and up):
+// a workgroup's first gw * wc waves take its row groups of gate, the others
+// the same row groups of up, and the epilogue writes h = bf16(silu(gate) *
+// up) instead of y. kRms (M <= MT): every workgroup first computes each
+// row's 1 / sqrt(mean(x^2) + eps) and the products read bf16(x * that *
+// gain). Each mode is its own instantiation, so the plain product keeps its
+// registers.
+template <int MT, int MODE>
 __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv(const GemvArgs a) {
   __shared__ float part[kMaxWaves][MT][8];
-  __shared__ uint64_t red[GREEDY ? kMaxWaves * MT : 1];
+  __shared__ uint64_t red[MODE == kGreedy ? kMaxWaves * MT : 1];
+  __shared__ float rinv[MODE == kRms ? MT : 1];
   __shared__ int flag;
   uint64_t keys[MT];
 #pragma unroll
   for (int mi = 0; mi < MT; ++mi) keys[mi] = 0;
   const int lane = threadIdx.x & 63, hl = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int C = a.C, K = a.K, M = a.M, Wc = a.wc, Gw = a.gw;
 
-  int p = 0;
-  while (p + 1 < a.nproj && (int)blockIdx.x >= a.proj[p + 1].wg_begin) ++p;
+  int p = 0, gi, wc;
+  if (MODE == kSwiglu) {
+    p = wave / (Gw * Wc);
+    const int rest = wave - p * Gw * Wc;
+    gi = rest / Wc;
+    wc = rest - gi * Wc;
+  } else {
+    while (p + 1 < a.nproj && (int)blockIdx.x >= a.proj[p + 1].wg_begin) ++p;
+    gi = wave / Wc;
+    wc = wave - gi * Wc;
+  }
   const ProjDesc& pd = a.proj[p];
   const int N = pd.N, G = (N + 7) >> 3;
-  const int C = a.C, K = a.K, M = a.M, Wc = a.wc, Gw = a.gw;
-  const int gi = wave / Wc, wc = wave - gi * Wc;
   const int g = ((int)blockIdx.x - pd.wg_begin) * Gw + gi;
   const bool gvalid = g < G;
   const float gs = *pd.gscale;
 
   for (int m0 = 0; m0 < M; m0 += MT) {
+    if (MODE == kRms) row_rms<MT>(a, m0, rinv, &part[0][0][0]);
     float acc[MT][4];
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi)
@@ -177,8 +254,20 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv(const GemvArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) f.x[mi][q] = ld16<0>(rx, off + q * 16);
       }
+      uint4 gn[4];
+      if (MODE == kRms) {
+        const __amdgpu_buffer_rsrc_t rg = rsrc(a.gain, K * 2);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) gn[q] = ld16<0>(rg, off + q * 16);
+      }
       // keep every load of the round ahead of the arithmetic
       __builtin_amdgcn_sched_barrier(0);
+      if (MODE == kRms) {
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) f.x[mi][q] = norm8(f.x[mi][q], gn[q], rinv[mi]);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         // row 2i + h: its two block scales are bytes 2(i&1), 2(i&1)+1 of word i >> 1
@@ -196,7 +285,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv(const GemvArgs a) {
     // ends in the lanes with hl % 8 == 0
     const int rr = 2 * (hl >> 3) + h;
     const bool holder = (hl & 7) == 0;
-    if (Wc == 1) {
+    if (Wc == 1 && MODE != kSwiglu) {
       const int n = 8 * g + rr;
 #pragma unroll
       for (int mi = 0; mi < MT; ++mi) {
@@ -204,7 +293,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv(const GemvArgs a) {
         if (holder && gvalid && n < N && m0 + mi < M) {
           const float v = gs * t;
           pd.y[(int64_t)(m0 + mi) * pd.ldy + n] = v;
-          if (GREEDY) keys[mi] = umax64(keys[mi], greedy_key(v, n));
+          if (MODE == kGreedy) keys[mi] = umax64(keys[mi], greedy_key(v, n));
         }
       }
     } else {
@@ -219,10 +308,16 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv(const GemvArgs a) {
         float s = 0.0f;
         for (int w = 0; w < Wc; ++w) s += part[gg * Wc + w][mi][r];   // chunk order
         const int n = 8 * (((int)blockIdx.x - pd.wg_begin) * Gw + gg) + r;
-        if (n < N && m0 + mi < M) {
+        if (MODE == kSwiglu) {
+          float su = 0.0f;
+          for (int w = 0; w < Wc; ++w) su += part[Gw * Wc + gg * Wc + w][mi][r];
+          const float vg = *a.proj[0].gscale * s, vu = *a.proj[1].gscale * su;
+          if (n < N && m0 + mi < M)
+            a.h[(int64_t)(m0 + mi) * a.ldh + n] = bf16_rne(vg / (1.0f + __expf(-vg)) * vu);
+        } else if (n < N && m0 + mi < M) {
           const float v = gs * s;
           pd.y[(int64_t)(m0 + mi) * pd.ldy + n] = v;
-          if (GREEDY) {
+          if (MODE == kGreedy) {
 #pragma unroll
             for (int j = 0; j < MT; ++j)
               if (j == mi) keys[j] = umax64(keys[j], greedy_key(v, n));
@@ -232,9 +327,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv(const GemvArgs a) {
       __syncthreads();
     }
   }
-  if (GREEDY) greedy_finish<MT>(a.greedy, keys, M, red, &flag);
+  if (MODE == kGreedy) greedy_finish<MT>(a.greedy, keys, M, red, &flag);
 }
-
 
 }  // namespace
 
@@ -275,9 +369,6 @@ static int64_t plan_mt(GemvArgs& a, int gw, int wc) {
   }
   int w = wc > 0 ? wc : (MT == 1 ? (a.C + rounds - 1) / rounds : (a.C + 2) / 3);
   a.wc = std::max(1, std::min(w, kMaxWaves));
-  // the greedy epilogue's last workgroup reads one key per workgroup and row:
-  // 8 waves per workgroup halve them against the default 4
-  if (gw <= 0 && a.greedy.idx) gw = std::max(1, 8 / a.wc);
   if (gw <= 0) {
     // about four waves per workgroup, but never so many row groups per
     // workgroup that the launch has fewer workgroups than CUs
@@ -297,11 +388,37 @@ template <int MT>
 static hipError_t launch_mt(GemvArgs a, hipStream_t s, int gw, int wc) {
   const int64_t wgs = plan_mt<MT>(a, gw, wc);
   a.greedy.S = (int32_t)wgs;
+  const dim3 grid((unsigned)wgs), block(64 * a.gw * a.wc);
   if (a.greedy.idx)
-    hipLaunchKernelGGL((k_gemv<MT, true>), dim3((unsigned)wgs), dim3(64 * a.gw * a.wc), 0, s, a);
+    hipLaunchKernelGGL((k_gemv<MT, kGreedy>), grid, block, 0, s, a);
+  else if (a.gain)
+    hipLaunchKernelGGL((k_gemv<MT, kRms>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((k_gemv<MT, false>), dim3((unsigned)wgs), dim3(64 * a.gw * a.wc), 0, s, a);
+    hipLaunchKernelGGL((k_gemv<MT, kPlain>), grid, block, 0, s, a);
   return hipGetLastError();
+}
+
+// The gate and up products of a gated MLP with the SwiGLU epilogue: the
+// geometry of the fused gate_up product (waves per row group as planned for
+// both projections together), with each workgroup taking the same row
+// groups of both, at most 16 waves in all.
+template <int MT>
+static hipError_t launch_swiglu_mt(GemvArgs a, hipStream_t s) {
+  plan_mt<MT>(a, 0, 0);
+  a.gw = std::max(1, std::min(a.gw, kMaxWaves / (2 * a.wc)));
+  if (2 * a.gw * a.wc > kMaxWaves) return hipErrorInvalidValue;
+  const int64_t wgs = (groups_of(a.proj[0].N) + a.gw - 1) / a.gw;
+  a.proj[0].wg_begin = a.proj[1].wg_begin = 0;
+  hipLaunchKernelGGL((k_gemv<MT, kSwiglu>), dim3((unsigned)wgs), dim3(64 * 2 * a.gw * a.wc), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_swiglu(const GemvArgs& a, hipStream_t s) {
+  if (a.nproj != 2 || a.proj[0].N != a.proj[1].N || !a.h) return hipErrorInvalidValue;
+  if (a.M == 1) return launch_swiglu_mt<1>(a, s);
+  if (a.M == 2) return launch_swiglu_mt<2>(a, s);
+  if (a.M <= 4) return launch_swiglu_mt<4>(a, s);
+  return hipErrorInvalidValue;
 }
 
 int64_t gemv_workgroups(const GemvArgs& a) {

@@ -519,19 +519,19 @@ int pairs_per_wg_for(const MmaArgs& a, bool eight) {
 
 }  // namespace
 
-size_t gemv_mma_ws_bytes(const GemvArgs& g) {
+size_t gemv_mma_partial_bytes(const GemvArgs& g) {
   if (g.C <= 1) return 0;
   const MmaArgs a = mma_args(g);
   if (a.npairs < 0) return 0;
-  return kWsHeaderBytes + (size_t)a.C * (size_t)a.npairs * 256 * sizeof(float);
+  return (size_t)a.C * (size_t)a.npairs * 256 * sizeof(float);
 }
 
-hipError_t launch_gemv_mma(const GemvArgs& g, const Workspace& ws, hipStream_t s, int ppw) {
+hipError_t launch_gemv_mma(const GemvArgs& g, float* partials, hipStream_t s, int ppw) {
   MmaArgs a = mma_args(g);
   if (a.npairs < 0) return hipErrorInvalidValue;
   const int64_t pairs = a.npairs;
-  const bool use_ws = a.C > 1 && ws.valid();
-  if (use_ws) a.ws = reinterpret_cast<float*>(ws.scratch());
+  const bool use_ws = a.C > 1 && partials;
+  if (use_ws) a.ws = partials;
   for (int m0 = 0; m0 < g.M; m0 += kMRows) {
     a.m0 = m0;
     const bool eight = g.M - m0 <= 8;

@@ -289,12 +289,47 @@ FP4_API int fp4_lm_head_greedy(int32_t *idx, float *logits, const void *x_bf16, 
 FP4_API int fp4_gemv_multi_noalloc(const fp4_proj *projs, int nproj, const void *x_bf16, int64_t M, int64_t K,
                                    void *stream);
 
+/* The attention block's products on the RMS-normalised stream: for each
+ * projection, y[m][n] = sum_k dequant(W)[n][k] * xn[m][k] with
+ *   xn[m][k] = bf16( x[m][k] / sqrt(mean_k x[m][k]^2 + eps) * gain[k] ),
+ * the mean over the K elements of the row, in fp32, rounded once to bf16
+ * (round to nearest even). A decode layer runs attention on its residual
+ * stream (page "1. The big picture", step 3); for the Qwen3 family the
+ * pages use as their example, Q, K and V read that stream RMS-normalised
+ * (eps 1e-6 there). gain: bf16 [K] (device, 16-byte aligned); eps finite
+ * and >= 0 (else FP4_ERR_SHAPE); projections and x as fp4_gemv_multi. Up
+ * to 2 rows on the vector ALUs: one launch, every workgroup computing the
+ * rows' sums of squares itself. Otherwise a norm kernel writes xn into the
+ * workspace (required then: fp4_workspace_bytes with FP4_OP_GEMV_RMSNORM;
+ * FP4_ERR_WORKSPACE without one), and the product reads it. */
+FP4_API int fp4_gemv_multi_rmsnorm(const fp4_proj *projs, int nproj, const void *x_bf16, const void *gain_bf16,
+                                   float eps, int64_t M, int64_t K, void *workspace, size_t workspace_bytes,
+                                   void *stream);
+
+/* The first half of a gated MLP: h[m][n] = bf16( silu(g[m][n]) * u[m][n] )
+ * with g = x * dequant(W_gate)^T, u = x * dequant(W_up)^T (each TILED
+ * [N][K] with its own tensor scale), silu(z) = z / (1 + e^-z), in fp32,
+ * rounded once to bf16 (nearest even); h is bf16 [M][ldh] (device, 2-byte
+ * aligned, ldh >= N) and feeds the down projection. The pages' example
+ * model family (Qwen3, page "1. The big picture") has this MLP; the gate,
+ * up and down names are the workload's. When the pair runs on the vector
+ * ALUs (see fp4_gemv) it is one launch: each workgroup computes the same
+ * rows of gate and up and writes h. Otherwise the two products go to fp32
+ * buffers in the workspace (required then: FP4_OP_GEMV_SWIGLU with
+ * Ns[0] = N; FP4_ERR_WORKSPACE without one) and an elementwise kernel
+ * writes h. */
+FP4_API int fp4_gemv_swiglu(void *h_bf16, int64_t ldh, const void *x_bf16, const void *gate_packed,
+                            const float *gate_gscale, const void *up_packed, const float *up_gscale, int64_t M,
+                            int64_t N, int64_t K, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Which call a workspace size is asked for. */
 typedef enum {
     FP4_OP_GEMV = 0,           /* fp4_gemv_ws, fp4_gemv_multi_ws */
     FP4_OP_GEMM_PREFILL = 1,   /* fp4_gemm_prefill_ws, fp4_gemm_prefill_multi_ws */
     FP4_OP_ARGMAX_ROWS = 2,    /* fp4_argmax_rows (K unused, Ns[0] = N) */
-    FP4_OP_LM_HEAD_GREEDY = 3  /* fp4_lm_head_greedy (Ns[0] = N) */
+    FP4_OP_LM_HEAD_GREEDY = 3, /* fp4_lm_head_greedy (Ns[0] = N) */
+    FP4_OP_GEMV_RMSNORM = 4,   /* fp4_gemv_multi_rmsnorm */
+    FP4_OP_GEMV_SWIGLU = 5     /* fp4_gemv_swiglu (Ns[0] = N) */
 } fp4_op;
 
 /* *bytes = the workspace bytes a call of `op` with M activation rows, K

@@ -24,7 +24,7 @@ def test_every_declared_symbol_is_exported():
                             "fp4_gemv_ws", "fp4_gemv_multi", "fp4_gemv_multi_ws", "fp4_gemm_prefill",
                             "fp4_gemm_prefill_ws", "fp4_gemm_prefill_multi", "fp4_gemm_prefill_multi_ws",
                             "fp4_argmax_rows", "fp4_lm_head_greedy", "fp4_quantize_fp8", "fp4_workspace_bytes",
-                            "fp4_gemv_multi_noalloc"])
+                            "fp4_gemv_multi_noalloc", "fp4_gemv_multi_rmsnorm", "fp4_gemv_swiglu"])
     lib = ctypes.CDLL(fp4.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -222,3 +222,26 @@ def test_binding_checks_fused_calls_before_any_gpu_work():
             call(x, [w], [y])
     with pytest.raises(ValueError, match=r"\[K\] or \[M\]\[K\]"):
         fp4.gemm_prefill_multi(torch.zeros(2, 2, 32, dtype=torch.bfloat16), [w], [y])
+
+
+def test_rmsnorm_and_swiglu_argument_errors():
+    L = fp4.raw()
+    P = (fp4._Proj * 1)(fp4._Proj(A, None, A, 8, A, 8))
+    assert L.fp4_gemv_multi_rmsnorm(P, 1, A, None, 1e-6, 1, 32, None, 0, None) == ENULL
+    assert L.fp4_gemv_multi_rmsnorm(P, 1, A, A + 2, 1e-6, 1, 32, None, 0, None) == EALIGN
+    assert L.fp4_gemv_multi_rmsnorm(P, 1, A, A, -1.0, 1, 32, None, 0, None) == ESHAPE
+    assert L.fp4_gemv_multi_rmsnorm(P, 1, A, A, float("nan"), 1, 32, None, 0, None) == ESHAPE
+    assert L.fp4_gemv_multi_rmsnorm(P, 1, A, A, 1e-6, 1, 24, None, 0, None) == ESHAPE
+    # 8 rows: the normalised rows go through the workspace, which is then required
+    assert fp4.workspace_bytes(fp4.OP_GEMV_RMSNORM, 8, 1024, [8]) >= 65536 + 8 * 1024 * 2
+    assert fp4.workspace_bytes(fp4.OP_GEMV_RMSNORM, 1, 1024, [8]) == 0
+    assert L.fp4_gemv_multi_rmsnorm(P, 1, A, A, 1e-6, 8, 1024, None, 0, None) == EWS
+    assert L.fp4_gemv_swiglu(None, 8, A, A, A, A, A, 1, 8, 32, None, 0, None) == ENULL
+    assert L.fp4_gemv_swiglu(A, 8, A, A, None, A, A, 1, 8, 32, None, 0, None) == ENULL
+    assert L.fp4_gemv_swiglu(A, 7, A, A, A, A, A, 1, 8, 32, None, 0, None) == ESHAPE     # ldh < N
+    assert L.fp4_gemv_swiglu(A + 1, 8, A, A, A, A, A, 1, 8, 32, None, 0, None) == EALIGN
+    assert L.fp4_gemv_swiglu(A, 8, A, A, A, A, A, 1, 8, 24, None, 0, None) == ESHAPE
+    assert fp4.workspace_bytes(fp4.OP_GEMV_SWIGLU, 1, 5120, [17408]) == 0
+    need = fp4.workspace_bytes(fp4.OP_GEMV_SWIGLU, 8, 5120, [17408])
+    assert need >= 65536 + 2 * 8 * 17408 * 4
+    assert L.fp4_gemv_swiglu(A, 17408, A, A, A, A, A, 8, 17408, 5120, None, 0, None) == EWS

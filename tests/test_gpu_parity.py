@@ -808,3 +808,93 @@ def test_two_streams_at_once():
         if use_ws:
             assert all(torch.equal(ys[0], y) for y in ys)
     assert torch.count_nonzero(wa[:65536]) == 0 and torch.count_nonzero(wb[:65536]) == 0
+
+
+# --------------------------------------------- fused neighbours: RMSNorm, SwiGLU
+def gain_bits(K, seed):
+    return float32_to_bf16_bits((1.0 + bf16_to_float32(bf16_tensor((K,), seed, 0.1))).astype(np.float32))
+
+
+# Bound of the normalised product: the product bound on the normalised rows,
+# plus one bf16 rounding (2^-9 relative) of each normalised input and the
+# fp32 norm's own error (below 1e-4 relative for K <= 2^20), all relative to
+# sum_k |w * xn|.
+RMS_TOL = 2e-3 + 2.0 ** -9 + 1e-4
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 8])
+def test_rmsnorm_then_qkv(M):
+    """Q, K and V of the Qwen3-0.6B-shaped layer 1 (2048, 1024, 1024 x 1024)
+    in one call on the RMS-normalised rows (gain ~ 1 + N(0, 0.1), eps 1e-6,
+    rows ~ N(0, 3)): M <= 2 inside the product's launch, M = 4 and 8 through
+    the norm kernel and a workspace. Against the oracle's fp64 norm and
+    product within RMS_TOL * sum|w * xn|; the plain product of the raw rows
+    does not meet that bound (the norm is really applied)."""
+    wl, K = "qwen3_0p6b_decode", 1024
+    names, Ns = ("q", "k", "v"), (2048, 1024, 1024)
+    ws = [gpu_quant(weight_bits(wl, "L1.%s" % t)) for t in names]
+    bx = bf16_tensor((M, K), 7100 + M, 3.0)
+    gb = gain_bits(K, 55)
+    x, gain = to_gpu_bf16(bx), to_gpu_bf16(gb)
+    qkv = torch.full((M, 4096), float("nan"), device=dev())
+    outs = [qkv, qkv[:, 2048:], qkv[:, 3072:]]
+    need = fp4.workspace_bytes(fp4.OP_GEMV_RMSNORM, M, K, list(Ns))
+    assert (need == 0) == (M <= 2)
+    work = fp4.new_workspace(need, dev()) if need else None
+    if need:
+        with pytest.raises(fp4.Fp4Error):
+            fp4.gemv_multi_rmsnorm(x, gain, 1e-6, ws, outs, [4096] * 3)
+    fp4.gemv_multi_rmsnorm(x, gain, 1e-6, ws, outs, [4096] * 3, workspace=work)
+    raw = fp4.gemv(x, ws[0])
+    torch.cuda.synchronize()
+    xn = oracle.rmsnorm(bx, gb, 1e-6)
+    off = 0
+    for i, (t, N) in enumerate(zip(names, Ns)):
+        p, s, g = oracle_quant(wl, "L1.%s" % t)
+        yr, l1 = oracle.gemv_f64(xn, p, s, g)
+        ok, worst = oracle.tolerance_ok(qkv[:, off:off + N].cpu().numpy().astype(np.float64), yr, l1, RMS_TOL)
+        assert ok, "%s M=%d worst %.3g" % (t, M, worst)
+        if i == 0:
+            assert not oracle.tolerance_ok(raw.cpu().numpy().astype(np.float64), yr, l1, RMS_TOL)[0]
+        off += N
+
+
+def swiglu_bound(g, u, l1g, l1u, h):
+    """|h_gpu - silu(g) u| bound from the product bounds on g and u
+    (|dg| <= 2e-3 l1g, |du| <= 2e-3 l1u), silu's slope (at most 1.1), one
+    bf16 rounding of the result and fp32 evaluation (2^-8 of |h|)."""
+    sg = np.abs(oracle.swiglu(g, np.ones_like(g)))
+    prod = 1.1 * 2e-3 * l1g * (np.abs(u) + 2e-3 * l1u) + sg * 2e-3 * l1u
+    return prod * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(h) + 1e-30
+
+
+@pytest.mark.parametrize("case,M", [("27b", 1), ("27b", 2), ("27b", 8), ("qwen", 1), ("qwen", 4)])
+def test_gemv_swiglu(case, M):
+    """h = bf16(silu(gate) * up) for the 27B-class gate/up (17408 x 5120) at
+    M = 1, 2 (one vector-ALU launch) and 8 (matrix-core product into the
+    workspace, then the elementwise kernel), and the Qwen3-0.6B-shaped layer
+    1 (3072 x 1024) at M = 1 and 4; against the oracle's fp64 products and
+    silu within swiglu_bound; the operands swapped do not meet it."""
+    if case == "27b":
+        wl, pre, K = "dense27b_layer", "", 5120
+        bx = act_bits(wl, "x_in") if M == 1 else act_bits("dense27b_smallm", "x_in_m%d" % M)
+    else:
+        wl, pre, K = "qwen3_0p6b_decode", "L1.", 1024
+        bx = bf16_tensor((M, K), 7300 + M, 1.0)
+    print("swiglu", case, M, flush=True)
+    wg, wu = gpu_quant(weight_bits(wl, pre + "gate")), gpu_quant(weight_bits(wl, pre + "up"))
+    N = wg.N
+    need = fp4.workspace_bytes(fp4.OP_GEMV_SWIGLU, M, K, [N])
+    work = fp4.new_workspace(need, dev()) if need else None
+    h = fp4.gemv_swiglu(to_gpu_bf16(bx), wg, wu, workspace=work)
+    torch.cuda.synchronize()
+    hg = bf16_to_float32(h.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+    pg, sg, gg = oracle_quant(wl, pre + "gate")
+    pu, su, gu = oracle_quant(wl, pre + "up")
+    g, l1g = oracle.gemv(bx, pg, sg, gg, threads=THREADS)
+    u, l1u = oracle.gemv(bx, pu, su, gu, threads=THREADS)
+    href = oracle.swiglu(g, u)
+    bound = swiglu_bound(g, u, l1g, l1u, href)
+    err = np.abs(hg - href)
+    assert np.all(err <= bound), "worst %.3g" % float((err / bound).max())
+    assert not np.all(np.abs(hg - oracle.swiglu(u, g)) <= swiglu_bound(u, g, l1u, l1g, oracle.swiglu(u, g)))
