@@ -78,6 +78,16 @@ def _L():
         lib.orc_swiglu.restype = None
         lib.orc_rmsnorm.argtypes = [P, P, I64, I64, ctypes.c_double, P]
         lib.orc_rmsnorm.restype = None
+        lib.orc_e8m0_value.argtypes = [ctypes.c_int]
+        lib.orc_e8m0_value.restype = ctypes.c_double
+        lib.orc_mx_quantize.argtypes = [P, I64, I64, P, P]
+        lib.orc_mx_quantize.restype = ctypes.c_int
+        lib.orc_mx_dequant.argtypes = [P, P, I64, I64, P]
+        lib.orc_mx_dequant.restype = None
+        lib.orc_mx_gemv.argtypes = [P, I64, P, P, I64, I64, P, P]
+        lib.orc_mx_gemv.restype = None
+        lib.orc_mx_tile.argtypes = [P, P, I64, I64, P]
+        lib.orc_mx_tile.restype = None
         for f in (lib.orc_argmax_rows_f64, lib.orc_argmax_rows_f32):
             f.argtypes = [P, I64, I64, I64, P]
             f.restype = None
@@ -222,6 +232,55 @@ def rmsnorm(x_bits: np.ndarray, gain_bits: np.ndarray, eps: float) -> np.ndarray
     out = np.empty((M, K), dtype=np.float64)
     _L().orc_rmsnorm(px, pg, M, K, float(eps), out.ctypes.data)
     return out
+
+
+def e8m0_value(code: int) -> float:
+    return _L().orc_e8m0_value(int(code))
+
+
+def mx_quantize(W_bits: np.ndarray):
+    """MXFP4: bf16 W [N][K] (K % 32 == 0) -> (packed uint8 [N][K/2], E8M0 scales uint8 [N][K/32])."""
+    W, pw = _c(W_bits, np.uint16)
+    N, K = W.shape
+    packed = np.empty((N, K // 2), dtype=np.uint8)
+    scales = np.empty((N, K // 32), dtype=np.uint8)
+    if _L().orc_mx_quantize(pw, N, K, packed.ctypes.data, scales.ctypes.data) != 0:
+        raise ValueError("mx_quantize: bad shape %r" % (W.shape,))
+    return packed, scales
+
+
+def mx_dequant(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    packed, pp = _c(packed, np.uint8)
+    scales, ps = _c(scales, np.uint8)
+    N, K = packed.shape[0], packed.shape[1] * 2
+    out = np.empty((N, K), dtype=np.float64)
+    _L().orc_mx_dequant(pp, ps, N, K, out.ctypes.data)
+    return out
+
+
+def mx_gemv(x_bits: np.ndarray, packed: np.ndarray, scales: np.ndarray):
+    """fp64 MXFP4 product (y [M][N], l1 [M][N]) for bf16 x [M][K]."""
+    x, px = _c(np.atleast_2d(x_bits), np.uint16)
+    packed, pp = _c(packed, np.uint8)
+    scales, ps = _c(scales, np.uint8)
+    M, K = x.shape
+    N = packed.shape[0]
+    assert packed.shape[1] * 2 == K and scales.shape == (N, K // 32)
+    y = np.empty((M, N), dtype=np.float64)
+    l1 = np.empty((M, N), dtype=np.float64)
+    _L().orc_mx_gemv(px, M, pp, ps, N, K, y.ctypes.data, l1.ctypes.data)
+    return y, l1
+
+
+def mx_tile(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Canonical MXFP4 -> the GPU library's MXFP4 tiled layout (4352-byte tiles)."""
+    packed, pp = _c(packed, np.uint8)
+    scales, ps = _c(scales, np.uint8)
+    N, K = packed.shape[0], packed.shape[1] * 2
+    G, C = (N + 7) // 8, (K + 1023) // 1024
+    t = np.empty(G * C * 4352, dtype=np.uint8)
+    _L().orc_mx_tile(pp, ps, N, K, t.ctypes.data)
+    return t
 
 
 def tile(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:

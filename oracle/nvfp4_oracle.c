@@ -367,6 +367,127 @@ void orc_rmsnorm(const uint16_t *x, const uint16_t *gain, int64_t M, int64_t K, 
     }
 }
 
+/* ---------------------------------------------------------------- MXFP4 */
+
+/* The README's quantisation row lists MXFP4 beside NVFP4. Read here as the
+ * OCP Microscaling v1.0 format of that name: the same E2M1 elements, one
+ * shared scale per 32 consecutive K-elements of a row, encoded E8M0 (an
+ * unsigned biased exponent, value 2^(c - 127), 0xFF NaN), no tensor scale.
+ * Quantisation, the OCP conversion: per block, shared exponent
+ * floor(log2(amax)) - 2 (2 = the exponent of E2M1's largest value, 6 =
+ * 1.5 * 2^2), clamped to [-127, 127]; each element w / 2^shared rounded to
+ * the nearest E2M1 value, ties to even, saturating at 6. Readings as for
+ * NVFP4: a block with amax 0 gets scale code 0 and element codes 0; the sign
+ * of an element code is the sign bit of w. Canonical layout: packed
+ * [N][K/2] (even k in the low nibble), scales [N][K/32]; K % 32 == 0. */
+
+double orc_e8m0_value(int code) {
+    if ((code & 0xFF) == 0xFF) return NAN;
+    return ldexp(1.0, (code & 0xFF) - 127);
+}
+
+/* W: bf16 bits [N][K]. Returns 0, or -1 for a bad shape. */
+int orc_mx_quantize(const uint16_t *W, int64_t N, int64_t K, uint8_t *packed, uint8_t *scales) {
+    if (N < 0 || K < 0 || K % 32 != 0) return -1;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t b = 0; b < K / 32; ++b) {
+            double w[32], amax = 0.0;
+            for (int j = 0; j < 32; ++j) {
+                w[j] = (double)bf16_to_f32(W[n * K + b * 32 + j]);
+                if (fabs(w[j]) > amax) amax = fabs(w[j]);
+            }
+            uint8_t codes[32];
+            if (amax == 0.0) {
+                scales[n * (K / 32) + b] = 0;
+                memset(codes, 0, sizeof codes);
+            } else {
+                int e;
+                frexp(amax, &e);                     /* amax = f * 2^e, f in [0.5, 1): floor(log2) = e - 1 */
+                int shared = (e - 1) - 2;
+                if (shared < -127) shared = -127;
+                if (shared > 127) shared = 127;
+                scales[n * (K / 32) + b] = (uint8_t)(shared + 127);
+                for (int j = 0; j < 32; ++j) {
+                    double v = ldexp(w[j], -shared);  /* exact: a power-of-two scaling of a bf16 value */
+                    codes[j] = orc_e2m1_encode((float)v);
+                }
+            }
+            for (int j = 0; j < 16; ++j)
+                packed[n * (K / 2) + b * 16 + j] = (uint8_t)(codes[2 * j] | (codes[2 * j + 1] << 4));
+        }
+    }
+    return 0;
+}
+
+/* Dequantised MXFP4 weights, fp64 [N][K]. */
+void orc_mx_dequant(const uint8_t *packed, const uint8_t *scales, int64_t N, int64_t K, double *out) {
+    tables();
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            uint8_t byte = packed[n * (K / 2) + k / 2];
+            int q = (k % 2 == 0) ? (byte & 15) : (byte >> 4);
+            out[n * K + k] = E2M1_TAB[q] * orc_e8m0_value(scales[n * (K / 32) + k / 32]);
+        }
+}
+
+/* y[m][n] = sum_b E8M0(sc[n][b]) * sum_{i<32} E2M1(q[n][32b+i]) * x[m][32b+i]
+ * and l1[m][n] = sum_k |dequant(W)[n][k] * x[m][k]|, fp64, in k order. */
+void orc_mx_gemv(const uint16_t *x, int64_t M, const uint8_t *packed, const uint8_t *scales, int64_t N, int64_t K,
+                 double *y, double *l1) {
+    tables();
+    for (int64_t n = 0; n < N; ++n) {
+        const uint8_t *q = packed + n * (K / 2);
+        const uint8_t *sc = scales + n * (K / 32);
+        for (int64_t m = 0; m < M; ++m) {
+            const uint16_t *xm = x + m * K;
+            double acc = 0.0, a1 = 0.0;
+            for (int64_t b = 0; b < K / 32; ++b) {
+                double s = orc_e8m0_value(sc[b]), inner = 0.0;
+                for (int64_t i = 0; i < 32; ++i) {
+                    int64_t k = b * 32 + i;
+                    uint8_t byte = q[k / 2];
+                    double e = E2M1_TAB[(k % 2 == 0) ? (byte & 15) : (byte >> 4)];
+                    double xv = (double)bf16_to_f32(xm[k]);
+                    inner += e * xv;
+                    a1 += fabs(e * s * xv);
+                }
+                acc += s * inner;
+            }
+            y[m * N + n] = acc;
+            if (l1) l1[m * N + n] = a1;
+        }
+    }
+}
+
+/* The GPU library's MXFP4 tiled layout: rows in groups of 8, K in chunks of
+ * 1024; tile (g, c) is the 4352 bytes at (g*C + c)*4352:
+ *   codes, bytes 0..4095: as the NVFP4 tile (row r's 32 pieces of 16 bytes
+ *       at r*512 + l*16; piece l = elements 1024c + 32l .. + 31);
+ *   scales, bytes 4096..4351: byte 4096 + h*128 + l*4 + i = scale of
+ *       (row 8g + 2i + h, block 32c + l), h < 2, l < 32, i < 4.
+ * Positions outside the tensor hold 0. */
+void orc_mx_tile(const uint8_t *packed, const uint8_t *scales, int64_t N, int64_t K, uint8_t *tiles) {
+    int64_t G = (N + 7) / 8, C = (K + 1023) / 1024;
+    for (int64_t g = 0; g < G; ++g)
+        for (int64_t c = 0; c < C; ++c) {
+            uint8_t *t = tiles + (g * C + c) * 4352;
+            for (int r = 0; r < 8; ++r)
+                for (int l = 0; l < 32; ++l) {
+                    int64_t row = 8 * g + r;
+                    for (int i = 0; i < 16; ++i) {
+                        int64_t kb = (1024 * c + 32 * l) / 2 + i;
+                        t[r * 512 + l * 16 + i] = (row < N && kb < K / 2) ? packed[row * (K / 2) + kb] : 0;
+                    }
+                }
+            for (int h = 0; h < 2; ++h)
+                for (int l = 0; l < 32; ++l)
+                    for (int i = 0; i < 4; ++i) {
+                        int64_t row = 8 * g + 2 * i + h, blk = 32 * c + l;
+                        t[4096 + h * 128 + l * 4 + i] = (row < N && blk < K / 32) ? scales[row * (K / 32) + blk] : 0;
+                    }
+        }
+}
+
 /* --------------------------------------------------------- device layout */
 
 /* The GPU library's tiled layout, written out as plain loops so that the

@@ -57,6 +57,12 @@ MUTANTS = [
     ("rmsnorm drops the gain", "* r * (double)bf16_to_f32(gain[k]);", "* r;"),
     ("fp64-activation product reads activation row 0", "const double *xdm = j->xd ? j->xd + m * K : NULL;",
      "const double *xdm = j->xd ? j->xd : NULL;"),
+    ("MX shared exponent one too large", "int shared = (e - 1) - 2;", "int shared = (e - 1) - 1;"),
+    ("MX shared exponent not clamped below", "if (shared < -127) shared = -127;", "if (shared < -128) shared = -128;"),
+    ("E8M0 decoded with bias 128", "return ldexp(1.0, (code & 0xFF) - 127);", "return ldexp(1.0, (code & 0xFF) - 128);"),
+    ("MX zero block takes the element encoder", "if (amax == 0.0) {", "if (amax < 0.0) {"),
+    ("MX product drops the block scale", "acc += s * inner;", "acc += inner;"),
+    ("MX tile swaps the half and row-pair fields", "t[4096 + h * 128 + l * 4 + i]", "t[4096 + i * 64 + l * 2 + h]"),
 ]
 
 

@@ -464,3 +464,112 @@ def test_gemv_f64_equals_bf16_entry_and_numpy():
     y3, l3 = oracle.gemv_f64(xd, p, s, g)
     assert np.allclose(y3, xd @ D.T, rtol=1e-12, atol=1e-14 * np.abs(D).sum())
     assert np.allclose(l3, np.abs(xd) @ np.abs(D).T, rtol=1e-12)
+
+
+# ------------------------------------------------------------------- MXFP4
+def load_mx_example():
+    rows, codes, scales = [], [], []
+    with open(os.path.join(GOLDEN, "mx_worked_example.txt")) as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            key, *vals = line.split()
+            if key == "row":
+                rows.append([float(v) for v in vals])
+            elif key == "codes":
+                codes.append([int(v, 16) for v in vals])
+            elif key == "scales":
+                scales.append([int(v, 16) for v in vals])
+    W = np.array(rows, dtype=np.float32)
+    Wb = float32_to_bf16_bits(W)
+    assert np.array_equal(bf16_to_float32(Wb), W) and np.array_equal(np.signbit(bf16_to_float32(Wb)), np.signbit(W))
+    c = np.array(codes, np.uint8)
+    packed = (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)   # even k in the low nibble
+    return Wb, packed, np.array(scales, np.uint8)
+
+
+def test_e8m0_decode_all_codes_match_torch():
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e8m0fnu).double().numpy()
+    for c in range(256):
+        v = oracle.e8m0_value(c)
+        if np.isnan(ref[c]):
+            assert np.isnan(v), c
+        else:
+            assert v == ref[c] == 2.0 ** (c - 127), c
+
+
+def test_mx_quantize_worked_example():
+    Wb, packed, scales = load_mx_example()
+    p, s = oracle.mx_quantize(Wb)
+    assert np.array_equal(s, scales), (s, scales)
+    assert np.array_equal(p, packed), np.flatnonzero(p != packed)
+
+
+def test_mx_round_trip_and_bounds():
+    """Blocks built from E2M1 values times a power of two whose largest
+    magnitude is 4 or 6 times it quantise back to themselves exactly; on
+    random bf16 weights every unclamped block has 4 X <= amax < 8 X
+    (X = E8M0 of its scale), its largest element encodes to 4 or 6, and
+    every element is within 2 X of its dequantised value."""
+    rng = np.random.default_rng(41)
+    N, K = 16, 256
+    mags = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    codes = rng.integers(0, 8, (N, K))
+    codes[:, ::32] = rng.choice([6, 7], (N, K // 32))        # each block's amax is 4 or 6 units
+    shared = rng.integers(-20, 20, (N, K // 32))
+    sign = rng.choice([-1.0, 1.0], (N, K))
+    W = sign * mags[codes] * np.repeat(2.0 ** shared, 32, axis=1)
+    Wb = float32_to_bf16_bits(W.astype(np.float32))
+    p, s = oracle.mx_quantize(Wb)
+    assert np.array_equal(s, (shared + 127).astype(np.uint8))
+    assert np.array_equal(oracle.mx_dequant(p, s), bf16_to_float32(Wb).astype(np.float64))
+    Wr = bf16_tensor((64, 512), 42, 0.02, outlier_p=0.01, outlier_scale=20.0)
+    p, s = oracle.mx_quantize(Wr)
+    X = np.array([[oracle.e8m0_value(c) for c in row] for row in s])
+    w = bf16_to_float32(Wr).astype(np.float64).reshape(64, 16, 32)
+    amax = np.abs(w).max(axis=2)
+    assert np.all((4 * X <= amax) & (amax < 8 * X))
+    D = oracle.mx_dequant(p, s).reshape(64, 16, 32)
+    assert np.all(np.abs(w - D) <= 2 * X[:, :, None])
+    at = np.abs(w).argmax(axis=2)
+    amax_code = np.take_along_axis((p[:, :, None] >> np.array([0, 4])).reshape(64, 16, 32) & 7, at[:, :, None], 2)
+    assert np.all(np.isin(amax_code, [6, 7]))
+
+
+def mx_dequant_from_bits(p, s):
+    e2 = np.array([float(minifloat_value(c, 2, 1, 1)) for c in range(16)])
+    e8 = torch.from_numpy(np.ascontiguousarray(s)).view(torch.float8_e8m0fnu).double().numpy()
+    q = np.stack([p & 15, p >> 4], axis=2).reshape(p.shape[0], -1)
+    return e2[q] * np.repeat(e8, 32, axis=1)
+
+
+def test_mx_gemv_matches_numpy_on_tiny_matrices():
+    rng = np.random.default_rng(43)
+    for N, K, M in [(1, 32, 1), (3, 64, 2), (9, 1024 + 32, 3)]:
+        W = float32_to_bf16_bits(rng.normal(0, 0.05, (N, K)).astype(np.float32))
+        x = float32_to_bf16_bits(rng.normal(0, 1, (M, K)).astype(np.float32))
+        p, s = oracle.mx_quantize(W)
+        D = mx_dequant_from_bits(p, s)
+        assert np.array_equal(oracle.mx_dequant(p, s), D)
+        xf = bf16_to_float32(x).astype(np.float64)
+        y, l1 = oracle.mx_gemv(x, p, s)
+        assert np.allclose(y, xf @ D.T, rtol=1e-13, atol=1e-15 * np.abs(D).sum())
+        assert np.allclose(l1, np.abs(xf) @ np.abs(D).T, rtol=1e-13)
+
+
+def test_mx_tile_matches_reshape_formulation():
+    """The MXFP4 device layout written as array reshapes: codes as in the
+    NVFP4 tile; scale (row 8g + 2i + h, block 32c + l) at 4096 + 128h + 4l + i."""
+    rng = np.random.default_rng(44)
+    for N, K in [(8, 1024), (13, 2080), (1, 32)]:
+        p = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+        s = rng.integers(0, 255, (N, K // 32), dtype=np.uint8)
+        G, C = (N + 7) // 8, (K + 1023) // 1024
+        pp = np.zeros((G * 8, C * 512), np.uint8)
+        pp[:N, :K // 2] = p
+        ss = np.zeros((G * 8, C * 32), np.uint8)
+        ss[:N, :K // 32] = s
+        codes = pp.reshape(G, 8, C, 512).transpose(0, 2, 1, 3).reshape(G, C, 4096)
+        sc = ss.reshape(G, 4, 2, C, 32).transpose(0, 3, 2, 4, 1).reshape(G, C, 256)   # [g][c][h][l][i]
+        ref = np.concatenate([codes, sc], axis=2).reshape(-1)
+        assert np.array_equal(oracle.mx_tile(p, s), ref), (N, K)
