@@ -24,10 +24,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfp4.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "fp4.h")
 
-ROWMAJOR, TILED = 0, 1
+ROWMAJOR, TILED, MX_ROWMAJOR, MX_TILED = 0, 1, 2, 3
 MAX_PROJ = 8
 OP_GEMV, OP_GEMM_PREFILL, OP_ARGMAX_ROWS, OP_LM_HEAD_GREEDY, OP_GEMV_RMSNORM, OP_GEMV_SWIGLU = 0, 1, 2, 3, 4, 5
-_LAYOUTS = {"rowmajor": ROWMAJOR, "tiled": TILED, ROWMAJOR: ROWMAJOR, TILED: TILED}
+_LAYOUTS = {"rowmajor": ROWMAJOR, "tiled": TILED, "mx_rowmajor": MX_ROWMAJOR, "mx_tiled": MX_TILED,
+            ROWMAJOR: ROWMAJOR, TILED: TILED, MX_ROWMAJOR: MX_ROWMAJOR, MX_TILED: MX_TILED}
 
 if not os.path.exists(LIB_PATH):
     raise ImportError("libfp4.so is not built: run `python -c 'import __graft_entry__ as g; g.build()'` "
@@ -59,12 +60,15 @@ _lib.fp4_gemm_prefill_multi_ws.argtypes = [ctypes.POINTER(_Proj), _I, _P, _I64, 
 _lib.fp4_argmax_rows.argtypes = [_P, _P, _I64, _I64, _I64, _P, _SZ, _P]
 _lib.fp4_lm_head_greedy.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P]
 _lib.fp4_workspace_bytes.argtypes = [_I, _I64, _I64, ctypes.POINTER(_I64), _I, ctypes.POINTER(_SZ)]
+_lib.fp4_quantize_mx.argtypes = [_P, _I64, _I64, _I, _P, _P, _P]
+_lib.fp4_gemv_mx.argtypes = [_P, _P, _P, _I64, _I64, _I64, _P]
+_lib.fp4_gemm_prefill_mx.argtypes = [_P, _P, _P, _I64, _I64, _I64, _P]
 _lib.fp4_gemv_multi_rmsnorm.argtypes = [ctypes.POINTER(_Proj), _I, _P, _P, ctypes.c_float, _I64, _I64, _P, _SZ, _P]
 _lib.fp4_gemv_swiglu.argtypes = [_P, _I64, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P]
 for _f in ("fp4_layout_bytes", "fp4_quantize", "fp4_quantize_fp8", "fp4_retile", "fp4_gemv", "fp4_gemv_ws",
            "fp4_gemv_multi", "fp4_gemv_multi_ws", "fp4_gemm_prefill", "fp4_gemm_prefill_ws", "fp4_gemm_prefill_multi",
            "fp4_gemm_prefill_multi_ws", "fp4_argmax_rows", "fp4_lm_head_greedy", "fp4_workspace_bytes",
-           "fp4_gemv_multi_rmsnorm", "fp4_gemv_swiglu"):
+           "fp4_gemv_multi_rmsnorm", "fp4_gemv_swiglu", "fp4_quantize_mx", "fp4_gemv_mx", "fp4_gemm_prefill_mx"):
     getattr(_lib, _f).restype = _I
 
 
@@ -155,6 +159,62 @@ def quantize(W: torch.Tensor, layout="tiled", out: Optional[NVFP4Weight] = None)
     _check(_lib.fp4_quantize(_dev(W, "W", torch.bfloat16), N, K, lay, _dev(out.packed, "packed", torch.uint8),
                              _opt(out.scales, "scales"), _dev(out.gscale, "gscale", torch.float32),
                              _stream(W.device)), "fp4_quantize")
+    return out
+
+
+@dataclass
+class MXFP4Weight:
+    """MXFP4 weight on the device: E2M1 codes and E8M0 scales per 32 elements
+    (no tensor scale). In the MX tiled layout `packed` holds both and
+    `scales` is None."""
+    packed: torch.Tensor
+    scales: Optional[torch.Tensor]
+    N: int
+    K: int
+    layout: int = MX_TILED
+
+
+def quantize_mx(W: torch.Tensor, layout="mx_tiled", out: Optional[MXFP4Weight] = None) -> MXFP4Weight:
+    """fp4_quantize_mx: bf16 W [N][K] (K % 32 == 0) -> MXFP4Weight in `layout`."""
+    N, K = W.shape
+    lay = _LAYOUTS[layout]
+    if lay not in (MX_ROWMAJOR, MX_TILED):
+        raise ValueError("quantize_mx takes an MX layout")
+    if out is None:
+        pb, sb = layout_bytes(N, K, lay)
+        out = MXFP4Weight(torch.empty(pb, dtype=torch.uint8, device=W.device),
+                          torch.empty(sb, dtype=torch.uint8, device=W.device) if lay == MX_ROWMAJOR else None, N, K, lay)
+    _check(_lib.fp4_quantize_mx(_dev(W, "W", torch.bfloat16), N, K, lay, _dev(out.packed, "packed", torch.uint8),
+                                _opt(out.scales, "scales"), _stream(W.device)), "fp4_quantize_mx")
+    return out
+
+
+def _mx_tiled(w: MXFP4Weight) -> None:
+    if w.layout != MX_TILED:
+        raise ValueError("the MXFP4 products take MX tiled weights (quantize_mx(..., 'mx_tiled'))")
+
+
+def gemv_mx(x: torch.Tensor, w: MXFP4Weight, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp4_gemv_mx: y[M][N] = x @ dequant(w)^T (fp32) for an MXFP4 weight."""
+    x, M, K = _x2d(x)
+    if K != w.K:
+        raise ValueError("x has K=%d, weight has K=%d" % (K, w.K))
+    _mx_tiled(w)
+    out = _out(out, (M, w.N), torch.float32, x.device, "out")
+    _check(_lib.fp4_gemv_mx(_dev(out, "y", torch.float32), _dev(x, "x", torch.bfloat16), _dev(w.packed, "packed"),
+                            M, w.N, K, _stream(x.device)), "fp4_gemv_mx")
+    return out
+
+
+def gemm_prefill_mx(x: torch.Tensor, w: MXFP4Weight, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp4_gemm_prefill_mx: the MXFP4 product on bf16 MFMA for prefill-sized M."""
+    x, M, K = _x2d(x)
+    if K != w.K:
+        raise ValueError("x has K=%d, weight has K=%d" % (K, w.K))
+    _mx_tiled(w)
+    out = _out(out, (M, w.N), torch.float32, x.device, "out")
+    _check(_lib.fp4_gemm_prefill_mx(_dev(out, "y", torch.float32), _dev(x, "x", torch.bfloat16),
+                                    _dev(w.packed, "packed"), M, w.N, K, _stream(x.device)), "fp4_gemm_prefill_mx")
     return out
 
 
@@ -363,5 +423,5 @@ def raw():
 __all__ = ["quantize", "quantize_fp8", "retile", "gemv", "gemv_multi", "gemm_prefill", "gemm_prefill_multi",
            "argmax_rows", "lm_head_greedy", "gemv_multi_rmsnorm", "gemv_swiglu", "layout_bytes", "workspace_bytes",
            "new_workspace", "NVFP4Weight", "OP_GEMV", "OP_GEMM_PREFILL", "OP_ARGMAX_ROWS", "OP_LM_HEAD_GREEDY",
-           "OP_GEMV_RMSNORM", "OP_GEMV_SWIGLU",
+           "OP_GEMV_RMSNORM", "OP_GEMV_SWIGLU", "MXFP4Weight", "quantize_mx", "gemv_mx", "gemm_prefill_mx",
            "Fp4Error", "raw", "ROWMAJOR", "TILED", "LIB_PATH", "HEADER_PATH"]

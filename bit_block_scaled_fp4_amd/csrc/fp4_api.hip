@@ -51,6 +51,15 @@ int fp4_layout_bytes(int64_t N, int64_t K, int layout, size_t* packed_bytes, siz
     const int64_t tiles = fp4::groups_of(N) * fp4::chunks_of(K);
     *packed_bytes = (size_t)(tiles * fp4::kTileBytes);   // codes and scales share each tile
     *scale_bytes = 0;
+  } else if (layout == FP4_LAYOUT_MX_ROWMAJOR || layout == FP4_LAYOUT_MX_TILED) {
+    if (K % 32 != 0) return FP4_ERR_SHAPE;
+    if (layout == FP4_LAYOUT_MX_ROWMAJOR) {
+      *packed_bytes = (size_t)(N * K / 2);
+      *scale_bytes = (size_t)(N * K / 32);
+    } else {
+      *packed_bytes = (size_t)(fp4::groups_of(N) * fp4::chunks_of(K) * fp4::kMxTileBytes);
+      *scale_bytes = 0;
+    }
   } else {
     return FP4_ERR_LAYOUT;
   }
@@ -83,6 +92,17 @@ int fp4_quantize_fp8(const void* W_fp8, const float* w_scale, int64_t N, int64_t
                                              layout == FP4_LAYOUT_TILED, static_cast<uint8_t*>(packed),
                                              static_cast<uint8_t*>(scales), gscale,
                                              static_cast<hipStream_t>(stream)));
+}
+
+int fp4_quantize_mx(const void* W_bf16, int64_t N, int64_t K, int layout, void* packed, void* scales, void* stream) {
+  if (layout != FP4_LAYOUT_MX_ROWMAJOR && layout != FP4_LAYOUT_MX_TILED) return FP4_ERR_LAYOUT;
+  if (!W_bf16 || !packed || (layout == FP4_LAYOUT_MX_ROWMAJOR && !scales)) return FP4_ERR_NULL;
+  if (int st = check_nk(N, K)) return st;
+  if (K % 32 != 0) return FP4_ERR_SHAPE;
+  if (!aligned(W_bf16, 16) || !aligned(packed, 16)) return FP4_ERR_ALIGN;
+  return hip_status(fp4::launch_quantize_mx(static_cast<const uint16_t*>(W_bf16), N, K, layout == FP4_LAYOUT_MX_TILED,
+                                            static_cast<uint8_t*>(packed), static_cast<uint8_t*>(scales),
+                                            static_cast<hipStream_t>(stream)));
 }
 
 int fp4_retile(const void* packed_rm, const void* scales_rm, int64_t N, int64_t K, void* packed_tiled,
@@ -395,6 +415,46 @@ int fp4_gemv_swiglu(void* h_bf16, int64_t ldh, const void* x_bf16, const void* g
   a.h = nullptr;
   if (int st = gemv_run(a, ws.scratch() + 2 * gu, s)) return st;
   return hip_status(fp4::launch_swiglu(g, u, M, N, static_cast<uint16_t*>(h_bf16), ldh, s));
+}
+
+// MXFP4 products: the same argument rules with the MX tiled layout, K % 32
+// == 0 and no tensor scale.
+static int mx_args(float* y, const void* x_bf16, const void* packed, int64_t M, int64_t N, int64_t K,
+                   fp4::GemvArgs& a) {
+  if (!y || !x_bf16 || !packed) return FP4_ERR_NULL;
+  if (int st = check_nk(N, K)) return st;
+  if (K % 32 != 0 || M < 1 || M > kMaxM || M * N > kMaxElems) return FP4_ERR_SHAPE;
+  if (!aligned(x_bf16, 16) || !aligned(packed, 16) || !aligned(y, 4)) return FP4_ERR_ALIGN;
+  a = fp4::GemvArgs{};
+  a.x = static_cast<const uint16_t*>(x_bf16);
+  a.M = (int32_t)M;
+  a.K = (int32_t)K;
+  a.C = (int32_t)fp4::chunks_of(K);
+  a.nproj = 1;
+  a.proj[0].tiles = static_cast<const uint8_t*>(packed);
+  a.proj[0].y = y;
+  a.proj[0].ldy = N;
+  a.proj[0].N = (int32_t)N;
+  a.mx = 1;
+  return FP4_OK;
+}
+
+int fp4_gemv_mx(float* y, const void* x_bf16, const void* packed, int64_t M, int64_t N, int64_t K, void* stream) {
+  fp4::GemvArgs a;
+  if (int st = mx_args(y, x_bf16, packed, M, N, K, a)) return st;
+  return hip_status(fp4::launch_gemv(a, static_cast<hipStream_t>(stream)));
+}
+
+int fp4_gemm_prefill_mx(float* y, const void* x_bf16, const void* packed, int64_t M, int64_t N, int64_t K,
+                        void* stream) {
+  fp4::GemvArgs a;
+  if (int st = mx_args(y, x_bf16, packed, M, N, K, a)) return st;
+  static const float one = 1.0f;   // the descriptor's scale pointer; the MX kernels read none
+  fp4_proj p{packed, nullptr, &one, N, y, N};
+  fp4::PrefillProjDesc d[FP4_MAX_PROJ];
+  if (int st = prefill_args(&p, 1, x_bf16, M, K, d)) return st;
+  return hip_status(fp4::launch_prefill(d, 1, static_cast<const uint16_t*>(x_bf16), M, K, fp4::Workspace{},
+                                        static_cast<hipStream_t>(stream), 0, 0, true));
 }
 
 int fp4_workspace_bytes(int op, int64_t M, int64_t K, const int64_t* Ns, int nproj, size_t* bytes) {

@@ -30,6 +30,15 @@ __host__ __device__ inline int tile_scale_offset(int r, int b) {
   return kTileCodes + (r & 1) * 256 + (b >> 1) * 8 + (r >> 1) * 2 + (b & 1);
 }
 
+// MXFP4 (OCP MX: E8M0 scale per 32 elements, no tensor scale) tiles: the
+// same 8-row x 1024-element codes, then 256 scale bytes; the scale of
+// (row 2i + h of the group, block l of the chunk) at kTileCodes + 128h + 4l +
+// i, so lane 32h + l of a wave finds the scales of its four rows as one
+// 4-byte word at kTileCodes + 4 * lane.
+constexpr int kMxTileScales = 256;
+constexpr int kMxTileBytes = kTileCodes + kMxTileScales;
+__host__ __device__ inline int mx_tile_scale_offset(int r, int l) { return kTileCodes + (r & 1) * 128 + l * 4 + (r >> 1); }
+
 // Caller-owned scratch memory (include/fp4.h, "Workspaces"). The first
 // kWsHeaderBytes hold counters, one per 128-byte line, that are zero before
 // a call and that every kernel using them puts back to zero; the bytes after
@@ -85,6 +94,7 @@ struct GemvArgs {
   // bf16(x[m][k] / sqrt(mean_k x[m][k]^2 + eps) * gain[k]) instead of x
   const uint16_t* gain;
   float eps;
+  int32_t mx;         // MXFP4 tiles (no tensor scale; vector-ALU kernel only)
 };
 
 hipError_t launch_quantize(const uint16_t* W, int64_t N, int64_t K, bool tiled, uint8_t* packed,
@@ -92,6 +102,9 @@ hipError_t launch_quantize(const uint16_t* W, int64_t N, int64_t K, bool tiled, 
 // The same rule for FP8 E4M3 codes times one fp32 scale (*w_scale, device).
 hipError_t launch_quantize_fp8(const uint8_t* W, const float* w_scale, int64_t N, int64_t K, bool tiled,
                                uint8_t* packed, uint8_t* scales, float* gscale, hipStream_t s);
+// MXFP4 quantisation of bf16 W (K % 32 == 0), one pass.
+hipError_t launch_quantize_mx(const uint16_t* W, int64_t N, int64_t K, bool tiled, uint8_t* packed, uint8_t* scales,
+                              hipStream_t s);
 hipError_t launch_retile(const uint8_t* packed, const uint8_t* scales, int64_t N, int64_t K, uint8_t* tiles,
                          hipStream_t s);
 // Vector-ALU product for M <= 4 activation rows (larger M: an error; those
@@ -133,7 +146,7 @@ struct PrefillProjDesc {
 };
 // Without a workspace the last round's tiles are never split.
 hipError_t launch_prefill(const PrefillProjDesc* projs, int nproj, const uint16_t* x, int64_t M, int64_t K,
-                          const Workspace& ws, hipStream_t s, int bn = 0, int splits = 0);
+                          const Workspace& ws, hipStream_t s, int bn = 0, int splits = 0, bool mx = false);   // mx: MXFP4 tiles
 // Workspace bytes a split of the last round's tiles needs (upper bound over
 // tile widths and splits; 0 when no split can happen).
 size_t prefill_ws_bytes(const PrefillProjDesc* projs, int nproj, int64_t M, int64_t K);

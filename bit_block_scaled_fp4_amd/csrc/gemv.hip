@@ -94,6 +94,13 @@ __device__ __forceinline__ bf16x2_t fp4x2(uint32_t w, int sel) {
   }
 }
 
+// E8M0 (OCP MX) byte `sel` of w -> fp32: 2^(c - 127) (code 0: 2^-127, an
+// fp32 subnormal; 255: NaN).
+__device__ __forceinline__ float e8m0(uint32_t w, int sel) {
+  const uint32_t c = (w >> (8 * sel)) & 0xFFu;
+  return c == 0u ? __uint_as_float(0x00400000u) : c == 255u ? __uint_as_float(0x7FC00000u) : __uint_as_float(c << 23);
+}
+
 // E4M3 (OCP) byte `sel` of w -> fp32.
 __device__ __forceinline__ float e4m3(uint32_t w, int sel) {
   switch (sel) {
@@ -197,9 +204,12 @@ __device__ __forceinline__ void row_rms(const GemvArgs& a, int m0, float* rinv, 
 // up) instead of y. kRms (M <= MT): every workgroup first computes each
 // row's 1 / sqrt(mean(x^2) + eps) and the products read bf16(x * that *
 // gain). Each mode is its own instantiation, so the plain product keeps its
-// registers.
-template <int MT, int MODE>
+// registers. MX (kPlain only): MXFP4 tiles (kMxTileBytes; one E8M0 scale per
+// 32-element piece, the four of a lane's rows in one word at kTileCodes +
+// 4 * lane; no tensor scale).
+template <int MT, int MODE, bool MX = false>
 __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv(const GemvArgs a) {
+  constexpr int TB = MX ? kMxTileBytes : kTileBytes;
   __shared__ float part[kMaxWaves][MT][8];
   __shared__ uint64_t red[MODE == kGreedy ? kMaxWaves * MT : 1];
   __shared__ float rinv[MODE == kRms ? MT : 1];
@@ -226,7 +236,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv(const GemvArgs a) {
   const int N = pd.N, G = (N + 7) >> 3;
   const int g = ((int)blockIdx.x - pd.wg_begin) * Gw + gi;
   const bool gvalid = g < G;
-  const float gs = *pd.gscale;
+  const float gs = MX ? 1.0f : *pd.gscale;
 
   for (int m0 = 0; m0 < M; m0 += MT) {
     if (MODE == kRms) row_rms<MT>(a, m0, rinv, &part[0][0][0]);
@@ -240,11 +250,15 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv(const GemvArgs a) {
       Round<MT> f;
       {
         const bool v = gvalid;
-        const __amdgpu_buffer_rsrc_t r = rsrc(pd.tiles + (v ? ((int64_t)g * C + c) * kTileBytes : 0), v ? kTileBytes : 0);
+        const __amdgpu_buffer_rsrc_t r = rsrc(pd.tiles + (v ? ((int64_t)g * C + c) * TB : 0), v ? TB : 0);
 #pragma unroll
         for (int q = 0; q < 4; ++q) f.w[q] = ld16<2>(r, q * 1024 + lane * 16);
-        const u32x2_t sv = __builtin_amdgcn_raw_buffer_load_b64(r, kTileCodes + lane * 8, 0, 0);
-        f.s = make_uint2(sv[0], sv[1]);
+        if (MX) {
+          f.s = make_uint2(__builtin_amdgcn_raw_buffer_load_b32(r, kTileCodes + lane * 4, 0, 0), 0u);
+        } else {
+          const u32x2_t sv = __builtin_amdgcn_raw_buffer_load_b64(r, kTileCodes + lane * 8, 0, 0);
+          f.s = make_uint2(sv[0], sv[1]);
+        }
       }
       const int off = (c * kChunkK + hl * 32) * 2;   // past K (ragged last chunk): zeros
 #pragma unroll
@@ -270,9 +284,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv(const GemvArgs a) {
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        // row 2i + h: its two block scales are bytes 2(i&1), 2(i&1)+1 of word i >> 1
+        // row 2i + h: NVFP4, its two block scales are bytes 2(i&1), 2(i&1)+1
+        // of word i >> 1; MXFP4, its one block scale is byte i
         const uint32_t sw = i < 2 ? f.s.x : f.s.y;
-        const float s0 = e4m3(sw, (i & 1) * 2), s1 = e4m3(sw, (i & 1) * 2 + 1);
+        const float s0 = MX ? e8m0(f.s.x, i) : e4m3(sw, (i & 1) * 2);
+        const float s1 = MX ? s0 : e4m3(sw, (i & 1) * 2 + 1);
         bf16x2_t d[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) d[e] = fp4x2(word(f.w[i], e >> 2), e & 3);
@@ -389,7 +405,9 @@ static hipError_t launch_mt(GemvArgs a, hipStream_t s, int gw, int wc) {
   const int64_t wgs = plan_mt<MT>(a, gw, wc);
   a.greedy.S = (int32_t)wgs;
   const dim3 grid((unsigned)wgs), block(64 * a.gw * a.wc);
-  if (a.greedy.idx)
+  if (a.mx)
+    hipLaunchKernelGGL((k_gemv<MT, kPlain, true>), grid, block, 0, s, a);
+  else if (a.greedy.idx)
     hipLaunchKernelGGL((k_gemv<MT, kGreedy>), grid, block, 0, s, a);
   else if (a.gain)
     hipLaunchKernelGGL((k_gemv<MT, kRms>), grid, block, 0, s, a);
@@ -431,8 +449,8 @@ int64_t gemv_workgroups(const GemvArgs& a) {
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t s, int gw, int wc) {
   if (a.M == 1) return launch_mt<1>(a, s, gw, wc);
   if (a.M == 2) return launch_mt<2>(a, s, gw, wc);
-  if (a.M <= 4) return launch_mt<4>(a, s, gw, wc);
-  return hipErrorInvalidValue;   // more rows go to the matrix-core kernel
+  if (a.M <= 4 || a.mx) return launch_mt<4>(a, s, gw, wc);   // MXFP4: passes of 4 rows
+  return hipErrorInvalidValue;   // more NVFP4 rows go to the matrix-core kernel
 }
 
 }  // namespace fp4

@@ -74,10 +74,13 @@ constexpr int BM = 256, BK = 64;
 constexpr int kWin = 4;                  // steps per weight window (256 K = 8 pieces of a row)
 constexpr int kAStage = BM * BK * 2;     // 32 KB of activations per stage
 
-template <int BN>
+// MX: MXFP4 tiles, whose window holds 64 scale bytes per 8-row group (one
+// E8M0 per piece) instead of 128, moved 16 groups per DMA instruction (the
+// stage rounded up to whole instructions).
+template <int BN, bool MX = false>
 struct Lds {
   static constexpr int kBStage = BN * 128;        // codes of one window
-  static constexpr int kSStage = BN / 8 * 128;    // scale bytes of one window
+  static constexpr int kSStage = MX ? (BN / 8 + 15) / 16 * 1024 : BN / 8 * 128;   // scale bytes of one window
   static constexpr int kA = 0, kB = 2 * kAStage, kS = kB + 2 * kBStage;
   static constexpr int kBytes = kS + 2 * kSStage;
 };
@@ -133,10 +136,18 @@ __device__ __forceinline__ uint32_t dec2(uint32_t w, int sel, float s) {
 }
 
 // Eight codes (word `slice` of a 16-byte piece) as a bf16x8 MFMA operand;
-// `sc` holds the piece's two block scales (slices 0, 1 use byte 0, slices
-// 2, 3 byte 1).
+// `sc` holds the piece's two E4M3 block scales (slices 0, 1 use byte 0,
+// slices 2, 3 byte 1) or, MX, its one E8M0 scale (byte 0; e2m1 * 2^(c-127)
+// is exact in bf16 for the scales a quantiser produces from bf16 weights).
+template <bool MX>
 __device__ __forceinline__ bf16x8_t decode8(const uint4& piece, uint32_t sc, int slice) {
-  const float s = slice < 2 ? __builtin_amdgcn_cvt_f32_fp8((int)sc, 0) : __builtin_amdgcn_cvt_f32_fp8((int)sc, 1);
+  float s;
+  if (MX) {
+    const uint32_t c = sc & 0xFFu;
+    s = c == 0u ? __uint_as_float(0x00400000u) : c == 255u ? __uint_as_float(0x7FC00000u) : __uint_as_float(c << 23);
+  } else {
+    s = slice < 2 ? __builtin_amdgcn_cvt_f32_fp8((int)sc, 0) : __builtin_amdgcn_cvt_f32_fp8((int)sc, 1);
+  }
   const uint32_t w = word(piece, slice);
   const uint4 o = make_uint4(dec2(w, 0, s), dec2(w, 1, s), dec2(w, 2, s), dec2(w, 3, s));
   return __builtin_bit_cast(bf16x8_t, o);
@@ -200,8 +211,9 @@ constexpr int kPartFloats = BM * BN;
 // SPLIT = false: workgroup b takes whole tile b' (XCD-contiguous order) of
 // the first dp_tiles; SPLIT = true: workgroup b takes K range b % S of tile
 // dp_tiles + b / S.
-template <int BN, bool SPLIT>
+template <int BN, bool SPLIT, bool MX = false>
 __global__ __launch_bounds__(256, 1) void k_prefill(const PrefillArgs a) {
+  constexpr int TB = MX ? kMxTileBytes : kTileBytes;
   // wave grid: WM x WN waves, each owning 256 / WM rows (MI 32-row MFMA
   // tiles) x BN / WN columns (NJ 32-column tiles); 1 x 4 where BN / 4 is a
   // multiple of 32, so each decoded weight operand feeds 8 MFMAs
@@ -210,8 +222,8 @@ __global__ __launch_bounds__(256, 1) void k_prefill(const PrefillArgs a) {
   constexpr int NJ = BN / (32 * WN);   // 32-column MFMA tiles per wave
   constexpr int NG = BN / 8;           // 8-row weight groups per tile
   constexpr int NBI = NG / 4;          // code DMA instructions per wave per window
-  constexpr int NSW = NG / 8;          // waves issuing one scale DMA per window
-  using L = Lds<BN>;
+  constexpr int NSW = MX ? (NG + 15) / 16 : NG / 8;   // waves issuing one scale DMA per window
+  using L = Lds<BN, MX>;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   __shared__ int last_piece;
   const int id = blockIdx.x, S = a.splits;
@@ -251,7 +263,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill(const PrefillArgs a) {
   const int mrows = min(BM, M - m0);
   const int ngroups = min(NG, G - (n0 >> 3));
   const i32x4_t rx = rsrc4(x + (int64_t)m0 * K, (uint32_t)(mrows * K * 2));
-  const i32x4_t rw = rsrc4(tiles + (int64_t)(n0 >> 3) * C * kTileBytes, (uint32_t)(ngroups * C * kTileBytes));
+  const i32x4_t rw = rsrc4(tiles + (int64_t)(n0 >> 3) * C * TB, (uint32_t)(ngroups * C * TB));
   const i32x4_t rnull = rsrc4(x, 0);
 
   // DMA lane roles. One instruction fills 8 LDS rows of 128 bytes: lane ->
@@ -287,20 +299,28 @@ __global__ __launch_bounds__(256, 1) void k_prefill(const PrefillArgs a) {
     for (int i = i0; i < i1; ++i) {
       const int g = NBI * wave + i;
       const int piece = ds ^ dr ^ (g & 1);
-      const uint32_t off = (uint32_t)((g * C + c) * kTileBytes + dr * 512 + (p0 + piece) * 16);
+      const uint32_t off = (uint32_t)((g * C + c) * TB + dr * 512 + (p0 + piece) * 16);
       dma16(rs, off, lds + g * 1024);
     }
   };
   // scales: wave w < NSW fills groups 8w .. 8w + 7, 128 bytes each: half
-  // (lane / 4) % 2 of the tile's scale area, 64 bytes from piece p0 on
+  // (lane / 4) % 2 of the tile's scale area, 64 bytes from piece p0 on.
+  // MX: groups 16w .. 16w + 15, 64 bytes each: lane / 4 picks the group,
+  // (lane / 2) % 2 the row parity h, lane % 2 which 16 of the 32 bytes of
+  // pieces p0 .. p0 + 7 (their four rows' scales, 4 bytes per piece).
   auto dma_s = [&](int win) {
     if (wave >= NSW) return;
     const bool live = win * kWin < kt1;
     const i32x4_t& rs = live ? rw : rnull;
     const int c = win >> 2, p0 = (win & 3) * 8;
-    const int g = 8 * wave + dr;
-    const uint32_t off = (uint32_t)((g * C + c) * kTileBytes + kTileCodes + ((lane >> 2) & 1) * 256 + p0 * 8 +
-                                    (lane & 3) * 16);
+    uint32_t off;
+    if (MX) {
+      const int g = 16 * wave + (lane >> 2);
+      off = (uint32_t)((g * C + c) * TB + kTileCodes + ((lane >> 1) & 1) * 128 + p0 * 4 + (lane & 1) * 16);
+    } else {
+      const int g = 8 * wave + dr;
+      off = (uint32_t)((g * C + c) * TB + kTileCodes + ((lane >> 2) & 1) * 256 + p0 * 8 + (lane & 3) * 16);
+    }
     dma16(rs, off, sbase + L::kS + (win & 1) * L::kSStage + wave * 1024);
   };
 
@@ -322,12 +342,15 @@ __global__ __launch_bounds__(256, 1) void k_prefill(const PrefillArgs a) {
     for (int j = 0; j < NJ; ++j) {
       const int n = wn * (BN / WN) + j * 32 + l32;
       p.w[j] = *reinterpret_cast<const uint4*>(Bs + n * 128 + ((q ^ swz(n)) * 16));
-      p.sc[j] = *reinterpret_cast<const uint16_t*>(Ss + (n >> 3) * 128 + (n & 1) * 64 + q * 8 + ((n & 7) >> 1) * 2);
+      if (MX)
+        p.sc[j] = Ss[(n >> 3) * 64 + (n & 1) * 32 + q * 4 + ((n & 7) >> 1)];
+      else
+        p.sc[j] = *reinterpret_cast<const uint16_t*>(Ss + (n >> 3) * 128 + (n & 1) * 64 + q * 8 + ((n & 7) >> 1) * 2);
     }
   };
   auto decode_b = [&](const Pieces<NJ>& p, int s, Frags<MI, NJ>& f) {
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) f.b[j] = decode8(p.w[j], p.sc[j], s);
+    for (int j = 0; j < NJ; ++j) f.b[j] = decode8<MX>(p.w[j], p.sc[j], s);
   };
 
   f32x16_t acc[MI][NJ];
@@ -436,7 +459,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill(const PrefillArgs a) {
     if (!last_piece) return;
     // y = gscale * (sum of the S partials in piece order), 4 rows of one
     // column per float4 (rows r0 + 8q .. + 3 of element group q)
-    const float gs = *pj.gscale;
+    const float gs = MX ? 1.0f : *pj.gscale;
     const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(pj.y + (int64_t)m0 * ldy, (short)0,
                                                                          (int)((int64_t)(mrows - 1) * ldy + N) * 4,
                                                                          kRsrcWord3);
@@ -465,7 +488,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill(const PrefillArgs a) {
   // epilogue: lane l of a 32x32 tile holds column l % 32 and rows
   // 8(e/4) + 4(l/32) + e%4 (e < 16). Buffer stores drop rows past M (past
   // the resource) and columns past N (bit 31 set in the offset).
-  const float gs = *pj.gscale;
+  const float gs = MX ? 1.0f : *pj.gscale;
   const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(pj.y + (int64_t)m0 * ldy, (short)0,
                                                                        (int)((int64_t)(mrows - 1) * ldy + N) * 4,
                                                                        kRsrcWord3);
@@ -555,9 +578,10 @@ static PrefillPlan plan_prefill(const PrefillProjDesc* projs, int nproj, int64_t
   return pl;
 }
 
-template <int BN>
+template <int BN, bool MX>
 static hipError_t launch_bn(PrefillArgs a, const PrefillProjDesc* projs, const PrefillPlan& pl, const Workspace& ws,
                             hipStream_t s) {
+  using L = Lds<BN, MX>;
   // more than 64 KB of dynamic LDS must be allowed once per kernel and device
   constexpr int kMaxDevices = 64;
   static std::atomic<bool> attr_set[kMaxDevices];
@@ -566,11 +590,11 @@ static hipError_t launch_bn(PrefillArgs a, const PrefillProjDesc* projs, const P
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   if (!attr_set[dev].load(std::memory_order_acquire)) {   // racing first calls set the same value
-    e = hipFuncSetAttribute((const void*)k_prefill<BN, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            Lds<BN>::kBytes);
+    e = hipFuncSetAttribute((const void*)k_prefill<BN, false, MX>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            L::kBytes);
     if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)k_prefill<BN, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              Lds<BN>::kBytes);
+      e = hipFuncSetAttribute((const void*)k_prefill<BN, true, MX>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              L::kBytes);
     if (e != hipSuccess) return e;
     attr_set[dev].store(true, std::memory_order_release);
   }
@@ -595,12 +619,12 @@ static hipError_t launch_bn(PrefillArgs a, const PrefillProjDesc* projs, const P
   // whole tiles, then the K pieces of the rest (a second launch: the split
   // epilogue in the same kernel would cost the whole-tile path registers)
   if (a.dp_tiles > 0) {
-    hipLaunchKernelGGL((k_prefill<BN, false>), dim3((unsigned)(8 * a.per_xcd)), dim3(256), Lds<BN>::kBytes, s, a);
+    hipLaunchKernelGGL((k_prefill<BN, false, MX>), dim3((unsigned)(8 * a.per_xcd)), dim3(256), L::kBytes, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (tail > 0) {
-    hipLaunchKernelGGL((k_prefill<BN, true>), dim3((unsigned)(tail * pl.S)), dim3(256), Lds<BN>::kBytes, s, a);
+    hipLaunchKernelGGL((k_prefill<BN, true, MX>), dim3((unsigned)(tail * pl.S)), dim3(256), L::kBytes, s, a);
     e = hipGetLastError();
   }
   return e;
@@ -613,7 +637,7 @@ size_t prefill_ws_bytes(const PrefillProjDesc* projs, int nproj, int64_t M, int6
 }
 
 hipError_t launch_prefill(const PrefillProjDesc* projs, int nproj, const uint16_t* x, int64_t M, int64_t K,
-                          const Workspace& ws, hipStream_t s, int bn, int splits) {
+                          const Workspace& ws, hipStream_t s, int bn, int splits, bool mx) {
   if (nproj < 1 || nproj > kMaxProj) return hipErrorInvalidValue;
   // buffer offsets are 32-bit: one 256-row slab of activations, of outputs
   // and of weights must each stay below 2 GB
@@ -639,10 +663,18 @@ hipError_t launch_prefill(const PrefillProjDesc* projs, int nproj, const uint16_
     pl.S = 1;   // the workspace is too small for this split (tuning calls only: the API checks the size)
     pl.tail = 0;
   }
+  if (mx) {
+    switch (pl.bn) {
+      case 128: return launch_bn<128, true>(a, projs, pl, ws, s);
+      case 192: return launch_bn<192, true>(a, projs, pl, ws, s);
+      case 256: return launch_bn<256, true>(a, projs, pl, ws, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (pl.bn) {
-    case 128: return launch_bn<128>(a, projs, pl, ws, s);
-    case 192: return launch_bn<192>(a, projs, pl, ws, s);
-    case 256: return launch_bn<256>(a, projs, pl, ws, s);
+    case 128: return launch_bn<128, false>(a, projs, pl, ws, s);
+    case 192: return launch_bn<192, false>(a, projs, pl, ws, s);
+    case 256: return launch_bn<256, false>(a, projs, pl, ws, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -203,6 +203,69 @@ __global__ __launch_bounds__(256) void k_encode(const Src src, int64_t N, int64_
   }
 }
 
+// MXFP4 (OCP MX v1.0): one thread per 32-element block, one pass (no tensor
+// scale). Shared exponent floor(log2(amax)) - 2 clamped to [-127, 127]: the
+// bf16 magnitude's exponent field gives floor(log2) directly (a subnormal
+// amax is below 2^-126, so its block clamps to -127). The elements are
+// multiplied by 2^-shared (exact: a power of two, and |w| 2^-shared < 8)
+// and rounded to E2M1 as in k_encode. A block with amax 0 keeps scale 0 and
+// codes 0. Tiled layout: rows and blocks over the padded space; the tile is
+// kMxTileBytes with the scale of (row 2i + h, block l) at
+// kTileCodes + 128h + 4l + i.
+// grid: rows * segs workgroups, segs = ceil(bpr / 256); block 256.
+__global__ __launch_bounds__(256) void k_mx_encode(const uint16_t* __restrict__ W, int64_t N, int64_t K, int tiled,
+                                                   uint8_t* __restrict__ packed, uint8_t* __restrict__ scales) {
+  const int64_t kb = K / 32;                          // blocks per row
+  const int64_t C = chunks_of(K);
+  const int64_t bpr = tiled ? C * 32 : kb;            // blocks per (padded) row
+  const uint32_t segs = (uint32_t)((bpr + 255) / 256);
+  const uint32_t wg = blockIdx.x;
+  const int64_t n = wg / segs;
+  const int64_t b = (int64_t)(wg - (uint32_t)n * segs) * 256 + threadIdx.x;
+  if (b >= bpr) return;
+
+  uint32_t sc = 0, q[4] = {0u, 0u, 0u, 0u};
+  if (n < N && b < kb) {
+    const uint4* src = reinterpret_cast<const uint4*>(W + n * K + b * 32);
+    uint32_t d[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 v = src[i];
+      d[4 * i] = v.x;
+      d[4 * i + 1] = v.y;
+      d[4 * i + 2] = v.z;
+      d[4 * i + 3] = v.w;
+    }
+    uint32_t bm = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) bm = max(bm, max(d[j] & 0x7FFFu, (d[j] >> 16) & 0x7FFFu));
+    if (bm != 0u) {
+      const int ef = (int)(bm >> 7);                 // exponent field of the bf16 amax
+      const int shared = max(-127, min(127, (ef == 0 ? -127 : ef - 127) - 2));
+      sc = (uint32_t)(shared + 127);
+      const float inv = __uint_as_float((uint32_t)(127 - shared) << 23);   // 2^-shared
+      float v[32];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        v[2 * j] = bf16_bits_to_float(d[j] & 0xFFFFu) * inv;
+        v[2 * j + 1] = bf16_bits_to_float(d[j] >> 16) * inv;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q[i] = e2m1_codes8(v + 8 * i);
+    }
+  }
+  if (!tiled) {
+    *reinterpret_cast<uint4*>(packed + n * (K / 2) + b * 16) = make_uint4(q[0], q[1], q[2], q[3]);
+    scales[n * kb + b] = (uint8_t)sc;
+  } else {
+    const int64_t g = n / kGroupRows, r = n % kGroupRows;
+    const int64_t c = b / 32, l = b % 32;
+    uint8_t* tile = packed + (g * C + c) * kMxTileBytes;
+    *reinterpret_cast<uint4*>(tile + r * 512 + l * 16) = make_uint4(q[0], q[1], q[2], q[3]);
+    tile[mx_tile_scale_offset((int)r, (int)l)] = (uint8_t)sc;
+  }
+}
+
 template <class Src>
 __global__ void k_finalize(const Src src, uint32_t* slot) {
   const float amax = src.amax(*slot);
@@ -280,6 +343,16 @@ hipError_t launch_quantize(const uint16_t* W, int64_t N, int64_t K, bool tiled, 
 hipError_t launch_quantize_fp8(const uint8_t* W, const float* w_scale, int64_t N, int64_t K, bool tiled,
                                uint8_t* packed, uint8_t* scales, float* gscale, hipStream_t s) {
   return launch_quantize_src(SrcFp8{W, w_scale}, W, N, K, tiled, packed, scales, gscale, s);
+}
+
+hipError_t launch_quantize_mx(const uint16_t* W, int64_t N, int64_t K, bool tiled, uint8_t* packed, uint8_t* scales,
+                              hipStream_t s) {
+  const int64_t rows = tiled ? groups_of(N) * kGroupRows : N;
+  const int64_t bpr = tiled ? chunks_of(K) * 32 : K / 32;
+  const int64_t wgs = rows * ((bpr + 255) / 256);
+  if (wgs > UINT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_mx_encode, dim3((unsigned)wgs), dim3(256), 0, s, W, N, K, tiled ? 1 : 0, packed, scales);
+  return hipGetLastError();
 }
 
 hipError_t launch_retile(const uint8_t* packed, const uint8_t* scales, int64_t N, int64_t K, uint8_t* tiles,

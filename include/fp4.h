@@ -103,14 +103,20 @@ typedef enum {
     FP4_ERR_WORKSPACE = -7    /* workspace smaller than fp4_workspace_bytes reports */
 } fp4_status;
 
-typedef enum { FP4_LAYOUT_ROWMAJOR = 0, FP4_LAYOUT_TILED = 1 } fp4_layout;
+typedef enum {
+    FP4_LAYOUT_ROWMAJOR = 0,     /* NVFP4, canonical */
+    FP4_LAYOUT_TILED = 1,        /* NVFP4, device tiles */
+    FP4_LAYOUT_MX_ROWMAJOR = 2,  /* MXFP4, canonical: packed [N][K/2], E8M0 scales [N][K/32] */
+    FP4_LAYOUT_MX_TILED = 3      /* MXFP4, device tiles of 4352 bytes (below) */
+} fp4_layout;
 
 /* Human-readable text for a status code (static storage, never NULL). */
 FP4_API const char *fp4_status_string(int status);
 
 /* Bytes of the packed and scale arrays for an N x K weight in `layout`.
  * ROWMAJOR: N*K/2 and N*K/16. TILED: G*C*4608 and 0 (the scales live in
- * the tiles, see above). Host-only; enqueues nothing. */
+ * the tiles, see above). MX_ROWMAJOR: N*K/2 and N*K/32; MX_TILED: G*C*4352
+ * and 0 (both need K % 32 == 0). Host-only; enqueues nothing. */
 FP4_API int fp4_layout_bytes(int64_t N, int64_t K, int layout, size_t *packed_bytes, size_t *scale_bytes);
 
 /* Quantise a bf16 weight W [N][K] (device) to NVFP4 in `layout`, writing
@@ -129,6 +135,33 @@ FP4_API int fp4_layout_bytes(int64_t N, int64_t K, int layout, size_t *packed_by
  * every weight once, on the GPU.) */
 FP4_API int fp4_quantize(const void *W_bf16, int64_t N, int64_t K, int layout, void *packed, void *scales,
                  float *gscale, void *stream);
+
+/* MXFP4, the other block-scaled four-bit format in the imp README's
+ * quantisation row, read as OCP Microscaling v1.0: the same E2M1 elements,
+ * one E8M0 scale (an exponent, value 2^(c - 127)) per 32 consecutive
+ * K-elements, no tensor scale. Quantise bf16 W [N][K] (K % 32 == 0) in one
+ * pass: per block the shared exponent floor(log2(amax)) - 2 clamped to
+ * [-127, 127], stored as code shared + 127; element code = E2M1 nearest-even
+ * of w / 2^shared, saturating at 6, sign from the sign bit; a block with
+ * amax 0 gets scale 0 and codes 0. layout MX_ROWMAJOR writes packed and
+ * scales; MX_TILED writes the tiles into `packed` (scales unused): rows in
+ * groups of 8, K in chunks of 1024, tile (g, c) the 4352 bytes at
+ * (g*C + c)*4352, codes as in the NVFP4 tile, then byte 4096 + h*128 + l*4 + i
+ * = scale of (row 8g + 2i + h, block 32c + l). The bytes are unique. */
+FP4_API int fp4_quantize_mx(const void *W_bf16, int64_t N, int64_t K, int layout, void *packed, void *scales,
+                            void *stream);
+
+/* y[M][N] = x * dequant(W)^T for MX_TILED weights W (dequant = E2M1 *
+ * E8M0), fp32 accumulation, y overwritten. Every M runs on the vector-ALU
+ * kernel (more than 4 rows in passes of 4 inside one launch). */
+FP4_API int fp4_gemv_mx(float *y, const void *x_bf16, const void *packed, int64_t M, int64_t N, int64_t K,
+                        void *stream);
+
+/* The same product on the matrix cores for prefill-sized M (the prefill
+ * kernel of fp4_gemm_prefill reading MX tiles: E2M1 * 2^(c - 127) decoded
+ * exactly to bf16 MFMA operands). No K split of the last round of tiles. */
+FP4_API int fp4_gemm_prefill_mx(float *y, const void *x_bf16, const void *packed, int64_t M, int64_t N, int64_t K,
+                                void *stream);
 
 /* The same quantisation for a checkpoint released in FP8 (the imp README:
  * its quantiser builds NVFP4 weights from BF16 or FP8 releases). W_fp8 is

@@ -24,7 +24,8 @@ def test_every_declared_symbol_is_exported():
                             "fp4_gemv_ws", "fp4_gemv_multi", "fp4_gemv_multi_ws", "fp4_gemm_prefill",
                             "fp4_gemm_prefill_ws", "fp4_gemm_prefill_multi", "fp4_gemm_prefill_multi_ws",
                             "fp4_argmax_rows", "fp4_lm_head_greedy", "fp4_quantize_fp8", "fp4_workspace_bytes",
-                            "fp4_gemv_multi_noalloc", "fp4_gemv_multi_rmsnorm", "fp4_gemv_swiglu"])
+                            "fp4_gemv_multi_noalloc", "fp4_gemv_multi_rmsnorm", "fp4_gemv_swiglu",
+                            "fp4_quantize_mx", "fp4_gemv_mx", "fp4_gemm_prefill_mx"])
     lib = ctypes.CDLL(fp4.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -245,3 +246,24 @@ def test_rmsnorm_and_swiglu_argument_errors():
     need = fp4.workspace_bytes(fp4.OP_GEMV_SWIGLU, 8, 5120, [17408])
     assert need >= 65536 + 2 * 8 * 17408 * 4
     assert L.fp4_gemv_swiglu(A, 17408, A, A, A, A, A, 8, 17408, 5120, None, 0, None) == EWS
+
+
+def test_mx_layout_bytes_and_argument_errors():
+    assert fp4.layout_bytes(1024, 1024, "mx_rowmajor") == (1024 * 512, 1024 * 32)
+    assert fp4.layout_bytes(1024, 1024, "mx_tiled") == (128 * 4352, 0)
+    assert fp4.layout_bytes(11, 1056, "mx_tiled") == (2 * 2 * 4352, 0)
+    with pytest.raises(fp4.Fp4Error) as e:
+        fp4.layout_bytes(8, 48, "mx_tiled")                      # K % 32 != 0
+    assert e.value.status == ESHAPE
+    L = fp4.raw()
+    assert L.fp4_quantize_mx(A, 8, 64, 1, A, A, None) == ELAYOUT     # an NVFP4 layout
+    assert L.fp4_quantize_mx(None, 8, 64, 3, A, None, None) == ENULL
+    assert L.fp4_quantize_mx(A, 8, 64, 2, A, None, None) == ENULL     # row-major needs the scale array
+    assert L.fp4_quantize_mx(A, 8, 48, 3, A, None, None) == ESHAPE
+    assert L.fp4_quantize_mx(A + 8, 8, 64, 3, A, None, None) == EALIGN
+    assert L.fp4_gemv_mx(None, A, A, 1, 8, 64, None) == ENULL
+    assert L.fp4_gemv_mx(A, A, A, 1, 8, 48, None) == ESHAPE
+    assert L.fp4_gemv_mx(A, A, A, 0, 8, 64, None) == ESHAPE
+    assert L.fp4_gemv_mx(A, A + 8, A, 1, 8, 64, None) == EALIGN
+    assert L.fp4_gemm_prefill_mx(A, A, None, 4, 8, 64, None) == ENULL
+    assert L.fp4_gemm_prefill_mx(A, A, A, 4, 8, 1 << 22, None) == ESHAPE

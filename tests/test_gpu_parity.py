@@ -898,3 +898,112 @@ def test_gemv_swiglu(case, M):
     err = np.abs(hg - href)
     assert np.all(err <= bound), "worst %.3g" % float((err / bound).max())
     assert not np.all(np.abs(hg - oracle.swiglu(u, g)) <= swiglu_bound(u, g, l1u, l1g, oracle.swiglu(u, g)))
+
+
+# ------------------------------------------------------------------- MXFP4
+_mx_cache = {}
+
+
+def mx_oracle_quant(wl, name):
+    key = (wl, name)
+    if key not in _mx_cache:
+        _mx_cache[key] = oracle.mx_quantize(weight_bits(wl, name))
+    return _mx_cache[key]
+
+
+def mx_edge_tensors():
+    from test_oracle_pins import load_mx_example
+    rng = np.random.default_rng(61)
+    out = {"worked_example": load_mx_example()[0]}
+    out["zeros"] = np.zeros((9, 64), np.uint16)
+    out["ragged_13x1056"] = bf16_tensor((13, 1056), 62, 0.02, outlier_p=0.01, outlier_scale=20)
+    out["tiny"] = float32_to_bf16_bits(rng.normal(0, 1e-30, (16, 64)).astype(np.float32))
+    out["huge"] = float32_to_bf16_bits(rng.normal(0, 1e30, (16, 64)).astype(np.float32))
+    wide = rng.normal(0, 1, (32, 256)) * np.exp(rng.uniform(-40, 40, (32, 256)))
+    out["wide_dynamic_range"] = float32_to_bf16_bits(wide.astype(np.float32))
+    return out
+
+
+def check_mx_bytes(bits, what):
+    p, s = oracle.mx_quantize(bits)
+    w = fp4.quantize_mx(to_gpu_bf16(bits), "mx_rowmajor")
+    wt = fp4.quantize_mx(to_gpu_bf16(bits), "mx_tiled")
+    torch.cuda.synchronize()
+    gp, gs = gpu_u8(w.packed).reshape(p.shape), gpu_u8(w.scales).reshape(s.shape)
+    assert np.array_equal(gs, s), (what, np.flatnonzero(gs != s)[:8])
+    assert np.array_equal(gp, p), (what, np.flatnonzero(gp != p)[:8])
+    assert np.array_equal(gpu_u8(wt.packed), oracle.mx_tile(p, s)), what
+    return p, s
+
+
+@pytest.mark.parametrize("name", list(mx_edge_tensors().keys()))
+def test_mx_quantize_bit_exact_edge_cases(name):
+    check_mx_bytes(mx_edge_tensors()[name], name)
+
+
+@pytest.mark.parametrize("wl,t", [("dense27b_layer", "gate"), ("dense27b_layer", "down"), ("lm_head", "w")])
+def test_mx_quantize_bit_exact_workloads(wl, t):
+    print("mx quantize", wl, t, flush=True)
+    bits = weight_bits(wl, t)
+    p, s = mx_oracle_quant(wl, t)
+    w = fp4.quantize_mx(to_gpu_bf16(bits), "mx_rowmajor")
+    wt = fp4.quantize_mx(to_gpu_bf16(bits), "mx_tiled")
+    torch.cuda.synchronize()
+    assert np.array_equal(gpu_u8(w.scales).reshape(s.shape), s)
+    assert np.array_equal(gpu_u8(w.packed).reshape(p.shape), p)
+    assert np.array_equal(gpu_u8(wt.packed), oracle.mx_tile(p, s))
+
+
+@pytest.mark.parametrize("N,K,M", [(8, 32, 1), (13, 1056, 1), (40, 2080, 3), (333, 3072, 5), (1000, 1024, 9),
+                                   (77, 17408 + 32, 2)])
+def test_mx_gemv_small_shapes(N, K, M):
+    bw = bf16_tensor((N, K), 6000 + N + K, 0.02, outlier_p=0.002, outlier_scale=20.0)
+    bx = bf16_tensor((M, K), 6100 + M, 1.0)
+    w = fp4.quantize_mx(to_gpu_bf16(bw), "mx_tiled")
+    y = fp4.gemv_mx(to_gpu_bf16(bx), w)
+    torch.cuda.synchronize()
+    p, s = oracle.mx_quantize(bw)
+    yr, l1 = oracle.mx_gemv(bx, p, s)
+    assert_within_tolerance(y.cpu().numpy(), yr, l1, "mx gemv %d %d %d" % (N, K, M))
+
+
+@pytest.mark.parametrize("wl,t,xname", [("dense27b_layer", "gate", "x_in"), ("dense27b_layer", "down", "x_mid"),
+                                        ("lm_head", "w", "x_m1"), ("lm_head", "w", "x_m8")])
+def test_mx_gemv_workloads(wl, t, xname):
+    """The 27B-class layer's projections at M = 1 and the LM head at M = 1
+    and 8, MXFP4-quantised from the same bf16 weights."""
+    print("mx gemv", wl, t, xname, flush=True)
+    bx = act_bits(wl, xname)
+    w = fp4.quantize_mx(to_gpu_bf16(weight_bits(wl, t)), "mx_tiled")
+    y = fp4.gemv_mx(to_gpu_bf16(bx), w)
+    torch.cuda.synchronize()
+    p, s = mx_oracle_quant(wl, t)
+    yr, l1 = oracle.mx_gemv(bx, p, s)
+    assert_within_tolerance(y.cpu().numpy(), yr, l1, "mx %s %s" % (t, xname))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 8, 32), (37, 300, 1056), (200, 129, 2048), (300, 1000, 5120),
+                                   (257, 16400, 1056)])
+def test_mx_prefill_small_shapes(M, N, K):
+    print("mx prefill", M, N, K, flush=True)
+    bw = bf16_tensor((N, K), 6200 + M + N + K, 0.02, outlier_p=0.002, outlier_scale=20.0)
+    bx = bf16_tensor((M, K), 6300 + M, 1.0)
+    w = fp4.quantize_mx(to_gpu_bf16(bw), "mx_tiled")
+    y = fp4.gemm_prefill_mx(to_gpu_bf16(bx), w)
+    torch.cuda.synchronize()
+    p, s = oracle.mx_quantize(bw)
+    yr, l1 = oracle.mx_gemv(bx, p, s)
+    assert_within_tolerance(y.cpu().numpy(), yr, l1, "mx prefill %d %d %d" % (M, N, K))
+
+
+def test_mx_prefill_full_size_sampled_rows():
+    """2048 tokens x the 27B-class gate projection 17408 x 5120 in MXFP4,
+    checked on 8 sampled token rows (all 17408 outputs each)."""
+    bx = act_bits("prefill", "x")
+    w = fp4.quantize_mx(to_gpu_bf16(weight_bits("dense27b_layer", "gate")), "mx_tiled")
+    y = fp4.gemm_prefill_mx(to_gpu_bf16(bx), w)
+    torch.cuda.synchronize()
+    rows = [0, 1, 255, 256, 1000, 1791, 1792, 2047]
+    p, s = mx_oracle_quant("dense27b_layer", "gate")
+    yr, l1 = oracle.mx_gemv(bx[rows], p, s)
+    assert_within_tolerance(y[rows].cpu().numpy(), yr, l1, "mx prefill full size")
