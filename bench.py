@@ -426,6 +426,22 @@ def other_configs(fp4, torch, timer, w27, gpu_bf16, dev, x_in0, x_mid0):
             fp4.gemv(xs[3072], ws["down"], out=d1)
     us = [u / 28 for u in timer.time_calls(token, 6)]
     res["c1_qwen3_0p6b_decode_28_layers"] = dict(line(us, 8847360), unit="per layer", launches_per_layer=4)
+    # the same layers with their neighbours fused: RMS norm (eps 1e-6) inside the QKV launch, SwiGLU inside
+    # the gate_up launch writing bf16 h, and the down projection reading that h
+    from workloads import bf16_tensor
+    gain = gpu_bf16(bf16_tensor((1024,), 55, 0.1))
+    h1 = torch.empty((1, 3072), dtype=torch.bfloat16, device=dev)
+
+    def token_fused(i):
+        for ws, xs in sets[i % len(sets)]:
+            fp4.gemv_multi_rmsnorm(xs[1024], gain, 1e-6, [ws["q"], ws["k"], ws["v"]],
+                                   [qkv, qkv[:, 2048:], qkv[:, 3072:]], [4096] * 3)
+            fp4.gemv(xs[2048], ws["o"], out=o)
+            fp4.gemv_swiglu(xs[1024], ws["gate"], ws["up"], out=h1)
+            fp4.gemv(h1, ws["down"], out=d1)
+    us = [u / 28 for u in timer.time_calls(token_fused, 6)]
+    res["c1_qwen3_0p6b_decode_28_layers_norm_swiglu_fused"] = dict(line(us, 8847360), unit="per layer",
+                                                                   launches_per_layer=4)
     del sets, layers
     # ---- config 2 at M = 1 is the headline; config 3: the same layer with M in {2, 4, 8, 16}
     wcp = [w27] + [{k: clone(w) for k, w in w27.items()} for _ in range(5)]
@@ -445,6 +461,15 @@ def other_configs(fp4, torch, timer, w27, gpu_bf16, dev, x_in0, x_mid0):
             fp4.gemv(xm, w["down"], out=yd, workspace=work)
         flops = 2.0 * M * (2 * INTER * HIDDEN + HIDDEN * INTER)
         res["c3_dense27b_layer_m%d" % M] = dict(line(timer.time_calls(layer, 24), B27, flops), unit="per layer")
+    # ---- config 2 as a real MLP: SwiGLU(gate, up) -> bf16 h -> down(h), M = 1
+    hh = torch.empty((1, INTER), dtype=torch.bfloat16, device=dev)
+    yd1 = torch.empty((1, HIDDEN), dtype=torch.float32, device=dev)
+
+    def mlp(i):
+        w = wcp[i % len(wcp)]
+        fp4.gemv_swiglu(x_in0, w["gate"], w["up"], out=hh)
+        fp4.gemv(hh, w["down"], out=yd1)
+    res["c2_dense27b_mlp_swiglu_then_down_m1"] = dict(line(timer.time_calls(mlp, 24), B27), unit="per layer")
     # ---- config 4a: LM head 151936 x 1024 at M = 1 and 8, product alone and with the greedy choice
     lm = workload("lm_head")
     bl = fp4.quantize(gpu_bf16(tensor_bits(lm.tensor("w"))), "tiled")
@@ -473,7 +498,38 @@ def other_configs(fp4, torch, timer, w27, gpu_bf16, dev, x_in0, x_mid0):
                                workspace=work)
     res["c4_prefill_2048x34816x5120"] = line(timer.time_calls(pf, 6, reps=5), flops=2.0 * 2048 * 2 * INTER * HIDDEN,
                                              mfma=True)
-    del yf, xp, wcp
+    del yf, wcp
+    # ---- MXFP4 (E8M0 scale per 32 elements): the 27B-class layer at M = 1 (gate, up, down), the LM head at
+    # M = 1 and the prefill product of the gate projection
+    wl2 = workload("dense27b_layer")
+    # gate and up stacked into one 34816 x 5120 weight (the rows are quantised independently, so stacking
+    # before or after quantisation gives the same bytes) and read by one launch
+    mxb = {n: fp4.quantize_mx(gpu_bf16(tensor_bits(wl2.tensor(n))), "mx_tiled") for n in ("gate", "down")}
+    mxb["gate_up"] = fp4.quantize_mx(torch.cat([gpu_bf16(tensor_bits(wl2.tensor(n))) for n in ("gate", "up")]),
+                                     "mx_tiled")
+    mxc = [mxb] + [{k: fp4.MXFP4Weight(w.packed.clone(), None, w.N, w.K) for k, w in mxb.items()} for _ in range(5)]
+    g2 = torch.empty((1, 2 * INTER), dtype=torch.float32, device=dev)
+
+    def mx_layer(i):
+        w = mxc[i % len(mxc)]
+        fp4.gemv_mx(x_in0, w["gate_up"], out=g2)
+        fp4.gemv_mx(x_mid0, w["down"], out=yd1)
+    Bmx = lambda N, K: N * K // 2 + N * K // 32   # noqa: E731
+    Bmx27 = 2 * Bmx(INTER, HIDDEN) + Bmx(HIDDEN, INTER)
+    res["mx_dense27b_layer_m1"] = dict(line(timer.time_calls(mx_layer, 24), Bmx27), unit="per layer", launches=2)
+    res["mx_down_5120x17408_m1"] = line(timer.time_calls(lambda i: fp4.gemv_mx(x_mid0, mxc[i % 6]["down"], out=yd1), 48),
+                                        Bmx(HIDDEN, INTER))
+    lmx = fp4.quantize_mx(gpu_bf16(tensor_bits(workload("lm_head").tensor("w"))), "mx_tiled")
+    lmxc = [lmx] + [fp4.MXFP4Weight(lmx.packed.clone(), None, lmx.N, lmx.K) for _ in range(6)]
+    xl = gpu_bf16(x_bits(workload("lm_head").x("x_m1")))
+    yl = torch.empty((1, 151936), dtype=torch.float32, device=dev)
+    res["mx_lm_head_m1"] = line(timer.time_calls(lambda i: fp4.gemv_mx(xl, lmxc[i % 7], out=yl), 56),
+                                Bmx(151936, 1024))
+    ypm = torch.empty((2048, INTER), dtype=torch.float32, device=dev)
+    res["mx_prefill_2048x17408x5120"] = line(timer.time_calls(lambda i: fp4.gemm_prefill_mx(xp, mxc[i % 6]["gate"],
+                                                                                          out=ypm), 6, reps=5),
+                                             flops=2.0 * 2048 * INTER * HIDDEN, mfma=True)
+    del mxb, mxc, lmx, lmxc, ypm, xp, g2
     # ---- load-time quantisation of the down projection from bf16 and from an FP8 release (the
     # rule reads the input twice: algorithmic bytes = 2 input reads + 9/16 byte per element written)
     Wb = gpu_bf16(tensor_bits(workload("dense27b_layer").tensor("down")))
