@@ -189,9 +189,9 @@ static int take_ws(void* workspace, size_t bytes, size_t need, fp4::Workspace& w
 }
 
 // The product; `scratch` (may be null) holds its partial sums.
-static int gemv_run(const fp4::GemvArgs& a, uint8_t* scratch, hipStream_t s) {
+static int gemv_run(const fp4::GemvArgs& a, const fp4::Workspace& ws, uint8_t* scratch, hipStream_t s) {
   if (gemv_on_valu(a)) return hip_status(fp4::launch_gemv(a, s));
-  return hip_status(fp4::launch_gemv_mma(a, reinterpret_cast<float*>(scratch), s));
+  return hip_status(fp4::launch_gemv_mma(a, reinterpret_cast<float*>(scratch), ws.valid() ? ws.counter(0) : nullptr, s));
 }
 
 static uint8_t* scratch_of(const fp4::Workspace& ws) { return ws.valid() ? ws.scratch() : nullptr; }
@@ -202,7 +202,7 @@ int fp4_gemv_multi_ws(const fp4_proj* projs, int nproj, const void* x_bf16, int6
   if (int st = gemv_args(projs, nproj, x_bf16, M, K, a)) return st;
   fp4::Workspace ws;
   if (int st = take_ws(workspace, workspace_bytes, gemv_ws_need(a), ws)) return st;
-  return gemv_run(a, scratch_of(ws), static_cast<hipStream_t>(stream));
+  return gemv_run(a, ws, scratch_of(ws), static_cast<hipStream_t>(stream));
 }
 
 int fp4_gemv_multi(const fp4_proj* projs, int nproj, const void* x_bf16, int64_t M, int64_t K, void* stream) {
@@ -328,9 +328,9 @@ int fp4_lm_head_greedy(int32_t* idx, float* logits, const void* x_bf16, const vo
   if (ws.valid() && greedy_fused(a)) {
     a.greedy.idx = idx;
     a.greedy.keys = reinterpret_cast<uint64_t*>(ws.p);   // the header: zero between calls
-    return gemv_run(a, scratch_of(ws), s);
+    return gemv_run(a, ws, scratch_of(ws), s);
   }
-  if (int st = gemv_run(a, scratch_of(ws), s)) return st;
+  if (int st = gemv_run(a, ws, scratch_of(ws), s)) return st;
   return hip_status(fp4::launch_argmax(idx, logits, M, N, N, ws, s));
 }
 
@@ -364,12 +364,12 @@ int fp4_gemv_multi_rmsnorm(const fp4_proj* projs, int nproj, const void* x_bf16,
   if (rms_fused(a)) {
     a.gain = static_cast<const uint16_t*>(gain_bf16);
     a.eps = eps;
-    return gemv_run(a, nullptr, s);
+    return gemv_run(a, fp4::Workspace{}, nullptr, s);
   }
   uint16_t* xn = reinterpret_cast<uint16_t*>(ws.scratch());
   if (int st = hip_status(fp4::launch_rmsnorm(a.x, static_cast<const uint16_t*>(gain_bf16), eps, M, K, xn, s))) return st;
   a.x = xn;
-  return gemv_run(a, ws.scratch() + align256((size_t)M * (size_t)K * 2), s);
+  return gemv_run(a, ws, ws.scratch() + align256((size_t)M * (size_t)K * 2), s);
 }
 
 // The gated MLP's first half: one vector-ALU launch computing gate and up and
@@ -413,7 +413,7 @@ int fp4_gemv_swiglu(void* h_bf16, int64_t ldh, const void* x_bf16, const void* g
   a.proj[1].y = u;
   a.proj[0].ldy = a.proj[1].ldy = N;
   a.h = nullptr;
-  if (int st = gemv_run(a, ws.scratch() + 2 * gu, s)) return st;
+  if (int st = gemv_run(a, ws, ws.scratch() + 2 * gu, s)) return st;
   return hip_status(fp4::launch_swiglu(g, u, M, N, static_cast<uint16_t*>(h_bf16), ldh, s));
 }
 

@@ -124,11 +124,14 @@ hipError_t launch_swiglu(const float* g, const float* u, int64_t M, int64_t N, u
                          hipStream_t s);
 // Small-M product on bf16 MFMA, split over K chunks (16 activation rows per
 // pass, more rows loop passes). With more than one chunk the chunk partial
-// sums meet in `partials` (gemv_mma_partial_bytes of scratch: a second
-// kernel adds them in chunk order) or, when it is null, are added
-// atomically into y after a fill kernel zeroes it (the summation order then
-// varies between calls).
-hipError_t launch_gemv_mma(const GemvArgs& a, float* partials, hipStream_t s, int ppw = 0);   // ppw > 0: pairs per workgroup (tuning)
+// sums meet in `partials` (gemv_mma_partial_bytes of scratch) and are added
+// in chunk order: inside the launch by the last-arriving workgroup of each
+// pair block when `counters` (the workspace header: zero on entry, left
+// zero) has room for the pair blocks, else by a second kernel. Without
+// `partials` they are added atomically into y after a fill kernel zeroes it
+// (the summation order then varies between calls).
+hipError_t launch_gemv_mma(const GemvArgs& a, float* partials, unsigned* counters, hipStream_t s,
+                           int ppw = 0);   // ppw > 0: pairs per workgroup (tuning)
 // Bytes of partial sums launch_gemv_mma keeps for `a` (0 when it keeps none).
 size_t gemv_mma_partial_bytes(const GemvArgs& a);
 

@@ -41,14 +41,21 @@
 //   double the MFMAs, which measured slower.
 //
 // Weight loads. In the operand layout one load instruction would touch 64
-// bytes of each of 16 rows (twice the cache lines of a contiguous kilobyte)
-// and the block scales would take many 2-byte loads per pair. Instead a wave
-// loads each tile of its pair as the M = 1 kernel does (four contiguous
-// kilobytes, rows 2i and 2i + 1 per load, and the tile's 512 scale bytes at
-// 8 bytes per lane) and moves them through a wave-private LDS region into the
-// operand layout, with XOR swizzles that keep the writes and the reads free
-// of bank conflicts. Only the wave that wrote the region reads it, and a
-// wave's LDS operations complete in order.
+// bytes of each of 16 rows (a streaming read of that shape ran about 20 %
+// slower than contiguous kilobytes on MI355X) and the block scales would take
+// many 2-byte loads per pair. Instead a wave loads each tile of its pair as
+// the M = 1 kernel does (four contiguous kilobytes, rows 2i and 2i + 1 per
+// load, and the tile's 512 scale bytes at 8 bytes per lane) and moves them
+// through a wave-private LDS region into the operand layout. Only the wave
+// that wrote the region reads it, and a wave's LDS operations complete in
+// order.
+//
+// LDS banks (measured on MI355X with replayed address patterns and the
+// SQ_LDS_BANK_CONFLICT counter): a 16-byte read of a half-wave is free of
+// conflicts when lanes l and l + 16 use the same 16-byte bank group (address
+// bits 4..7) or the same address, and the 16 lane positions use distinct
+// groups (or the same address); 4-byte accesses of a wave are free when
+// their 64 banks differ. The 8-row kernel's layouts follow that rule.
 #include <algorithm>
 
 #include <atomic>
@@ -68,6 +75,8 @@ constexpr int kWaves = 4;                 // waves per workgroup
 constexpr int kMRows = 16;                // activation rows per pass (MFMA M)
 constexpr int kPairRows = 16;             // weight rows per pair (MFMA N)
 constexpr int kTrBytes = 8192 + 1024;    // per wave: one pair's codes and scales
+constexpr int kSc1 = 16;                  // buffer cache-policy bit: device scope
+constexpr int kCntStride = kWsCounterWords;   // one 128-byte header line per arrival counter
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
@@ -127,6 +136,8 @@ __device__ __forceinline__ float fp8_f32(uint32_t w, int sel) {
 struct MmaArgs {
   const uint16_t* x;   // bf16 [M][K]
   float* ws;           // [C][npairs][16][16] partials (C > 1; nullptr: atomic adds into y)
+  unsigned* cnt;       // with ws: arrivals per pair block (kCntStride apart, the workspace header, zero
+                       // between launches); nullptr: a second kernel adds the partials
   int M, K, C, m0;     // m0: first activation row of this pass
   int nproj;
   int npairs;          // pairs over all projections
@@ -165,8 +176,56 @@ __device__ __forceinline__ void pair_out(const MmaArgs& a, int pair, int c, int 
       }
     }
   } else if (a.m0 + 4 * q < a.M) {   // rows past M are never read back
-    float* dst = a.ws + ((int64_t)c * a.npairs + pair) * 256 + n16 * 16 + 4 * q;
-    *reinterpret_cast<f32x4_t*>(dst) = v;
+    // device-scope store (through to the memory side): the workgroup that adds
+    // the partials may run on another XCD
+    const __amdgpu_buffer_rsrc_t r = rsrc(a.ws + ((int64_t)c * a.npairs + pair) * 256, 1024);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, (n16 * 16 + 4 * q) * 4, 0, kSc1);
+  }
+}
+
+// Split K inside the launch. Every workgroup (b, c) stores its partials,
+// waits for the stores and counts itself in on counter b; the last of the C
+// arrivals resets the counter, reads the C partials of its pairs back with
+// device-scope loads and writes y = gscale * (their sum in chunk order), so
+// the result does not depend on the arrival order.
+__device__ __forceinline__ void split_fixup(const MmaArgs& a, int pb, int pe) {
+  __shared__ int last;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's partial stores are done
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned* ctr = a.cnt + (int64_t)blockIdx.x * kCntStride;
+    const unsigned n = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = n == (unsigned)(a.C - 1);
+    if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!last) return;
+  const int r4 = (min(kMRows, a.M - a.m0) + 3) >> 2;
+  const int items = (pe - pb) * 16 * r4;   // (pair, n16, m4)
+  for (int t = threadIdx.x; t < items; t += blockDim.x) {
+    const int m4 = t % r4, pn = t / r4, pair = pb + (pn >> 4), n16 = pn & 15;
+    const int p = proj_of(a, pair);
+    const int n = 16 * (pair - a.proj[p].pair_begin) + n16;
+    if (n >= a.proj[p].N) continue;
+    f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < a.C; c0 += 8) {
+      f32x4_t v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {   // chunks past C: an empty resource, zeros
+        const int c = c0 + i;
+        const __amdgpu_buffer_rsrc_t r =
+            rsrc(a.ws + ((int64_t)min(c, a.C - 1) * a.npairs + pair) * 256, c < a.C ? 1024 : 0);
+        v[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (n16 * 16 + 4 * m4) * 4, 0, kSc1));
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sum += v[i];
+    }
+    const float gs = *a.proj[p].gscale;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = a.m0 + 4 * m4 + i;
+      if (m < a.M) a.proj[p].y[(int64_t)m * a.proj[p].ldy + n] = gs * sum[i];
+    }
   }
 }
 
@@ -222,20 +281,23 @@ __global__ __launch_bounds__(64 * kWaves) void k_gemv_mma8(const MmaArgs a) {
   const int pe = min(pb + a.pairs_per_wg, a.npairs);
 
   // Wave-private region in the operand layout. Pair row n (0..15: tile n / 8,
-  // row n % 8) keeps its 512 code bytes at 512 n, word w of piece p at dword
-  // ((w ^ a_n) << 5) + (((p >> 2) ^ c_n) << 2) + (p & 3), a_n = (n >> 3) ^
-  // (n & 1), c_n = n & 7: word w of four consecutive pieces is one 16-byte
-  // read, the writes (one row per half-wave) and the reads (16 rows per 16
-  // lanes) spread over all banks. Its 64 scale bytes sit at 8192 + 64 n, the
-  // scale of block 2p + b in 16-byte group (2b + (p >> 4)) ^ s_n at byte
-  // p & 15, s_n = ((n >> 1) ^ (n >> 3)) & 3.
+  // row n % 8) keeps its 512 code bytes at 512 n; word w of piece p sits at
+  // byte ((w & 1) << 8) + ((((w >> 1) ^ e_n) & 1) << 7) + ((((p >> 2) ^ c_n)
+  // & 7) << 4) + 4 (p & 3), e_n = (n & 1) ^ (n >> 3), c_n = (n >> 1) & 7, so
+  // word w of four consecutive pieces is one 16-byte read. The reads meet the
+  // 16-byte rule of LDS banks (lanes l and l + 16 of a half-wave in the same
+  // 16-byte bank group of 256 bytes, or at the same address; the 16 lane
+  // positions in distinct groups; measured on MI355X) and each b32 write
+  // covers all 64 banks. Its 64 scale bytes sit at 8192 + 64 n, the scale of
+  // block 2p + b in 16-byte group (2b + (p >> 4)) ^ s_n at byte p & 15,
+  // s_n = ((n >> 1) ^ (n >> 3)) & 3.
   uint8_t* tw = tr + wave * kTrBytes;
-  // Write addresses with the fields that depend on (T, i, w) left at zero:
-  // a write XORs (w ^ T) into bits 7..8 (the word field, a_n = T ^ h) and 2i
-  // into bits 4..6 (the piece-group field, c_n = 2i + h), then adds the row
-  // base 512 (8T + 2i); likewise for the scales (s_n = (i ^ T) & 3).
+  // Write addresses with the fields that depend on (T, i, w) left at zero: a
+  // write XORs (w >> 1) ^ T into bit 7 (e_n = h ^ T) and i + 4T into bits 4..6
+  // (c_n), then adds the row base 512 (8T + 2i) and (w & 1) << 8; the scales
+  // XOR their group field likewise (s_n = (i ^ T) & 3).
   const int h = lane >> 5, l = lane & 31;
-  const int wr_code = h * 512 + (h << 7) + (((l >> 2) ^ h) << 4) + ((l & 3) << 2);
+  const int wr_code = h * 512 + (h << 7) + ((l >> 2) << 4) + ((l & 3) << 2);
   const int wr_scale = 8192 + h * 64 + l;
   auto transpose_in = [&](const PairFrag& f) {
 #pragma unroll
@@ -245,7 +307,8 @@ __global__ __launch_bounds__(64 * kWaves) void k_gemv_mma8(const MmaArgs a) {
         const uint32_t wv[4] = {f.w[T][i].x, f.w[T][i].y, f.w[T][i].z, f.w[T][i].w};
 #pragma unroll
         for (int w = 0; w < 4; ++w)
-          *reinterpret_cast<uint32_t*>(tw + ((wr_code ^ (((w ^ T) << 7) | ((2 * i) << 4))) + (8 * T + 2 * i) * 512)) = wv[w];
+          *reinterpret_cast<uint32_t*>(tw + ((wr_code ^ ((((w >> 1) ^ T) << 7) | ((i + 4 * T) << 4))) +
+                                             (8 * T + 2 * i) * 512 + ((w & 1) << 8))) = wv[w];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {   // scale of row n, block 2l + j: byte 2i + j
           const int byte = 2 * i + j;
@@ -257,33 +320,39 @@ __global__ __launch_bounds__(64 * kWaves) void k_gemv_mma8(const MmaArgs a) {
   };
   // Lane (q, n) reads word q of the pieces of row n (elements 8q .. 8q+7 of
   // each, block parity q / 2) and the 32 scales of that parity.
-  const int an = (n16 >> 3) ^ (n16 & 1), cn = n16 & 7, sn = ((n16 >> 1) ^ (n16 >> 3)) & 3;
+  const int en = (n16 & 1) ^ (n16 >> 3), cn = (n16 >> 1) & 7, sn = ((n16 >> 1) ^ (n16 >> 3)) & 3;
   const int beta = q >> 1;
-  const int rd_code = n16 * 512 + ((q ^ an) << 7) + (cn << 4);
+  const int rd_code = n16 * 512 + ((q & 1) << 8) + ((((q >> 1) ^ en) & 1) << 7) + (cn << 4);
   const int rd_scale0 = 8192 + n16 * 64 + (((2 * beta) ^ sn) << 4);
   const int rd_scale1 = 8192 + n16 * 64 + (((2 * beta + 1) ^ sn) << 4);
   // A lane (q, r) feeds MFMA row r = (activation row r % 8, parity r / 8): the
-  // activations if its k range has that parity, else zeros.
+  // activations if its k range has that parity, else zeros. It reads unit u =
+  // 16g + 4j + q of its row (see the staging below); the zero lanes read the
+  // window at the group that continues their half-wave's row groups.
   const bool a_valid = (n16 >> 3) == beta;
-  const int a_base = a_valid ? (n16 & 7) * kXsRow8 + 16 * q : 8 * kXsRow8;
-  const int a_step = a_valid ? 256 : 0;
+  const int a_base = (a_valid ? (n16 & 7) * kXsRow8 + ((q & 1) << 10) : 8 * kXsRow8) + ((q >> 1) << 4);
+  const int a_step2 = a_valid ? 256 : 0;   // per two piece groups (the window repeats every two)
 
   PairFrag cur;
   load_pair(a, pb + wave, pb, pe, c, lane, cur);   // in flight while the activations are staged
 
   // activations of chunk c, rows m0 .. m0+7: row m at kXsRow8 * m, 16-byte
-  // unit u (elements 8u .. 8u+7) at 16u; then the zero window
+  // unit u (elements 8u .. 8u+7) at ((u & 1) << 10) + ((u >> 1) << 4), so the
+  // units 8q and 8q + 8 of the A lanes q and q + 1 share a bank group; then
+  // the zero window. Thread t stages unit u of row m with lanes l and l + 16
+  // on units 2k and 2k + 1 (the same 16-byte rule for the writes).
   {
     const int rows = min(8, a.M - a.m0);
     for (int t = threadIdx.x; t < 8 * 128; t += 64 * kWaves) {
-      const int m = t >> 7, u = t & 127;
+      const int kk = t >> 6, L = t & 63;
+      const int m = kk >> 1, u = 64 * (kk & 1) + 32 * (L >> 5) + 2 * (L & 15) + ((L >> 4) & 1);
       uint4 v = make_uint4(0, 0, 0, 0);
       if (m < rows) {
         const __amdgpu_buffer_rsrc_t rx = rsrc(a.x + (int64_t)(a.m0 + m) * K, K * 2);
         const u32x4_t r = __builtin_amdgcn_raw_buffer_load_b128(rx, (c * kChunkK + u * 8) * 2, 0, 0);   // past K: 0
         v = make_uint4(r[0], r[1], r[2], r[3]);
       }
-      *reinterpret_cast<uint4*>(xs + m * kXsRow8 + u * 16) = v;
+      *reinterpret_cast<uint4*>(xs + m * kXsRow8 + ((u & 1) << 10) + ((u >> 1) << 4)) = v;
     }
     if (threadIdx.x < kZeroWin / 16) *reinterpret_cast<uint4*>(xs + 8 * kXsRow8 + threadIdx.x * 16) = make_uint4(0, 0, 0, 0);
   }
@@ -302,14 +371,14 @@ __global__ __launch_bounds__(64 * kWaves) void k_gemv_mma8(const MmaArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       const uint4 cw = *reinterpret_cast<const uint4*>(tw + (rd_code ^ (g << 4)));
       const uint32_t cws[4] = {cw.x, cw.y, cw.z, cw.w};
-      const int ab = a_base + g * a_step;
+      const int ab = a_base + (g & 1) * 128 + (g >> 1) * a_step2;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {   // piece p = 4g + j
         uint32_t o[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = fp4x2_bf16(cws[j], e);
         const bf16x8_t b = __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
-        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(xs + ab + 64 * j);
+        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(xs + ab + 32 * j);
         const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
         const float sc = fp8_f32(sw[g], j);   // scale of block 2p + q / 2
 #pragma unroll
@@ -324,6 +393,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_gemv_mma8(const MmaArgs a) {
     if (q < 2) pair_out(a, pair, c, q, n16, tot);   // rows 4q .. 4q+3
     cur = nxt;
   }
+  if (a.cnt && a.C > 1) split_fixup(a, pb, pe);
 }
 
 // 9 to 16 activation rows (m0 .. m0+15) per launch; grid and block as above.
@@ -405,6 +475,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_gemv_mma16(const MmaArgs a) {
     pair_out(a, pair, c, q, n16, acc);
     cur = nxt;
   }
+  if (a.cnt && a.C > 1) split_fixup(a, pb, pe);
 }
 
 // y[m][n] = gscale * sum over chunks (in order) of the partials. A thread
@@ -526,7 +597,7 @@ size_t gemv_mma_partial_bytes(const GemvArgs& g) {
   return (size_t)a.C * (size_t)a.npairs * 256 * sizeof(float);
 }
 
-hipError_t launch_gemv_mma(const GemvArgs& g, float* partials, hipStream_t s, int ppw) {
+hipError_t launch_gemv_mma(const GemvArgs& g, float* partials, unsigned* counters, hipStream_t s, int ppw) {
   MmaArgs a = mma_args(g);
   if (a.npairs < 0) return hipErrorInvalidValue;
   const int64_t pairs = a.npairs;
@@ -544,12 +615,18 @@ hipError_t launch_gemv_mma(const GemvArgs& g, float* partials, hipStream_t s, in
       const int64_t blocks = std::min<int64_t>((most + 255) / 256, 4096);
       hipLaunchKernelGGL(k_zero_rows, dim3((unsigned)blocks, (unsigned)a.nproj), dim3(256), 0, s, a, rows);
     }
+    // In-launch fixup for passes of at most 8 rows (its arrivals need one
+    // header counter per pair block). MI355X, graph-timed: fused gate_up
+    // 2 x 17408 x 5120 at M = 4 27.5 against 29.3 us with the second kernel,
+    // M = 8 29.4 against 30.3; at M = 16 the last workgroups' sums of 16 rows
+    // form a tail (38.7 against 33.9 us), so those passes keep the kernel.
+    a.cnt = use_ws && eight && counters && wgx <= kWsCounters ? counters : nullptr;
     const dim3 grid((unsigned)wgx, (unsigned)a.C), block(64 * kWaves);
     if (eight)
       hipLaunchKernelGGL(k_gemv_mma8, grid, block, 0, s, a);
     else
       hipLaunchKernelGGL(k_gemv_mma16, grid, block, 0, s, a);
-    if (use_ws) {
+    if (use_ws && !a.cnt) {
       const int64_t n = pairs * 16 * ((rows + 3) / 4);
       hipLaunchKernelGGL(k_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
     }

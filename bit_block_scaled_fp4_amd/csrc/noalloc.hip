@@ -10,8 +10,9 @@
 // call there, and only that address reaches kernels. All calls on one GPU
 // share the array, so calls that may overlap in time on one GPU race (use
 // fp4_gemv_multi_ws with separate workspaces for those). The array starts
-// zeroed (static storage); the product's kernels use no counters, only
-// partial sums that each call writes before it reads them.
+// zeroed (static storage), as the workspace contract asks: its header holds
+// the arrival counters of the split products, which every call leaves at
+// zero, and the rest partial sums that each call writes before it reads them.
 #include "../../include/fp4.h"
 
 #include <atomic>

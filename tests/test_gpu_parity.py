@@ -367,14 +367,16 @@ def ws_for(op, M, K, Ns):
     return fp4.new_workspace(fp4.workspace_bytes(op, M, K, Ns), dev())
 
 
-@pytest.mark.parametrize("M", [5, 9])
+@pytest.mark.parametrize("M", [5, 8, 9])
 def test_gemv_multi_matrix_core_ragged_projections(M):
     """Several projections of unequal, ragged row counts (333, 16, 1000 rows;
     K = 3008: three chunks, so the K split runs) in one launch on the
-    matrix-core path (M >= 5; M = 9 stages 16 activation rows, M = 5 eight),
-    each equal to the oracle within the tolerance: with a workspace (chunk
-    partials added in order by a second kernel: repeatable bit for bit) and
-    without (y zeroed, then atomic adds; outputs start as NaN)."""
+    matrix-core path (M >= 5; M = 9 stages 16 activation rows, M = 5 and 8
+    eight), each equal to the oracle within the tolerance: with a workspace
+    (chunk partials added in chunk order, for 8-row passes inside the launch
+    by the last workgroup of each pair block to arrive, for 16-row passes by a
+    second kernel: repeatable bit for bit, the counter header left at zero)
+    and without (y zeroed, then atomic adds; outputs start as NaN)."""
     print("gemv_multi mfma", M, flush=True)
     Ns, K = (333, 16, 1000), 3008
     bws = [bf16_tensor((N, K), 800 + N, 0.02, outlier_p=0.002, outlier_scale=20.0) for N in Ns]
