@@ -33,7 +33,6 @@ import hashlib
 import json
 import os
 import statistics
-import subprocess
 import sys
 import time
 
@@ -69,18 +68,46 @@ def load_traffic():
     return t.get("traffic_bytes_per_launch")
 
 
+def progress(msg):
+    """One line on stderr per finished stage (the JSON line stays alone on stdout)."""
+    print("[bench] %s" % msg, file=sys.stderr, flush=True)
+
+
+class _Results(dict):
+    """The per-config results; reports each line as it is measured."""
+
+    def __setitem__(self, key, value):
+        super().__setitem__(key, value)
+        progress("%s measured" % key)
+
+
 def stats(xs):
     return {"median": round(statistics.median(xs), 4), "min": round(min(xs), 4), "max": round(max(xs), 4)}
 
 
 def clocks():
-    """GPU clock readings (rocm-smi), or the error text."""
+    """The GPU's current core and memory clock levels from sysfs (the DPM
+    tables with the active level marked), or the reason they are missing.
+    Read from files so that no program is started from this process."""
+    import glob
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
-        d = json.loads(r.stdout)
-        card = d[sorted(d)[0]]
-        return {k: v for k, v in card.items() if "clock" in k.lower() or "sclk" in k.lower() or "mclk" in k.lower()}
-    except Exception as e:  # noqa: BLE001  (a missing tool must not stop the benchmark)
+        out = {}
+        for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+            try:
+                with open(os.path.join(dev, "vendor")) as f:
+                    if f.read().strip() != "0x1002":
+                        continue
+                for name in ("pp_dpm_sclk", "pp_dpm_mclk"):
+                    with open(os.path.join(dev, name)) as f:
+                        cur = [ln.strip() for ln in f if ln.strip().endswith("*")]
+                    out[name] = cur[0] if cur else None
+            except OSError:
+                continue
+            if out:
+                out["device"] = dev
+                return out
+        return {"error": "no readable AMD DPM clock tables in sysfs"}
+    except Exception as e:  # noqa: BLE001  (missing clocks must not stop the benchmark)
         return {"error": str(e)[:200]}
 
 
@@ -306,6 +333,7 @@ def main():
         del gw
     g_step = timer.graph(step, args.steps)
     win = timer.windows(g_step, args.steps)
+    progress("headline steps timed")
     del g_step
     t_step = statistics.median(win) * 1e-6
 
@@ -325,7 +353,9 @@ def main():
     value = B_step / t_step / 1e9
     tiled_d = fp4.layout_bytes(HIDDEN, INTER)[0]
     tiled_gu = 2 * fp4.layout_bytes(INTER, HIDDEN)[0]
+    progress("per-kernel launches timed")
     ceil = read_ceiling(fp4, torch, timer, [tiled_d, tiled_gu])
+    progress("read ceiling measured")
     c_d, c_gu = ceil[tiled_d]["us"], ceil[tiled_gu]["us"]
 
     out = {
@@ -378,7 +408,7 @@ def other_configs(fp4, torch, timer, w27, gpu_bf16, dev, x_in0, x_mid0):
     windows. Products with a K split use a workspace (fp4_*_ws forms)."""
     from workloads import fp8_release, tensor_bits, x_bits, workload
 
-    res = {}
+    res = _Results()
 
     def clone(w):
         return fp4.NVFP4Weight(w.packed.clone(), None, w.gscale.clone(), w.N, w.K)
@@ -428,8 +458,8 @@ def other_configs(fp4, torch, timer, w27, gpu_bf16, dev, x_in0, x_mid0):
     res["c1_qwen3_0p6b_decode_28_layers"] = dict(line(us, 8847360), unit="per layer", launches_per_layer=4)
     # the same layers with their neighbours fused: RMS norm (eps 1e-6) inside the QKV launch, SwiGLU inside
     # the gate_up launch writing bf16 h, and the down projection reading that h
-    from workloads import bf16_tensor
-    gain = gpu_bf16(bf16_tensor((1024,), 55, 0.1))
+    from workloads import norm_gain
+    gain = gpu_bf16(norm_gain(1024, 55))
     h1 = torch.empty((1, 3072), dtype=torch.bfloat16, device=dev)
 
     def token_fused(i):

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle
-from workloads import bf16_to_float32, float32_to_bf16_bits, bf16_tensor, fp8_release
+from workloads import bf16_to_float32, float32_to_bf16_bits, bf16_tensor, fp8_release, norm_gain
 
 from gpu_common import (THREADS, act_bits, assert_within_tolerance, dev, gpu_u8, oracle_quant, to_gpu_bf16,
                         weight_bits)
@@ -814,7 +814,7 @@ def test_two_streams_at_once():
 
 # --------------------------------------------- fused neighbours: RMSNorm, SwiGLU
 def gain_bits(K, seed):
-    return float32_to_bf16_bits((1.0 + bf16_to_float32(bf16_tensor((K,), seed, 0.1))).astype(np.float32))
+    return norm_gain(K, seed)
 
 
 # Bound of the normalised product: the product bound on the normalised rows,

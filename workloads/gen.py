@@ -152,3 +152,12 @@ def fp8_release(shape, seed: int, sigma: float, outlier_p: float = 0.0, outlier_
     q = np.clip(w / scale, -448.0, 448.0).astype(np.float32)
     codes = torch.from_numpy(q).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     return codes, scale
+
+
+def norm_gain(K: int, seed: int, sigma: float = 0.1) -> np.ndarray:
+    """A synthetic RMS-norm gain vector (uint16 bf16 bits, length ``K``): 1 +
+    sigma*N(0,1) with the normal draws of ``bf16_tensor`` (seed ``seed``),
+    the sum rounded once to bf16 (nearest even), the shape of a trained
+    norm's gains around one."""
+    g = 1.0 + bf16_to_float32(bf16_tensor((K,), seed, sigma)).astype(np.float64)
+    return float32_to_bf16_bits(g.astype(np.float32))
