@@ -106,9 +106,22 @@ def clocks():
             if out:
                 out["device"] = dev
                 return out
-        return {"error": "no readable AMD DPM clock tables in sysfs"}
+    except Exception:  # noqa: BLE001  (fall through to the library)
+        pass
+    try:  # the amd-smi library (no subprocess)
+        import amdsmi
+        amdsmi.amdsmi_init()
+        try:
+            h = amdsmi.amdsmi_get_processor_handles()[0]
+            out = {}
+            for name, kind in (("gfx", amdsmi.AmdSmiClkType.GFX), ("mem", amdsmi.AmdSmiClkType.MEM)):
+                info = amdsmi.amdsmi_get_clock_info(h, kind)
+                out[name + "_mhz"] = {k: info[k] for k in ("clk", "min_clk", "max_clk") if k in info}
+            return out
+        finally:
+            amdsmi.amdsmi_shut_down()
     except Exception as e:  # noqa: BLE001  (missing clocks must not stop the benchmark)
-        return {"error": str(e)[:200]}
+        return {"error": "no clock source: %s" % str(e)[:200]}
 
 
 def cpu_model():

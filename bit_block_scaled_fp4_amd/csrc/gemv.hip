@@ -42,6 +42,14 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
 constexpr int kMaxWaves = 16;
+// Passes of at least this many rows share the activation loads between the
+// half-waves. MI355X, graph-timed, same box, two alternating passes: at 4
+// rows fused gate_up 2 x 17408 x 5120 29.4 against 30.7 us and the LM head
+// 27.1 against 28.2 us; at 1 and 2 rows the down projection was 0.3-0.5 us
+// slower with sharing and the other shapes equal.
+#ifndef FP4_SHARE_X_MIN_ROWS
+#define FP4_SHARE_X_MIN_ROWS 4
+#endif
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
@@ -261,12 +269,21 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv(const GemvArgs a) {
         }
       }
       const int off = (c * kChunkK + hl * 32) * 2;   // past K (ragged last chunk): zeros
+      // Both half-waves need the same 32 activations per lane. With kShareX
+      // each half loads two of the four 16-byte units (half h: units 2h,
+      // 2h + 1) and a lane swap hands each lane the other half's pair.
+      constexpr bool kShareX = MT >= FP4_SHARE_X_MIN_ROWS;
 #pragma unroll
       for (int mi = 0; mi < MT; ++mi) {
         const int row = min(m0 + mi, M - 1);
         const __amdgpu_buffer_rsrc_t rx = rsrc(a.x + (int64_t)row * K, K * 2);
+        if (kShareX) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) f.x[mi][q] = ld16<0>(rx, off + q * 16);
+          for (int q = 0; q < 2; ++q) f.x[mi][q] = ld16<0>(rx, off + (2 * h + q) * 16);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) f.x[mi][q] = ld16<0>(rx, off + q * 16);
+        }
       }
       uint4 gn[4];
       if (MODE == kRms) {
@@ -276,6 +293,26 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv(const GemvArgs a) {
       }
       // keep every load of the round ahead of the arithmetic
       __builtin_amdgcn_sched_barrier(0);
+      if (kShareX) {
+        // permlane32_swap(v, v) returns the low half-wave's v in every lane as
+        // its first result and the high half's as its second (checked on
+        // MI355X): units 0, 1 come from half 0, units 2, 3 from half 1
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi) {
+          uint32_t lo[8], hi[8];
+#pragma unroll
+          for (int d = 0; d < 8; ++d) {
+            const uint32_t v = word(f.x[mi][d >> 2], d & 3);
+            const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+            lo[d] = r[0];
+            hi[d] = r[1];
+          }
+          f.x[mi][0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+          f.x[mi][1] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
+          f.x[mi][2] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+          f.x[mi][3] = make_uint4(hi[4], hi[5], hi[6], hi[7]);
+        }
+      }
       if (MODE == kRms) {
 #pragma unroll
         for (int mi = 0; mi < MT; ++mi)

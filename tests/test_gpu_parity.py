@@ -166,7 +166,11 @@ def run_gemv(bits_w, bits_x):
                                    (520, 3072, 32), (130, 4096, 40), (64, 1024, 64),
                                    # M = 1 with more than 16 chunks: about one workgroup per CU, every
                                    # wave streaming several chunks (1 and 2 row groups per workgroup)
-                                   (100, 17424, 1), (3000, 20480, 1)])
+                                   (100, 17424, 1), (3000, 20480, 1),
+                                   # several row groups per workgroup, each over several rounds: the
+                                   # workgroup's tiles go round-robin over its waves (a ragged last
+                                   # workgroup with one valid group; M = 2 and 4 with three and five chunks)
+                                   (2056, 17472, 1), (4100, 3008, 2), (4104, 5120, 4)])
 def test_gemv_small_shapes(N, K, M):
     print("gemv", N, K, M, flush=True)
     bw = bf16_tensor((N, K), N * 7 + K, 0.03, outlier_p=0.002, outlier_scale=20.0)
