@@ -469,6 +469,51 @@ def other_configs(fp4, torch, timer, w27, gpu_bf16, dev, x_in0, x_mid0):
             fp4.gemv(xs[3072], ws["down"], out=d1)
     us = [u / 28 for u in timer.time_calls(token, 6)]
     res["c1_qwen3_0p6b_decode_28_layers"] = dict(line(us, 8847360), unit="per layer", launches_per_layer=4)
+    # the same step with the next projection's weights streamed into the caches during each product: a
+    # forked branch of the graph (a second stream of the same priority, joined at the end) runs the
+    # streaming-read probe on the next call's weight tiles while the current call computes; the products
+    # keep their order on the main stream
+    lib = fp4.raw()
+    lib.fp4_bench_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    side = torch.cuda.Stream()
+    psink = torch.zeros(1 << 12, dtype=torch.int32, device=dev)
+
+    def calls(layer_set):
+        out = []
+        for ws, xs in layer_set:
+            out.append(((lambda ws=ws, xs=xs: fp4.gemv_multi(xs[1024], [ws["q"], ws["k"], ws["v"]],
+                                                               [qkv, qkv[:, 2048:], qkv[:, 3072:]], [4096] * 3)),
+                        [ws["q"], ws["k"], ws["v"]]))
+            out.append(((lambda ws=ws, xs=xs: fp4.gemv(xs[2048], ws["o"], out=o)), [ws["o"]]))
+            out.append(((lambda ws=ws, xs=xs: fp4.gemv_multi(xs[1024], [ws["gate"], ws["up"]], [gu1, gu1[:, 3072:]],
+                                                               [6144] * 2)), [ws["gate"], ws["up"]]))
+            out.append(((lambda ws=ws, xs=xs: fp4.gemv(xs[3072], ws["down"], out=d1)), [ws["down"]]))
+        return out
+    seqs = [calls(ls) for ls in sets]
+
+    def token_prefetch(i):
+        seq = seqs[i % len(seqs)]
+        main = torch.cuda.current_stream()
+        for k, (call, _) in enumerate(seq):
+            if k + 1 < len(seq):
+                ev = torch.cuda.Event()
+                ev.record(main)
+                side.wait_event(ev)
+                for w in seq[k + 1][1]:
+                    nb = w.packed.numel() // 1024 * 1024
+                    rc = lib.fp4_bench_stream_read(w.packed.data_ptr(), nb, 64, 4, 1, 0, 0, psink.data_ptr(),
+                                                   side.cuda_stream)
+                    if rc != 0:
+                        raise RuntimeError("fp4_bench_stream_read: %d" % rc)
+            call()
+        done = torch.cuda.Event()
+        done.record(side)
+        main.wait_event(done)
+    us = [u / 28 for u in timer.time_calls(token_prefetch, 6)]
+    res["c1_qwen3_0p6b_decode_28_layers_next_weights_prefetched"] = dict(line(us, 8847360), unit="per layer",
+                                                                        launches_per_layer=4)
+    del seqs
     # the same layers with their neighbours fused: RMS norm (eps 1e-6) inside the QKV launch, SwiGLU inside
     # the gate_up launch writing bf16 h, and the down projection reading that h
     from workloads import norm_gain
