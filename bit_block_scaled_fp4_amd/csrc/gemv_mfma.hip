@@ -51,11 +51,17 @@
 // order.
 //
 // LDS banks (measured on MI355X with replayed address patterns and the
-// SQ_LDS_BANK_CONFLICT counter): a 16-byte read of a half-wave is free of
-// conflicts when lanes l and l + 16 use the same 16-byte bank group (address
-// bits 4..7) or the same address, and the 16 lane positions use distinct
-// groups (or the same address); 4-byte accesses of a wave are free when
-// their 64 banks differ. The 8-row kernel's layouts follow that rule.
+// SQ_LDS_BANK_CONFLICT counter):
+//   - 16-byte reads and writes of a half-wave are free of conflicts when
+//     lanes l and l + 16 use the same 16-byte bank group (address bits 4..7)
+//     or the same address, and the 16 lane positions use distinct groups (or
+//     the same address);
+//   - 8-byte reads and writes: 32 lanes a cycle over 64 four-byte banks, one
+//     address read by several lanes is a broadcast;
+//   - 4-byte accesses are free when the 64 lanes use 64 distinct banks;
+//     4- and 2-byte reads that put several lanes on one dword cost about two
+//     conflict cycles an instruction.
+// Every LDS access of both kernels follows these rules (conflict counter 0).
 #include <algorithm>
 
 #include <atomic>
@@ -407,12 +413,24 @@ __global__ __launch_bounds__(64 * kWaves) void k_gemv_mma16(const MmaArgs a) {
   const int pe = min(pb + a.pairs_per_wg, a.npairs);
   const int rr = n16 & 7;
 
-  // Lane (q, n) takes the 16-byte piece 4t + q (t = 0..7) of weight row n and
-  // feeds its elements 8j .. 8j+7 to MFMA (t, j); the A lane (q, m) reads the
-  // matching activations x[m][32(4t + q) + 8j ..]. Wave-private region: codes
-  // [T][row][piece ^ (row + 8T)] x 16 B (the writes, 8 lanes of one row, and
-  // the reads, 16 lanes of consecutive rows, spread over all banks), then the
-  // two tiles' 512 scale bytes as loaded.
+  // Lane (q, n) takes the 16-byte piece P = 16 (q % 2) + 2t + q / 2 (t =
+  // 0..7) of weight row n and feeds its elements 8j .. 8j+7 to MFMA (t, j);
+  // the A lane (q, m) reads the matching activations x[m][32P + 8j ..]. In
+  // each half-wave the lanes n and n + 16 thus read pieces P and P + 16 of
+  // one row. Every LDS access below follows the 16-byte bank rule (lanes l
+  // and l + 16 of a half-wave in one bank group or at one address, the 16
+  // lane positions in distinct groups) or the 8-byte one (32 lanes a cycle,
+  // 64 banks, one address broadcasts; 4- and 2-byte reads with several lanes
+  // on one dword measured about two conflict cycles each):
+  //   - codes: row n (0..15 over the pair) at 512 n, piece P at ((P / 16)
+  //     << 8) + (((P % 16) ^ n) << 4): written from the loads as they come
+  //     (lane (h, l) holds piece l), read as above;
+  //   - activations: row m at 2048 m, 16-byte unit u at ((u / 64) << 10) +
+  //     (((u % 64) ^ m) << 4);
+  //   - scales: tile T's 512 bytes in 8-byte slots (row parity h, block
+  //     pair l) at 8192 + 512 T + 256 h + 8 (l ^ (2T + h)), written 8
+  //     bytes a lane as loaded; a lane reads its whole slot and keeps bytes
+  //     2i and 2i + 1 (i = rr / 2: blocks 2P and 2P + 1 of its row).
   uint8_t* tw = tr + wave * kTrBytes;
   auto transpose_in = [&](const PairFrag& f) {
     const int h = lane >> 5, l = lane & 31;
@@ -420,28 +438,30 @@ __global__ __launch_bounds__(64 * kWaves) void k_gemv_mma16(const MmaArgs a) {
     for (int T = 0; T < 2; ++T) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 2 * i + h;
-        *reinterpret_cast<uint4*>(tw + T * 4096 + r * 512 + ((l ^ (r + 8 * T)) * 16)) = f.w[T][i];
+        const int n = 8 * T + 2 * i + h;
+        *reinterpret_cast<uint4*>(tw + n * 512 + ((l >> 4) << 8) + (((l & 15) ^ n) << 4)) = f.w[T][i];
       }
-      *reinterpret_cast<uint2*>(tw + 8192 + T * 512 + lane * 8) = f.s[T];
+      *reinterpret_cast<uint2*>(tw + 8192 + T * 512 + h * 256 + ((l ^ (2 * T + h)) << 3)) = f.s[T];
     }
   };
+  auto xaddr = [](int m, int u) { return m * 2048 + ((u >> 6) << 10) + (((u & 63) ^ m) << 4); };
   PairFrag cur;
   load_pair(a, pb + wave, pb, pe, c, lane, cur);   // in flight while the activations are staged
 
-  // activations of chunk c, rows m0 .. m0+15: row m at 2048m, 16-byte unit u
-  // stored at position (u + m) & 127
+  // activations of chunk c, rows m0 .. m0+15: half-wave e (of 64) stages
+  // row e / 4, units 16 (e % 4) + l % 16 and 64 more (lanes l and l + 16)
   {
     const int rows = min(kMRows, a.M - a.m0);
     for (int t = threadIdx.x; t < kMRows * 128; t += 64 * kWaves) {
-      const int m = t >> 7, u = t & 127;
+      const int L = t & 63, e = ((t >> 6) << 1) + (L >> 5);
+      const int m = e >> 2, u = (((L >> 4) & 1) << 6) + ((e & 3) << 4) + (L & 15);
       uint4 v = make_uint4(0, 0, 0, 0);
       if (m < rows) {
         const __amdgpu_buffer_rsrc_t rx = rsrc(a.x + (int64_t)(a.m0 + m) * K, K * 2);
         const u32x4_t r = __builtin_amdgcn_raw_buffer_load_b128(rx, (c * kChunkK + u * 8) * 2, 0, 0);   // past K: 0
         v = make_uint4(r[0], r[1], r[2], r[3]);
       }
-      *reinterpret_cast<uint4*>(xs + m * 2048 + ((u + m) & 127) * 16) = v;
+      *reinterpret_cast<uint4*>(xs + xaddr(m, u)) = v;
     }
   }
   __syncthreads();
@@ -457,16 +477,16 @@ __global__ __launch_bounds__(64 * kWaves) void k_gemv_mma16(const MmaArgs a) {
     for (int t = 0; t < 8; ++t) {
       // one piece at a time: keeps the compiler from hoisting every operand
       __builtin_amdgcn_sched_barrier(0);
-      const int P = 4 * t + q;
-      const uint4 wv = *reinterpret_cast<const uint4*>(tw + T * 4096 + rr * 512 + ((P ^ (rr + 8 * T)) * 16));
-      const uint32_t sc = *reinterpret_cast<const uint16_t*>(tw + 8192 + T * 512 + (rr & 1) * 256 + P * 8 + (rr >> 1) * 2);
+      const int P = ((q & 1) << 4) + 2 * t + (q >> 1);
+      const uint4 wv = *reinterpret_cast<const uint4*>(tw + n16 * 512 + ((P >> 4) << 8) + (((P & 15) ^ n16) << 4));
+      const uint2 sv = *reinterpret_cast<const uint2*>(tw + 8192 + T * 512 + (rr & 1) * 256 + ((P ^ (2 * T + (rr & 1))) << 3));
+      const uint32_t sc = (rr & 4 ? sv.y : sv.x) >> ((rr & 2) << 3);   // bytes 2i, 2i + 1 of the slot, i = rr / 2
       const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)sc, 0);
       const float s1 = __builtin_amdgcn_cvt_f32_fp8((int)sc, 1);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const bf16x8_t b = decode8(word(wv, j), j < 2 ? s0 : s1);
-        const int u = 16 * t + 4 * q + j;
-        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(xs + n16 * 2048 + ((u + n16) & 127) * 16);
+        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(xs + xaddr(n16, 4 * P + j));
         acc2[t & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b, acc2[t & 1], 0, 0, 0);
       }
     }
