@@ -389,7 +389,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv(const GemvArgs a) {
 // one tile per wave per round, rounds issued one after the other (a second
 // tile in flight per wave measured no faster). Short K packs about four
 // waves per workgroup.
-//   M > 1: wc = ceil(C / 3).
+//   M > 1: wc = ceil(C / 3) below 8 chunks; from 8 chunks on, one row
+//     group of 8 waves per workgroup (two waves per SIMD; 7 or 9 leave the
+//     SIMDs unevenly loaded): down 5120 x 17408 at M = 2 / 3 / 4 13.7 /
+//     18.0 / 18.7 against 14.5 / 20.3 / 20.6 us with 6 waves, 16.6 / 22.1 /
+//     22.3 with 9.
 //   M = 1, at most 16 chunks: one round (wc = C), unless the launch has at
 //     least 8 row groups per CU, where two rounds (wc = ceil(C / 2)) are
 //     faster (gate_up 34816 x 5120: 17.6 against 18.0-18.7 us).
@@ -420,7 +424,7 @@ static int64_t plan_mt(GemvArgs& a, int gw, int wc) {
       wc = (a.C + 1) / 2;
     }
   }
-  int w = wc > 0 ? wc : (MT == 1 ? (a.C + rounds - 1) / rounds : (a.C + 2) / 3);
+  int w = wc > 0 ? wc : (MT == 1 ? (a.C + rounds - 1) / rounds : a.C >= 8 ? 8 : (a.C + 2) / 3);
   a.wc = std::max(1, std::min(w, kMaxWaves));
   if (gw <= 0) {
     // about four waves per workgroup, but never so many row groups per

@@ -170,7 +170,11 @@ def run_gemv(bits_w, bits_x):
                                    # several row groups per workgroup, each over several rounds: the
                                    # workgroup's tiles go round-robin over its waves (a ragged last
                                    # workgroup with one valid group; M = 2 and 4 with three and five chunks)
-                                   (2056, 17472, 1), (4100, 3008, 2), (4104, 5120, 4)])
+                                   (2056, 17472, 1), (4100, 3008, 2), (4104, 5120, 4),
+                                   # M = 2..4 with at least 8 chunks: one row group of 8 waves per
+                                   # workgroup, waves taking chunks j, j + 8, ... (a ragged K tail;
+                                   # 17 chunks and a partial last row group)
+                                   (300, 8208, 2), (9, 16400, 3)])
 def test_gemv_small_shapes(N, K, M):
     print("gemv", N, K, M, flush=True)
     bw = bf16_tensor((N, K), N * 7 + K, 0.03, outlier_p=0.002, outlier_scale=20.0)
