@@ -500,10 +500,14 @@ __global__ __launch_bounds__(64 * kWaves) void k_gemv_mma16(const MmaArgs a) {
 
 // y[m][n] = gscale * sum over chunks (in order) of the partials. A thread
 // owns four rows (m, ..., m + 3) of one output column: one 16-byte partial
-// per chunk, up to 16 chunks loaded together (indices past the last chunk
-// are clamped to it and their values dropped), then added in chunk order.
+// per chunk, P chunks loaded together (indices past the last chunk are
+// clamped to it and their values dropped), then added in chunk order. P is
+// the smallest of 8, 16, 24, 32 that covers C (one round of loads up to 32
+// chunks). 64-thread workgroups spread a small launch over the CUs (the
+// 16-row down projection 5120 x 17408: 320 workgroups instead of 80).
 // grid: npairs * 16 * ceil(rows / 4) threads, rows = min(16, M - m0).
-__global__ __launch_bounds__(256) void k_reduce(const MmaArgs a) {
+template <int P>
+__global__ __launch_bounds__(64) void k_reduce(const MmaArgs a) {
   const int r4 = (min(kMRows, a.M - a.m0) + 3) >> 2;
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (pair, n16, m4)
   if (t >= (int64_t)a.npairs * 16 * r4) return;
@@ -517,12 +521,12 @@ __global__ __launch_bounds__(256) void k_reduce(const MmaArgs a) {
   const int64_t cstride = (int64_t)a.npairs * 64;   // in f32x4
   const f32x4_t* src = reinterpret_cast<const f32x4_t*>(a.ws) + (int64_t)pair * 64 + n16 * 4 + m4;
   f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-  for (int c0 = 0; c0 < a.C; c0 += 16) {
-    f32x4_t v[16];
+  for (int c0 = 0; c0 < a.C; c0 += P) {
+    f32x4_t v[P];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = src[(int64_t)min(c0 + i, a.C - 1) * cstride];
+    for (int i = 0; i < P; ++i) v[i] = src[(int64_t)min(c0 + i, a.C - 1) * cstride];
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
+    for (int i = 0; i < P; ++i)
       if (c0 + i < a.C) s += v[i];
   }
 #pragma unroll
@@ -648,7 +652,15 @@ hipError_t launch_gemv_mma(const GemvArgs& g, float* partials, unsigned* counter
       hipLaunchKernelGGL(k_gemv_mma16, grid, block, 0, s, a);
     if (use_ws && !a.cnt) {
       const int64_t n = pairs * 16 * ((rows + 3) / 4);
-      hipLaunchKernelGGL(k_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+      const dim3 rg((unsigned)((n + 63) / 64)), rb(64);
+      if (a.C <= 8)
+        hipLaunchKernelGGL(k_reduce<8>, rg, rb, 0, s, a);
+      else if (a.C <= 16)
+        hipLaunchKernelGGL(k_reduce<16>, rg, rb, 0, s, a);
+      else if (a.C <= 24)
+        hipLaunchKernelGGL(k_reduce<24>, rg, rb, 0, s, a);
+      else
+        hipLaunchKernelGGL(k_reduce<32>, rg, rb, 0, s, a);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
