@@ -14,9 +14,11 @@
 // activation rows of its chunk into LDS; its waves then walk the pairs, each
 // pair needing only weight loads. With one chunk the kernel writes y
 // directly. Otherwise the chunk partials meet in one of two ways:
-//   - in the caller's workspace [C][pairs][16 n][16 m], and a second kernel
-//     adds the C partials of every output in chunk order and applies the
-//     tensor scale (deterministic);
+//   - in the caller's workspace [C][pairs][16 n][16 m], added in chunk order
+//     with the tensor scale applied (deterministic): for passes of at most 8
+//     rows by the last of a pair block's C workgroups to finish, inside the
+//     launch (header counters of the workspace); for 16-row passes by a
+//     second kernel;
 //   - without a workspace, a fill kernel first zeroes y and every workgroup
 //     adds its scaled partials into y with fp32 atomics (the order of the
 //     chunk sums, and so the last bits of y, can vary between calls).

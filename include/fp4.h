@@ -201,8 +201,9 @@ FP4_API int fp4_gemv(float *y, const void *x_bf16, const void *packed, const voi
              int64_t M, int64_t N, int64_t K, void *stream);
 
 /* fp4_gemv with a workspace (see Conventions; NULL = fp4_gemv). A chunked
- * matrix-core product keeps the chunk partial sums in the workspace and a
- * second kernel adds them in chunk order: results are deterministic. */
+ * matrix-core product keeps the chunk partial sums in the workspace and adds
+ * them in chunk order (inside the launch for passes of at most 8 rows, in a
+ * second kernel for 16-row passes): results are deterministic. */
 FP4_API int fp4_gemv_ws(float *y, const void *x_bf16, const void *packed, const void *scales, const float *gscale,
                         int64_t M, int64_t N, int64_t K, void *workspace, size_t workspace_bytes, void *stream);
 
