@@ -135,20 +135,34 @@ __device__ __forceinline__ uint32_t dec2(uint32_t w, int sel, float s) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{e[0] * s, e[1] * s}, bf16x2_t));
 }
 
+// Two E2M1 codes (byte `sel` of w) times 2^(c - 127) as packed bf16, in one
+// v_cvt_scalef32_pk_bf16_fp4: the conversion applies the exponent field of
+// its fp32 scale operand, here c << 23. Checked on MI355X against the fp32
+// product path for every code byte and every c: bit-identical for c <= 254,
+// subnormal results included; c = 255 (a NaN scale, which no quantiser here
+// writes) gives a NaN of the other sign.
+__device__ __forceinline__ uint32_t dec2_e8m0(uint32_t w, int sel, float s) {
+  switch (sel) {
+    case 0: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0));
+    case 1: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1));
+    case 2: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2));
+    default: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3));
+  }
+}
+
 // Eight codes (word `slice` of a 16-byte piece) as a bf16x8 MFMA operand;
 // `sc` holds the piece's two E4M3 block scales (slices 0, 1 use byte 0,
 // slices 2, 3 byte 1) or, MX, its one E8M0 scale (byte 0; e2m1 * 2^(c-127)
 // is exact in bf16 for the scales a quantiser produces from bf16 weights).
 template <bool MX>
 __device__ __forceinline__ bf16x8_t decode8(const uint4& piece, uint32_t sc, int slice) {
-  float s;
-  if (MX) {
-    const uint32_t c = sc & 0xFFu;
-    s = c == 0u ? __uint_as_float(0x00400000u) : c == 255u ? __uint_as_float(0x7FC00000u) : __uint_as_float(c << 23);
-  } else {
-    s = slice < 2 ? __builtin_amdgcn_cvt_f32_fp8((int)sc, 0) : __builtin_amdgcn_cvt_f32_fp8((int)sc, 1);
-  }
   const uint32_t w = word(piece, slice);
+  if (MX) {
+    const float s = __uint_as_float((sc & 0xFFu) << 23);
+    const uint4 o = make_uint4(dec2_e8m0(w, 0, s), dec2_e8m0(w, 1, s), dec2_e8m0(w, 2, s), dec2_e8m0(w, 3, s));
+    return __builtin_bit_cast(bf16x8_t, o);
+  }
+  const float s = slice < 2 ? __builtin_amdgcn_cvt_f32_fp8((int)sc, 0) : __builtin_amdgcn_cvt_f32_fp8((int)sc, 1);
   const uint4 o = make_uint4(dec2(w, 0, s), dec2(w, 1, s), dec2(w, 2, s), dec2(w, 3, s));
   return __builtin_bit_cast(bf16x8_t, o);
 }
