@@ -35,8 +35,9 @@
 //   weight rows and returns the two blocks' sums separately, so the E4M3
 //   block scale (which has a mantissa) multiplies the fp32 result once per
 //   block: the codes convert straight to unscaled bf16
-//   (v_cvt_scalef32_pk_bf16_fp4 at scale 1, two per instruction). About 300
-//   vector instructions per pair instead of about 670 for the scaled decode.
+//   (v_cvt_scalef32_pk_bf16_fp4 at scale 1, two per instruction). About 450
+//   vector instructions per pair (SQ_INSTS_VALU on MI355X) against about
+//   690 for the scaled decode of the 16-row kernel.
 // - k_gemv_mma16 (9 to 16 rows): A rows are the 16 activation rows and each
 //   weight is decoded with its block scale to exact bf16 (E2M1 * E4M3 has at
 //   most 6 significant bits) before the MFMA; splitting blocks there would
