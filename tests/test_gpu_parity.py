@@ -174,7 +174,9 @@ def run_gemv(bits_w, bits_x):
                                    # M = 2..4 with at least 8 chunks: one row group of 8 waves per
                                    # workgroup, waves taking chunks j, j + 8, ... (a ragged K tail;
                                    # 17 chunks and a partial last row group)
-                                   (300, 8208, 2), (9, 16400, 3)])
+                                   (300, 8208, 2), (9, 16400, 3),
+                                   # 9 to 16 rows over 17, 25 and 40 chunks without a workspace (atomic adds)
+                                   (56, 17408, 10), (24, 25600, 16), (40, 40960, 12)])
 def test_gemv_small_shapes(N, K, M):
     print("gemv", N, K, M, flush=True)
     bw = bf16_tensor((N, K), N * 7 + K, 0.03, outlier_p=0.002, outlier_scale=20.0)
@@ -407,6 +409,29 @@ def test_gemv_multi_matrix_core_ragged_projections(M):
         assert_within_tolerance(o.cpu().numpy(), yr, l1, "multi mfma ws M=%d" % M)
         assert_within_tolerance(on.cpu().numpy(), yr, l1, "multi mfma atomic M=%d" % M)
         assert torch.equal(o, o2)
+
+
+@pytest.mark.parametrize("N,K,M", [(56, 17408, 10), (24, 25600, 16), (40, 40960, 12), (30, 5120, 9)])
+def test_gemv_chunk_sums_16_rows(N, K, M):
+    """16-row matrix-core passes with a workspace: the second kernel adds all
+    chunk partials of an output in chunk order, loading 8, 16, 24 or 32 of
+    them per round (5, 17, 25 chunks: one round; 40: two rounds of 32, the
+    second clamped). Within the tolerance of the oracle, repeatable bit for
+    bit, the counter header left at zero."""
+    print("chunk sums", N, K, M, flush=True)
+    bw = bf16_tensor((N, K), 3 * N + K, 0.02, outlier_p=0.002, outlier_scale=20.0)
+    bx = bf16_tensor((M, K), 70 + M, 1.0)
+    w = gpu_quant(bw)
+    x = to_gpu_bf16(bx)
+    work = ws_for(fp4.OP_GEMV, M, K, [N])
+    y = fp4.gemv(x, w, workspace=work)
+    y2 = fp4.gemv(x, w, workspace=work)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(work[:65536]) == 0
+    assert torch.equal(y, y2)
+    p, s, g = oracle.quantize(bw)
+    yr, l1 = oracle.gemv(bx, p, s, g, threads=THREADS)
+    assert_within_tolerance(y.cpu().numpy(), yr, l1, "chunk sums %dx%d M=%d" % (N, K, M))
 
 
 def test_workspace_too_small_is_an_error():
