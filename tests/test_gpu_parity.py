@@ -935,6 +935,46 @@ def test_gemv_swiglu(case, M):
     assert not np.all(np.abs(hg - oracle.swiglu(u, g)) <= swiglu_bound(u, g, l1u, l1g, oracle.swiglu(u, g)))
 
 
+def test_neighbours_long_k_two_rows():
+    """The fused neighbours at M = 2 over 8 or more K chunks, where the
+    vector-ALU launch runs one row group of 8 waves per projection (SwiGLU:
+    gate and up together, 16 waves): SwiGLU at K = 9216 (9 chunks, 136 rows)
+    within swiglu_bound, and RMSNorm before two projections (200 and 64 rows)
+    at K = 8192 within RMS_TOL * sum|w * xn|."""
+    M = 2
+    K = 9216
+    bg, bu = (bf16_tensor((136, K), s, 0.03, outlier_p=0.002, outlier_scale=20.0) for s in (401, 402))
+    bx = bf16_tensor((M, K), 403, 1.0)
+    wg, wu = gpu_quant(bg), gpu_quant(bu)
+    need = fp4.workspace_bytes(fp4.OP_GEMV_SWIGLU, M, K, [136])
+    h = fp4.gemv_swiglu(to_gpu_bf16(bx), wg, wu, workspace=fp4.new_workspace(need, dev()) if need else None)
+    torch.cuda.synchronize()
+    hg = bf16_to_float32(h.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+    g, l1g = oracle.gemv(bx, *oracle.quantize(bg), threads=THREADS)
+    u, l1u = oracle.gemv(bx, *oracle.quantize(bu), threads=THREADS)
+    href = oracle.swiglu(g, u)
+    err = np.abs(hg - href)
+    bound = swiglu_bound(g, u, l1g, l1u, href)
+    assert np.all(err <= bound), "swiglu worst %.3g" % float((err / bound).max())
+
+    K = 8192
+    Ns = (200, 64)
+    bws = [bf16_tensor((N, K), 410 + N, 0.03, outlier_p=0.002, outlier_scale=20.0) for N in Ns]
+    ws = [gpu_quant(b) for b in bws]
+    bx = bf16_tensor((M, K), 411, 3.0)
+    gb = gain_bits(K, 56)
+    outs = [torch.full((M, N), float("nan"), device=dev()) for N in Ns]
+    need = fp4.workspace_bytes(fp4.OP_GEMV_RMSNORM, M, K, list(Ns))
+    fp4.gemv_multi_rmsnorm(to_gpu_bf16(bx), to_gpu_bf16(gb), 1e-6, ws, outs, list(Ns),
+                           workspace=fp4.new_workspace(need, dev()) if need else None)
+    torch.cuda.synchronize()
+    xn = oracle.rmsnorm(bx, gb, 1e-6)
+    for b, o in zip(bws, outs):
+        yr, l1 = oracle.gemv_f64(xn, *oracle.quantize(b))
+        ok, worst = oracle.tolerance_ok(o.cpu().numpy().astype(np.float64), yr, l1, RMS_TOL)
+        assert ok, "rmsnorm worst %.3g" % worst
+
+
 # ------------------------------------------------------------------- MXFP4
 _mx_cache = {}
 
