@@ -1071,6 +1071,29 @@ def test_mx_prefill_small_shapes(M, N, K):
     assert_within_tolerance(y.cpu().numpy(), yr, l1, "mx prefill %d %d %d" % (M, N, K))
 
 
+@pytest.mark.parametrize("name", list(mx_edge_tensors().keys()))
+def test_mx_products_on_edge_tensors(name):
+    """The MXFP4 decode product and prefill on the edge tensors (zeros, tiny
+    ~1e-30 and huge ~1e30 weights, a wide dynamic range, a ragged shape, the
+    worked example): the prefill decodes E8M0-scaled codes in one conversion
+    whose scale operand carries the shared exponent, far from 2^0 here. Both
+    within the tolerance of the oracle (products of zero rows exactly 0)."""
+    bw = mx_edge_tensors()[name]
+    N, K = bw.shape
+    print("mx edge products", name, N, K, flush=True)
+    w = fp4.quantize_mx(to_gpu_bf16(bw), "mx_tiled")
+    p, s = oracle.mx_quantize(bw)
+    for M in (1, 37):
+        bx = bf16_tensor((M, K), 6400 + M + N, 1.0)
+        x = to_gpu_bf16(bx)
+        yg = fp4.gemv_mx(x, w)
+        yp = fp4.gemm_prefill_mx(x, w)
+        torch.cuda.synchronize()
+        yr, l1 = oracle.mx_gemv(bx, p, s)
+        assert_within_tolerance(yg.cpu().numpy(), yr, l1, "mx edge gemv %s M=%d" % (name, M))
+        assert_within_tolerance(yp.cpu().numpy(), yr, l1, "mx edge prefill %s M=%d" % (name, M))
+
+
 def test_mx_prefill_full_size_sampled_rows():
     """2048 tokens x the 27B-class gate projection 17408 x 5120 in MXFP4,
     checked on 8 sampled token rows (all 17408 outputs each)."""
