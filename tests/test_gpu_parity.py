@@ -77,6 +77,33 @@ def test_quantize_bit_exact_edge_cases(name):
     check_quant_bytes(edge_tensors()[name], name)
 
 
+@pytest.mark.parametrize("name", list(edge_tensors().keys()))
+def test_products_on_edge_tensors(name):
+    """The decode products and the prefill on the quantiser's edge tensors
+    (rounding ties, zeros, tiny ~1e-30 and huge ~1e30 weights, a wide dynamic
+    range, ragged shapes, the worked example): 1 row on the vector ALUs, 3 and
+    8 rows on the 8-row matrix-core kernel with and without a workspace, 12
+    rows on the 16-row kernel, 37 rows through the prefill. Every result
+    within the tolerance of the oracle (products of zero rows exactly 0)."""
+    bw = edge_tensors()[name]
+    N, K = bw.shape
+    print("edge products", name, N, K, flush=True)
+    w = gpu_quant(bw)
+    p, s, g = oracle.quantize(bw)
+    for M in (1, 3, 8, 12, 37):
+        bx = bf16_tensor((M, K), 6500 + M + N, 1.0)
+        x = to_gpu_bf16(bx)
+        yr, l1 = oracle.gemv(bx, p, s, g, threads=THREADS)
+        if M == 37:
+            got = [("prefill", fp4.gemm_prefill(x, w))]
+        else:
+            work = ws_for(fp4.OP_GEMV, M, K, [N])
+            got = [("gemv", fp4.gemv(x, w)), ("gemv ws", fp4.gemv(x, w, workspace=work))]
+        torch.cuda.synchronize()
+        for what, y in got:
+            assert_within_tolerance(y.cpu().numpy(), yr, l1, "edge %s %s M=%d" % (name, what, M))
+
+
 @pytest.mark.parametrize("wl,t", [("gemv_1024", "w"), ("qwen3_0p6b_decode", "L1.q"), ("qwen3_0p6b_decode", "L1.o"),
                                   ("qwen3_0p6b_decode", "L28.down"), ("dense27b_layer", "gate"),
                                   ("dense27b_layer", "up"), ("dense27b_layer", "down"), ("lm_head", "w")])
