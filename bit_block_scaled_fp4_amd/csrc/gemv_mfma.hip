@@ -342,35 +342,40 @@ __global__ __launch_bounds__(64 * kWaves) void k_gemv_mma8(const MmaArgs a) {
   const int a_base = (a_valid ? (n16 & 7) * kXsRow8 + ((q & 1) << 10) : 8 * kXsRow8) + ((q >> 1) << 4);
   const int a_step2 = a_valid ? 256 : 0;   // per two piece groups (the window repeats every two)
 
-  PairFrag cur;
-  load_pair(a, pb + wave, pb, pe, c, lane, cur);   // in flight while the activations are staged
-
   // activations of chunk c, rows m0 .. m0+7: row m at kXsRow8 * m, 16-byte
   // unit u (elements 8u .. 8u+7) at ((u & 1) << 10) + ((u >> 1) << 4), so the
   // units 8q and 8q + 8 of the A lanes q and q + 1 share a bank group; then
   // the zero window. Thread t stages unit u of row m with lanes l and l + 16
-  // on units 2k and 2k + 1 (the same 16-byte rule for the writes).
+  // on units 2k and 2k + 1 (the same 16-byte rule for the writes). The
+  // activation loads go out first and the first pair's weight loads after
+  // them, so the staging writes wait for the activations only.
+  constexpr int kXUnits8 = 8 * 128 / (64 * kWaves);
+  uint4 xv[kXUnits8];
   {
     const int rows = min(8, a.M - a.m0);
-    for (int t = threadIdx.x; t < 8 * 128; t += 64 * kWaves) {
-      const int kk = t >> 6, L = t & 63;
+#pragma unroll
+    for (int s = 0; s < kXUnits8; ++s) {
+      const int kk = wave + s * kWaves, L = lane;   // kk: uniform over the wave
       const int m = kk >> 1, u = 64 * (kk & 1) + 32 * (L >> 5) + 2 * (L & 15) + ((L >> 4) & 1);
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (m < rows) {
-        const __amdgpu_buffer_rsrc_t rx = rsrc(a.x + (int64_t)(a.m0 + m) * K, K * 2);
-        const u32x4_t r = __builtin_amdgcn_raw_buffer_load_b128(rx, (c * kChunkK + u * 8) * 2, 0, 0);   // past K: 0
-        v = make_uint4(r[0], r[1], r[2], r[3]);
-      }
-      *reinterpret_cast<uint4*>(xs + m * kXsRow8 + ((u & 1) << 10) + ((u >> 1) << 4)) = v;
+      // rows past M: a zero-byte resource, zeros
+      const __amdgpu_buffer_rsrc_t rx = rsrc(a.x + (int64_t)(a.m0 + min(m, rows - 1)) * K, m < rows ? K * 2 : 0);
+      const u32x4_t r = __builtin_amdgcn_raw_buffer_load_b128(rx, (c * kChunkK + u * 8) * 2, 0, 0);   // past K: 0
+      xv[s] = make_uint4(r[0], r[1], r[2], r[3]);
     }
-    if (threadIdx.x < kZeroWin / 16) *reinterpret_cast<uint4*>(xs + 8 * kXsRow8 + threadIdx.x * 16) = make_uint4(0, 0, 0, 0);
   }
+  PairFrag cur;
+  load_pair(a, pb + wave, pb, pe, c, lane, cur);   // in flight while the activations are staged
+#pragma unroll
+  for (int s = 0; s < kXUnits8; ++s) {
+    const int kk = wave + s * kWaves, L = lane;
+    const int m = kk >> 1, u = 64 * (kk & 1) + 32 * (L >> 5) + 2 * (L & 15) + ((L >> 4) & 1);
+    *reinterpret_cast<uint4*>(xs + m * kXsRow8 + ((u & 1) << 10) + ((u >> 1) << 4)) = xv[s];
+  }
+  if (threadIdx.x < kZeroWin / 16) *reinterpret_cast<uint4*>(xs + 8 * kXsRow8 + threadIdx.x * 16) = make_uint4(0, 0, 0, 0);
   __syncthreads();
 
-  for (int pair = pb + wave; pair < pe; pair += kWaves) {
-    PairFrag nxt;
-    load_pair(a, pair + kWaves, pb, pe, c, lane, nxt);   // next pair's loads overlap this pair's arithmetic
-    transpose_in(cur);
+  auto step = [&](int pair, const PairFrag& cf) {
+    transpose_in(cf);
     const uint4 sv0 = *reinterpret_cast<const uint4*>(tw + rd_scale0);
     const uint4 sv1 = *reinterpret_cast<const uint4*>(tw + rd_scale1);
     const uint32_t sw[8] = {sv0.x, sv0.y, sv0.z, sv0.w, sv1.x, sv1.y, sv1.z, sv1.w};   // byte p: piece p
@@ -400,7 +405,18 @@ __global__ __launch_bounds__(64 * kWaves) void k_gemv_mma8(const MmaArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) tot[i] = acc[i] + __shfl_xor(acc[i], 32);
     if (q < 2) pair_out(a, pair, c, q, n16, tot);   // rows 4q .. 4q+3
-    cur = nxt;
+  };
+  // Two register sets in turn, with no copy between them: a copy would wait
+  // for every outstanding memory operation, the previous pair's partial
+  // stores included, before the next loads go out. The next pair's loads
+  // overlap this pair's arithmetic.
+  PairFrag alt;
+  for (int pair = pb + wave; pair < pe; pair += 2 * kWaves) {
+    load_pair(a, pair + kWaves, pb, pe, c, lane, alt);
+    step(pair, cur);
+    if (pair + kWaves >= pe) break;
+    load_pair(a, pair + 2 * kWaves, pb, pe, c, lane, cur);
+    step(pair + kWaves, alt);
   }
   if (a.cnt && a.C > 1) split_fixup(a, pb, pe);
 }
@@ -448,33 +464,38 @@ __global__ __launch_bounds__(64 * kWaves) void k_gemv_mma16(const MmaArgs a) {
     }
   };
   auto xaddr = [](int m, int u) { return m * 2048 + ((u >> 6) << 10) + (((u & 63) ^ m) << 4); };
-  PairFrag cur;
-  load_pair(a, pb + wave, pb, pe, c, lane, cur);   // in flight while the activations are staged
-
   // activations of chunk c, rows m0 .. m0+15: half-wave e (of 64) stages
-  // row e / 4, units 16 (e % 4) + l % 16 and 64 more (lanes l and l + 16)
+  // row e / 4, units 16 (e % 4) + l % 16 and 64 more (lanes l and l + 16).
+  // The activation loads go out before the first pair's weight loads, so the
+  // staging writes wait for the activations only.
+  constexpr int kXUnits16 = kMRows * 128 / (64 * kWaves);
+  uint4 xv[kXUnits16];
   {
     const int rows = min(kMRows, a.M - a.m0);
-    for (int t = threadIdx.x; t < kMRows * 128; t += 64 * kWaves) {
-      const int L = t & 63, e = ((t >> 6) << 1) + (L >> 5);
-      const int m = e >> 2, u = (((L >> 4) & 1) << 6) + ((e & 3) << 4) + (L & 15);
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (m < rows) {
-        const __amdgpu_buffer_rsrc_t rx = rsrc(a.x + (int64_t)(a.m0 + m) * K, K * 2);
-        const u32x4_t r = __builtin_amdgcn_raw_buffer_load_b128(rx, (c * kChunkK + u * 8) * 2, 0, 0);   // past K: 0
-        v = make_uint4(r[0], r[1], r[2], r[3]);
-      }
-      *reinterpret_cast<uint4*>(xs + xaddr(m, u)) = v;
+#pragma unroll
+    for (int s = 0; s < kXUnits16; ++s) {
+      const int L = lane, e = ((wave + s * kWaves) << 1) + (L >> 5);
+      const int m = (wave + s * kWaves) >> 1, u = (((L >> 4) & 1) << 6) + ((e & 3) << 4) + (L & 15);   // m = e / 4, uniform
+      // rows past M: a zero-byte resource, zeros
+      const __amdgpu_buffer_rsrc_t rx = rsrc(a.x + (int64_t)(a.m0 + min(m, rows - 1)) * K, m < rows ? K * 2 : 0);
+      const u32x4_t r = __builtin_amdgcn_raw_buffer_load_b128(rx, (c * kChunkK + u * 8) * 2, 0, 0);   // past K: 0
+      xv[s] = make_uint4(r[0], r[1], r[2], r[3]);
     }
+  }
+  PairFrag cur;
+  load_pair(a, pb + wave, pb, pe, c, lane, cur);   // in flight while the activations are staged
+#pragma unroll
+  for (int s = 0; s < kXUnits16; ++s) {
+    const int L = lane, e = ((wave + s * kWaves) << 1) + (L >> 5);
+    const int m = (wave + s * kWaves) >> 1, u = (((L >> 4) & 1) << 6) + ((e & 3) << 4) + (L & 15);
+    *reinterpret_cast<uint4*>(xs + xaddr(m, u)) = xv[s];
   }
   __syncthreads();
 
-  for (int pair = pb + wave; pair < pe; pair += kWaves) {
-    PairFrag nxt;
-    load_pair(a, pair + kWaves, pb, pe, c, lane, nxt);   // next pair's loads overlap this pair's arithmetic
+  auto step = [&](int pair, const PairFrag& cf) {
     // two accumulators (even and odd pieces) halve the dependent MFMA chain
     f32x4_t acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    transpose_in(cur);
+    transpose_in(cf);
     const int T = n16 >> 3;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -496,7 +517,15 @@ __global__ __launch_bounds__(64 * kWaves) void k_gemv_mma16(const MmaArgs a) {
     const f32x4_t acc = acc2[0] + acc2[1];
     // lane (q, n16) holds D[m = 4q + i][n = n16]
     pair_out(a, pair, c, q, n16, acc);
-    cur = nxt;
+  };
+  // two register sets in turn, as in k_gemv_mma8
+  PairFrag alt;
+  for (int pair = pb + wave; pair < pe; pair += 2 * kWaves) {
+    load_pair(a, pair + kWaves, pb, pe, c, lane, alt);
+    step(pair, cur);
+    if (pair + kWaves >= pe) break;
+    load_pair(a, pair + 2 * kWaves, pb, pe, c, lane, cur);
+    step(pair + kWaves, alt);
   }
   if (a.cnt && a.C > 1) split_fixup(a, pb, pe);
 }
