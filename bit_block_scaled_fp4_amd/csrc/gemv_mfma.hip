@@ -587,19 +587,21 @@ int resident_per_cu() {
 // Pairs per workgroup. The four waves of a workgroup take its pairs in
 // turn, so a workgroup lasts about ceil(ppw / 4) pair steps, and the grid
 // runs in ceil(workgroups / slots) rounds (slots: workgroups resident on the
-// whole device). The choice minimises rounds x steps over ppw = 4 .. 32,
-// ties to the larger ppw. Sweeps on MI355X (graph-timed, rotating weights)
-// agree within run-to-run noise: e.g. M = 16, gate_up 34816 x 5120 24 pairs
-// (34.0 us against 37-38 with 16), down 5120 x 17408 12 (22.9 against 25.8
-// with 8), LM head 151936 x 1024 20 (27.4 against 35 with 16).
-int pick_pairs_per_wg(int64_t pairs, int C, int64_t slots) {
+// whole device). The choice minimises rounds x steps over ppw = 4 .. 32.
+// Ties go to two steps per wave (ppw 8) for the 8-row kernel, else to the
+// larger ppw. Sweeps on MI355X (graph-timed, rotating weights): at 16 rows
+// gate_up 34816 x 5120 24 pairs (30.5 us against 32.6 with 8), down 5120 x
+// 17408 12 (19.8 against 20.1), LM head 151936 x 1024 20 (25.5 against 28.1
+// with 8); at 8 rows gate_up 8 (27.0 against 28.7 with 16), down 8 (18.5
+// against 19.5 with 4), LM head 8 (23.4 against 23.8 with 16).
+int pick_pairs_per_wg(int64_t pairs, int C, int64_t slots, bool eight) {
   if (slots <= 0) return C <= 8 ? 16 : 8;
   int best = 16;
   int64_t best_cost = -1;
   for (int p = 4; p <= 32; p += 4) {
     const int64_t wgs = (pairs + p - 1) / p * C;
     const int64_t cost = (wgs + slots - 1) / slots * (p / 4);
-    if (best_cost < 0 || cost <= best_cost) {
+    if (best_cost < 0 || cost < best_cost || (cost == best_cost && !(eight && best == 8))) {
       best_cost = cost;
       best = p;
     }
@@ -641,7 +643,7 @@ MmaArgs mma_args(const GemvArgs& g) {
 
 int pairs_per_wg_for(const MmaArgs& a, bool eight) {
   const int64_t ncu = device_cu_count();
-  return pick_pairs_per_wg(a.npairs, a.C, ncu * (eight ? resident_per_cu<true>() : resident_per_cu<false>()));
+  return pick_pairs_per_wg(a.npairs, a.C, ncu * (eight ? resident_per_cu<true>() : resident_per_cu<false>()), eight);
 }
 
 }  // namespace
