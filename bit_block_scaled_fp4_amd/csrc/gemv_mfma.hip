@@ -14,7 +14,9 @@
 // activation rows of its chunk into LDS; its waves then walk the pairs, each
 // pair needing only weight loads. With one chunk the kernel writes y
 // directly. Otherwise the chunk partials meet in one of two ways:
-//   - in the caller's workspace [C][pairs][16 n][16 m], added in chunk order
+//   - in the caller's workspace [C][pairs][16 n][R][4 m] (R = ceil(rows /
+//     4) row quads of the pass, so a pair's partials are one contiguous run
+//     of whole cache lines), added in chunk order
 //     with the tensor scale applied (deterministic): for passes of at most 8
 //     rows by the last of a pair block's C workgroups to finish, inside the
 //     launch (header counters of the workspace); for 16-row passes by a
@@ -144,7 +146,8 @@ __device__ __forceinline__ float fp8_f32(uint32_t w, int sel) {
 
 struct MmaArgs {
   const uint16_t* x;   // bf16 [M][K]
-  float* ws;           // [C][npairs][16][16] partials (C > 1; nullptr: atomic adds into y)
+  float* ws;           // [C][npairs][16 n][r4][4 m] partials, r4 = row quads of the pass (C > 1; nullptr: atomic
+                       // adds into y)
   unsigned* cnt;       // with ws: arrivals per pair block (kCntStride apart, the workspace header, zero
                        // between launches); nullptr: a second kernel adds the partials
   int M, K, C, m0;     // m0: first activation row of this pass
@@ -162,6 +165,9 @@ struct MmaArgs {
 };
 
 __device__ __forceinline__ int proj_of(const struct MmaArgs& a, int pair);
+
+// Row quads of the pass (rows m0 .. min(m0 + 16, M) - 1, four per quad).
+__device__ __forceinline__ int row_quads(const MmaArgs& a) { return (min(kMRows, a.M - a.m0) + 3) >> 2; }
 
 // Epilogue of one pair: lane (q, n16) holds rows m0 + 4q + i (i < 4) of
 // output column n16 of the pair in v[i]. C == 1: y = gscale * v; with a
@@ -184,11 +190,14 @@ __device__ __forceinline__ void pair_out(const MmaArgs& a, int pair, int c, int 
         }
       }
     }
-  } else if (a.m0 + 4 * q < a.M) {   // rows past M are never read back
-    // device-scope store (through to the memory side): the workgroup that adds
-    // the partials may run on another XCD
-    const __amdgpu_buffer_rsrc_t r = rsrc(a.ws + ((int64_t)c * a.npairs + pair) * 256, 1024);
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, (n16 * 16 + 4 * q) * 4, 0, kSc1);
+  } else {
+    const int r4 = row_quads(a);
+    if (q < r4) {   // rows past M are never read back
+      // device-scope store (through to the memory side): the workgroup that
+      // adds the partials may run on another XCD
+      const __amdgpu_buffer_rsrc_t r = rsrc(a.ws + ((int64_t)c * a.npairs + pair) * 64 * r4, 256 * r4);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, (n16 * r4 + q) * 16, 0, kSc1);
+    }
   }
 }
 
@@ -209,7 +218,7 @@ __device__ __forceinline__ void split_fixup(const MmaArgs& a, int pb, int pe) {
   }
   __syncthreads();
   if (!last) return;
-  const int r4 = (min(kMRows, a.M - a.m0) + 3) >> 2;
+  const int r4 = row_quads(a);
   const int items = (pe - pb) * 16 * r4;   // (pair, n16, m4)
   for (int t = threadIdx.x; t < items; t += blockDim.x) {
     const int m4 = t % r4, pn = t / r4, pair = pb + (pn >> 4), n16 = pn & 15;
@@ -223,8 +232,8 @@ __device__ __forceinline__ void split_fixup(const MmaArgs& a, int pb, int pe) {
       for (int i = 0; i < 8; ++i) {   // chunks past C: an empty resource, zeros
         const int c = c0 + i;
         const __amdgpu_buffer_rsrc_t r =
-            rsrc(a.ws + ((int64_t)min(c, a.C - 1) * a.npairs + pair) * 256, c < a.C ? 1024 : 0);
-        v[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (n16 * 16 + 4 * m4) * 4, 0, kSc1));
+            rsrc(a.ws + ((int64_t)min(c, a.C - 1) * a.npairs + pair) * 64 * r4, c < a.C ? 256 * r4 : 0);
+        v[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (n16 * r4 + m4) * 16, 0, kSc1));
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) sum += v[i];
@@ -540,7 +549,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_gemv_mma16(const MmaArgs a) {
 // grid: npairs * 16 * ceil(rows / 4) threads, rows = min(16, M - m0).
 template <int P>
 __global__ __launch_bounds__(64) void k_reduce(const MmaArgs a) {
-  const int r4 = (min(kMRows, a.M - a.m0) + 3) >> 2;
+  const int r4 = row_quads(a);
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (pair, n16, m4)
   if (t >= (int64_t)a.npairs * 16 * r4) return;
   const int m4 = (int)(t % r4);
@@ -550,8 +559,8 @@ __global__ __launch_bounds__(64) void k_reduce(const MmaArgs a) {
   const int n = 16 * (pair - a.proj[p].pair_begin) + n16;
   if (n >= a.proj[p].N) return;
   const float gs = *a.proj[p].gscale;
-  const int64_t cstride = (int64_t)a.npairs * 64;   // in f32x4
-  const f32x4_t* src = reinterpret_cast<const f32x4_t*>(a.ws) + (int64_t)pair * 64 + n16 * 4 + m4;
+  const int64_t cstride = (int64_t)a.npairs * 16 * r4;   // in f32x4
+  const f32x4_t* src = reinterpret_cast<const f32x4_t*>(a.ws) + ((int64_t)pair * 16 + n16) * r4 + m4;
   f32x4_t s = {0.f, 0.f, 0.f, 0.f};
   for (int c0 = 0; c0 < a.C; c0 += P) {
     f32x4_t v[P];
