@@ -116,19 +116,20 @@ int fp4_retile(const void* packed_rm, const void* scales_rm, int64_t N, int64_t 
 }
 
 // Whether 3 or 4 activation rows go to the matrix cores: at least 32 MiB
-// of weights in at most 8 K chunks.
+// of weights.
 static bool gemv_mma_pays(int64_t groups, int64_t chunks) {
-  return chunks <= 8 && groups * chunks * fp4::kTileBytes >= (int64_t(32) << 20);
+  return groups * chunks * fp4::kTileBytes >= (int64_t(32) << 20);
 }
 
 // Few activation rows: the vector-ALU kernel (decode once, two products per
-// weight and row, no second launch). From five rows on, and from three on
-// large launches with few K chunks, the matrix cores: their 8-row kernel
-// costs about the same at 3 to 8 rows, and their split over K chunks adds a
-// second launch that a large launch with few chunks amortises. MI355X, 4
-// rows: fused gate_up 2 x 17408 x 5120 28.2 against 30.7 us, LM head
-// 151936 x 1024 24.3 against 29.8 us; down 5120 x 17408 (17 chunks) 22.8
-// against 21.3 us, so it stays on the vector ALUs.
+// weight and row). From five rows on, and from three on large launches, the
+// matrix cores: their 8-row kernel costs about the same at 3 to 8 rows.
+// MI355X, graph-timed with a workspace, vector ALUs against matrix cores at
+// 3 / 4 rows: fused gate_up 2 x 17408 x 5120 at 4 rows 30.3 against 25.6
+// us; down 5120 x 17408 19.4 / 18.9 against 16.5 / 16.5; 8192 x 28672 39.5
+// / 37.3 against 34.2 / 34.0; 4096 x 14336 (33 MB) 14.0 / 13.1 against 12.5
+// / 12.7; 28672 x 8192 46.0 / 44.2 against 32.1 / 32.0; 2048 x 65536 (64
+// chunks) 26.0 / 23.8 against 23.8 / 23.9.
 static bool gemv_on_valu(const fp4::GemvArgs& a) {
   int64_t groups = 0;
   for (int i = 0; i < a.nproj; ++i) groups += fp4::groups_of(a.proj[i].N);

@@ -220,21 +220,24 @@ __device__ __forceinline__ void split_fixup(const MmaArgs& a, int pb, int pe) {
   if (!last) return;
   const int r4 = row_quads(a);
   const int items = (pe - pb) * 16 * r4;   // (pair, n16, m4)
+  const int cstep = a.npairs * 256 * r4;   // bytes per chunk
+  const __amdgpu_buffer_rsrc_t rw = rsrc(a.ws, a.C * cstep);
   for (int t = threadIdx.x; t < items; t += blockDim.x) {
     const int m4 = t % r4, pn = t / r4, pair = pb + (pn >> 4), n16 = pn & 15;
     const int p = proj_of(a, pair);
     const int n = 16 * (pair - a.proj[p].pair_begin) + n16;
     if (n >= a.proj[p].N) continue;
+    const int off0 = pair * 256 * r4 + (n16 * r4 + m4) * 16;
+    // One resource over the pass's partials (the launcher keeps them and
+    // the offsets of up to 8 chunks past the last below 2^31 bytes): an
+    // offset past the last chunk reads zeros. One descriptor instead of one
+    // per load: the 8-row down 5120 x 17408 at M = 4 15.9 against 19.9 us.
     f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
     for (int c0 = 0; c0 < a.C; c0 += 8) {
       f32x4_t v[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {   // chunks past C: an empty resource, zeros
-        const int c = c0 + i;
-        const __amdgpu_buffer_rsrc_t r =
-            rsrc(a.ws + ((int64_t)min(c, a.C - 1) * a.npairs + pair) * 64 * r4, c < a.C ? 256 * r4 : 0);
-        v[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (n16 * r4 + m4) * 16, 0, kSc1));
-      }
+      for (int i = 0; i < 8; ++i)
+        v[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, off0 + (c0 + i) * cstep, 0, kSc1));
 #pragma unroll
       for (int i = 0; i < 8; ++i) sum += v[i];
     }
@@ -683,11 +686,14 @@ hipError_t launch_gemv_mma(const GemvArgs& g, float* partials, unsigned* counter
       hipLaunchKernelGGL(k_zero_rows, dim3((unsigned)blocks, (unsigned)a.nproj), dim3(256), 0, s, a, rows);
     }
     // In-launch fixup for passes of at most 8 rows (its arrivals need one
-    // header counter per pair block). MI355X, graph-timed: fused gate_up
-    // 2 x 17408 x 5120 at M = 4 27.5 against 29.3 us with the second kernel,
-    // M = 8 29.4 against 30.3; at M = 16 the last workgroups' sums of 16 rows
-    // form a tail (38.7 against 33.9 us), so those passes keep the kernel.
-    a.cnt = use_ws && eight && counters && wgx <= kWsCounters ? counters : nullptr;
+    // header counter per pair block, and its loads address the pass's
+    // partials with 32-bit offsets, up to 8 chunks past the last). MI355X,
+    // graph-timed: fused gate_up 2 x 17408 x 5120 at M = 4 27.5 against 29.3
+    // us with the second kernel, M = 8 29.4 against 30.3; at M = 16 the last
+    // workgroups' sums of 16 rows form a tail (38.7 against 33.9 us), so
+    // those passes keep the kernel.
+    const bool small_ws = ((int64_t)a.C + 8) * pairs * 256 * ((rows + 3) / 4) < (int64_t(1) << 31);
+    a.cnt = use_ws && eight && counters && wgx <= kWsCounters && small_ws ? counters : nullptr;
     const dim3 grid((unsigned)wgx, (unsigned)a.C), block(64 * kWaves);
     if (eight)
       hipLaunchKernelGGL(k_gemv_mma8, grid, block, 0, s, a);

@@ -190,8 +190,9 @@ FP4_API int fp4_retile(const void *packed_rm, const void *scales_rm, int64_t N, 
  * the weights (page "1. The big picture", the batching and speculative
  * decoding bullets of "The most important number in this book").
  * Any M >= 1 is accepted. `packed` holds the tiles; `scales` is unused.
- * Up to 4 rows (and 3-4 rows on large launches with few K chunks aside)
- * run on the vector ALUs, more on the matrix cores in passes of 16 rows.
+ * Up to 4 rows run on the vector ALUs (3-4 rows of a launch reading at
+ * least 32 MiB of weights aside), more on the matrix cores in passes of 16
+ * rows.
  * The matrix-core path splits K into chunks of 1024 over workgroups; with
  * more than one chunk this call (no workspace) first zeroes y with a fill
  * kernel and adds the chunk sums into y with fp32 atomics, so the last

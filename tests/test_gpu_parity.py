@@ -367,10 +367,26 @@ def test_gemv_workload_lm_head(M):
 
 @pytest.mark.parametrize("M", [3, 4])
 def test_gemv_lm_head_three_and_four_rows(M):
-    """3 or 4 rows on a call of at least 32 MiB with at most 8 K chunks go to
+    """3 or 4 rows on a call of at least 32 MiB go to
     the matrix cores (the LM head: one chunk, 87 MB); the rows are the first
     M of the LM head's 8-row activations."""
     bw, bx = weight_bits("lm_head", "w"), act_bits("lm_head", "x_m8")[:M]
+    w = gpu_quant(bw)
+    y = fp4.gemv(to_gpu_bf16(bx), w)
+    torch.cuda.synchronize()
+    p, s, g = oracle_quant("lm_head", "w")
+    yr, l1 = oracle.gemv(bx, p, s, g, threads=THREADS)
+    assert_within_tolerance(y.cpu().numpy(), yr, l1, "lm_head M=%d" % M)
+
+
+@pytest.mark.parametrize("M", [12, 16])
+def test_gemv_lm_head_twelve_and_sixteen_rows(M):
+    """9 to 16 rows of the LM head run the 16-row matrix-core kernel on its
+    one K chunk, writing y without chunk sums. Its launch plan gives each
+    wave five pairs, an odd count, so the pair loop (two register sets in
+    turn) ends halfway through its last iteration. Activations: seeded N(0, 1)
+    rows of the LM head's width."""
+    bw, bx = weight_bits("lm_head", "w"), bf16_tensor((M, 1024), 430 + M, 1.0)
     w = gpu_quant(bw)
     y = fp4.gemv(to_gpu_bf16(bx), w)
     torch.cuda.synchronize()
