@@ -220,6 +220,11 @@ __device__ __forceinline__ void split_fixup(const MmaArgs& a, int pb, int pe) {
   if (!last) return;
   const int r4 = row_quads(a);
   const int items = (pe - pb) * 16 * r4;   // (pair, n16, m4)
+  // One buffer resource over the pass's partials (the launcher keeps them,
+  // and the offsets of up to 8 chunks past the last, below 2^31 bytes); an
+  // offset past the last chunk reads zeros. A resource built per load (its
+  // base differs by chunk and lane) cost about 4 us on the 8-row down 5120 x
+  // 17408 at M = 4: 19.9 against 15.9 us.
   const int cstep = a.npairs * 256 * r4;   // bytes per chunk
   const __amdgpu_buffer_rsrc_t rw = rsrc(a.ws, a.C * cstep);
   for (int t = threadIdx.x; t < items; t += blockDim.x) {
@@ -228,10 +233,6 @@ __device__ __forceinline__ void split_fixup(const MmaArgs& a, int pb, int pe) {
     const int n = 16 * (pair - a.proj[p].pair_begin) + n16;
     if (n >= a.proj[p].N) continue;
     const int off0 = pair * 256 * r4 + (n16 * r4 + m4) * 16;
-    // One resource over the pass's partials (the launcher keeps them and
-    // the offsets of up to 8 chunks past the last below 2^31 bytes): an
-    // offset past the last chunk reads zeros. One descriptor instead of one
-    // per load: the 8-row down 5120 x 17408 at M = 4 15.9 against 19.9 us.
     f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
     for (int c0 = 0; c0 < a.C; c0 += 8) {
       f32x4_t v[8];
