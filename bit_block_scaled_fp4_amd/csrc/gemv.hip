@@ -102,11 +102,18 @@ __device__ __forceinline__ bf16x2_t fp4x2(uint32_t w, int sel) {
   }
 }
 
-// E8M0 (OCP MX) byte `sel` of w -> fp32: 2^(c - 127) (code 0: 2^-127, an
-// fp32 subnormal; 255: NaN).
-__device__ __forceinline__ float e8m0(uint32_t w, int sel) {
-  const uint32_t c = (w >> (8 * sel)) & 0xFFu;
-  return c == 0u ? __uint_as_float(0x00400000u) : c == 255u ? __uint_as_float(0x7FC00000u) : __uint_as_float(c << 23);
+// Byte `sel` of w holds two E2M1 codes; returns them times 2^(c - 127) as
+// two bf16, where `s` carries c in its exponent field (c << 23): the
+// conversion applies only that field. Bit-identical on MI355X to the fp32
+// product for every code byte and every c <= 254, subnormal results
+// included (c = 255, a NaN scale, gives a NaN of the other sign).
+__device__ __forceinline__ bf16x2_t fp4x2_e8m0(uint32_t w, int sel, float s) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3);
+  }
 }
 
 // E4M3 (OCP) byte `sel` of w -> fp32.
@@ -321,11 +328,22 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv(const GemvArgs a) {
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        // row 2i + h: NVFP4, its two block scales are bytes 2(i&1), 2(i&1)+1
-        // of word i >> 1; MXFP4, its one block scale is byte i
+        if (MX) {
+          // row 2i + h, its one E8M0 block scale (byte i) applied by the
+          // conversion itself: exact bf16 weights, no scale multiply
+          const float sc = __uint_as_float(((f.s.x >> (8 * i)) & 0xFFu) << 23);
+          bf16x2_t d[16];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) d[e] = fp4x2_e8m0(word(f.w[i], e >> 2), e & 3, sc);
+#pragma unroll
+          for (int mi = 0; mi < MT; ++mi) acc[mi][i] = dot_block2(d, f.x[mi], 1.0f, 1.0f, acc[mi][i]);
+          continue;
+        }
+        // row 2i + h: its two block scales are bytes 2(i&1), 2(i&1)+1 of
+        // word i >> 1
         const uint32_t sw = i < 2 ? f.s.x : f.s.y;
-        const float s0 = MX ? e8m0(f.s.x, i) : e4m3(sw, (i & 1) * 2);
-        const float s1 = MX ? s0 : e4m3(sw, (i & 1) * 2 + 1);
+        const float s0 = e4m3(sw, (i & 1) * 2);
+        const float s1 = e4m3(sw, (i & 1) * 2 + 1);
         bf16x2_t d[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) d[e] = fp4x2(word(f.w[i], e >> 2), e & 3);
