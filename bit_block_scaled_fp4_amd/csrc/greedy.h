@@ -85,9 +85,12 @@ __device__ void greedy_finish(const GreedyArgs& g, const uint64_t (&k)[NR], int 
     __hip_atomic_store(g.keys + (int64_t)threadIdx.x * S + wg, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (wg != S - 1) return;
-  // J keys per row and thread in one round of loads (NR * J = 16: the
-  // round's loads stay within the product's register budget)
-  constexpr int J = NR >= 16 ? 1 : 16 / NR;
+  // J keys per row and thread in one round of loads, NR * J = 8. MI355X,
+  // LM head 151936 x 1024 at M = 1 (4748 slots), over the plain product:
+  // +3.2-3.3 us with 8 keys a thread and round, +3.7-3.8 with 16, +3.4-3.7
+  // with 4, +4.5-4.6 with 2, +7.2-7.3 with 24 (97 VGPRs: fewer waves for
+  // the product itself).
+  constexpr int J = NR >= 8 ? 1 : 8 / NR;
   uint64_t acc[NR];
   int poll = 0;
   for (;; ++poll) {
