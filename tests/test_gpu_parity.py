@@ -477,6 +477,32 @@ def test_gemv_chunk_sums_16_rows(N, K, M):
     assert_within_tolerance(y.cpu().numpy(), yr, l1, "chunk sums %dx%d M=%d" % (N, K, M))
 
 
+@pytest.mark.parametrize("N,K,M", [(131072, 1040, 6), (4100, 17408, 4)])
+def test_gemv_chunk_sums_8_rows(N, K, M):
+    """Passes of at most 8 rows with a workspace. 131072 x 1040 at 6 rows has
+    more pair blocks (1024 of 8 pairs) than the workspace header has arrival
+    counters (512), so its chunk sums (2 chunks, the second 16 wide) go to
+    the second kernel; 4100 x 17408 at 4 rows adds its 17 chunks inside the
+    launch (the
+    last workgroup of each pair block, three rounds of loads through one
+    buffer resource, a partial last pair). Within the tolerance of the
+    oracle, repeatable bit for bit, the counter header left at zero."""
+    print("chunk sums", N, K, M, flush=True)
+    bw = bf16_tensor((N, K), 5 * N + K, 0.02, outlier_p=0.002, outlier_scale=20.0)
+    bx = bf16_tensor((M, K), 80 + M, 1.0)
+    w = gpu_quant(bw)
+    x = to_gpu_bf16(bx)
+    work = ws_for(fp4.OP_GEMV, M, K, [N])
+    y = fp4.gemv(x, w, workspace=work)
+    y2 = fp4.gemv(x, w, workspace=work)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(work[:65536]) == 0
+    assert torch.equal(y, y2)
+    p, s, g = oracle.quantize(bw)
+    yr, l1 = oracle.gemv(bx, p, s, g, threads=THREADS)
+    assert_within_tolerance(y.cpu().numpy(), yr, l1, "chunk sums %dx%d M=%d" % (N, K, M))
+
+
 def test_workspace_too_small_is_an_error():
     """A workspace smaller than fp4_workspace_bytes reports is rejected before
     any launch; one that is large enough but not 256-byte aligned too."""
