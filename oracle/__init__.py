@@ -272,6 +272,21 @@ def mx_gemv(x_bits: np.ndarray, packed: np.ndarray, scales: np.ndarray):
     return y, l1
 
 
+def mx_a4_product(xq_packed: np.ndarray, xq_scales: np.ndarray, w_packed: np.ndarray, w_scales: np.ndarray):
+    """fp64 product of two MXFP4 operands (y [M][N], l1 [M][N]): activation
+    rows quantised by mx_quantize (the rows of x taken as the rows of a
+    matrix) times MXFP4 weights, y = dequant(xq) @ dequant(w)^T and the error
+    scale l1 = |dequant(xq)| @ |dequant(w)|^T, with fp64 sums (a library
+    matrix product as the summation step). Page "github.com/kekzl/imp", the
+    feature table: MXFP4 in the quantisation row and a block-scaled GEMM in
+    the engine row; both operands block-scaled FP4 is the form that runs at
+    the matrix cores' FP4 rate."""
+    A = mx_dequant(xq_packed, xq_scales)
+    B = mx_dequant(w_packed, w_scales)
+    assert A.shape[1] == B.shape[1]
+    return A @ B.T, np.abs(A) @ np.abs(B).T
+
+
 def mx_tile(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """Canonical MXFP4 -> the GPU library's MXFP4 tiled layout (4352-byte tiles)."""
     packed, pp = _c(packed, np.uint8)

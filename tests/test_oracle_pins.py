@@ -557,6 +557,73 @@ def test_mx_gemv_matches_numpy_on_tiny_matrices():
         assert np.allclose(l1, np.abs(xf) @ np.abs(D).T, rtol=1e-13)
 
 
+def test_mx_a4_product_matches_bit_field_decodes():
+    """Both operands MXFP4: the product equals the one built from decodes
+    that do not use the oracle (E2M1 bit fields, E8M0 through
+    torch.float8_e8m0fnu), and not the one with an operand's K order
+    reversed."""
+    rng = np.random.default_rng(45)
+    for M, N, K in [(1, 1, 32), (2, 3, 64), (5, 9, 1024 + 32)]:
+        x = float32_to_bf16_bits(rng.normal(0, 1, (M, K)).astype(np.float32))
+        W = float32_to_bf16_bits(rng.normal(0, 0.05, (N, K)).astype(np.float32))
+        xp, xs = oracle.mx_quantize(x)
+        wp, ws = oracle.mx_quantize(W)
+        A, B = mx_dequant_from_bits(xp, xs), mx_dequant_from_bits(wp, ws)
+        y, l1 = oracle.mx_a4_product(xp, xs, wp, ws)
+        assert np.allclose(y, A @ B.T, rtol=1e-13, atol=1e-15 * (np.abs(A) @ np.abs(B).T).max())
+        assert np.allclose(l1, np.abs(A) @ np.abs(B).T, rtol=1e-13)
+        if K > 32:
+            assert not np.allclose(y, A[:, ::-1] @ B.T)
+
+
+def test_mx_a4_product_equals_the_bf16_product_on_representable_activations():
+    """Activations that MXFP4 holds exactly (per 32-block: E2M1 values times
+    2^e with a block maximum of 4 or 6, so the shared exponent is e) round-trip
+    through mx_quantize, and then the product of the two MXFP4 operands equals
+    the oracle's MXFP4 x bf16 product (its C path) up to the order of fp64
+    sums."""
+    rng = np.random.default_rng(46)
+    vals = np.array([0, .5, 1, 1.5, 2, 3, 4, 6])
+    M, N, K = 3, 7, 96
+    x = rng.choice(vals, (M, K)) * rng.choice([-1, 1], (M, K))
+    x = x.reshape(M, K // 32, 32)
+    x[:, :, 0] = rng.choice([4.0, -6.0, 6.0, -4.0], (M, K // 32))   # the block maximum
+    x = (x * 2.0 ** rng.integers(-6, 7, (M, K // 32, 1))).reshape(M, K)
+    xb = float32_to_bf16_bits(x.astype(np.float32))
+    assert np.array_equal(bf16_to_float32(xb).astype(np.float64), x)
+    xp, xs = oracle.mx_quantize(xb)
+    assert np.array_equal(oracle.mx_dequant(xp, xs), x)
+    W = float32_to_bf16_bits(rng.normal(0, 0.05, (N, K)).astype(np.float32))
+    wp, ws = oracle.mx_quantize(W)
+    y, l1 = oracle.mx_a4_product(xp, xs, wp, ws)
+    y2, l2 = oracle.mx_gemv(xb, wp, ws)
+    assert np.allclose(y, y2, rtol=1e-13, atol=1e-15 * l2.max())
+    assert np.allclose(l1, l2, rtol=1e-13)
+
+
+def test_mx_a4_product_exact_against_rationals():
+    """One row of x and one weight row of 32 elements each, the weight from
+    the MXFP4 worked example: every product and sum is a short binary
+    fraction, so the fp64 result equals exact rational arithmetic over the
+    codes' bit-field values and the scales' exponents."""
+    Wb, wp, ws = load_mx_example()
+    rng = np.random.default_rng(47)
+    K = wp.shape[1] * 2
+    xv = rng.choice([0, .5, 1, 1.5, 2, 3, 4, 6], (1, K)) * rng.choice([-1, 1], (1, K))
+    xv.reshape(1, K // 32, 32)[:, :, 0] = 6.0
+    xb = float32_to_bf16_bits((xv * 2.0 ** -3).astype(np.float32))
+    xp, xs = oracle.mx_quantize(xb)
+    y, _ = oracle.mx_a4_product(xp, xs, wp, ws)
+    e2 = [minifloat_value(c, 2, 1, 1) for c in range(16)]
+    for n in range(wp.shape[0]):
+        acc = Fraction(0)
+        for k in range(K):
+            qa = xp[0, k // 2] >> (4 * (k % 2)) & 15
+            qw = wp[n, k // 2] >> (4 * (k % 2)) & 15
+            acc += (e2[qa] * Fraction(2) ** (int(xs[0, k // 32]) - 127)) * (e2[qw] * Fraction(2) ** (int(ws[n, k // 32]) - 127))
+        assert y[0, n] == float(acc)
+
+
 def test_mx_tile_matches_reshape_formulation():
     """The MXFP4 device layout written as array reshapes: codes as in the
     NVFP4 tile; scale (row 8g + 2i + h, block 32c + l) at 4096 + 128h + 4l + i."""
