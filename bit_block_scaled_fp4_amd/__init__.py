@@ -63,6 +63,7 @@ _lib.fp4_workspace_bytes.argtypes = [_I, _I64, _I64, ctypes.POINTER(_I64), _I, c
 _lib.fp4_quantize_mx.argtypes = [_P, _I64, _I64, _I, _P, _P, _P]
 _lib.fp4_gemv_mx.argtypes = [_P, _P, _P, _I64, _I64, _I64, _P]
 _lib.fp4_gemm_prefill_mx.argtypes = [_P, _P, _P, _I64, _I64, _I64, _P]
+_lib.fp4_gemm_mx_a4.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _P]
 _lib.fp4_gemv_multi_rmsnorm.argtypes = [ctypes.POINTER(_Proj), _I, _P, _P, ctypes.c_float, _I64, _I64, _P, _SZ, _P]
 _lib.fp4_gemv_swiglu.argtypes = [_P, _I64, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P]
 for _f in ("fp4_layout_bytes", "fp4_quantize", "fp4_quantize_fp8", "fp4_retile", "fp4_gemv", "fp4_gemv_ws",
@@ -203,6 +204,22 @@ def gemv_mx(x: torch.Tensor, w: MXFP4Weight, out: Optional[torch.Tensor] = None)
     out = _out(out, (M, w.N), torch.float32, x.device, "out")
     _check(_lib.fp4_gemv_mx(_dev(out, "y", torch.float32), _dev(x, "x", torch.bfloat16), _dev(w.packed, "packed"),
                             M, w.N, K, _stream(x.device)), "fp4_gemv_mx")
+    return out
+
+
+def gemm_mx_a4(xq: MXFP4Weight, w: MXFP4Weight, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp4_gemm_mx_a4: y[M][N] = dequant(xq) @ dequant(w)^T (fp32) with both
+    operands MXFP4: xq the activation rows from quantize_mx(x, "mx_rowmajor"),
+    w an MX tiled weight."""
+    if xq.layout != MX_ROWMAJOR or xq.scales is None:
+        raise ValueError("xq must come from quantize_mx(x, 'mx_rowmajor')")
+    if xq.K != w.K:
+        raise ValueError("xq has K=%d, weight has K=%d" % (xq.K, w.K))
+    _mx_tiled(w)
+    out = _out(out, (xq.N, w.N), torch.float32, xq.packed.device, "out")
+    _check(_lib.fp4_gemm_mx_a4(_dev(out, "y", torch.float32), _dev(xq.packed, "xq_packed", torch.uint8),
+                               _dev(xq.scales, "xq_scales", torch.uint8), _dev(w.packed, "packed"), xq.N, w.N, w.K,
+                               _stream(xq.packed.device)), "fp4_gemm_mx_a4")
     return out
 
 
@@ -423,5 +440,5 @@ def raw():
 __all__ = ["quantize", "quantize_fp8", "retile", "gemv", "gemv_multi", "gemm_prefill", "gemm_prefill_multi",
            "argmax_rows", "lm_head_greedy", "gemv_multi_rmsnorm", "gemv_swiglu", "layout_bytes", "workspace_bytes",
            "new_workspace", "NVFP4Weight", "OP_GEMV", "OP_GEMM_PREFILL", "OP_ARGMAX_ROWS", "OP_LM_HEAD_GREEDY",
-           "OP_GEMV_RMSNORM", "OP_GEMV_SWIGLU", "MXFP4Weight", "quantize_mx", "gemv_mx", "gemm_prefill_mx",
+           "OP_GEMV_RMSNORM", "OP_GEMV_SWIGLU", "MXFP4Weight", "quantize_mx", "gemv_mx", "gemm_prefill_mx", "gemm_mx_a4",
            "Fp4Error", "raw", "ROWMAJOR", "TILED", "LIB_PATH", "HEADER_PATH"]

@@ -31,7 +31,8 @@ COMMON = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-fvis
 # v_accvgpr_read per value).
 PER_FILE = {"quantize.hip": ["-ffp-contract=off"],
             "gemv_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
-SOURCES = ["fp4_api.hip", "quantize.hip", "gemv.hip", "gemv_mfma.hip", "prefill.hip", "argmax.hip", "device.hip", "read_probe.hip", "noalloc.hip", "neighbours.hip"]
+SOURCES = ["fp4_api.hip", "quantize.hip", "gemv.hip", "gemv_mfma.hip", "prefill.hip", "prefill_a4.hip", "argmax.hip", "device.hip",
+           "read_probe.hip", "noalloc.hip", "neighbours.hip"]
 
 
 def _compile(src: str) -> str:

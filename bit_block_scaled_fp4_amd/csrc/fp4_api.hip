@@ -458,6 +458,17 @@ int fp4_gemm_prefill_mx(float* y, const void* x_bf16, const void* packed, int64_
                                         static_cast<hipStream_t>(stream), 0, 0, true));
 }
 
+int fp4_gemm_mx_a4(float* y, const void* xq_packed, const void* xq_scales, const void* packed, int64_t M, int64_t N,
+                   int64_t K, void* stream) {
+  if (!y || !xq_packed || !xq_scales || !packed) return FP4_ERR_NULL;
+  if (int st = check_nk(N, K)) return st;
+  if (K % 128 != 0 || M < 1 || M > 65535 * 256 || M * N > kMaxElems) return FP4_ERR_SHAPE;
+  if ((N + 7) / 8 * fp4::chunks_of(K) * fp4::kMxTileBytes >= (int64_t(1) << 31)) return FP4_ERR_SHAPE;
+  if (!aligned(xq_packed, 16) || !aligned(packed, 16) || !aligned(xq_scales, 4) || !aligned(y, 4)) return FP4_ERR_ALIGN;
+  return hip_status(fp4::launch_mx_a4(y, static_cast<const uint8_t*>(xq_packed), static_cast<const uint8_t*>(xq_scales),
+                                      static_cast<const uint8_t*>(packed), M, N, K, static_cast<hipStream_t>(stream)));
+}
+
 int fp4_workspace_bytes(int op, int64_t M, int64_t K, const int64_t* Ns, int nproj, size_t* bytes) {
   if (!bytes || !Ns) return FP4_ERR_NULL;
   if (nproj < 1 || nproj > FP4_MAX_PROJ || M < 1 || M > kMaxM) return FP4_ERR_SHAPE;

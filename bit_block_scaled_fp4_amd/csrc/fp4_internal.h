@@ -111,6 +111,11 @@ hipError_t launch_retile(const uint8_t* packed, const uint8_t* scales, int64_t N
 // go to launch_gemv_mma). Positive gw (row groups per workgroup) and wc
 // (waves per row group) override the automatic geometry (tuning).
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t s, int gw = 0, int wc = 0);
+
+// Both operands MXFP4 on the block-scaled FP4 matrix cores (prefill_a4.hip):
+// y [M][N] from activation codes [M][K/2] and scales [M][K/32] and MX tiles.
+hipError_t launch_mx_a4(float* y, const uint8_t* xq_codes, const uint8_t* xq_scales, const uint8_t* w_tiles, int64_t M,
+                        int64_t N, int64_t K, hipStream_t s);
 // Workgroups launch_gemv would launch for `a` (geometry as chosen there).
 int64_t gemv_workgroups(const GemvArgs& a);
 // The SwiGLU launch of the vector-ALU kernel (a.h set, two projections).

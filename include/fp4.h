@@ -163,6 +163,23 @@ FP4_API int fp4_gemv_mx(float *y, const void *x_bf16, const void *packed, int64_
 FP4_API int fp4_gemm_prefill_mx(float *y, const void *x_bf16, const void *packed, int64_t M, int64_t N, int64_t K,
                                 void *stream);
 
+/* Both operands MXFP4, on gfx950's block-scaled FP4 matrix cores (page
+ * "github.com/kekzl/imp", the feature table: MXFP4 in the quantisation
+ * row, a block-scaled GEMM in the engine row). y[M][N] (fp32, ldy = N,
+ * overwritten) = dequant(xq) * dequant(W)^T, where xq holds the activation
+ * rows x[M][K] quantised by fp4_quantize_mx with layout MX_ROWMAJOR
+ * (codes [M][K/2], E8M0 scales [M][K/32], device) and W is an MX_TILED
+ * weight. Each product of two scaled E2M1 values is exact and the sums
+ * are fp32, so y matches that definition closely; against the product with
+ * bf16 activations (fp4_gemm_prefill_mx) it carries the activations' own
+ * quantisation error (E2M1 keeps one mantissa bit), in exchange for the
+ * matrix cores' FP4 rate. K % 128 == 0 and M <= 16776960 (FP4_ERR_SHAPE
+ * otherwise), the tiles below 2^31 bytes; xq_packed and packed 16-byte
+ * aligned, xq_scales and y 4-byte aligned. No workspace, nothing
+ * allocated. */
+FP4_API int fp4_gemm_mx_a4(float *y, const void *xq_packed, const void *xq_scales, const void *packed, int64_t M,
+                           int64_t N, int64_t K, void *stream);
+
 /* The same quantisation for a checkpoint released in FP8 (the imp README:
  * its quantiser builds NVFP4 weights from BF16 or FP8 releases). W_fp8 is
  * [N][K] OCP E4M3 ("fn") codes, one byte per element (device, 16-byte

@@ -25,7 +25,7 @@ def test_every_declared_symbol_is_exported():
                             "fp4_gemm_prefill_ws", "fp4_gemm_prefill_multi", "fp4_gemm_prefill_multi_ws",
                             "fp4_argmax_rows", "fp4_lm_head_greedy", "fp4_quantize_fp8", "fp4_workspace_bytes",
                             "fp4_gemv_multi_noalloc", "fp4_gemv_multi_rmsnorm", "fp4_gemv_swiglu",
-                            "fp4_quantize_mx", "fp4_gemv_mx", "fp4_gemm_prefill_mx"])
+                            "fp4_quantize_mx", "fp4_gemv_mx", "fp4_gemm_prefill_mx", "fp4_gemm_mx_a4"])
     lib = ctypes.CDLL(fp4.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -267,3 +267,12 @@ def test_mx_layout_bytes_and_argument_errors():
     assert L.fp4_gemv_mx(A, A + 8, A, 1, 8, 64, None) == EALIGN
     assert L.fp4_gemm_prefill_mx(A, A, None, 4, 8, 64, None) == ENULL
     assert L.fp4_gemm_prefill_mx(A, A, A, 4, 8, 1 << 22, None) == ESHAPE
+    # both operands MXFP4: K % 128, the row limit of the grid, alignment
+    L.fp4_gemm_mx_a4.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + [ctypes.c_void_p]
+    assert L.fp4_gemm_mx_a4(A, A, None, A, 4, 8, 128, None) == ENULL
+    assert L.fp4_gemm_mx_a4(None, A, A, A, 4, 8, 128, None) == ENULL
+    assert L.fp4_gemm_mx_a4(A, A, A, A, 4, 8, 96, None) == ESHAPE        # K % 128 != 0
+    assert L.fp4_gemm_mx_a4(A, A, A, A, 0, 8, 128, None) == ESHAPE
+    assert L.fp4_gemm_mx_a4(A, A, A, A, 65535 * 256 + 1, 8, 128, None) == ESHAPE
+    assert L.fp4_gemm_mx_a4(A, A + 8, A, A, 4, 8, 128, None) == EALIGN   # codes not 16-byte aligned
+    assert L.fp4_gemm_mx_a4(A, A, A + 2, A, 4, 8, 128, None) == EALIGN   # scales not 4-byte aligned

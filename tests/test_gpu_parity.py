@@ -1174,3 +1174,54 @@ def test_mx_prefill_full_size_sampled_rows():
     p, s = mx_oracle_quant("dense27b_layer", "gate")
     yr, l1 = oracle.mx_gemv(bx[rows], p, s)
     assert_within_tolerance(y[rows].cpu().numpy(), yr, l1, "mx prefill full size")
+
+
+# ------------------------------------------------ both operands MXFP4 (R28)
+def check_mx_a4(y_gpu, y_ref, l1, what):
+    """The block-scaled FP4 product against the oracle's fp64 product of the
+    two dequantised operands: every product is exact and the sums are fp32,
+    so the bar is 1e-4 of sum |a*w| (twenty times tighter than the products
+    with bf16 activations)."""
+    y_gpu = np.asarray(y_gpu, dtype=np.float64).reshape(y_ref.shape)
+    assert np.all(np.isfinite(y_gpu)), what
+    ok, worst = oracle.tolerance_ok(y_gpu, y_ref, l1, rel=1e-4)
+    assert ok, "%s: |y_gpu - y_ref| exceeds 1e-4*sum|a*w| (worst ratio %.3g)" % (what, worst)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 8, 128), (37, 300, 1152), (256, 128, 128), (300, 520, 2048),
+                                   (513, 1000, 5120)])
+def test_mx_a4_small_shapes(M, N, K):
+    """Both operands MXFP4 on the block-scaled FP4 matrix cores: the
+    activations quantised on the GPU bit-exact against the oracle's MXFP4
+    rule, and the product within 1e-4 of sum |a*w|. Shapes: one row; ragged
+    rows and columns over several 256 x 128 tiles (a last row tile of one
+    row, last column tiles of 44 and 104 columns, a ragged last weight row
+    group); 1, 9, 16 and 40 K steps, K a whole or a partial tile chunk."""
+    print("mx a4", M, N, K, flush=True)
+    bw = bf16_tensor((N, K), 9 * N + K, 0.03, outlier_p=0.002, outlier_scale=20.0)
+    bx = bf16_tensor((M, K), 13 * M + K, 1.0, outlier_p=0.002, outlier_scale=20.0)
+    w = fp4.quantize_mx(to_gpu_bf16(bw), "mx_tiled")
+    xq = fp4.quantize_mx(to_gpu_bf16(bx), "mx_rowmajor")
+    y = fp4.gemm_mx_a4(xq, w)
+    torch.cuda.synchronize()
+    xp, xs = oracle.mx_quantize(bx)
+    assert np.array_equal(xq.packed.cpu().numpy().reshape(M, K // 2), xp)
+    assert np.array_equal(xq.scales.cpu().numpy().reshape(M, K // 32), xs)
+    wp, ws = oracle.mx_quantize(bw)
+    yr, l1 = oracle.mx_a4_product(xp, xs, wp, ws)
+    check_mx_a4(y.cpu().numpy(), yr, l1, "mx a4 %dx%dx%d" % (M, N, K))
+
+
+def test_mx_a4_full_size_sampled_rows():
+    """2048 tokens x the 27B-class gate projection 17408 x 5120, both operands
+    MXFP4, checked on 8 sampled token rows (all 17408 outputs each)."""
+    bx = act_bits("prefill", "x")
+    w = fp4.quantize_mx(to_gpu_bf16(weight_bits("dense27b_layer", "gate")), "mx_tiled")
+    xq = fp4.quantize_mx(to_gpu_bf16(bx), "mx_rowmajor")
+    y = fp4.gemm_mx_a4(xq, w)
+    torch.cuda.synchronize()
+    rows = [0, 1, 255, 256, 1000, 1791, 1792, 2047]
+    p, s = mx_oracle_quant("dense27b_layer", "gate")
+    xp, xs = oracle.mx_quantize(bx[rows])
+    yr, l1 = oracle.mx_a4_product(xp, xs, p, s)
+    check_mx_a4(y[rows].cpu().numpy(), yr, l1, "mx a4 full size")
