@@ -18,18 +18,22 @@
 //
 // Tiling. A 256-thread workgroup computes 256 rows x 128 columns; its four
 // waves form a 2 x 2 grid of 128 x 64 (4 x 2 result blocks each). K
-// advances 128 per step (two MFMA steps). Each step's operands are loaded
-// into registers one step ahead and written to one of two LDS stages: per
-// row 64 code bytes (4 chunks of 16) and the 4 scale bytes of the step. A
-// row's chunk j sits in slot j ^ ((row / 4) % 4), which keeps the 16-byte
-// operand reads and the writes of a half-wave in distinct bank groups
-// (rows r and r + 16 in the same group). One barrier per step.
+// advances 128 per step (two MFMA steps). Every global read is a
+// direct-to-LDS buffer load into one of three stages, issued two steps
+// ahead: per stage 256 activation rows and 128 weight rows of 64 code bytes
+// (4 chunks of 16), the activations' 4 scale bytes per row and the weight
+// groups' scale chunks. A row's chunk j sits in slot j ^ ((row / 4) % 4),
+// which keeps the 16-byte operand reads of a half-wave in distinct bank
+// groups (rows r and r + 16 in the same group). Each wave issues the same
+// eight loads per step, so one wait for all but the newest eight and one
+// barrier close a step.
 //
 // Bounds: K is a multiple of 128 (the launcher checks); activation rows
-// past M and weight row groups past N read zeros (buffer loads past the
+// past M and weight row groups past N read zeros (offsets past the
 // resource; the tiled layout pads a ragged last group with zero codes), and
 // the stores skip rows past M and columns past N.
 #include <algorithm>
+#include <atomic>
 
 #include "fp4_internal.h"
 
@@ -38,7 +42,6 @@ namespace {
 
 typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
 constexpr int kBM = 256, kBN = 128, kKS = 128;
@@ -46,7 +49,6 @@ constexpr int kACodes = kBM * 64;              // one stage: 64 code bytes per r
 constexpr int kAScales = kBM * 4;              // 4 scale bytes per row
 constexpr int kBCodes = kBN * 64;
 constexpr int kBScales = (kBN / 8) * 2 * 16;   // 16 row groups x 2 row parities x 16 bytes
-constexpr int kStage = kACodes + kAScales + kBCodes + kBScales;
 
 struct A4Args {
   const uint8_t* xa;   // activation codes [M][K/2]
@@ -57,65 +59,92 @@ struct A4Args {
   int64_t ldy;
 };
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
-}
-
-__device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, int off) {
-  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 
 // slot of 16-byte chunk j of LDS row r
 __device__ __forceinline__ int slot(int r, int j) { return (j ^ ((r >> 2) & 3)) << 4; }
 
+// Buffer resource as four scalars (base, num_records, raw 32-bit format):
+// num_records bytes are readable, anything past them reads as zero.
+__device__ __forceinline__ i32x4_t rsrc4(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  i32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffff));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = kRsrcWord3;
+  return r;
+}
+
+// Direct-to-LDS loads: 16 (dma16) or 4 (dma4) bytes per lane, lane L's
+// bytes landing at lds + 16 L (+ 4 L), lds wave-uniform. Written as
+// assembly (no result registers: the data goes to LDS); completion is
+// awaited explicitly with dma_wait before the barrier that publishes it. M0
+// (reserved, so not listed as clobbered) is written by these statements
+// only: nothing else in this kernel uses it.
+__device__ __forceinline__ void dma16(const i32x4_t& rs, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs),
+               "s"(lds)
+               : "memory");
+}
+__device__ __forceinline__ void dma4(const i32x4_t& rs, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rs),
+               "s"(lds)
+               : "memory");
+}
+template <int N>
+__device__ __forceinline__ void dma_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+constexpr int kStages = 3;
+constexpr int kDmaPerStep = 8;   // per wave: 4 activation code, 2 weight code, 1 activation scale, 1 weight scale
+constexpr int kOffA = 0, kOffB = kACodes, kOffAS = kOffB + kBCodes, kOffBS = kOffAS + kAScales;
+constexpr int kStageBytes = kOffBS + 2 * kBScales;   // the weight scale load fills twice that (lanes 32..63: zeros)
+constexpr int kLdsBytes = kStages * kStageBytes;
+
 __global__ __launch_bounds__(256) void k_mx_a4(const A4Args a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage];
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int n0 = blockIdx.x * kBN, m0 = blockIdx.y * kBM;
-  const int K = a.K, Kh = K >> 1, Ks = K >> 5;
+  const int K = a.K, Kh = K >> 1, Ks = K >> 5, C = a.C;
   const int rows = min(kBM, a.M - m0);
-  const __amdgpu_buffer_rsrc_t ra = rsrc(a.xa + (int64_t)m0 * Kh, (uint32_t)rows * Kh);
-  const __amdgpu_buffer_rsrc_t rs = rsrc(a.xs + (int64_t)m0 * Ks, (uint32_t)rows * Ks);
-  const __amdgpu_buffer_rsrc_t rw = rsrc(a.w, (uint32_t)a.G * a.C * kMxTileBytes);
+  const int g0 = n0 >> 3, ngroups = min(kBN / 8, a.G - g0);
+  const i32x4_t ra = rsrc4(a.xa + (int64_t)m0 * Kh, (uint32_t)rows * Kh);
+  const i32x4_t rs = rsrc4(a.xs + (int64_t)m0 * Ks, (uint32_t)rows * Ks);
+  const i32x4_t rw = rsrc4(a.w + (int64_t)g0 * C * kMxTileBytes, (uint32_t)ngroups * C * kMxTileBytes);
+  const uint32_t sbase = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
 
-  // Loads of one step into registers, all unconditional: a row group past N
-  // (or a lane without a scale chunk) takes an offset past the resource
-  // instead of a branch, so the loads stay in flight through the step's
-  // arithmetic. K is a multiple of the step. Thread t: activation row t
-  // (four code chunks, the step's four scale bytes as one word); weight row
-  // n = t % 128, code chunks 2 (t / 128) and 2 (t / 128) + 1; threads t <
-  // 32: the scale chunk of row group t / 2, row parity t % 2.
-  constexpr int kOut = 0x7ffffff0;   // past every resource (the launcher keeps them below 2^31 bytes)
-  uint4 pa[4], pb[2], ps;
-  uint32_t pas;
-  const int bn = t & 127, bg = (n0 + bn) >> 3, br = (n0 + bn) & 7, bv0 = 2 * (t >> 7);
-  const bool bvalid = bg < a.G;
-  const int sg = (n0 >> 3) + (t >> 1), sh = t & 1;
-  const bool svalid = t < 32 && sg < a.G;
-  auto load = [&](int s) {
-    const int k0 = s * kKS;
+  // DMA lane roles. A code instruction fills 16 LDS rows of 64 bytes: lane
+  // -> row lane / 4 of the 16, slot lane % 4, which holds chunk (lane % 4) ^
+  // ((lane / 16) % 4) (rows of 16-aligned blocks: (row / 4) % 4 is lane / 16).
+  const int dr = lane >> 2, dj = (lane & 3) ^ ((lane >> 4) & 3);
+  // weight row n = 16 e + dr of the block: group 2 e + lane / 32, row
+  // (lane / 4) % 8 of the group: pair q = row / 2, parity h = row % 2
+  const int bq = (dr & 7) >> 1, bh = dr & 1;
+  constexpr uint32_t kOut = 0x80000000u;   // an offset past every resource
+  // weight scale chunk of lane L < 32: group L / 2, row parity L % 2
+  const int sj = lane >> 1, sh = lane & 1;
+  auto issue = [&](int step, int stage) {
+    const int k0 = step * kKS, c = k0 >> 10, p0 = (k0 & 1023) >> 5;
+    const uint32_t st = sbase + stage * kStageBytes;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) pa[u] = ld16(ra, t * Kh + ((k0 + 32 * u) >> 1));
-    pas = __builtin_amdgcn_raw_buffer_load_b32(rs, t * Ks + (k0 >> 5), 0, 0);
-    const int c = k0 >> 10, p0 = (k0 & 1023) >> 5;
-    const int tile = (bg * a.C + c) * kMxTileBytes;
+    for (int i = 0; i < 4; ++i) {   // activation codes: rows 16 d .. 16 d + 15, d = 4 wave + i
+      const int d = 4 * wave + i;
+      dma16(ra, (uint32_t)((16 * d + dr) * Kh + (k0 >> 1) + 16 * dj), st + kOffA + d * 1024);
+    }
 #pragma unroll
-    for (int v = 0; v < 2; ++v)
-      pb[v] = ld16(rw, bvalid ? tile + (br >> 1) * 1024 + (br & 1) * 512 + (p0 + bv0 + v) * 16 : kOut);
-    ps = ld16(rw, svalid ? (sg * a.C + c) * kMxTileBytes + 4096 + sh * 128 + p0 * 4 : kOut);
-  };
-  auto store = [&](int st) {
-    uint8_t* s = lds + st * kStage;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) *reinterpret_cast<uint4*>(s + t * 64 + slot(t, u)) = pa[u];
-    *reinterpret_cast<uint32_t*>(s + kACodes + t * 4) = pas;
-#pragma unroll
-    for (int v = 0; v < 2; ++v)
-      *reinterpret_cast<uint4*>(s + kACodes + kAScales + bn * 64 + slot(bn, bv0 + v)) = pb[v];
-    if (t < 32) *reinterpret_cast<uint4*>(s + kACodes + kAScales + kBCodes + t * 16) = ps;
+    for (int i = 0; i < 2; ++i) {   // weight codes: rows 16 e .. 16 e + 15, e = 2 wave + i
+      const int e = 2 * wave + i, g = 2 * e + (lane >> 5);
+      dma16(rw, (uint32_t)((g * C + c) * kMxTileBytes + bq * 1024 + bh * 512 + (p0 + dj) * 16), st + kOffB + e * 1024);
+    }
+    // activation scales: rows 64 wave + lane, the step's 4 bytes (K / 32 is a multiple of 4)
+    dma4(rs, (uint32_t)((64 * wave + lane) * Ks + (k0 >> 5)), st + kOffAS + wave * 256);
+    // weight scales (every wave loads the same bytes; lanes 32..63 write zeros)
+    dma16(rw, lane < 32 && sj < ngroups ? (uint32_t)((sj * C + c) * kMxTileBytes + 4096 + sh * 128 + p0 * 4) : kOut,
+          st + kOffBS);
   };
 
   f32x16_t acc[4][2];
@@ -127,8 +156,8 @@ __global__ __launch_bounds__(256) void k_mx_a4(const A4Args a) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   const int r32 = lane & 31, kb = lane >> 5;
-  auto compute = [&](int st) {
-    const uint8_t* s = lds + st * kStage;
+  auto compute = [&](int stage) {
+    const uint8_t* s = lds + stage * kStageBytes;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int j = 2 * ks + kb;   // this lane's 32-element block of the step
@@ -137,16 +166,16 @@ __global__ __launch_bounds__(256) void k_mx_a4(const A4Args a) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const int row = 128 * wm + 32 * mt + r32;
-        const uint4 v = *reinterpret_cast<const uint4*>(s + row * 64 + slot(row, j));
+        const uint4 v = *reinterpret_cast<const uint4*>(s + kOffA + row * 64 + slot(row, j));
         av[mt] = i32x8_t{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-        as[mt] = s[kACodes + row * 4 + j];
+        as[mt] = s[kOffAS + row * 4 + j];
       }
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         const int n = 64 * wn + 32 * nt + r32;
-        const uint4 v = *reinterpret_cast<const uint4*>(s + kACodes + kAScales + n * 64 + slot(n, j));
+        const uint4 v = *reinterpret_cast<const uint4*>(s + kOffB + n * 64 + slot(n, j));
         bv[nt] = i32x8_t{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-        bs[nt] = s[kACodes + kAScales + kBCodes + ((n >> 3) * 2 + (n & 1)) * 16 + j * 4 + ((n & 7) >> 1)];
+        bs[nt] = s[kOffBS + ((n >> 3) * 2 + (n & 1)) * 16 + j * 4 + ((n & 7) >> 1)];
       }
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
@@ -157,19 +186,26 @@ __global__ __launch_bounds__(256) void k_mx_a4(const A4Args a) {
     }
   };
 
-  const int nsteps = (K + kKS - 1) / kKS;
-  load(0);
-  store(0);
+  const int nsteps = K / kKS;
+  issue(0, 0);
+  if (nsteps > 1) {
+    issue(1, 1);
+    dma_wait<kDmaPerStep>();
+  } else {
+    dma_wait<0>();
+  }
   __syncthreads();
+  int stage = 0;
   for (int s = 0; s < nsteps; ++s) {
-    const bool more = s + 1 < nsteps;
-    if (more) load(s + 1);
-    // the next step's loads stay in flight through this step's arithmetic
-    __builtin_amdgcn_sched_barrier(0);
-    compute(s & 1);
-    __builtin_amdgcn_sched_barrier(0);
-    if (more) store((s + 1) & 1);
+    const bool ahead = s + 2 < nsteps;
+    if (ahead) issue(s + 2, stage == 0 ? 2 : stage - 1);   // the stage step s - 1 used
+    compute(stage);
+    if (ahead)
+      dma_wait<kDmaPerStep>();   // step s + 1 landed; step s + 2 may still be in flight
+    else
+      dma_wait<0>();
     __syncthreads();
+    stage = stage == 2 ? 0 : stage + 1;
   }
 
 #pragma unroll
@@ -200,8 +236,20 @@ hipError_t launch_mx_a4(float* y, const uint8_t* xq_codes, const uint8_t* xq_sca
   a.G = (int)((N + 7) / 8);
   a.C = (int)chunks_of(K);
   a.ldy = N;
+  // more than 64 KB of dynamic LDS must be allowed once per device
+  constexpr int kMaxDevices = 64;
+  static std::atomic<bool> attr_set[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  if (!attr_set[dev].load(std::memory_order_acquire)) {   // racing first calls set the same value
+    e = hipFuncSetAttribute((const void*)k_mx_a4, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    if (e != hipSuccess) return e;
+    attr_set[dev].store(true, std::memory_order_release);
+  }
   const dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM)), block(256);
-  hipLaunchKernelGGL(k_mx_a4, grid, block, 0, s, a);
+  hipLaunchKernelGGL(k_mx_a4, grid, block, kLdsBytes, s, a);
   return hipGetLastError();
 }
 
