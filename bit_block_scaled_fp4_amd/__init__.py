@@ -24,11 +24,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfp4.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "fp4.h")
 
-ROWMAJOR, TILED, MX_ROWMAJOR, MX_TILED = 0, 1, 2, 3
+ROWMAJOR, TILED, MX_ROWMAJOR, MX_TILED, MX_ACT = 0, 1, 2, 3, 4
 MAX_PROJ = 8
 OP_GEMV, OP_GEMM_PREFILL, OP_ARGMAX_ROWS, OP_LM_HEAD_GREEDY, OP_GEMV_RMSNORM, OP_GEMV_SWIGLU = 0, 1, 2, 3, 4, 5
-_LAYOUTS = {"rowmajor": ROWMAJOR, "tiled": TILED, "mx_rowmajor": MX_ROWMAJOR, "mx_tiled": MX_TILED,
-            ROWMAJOR: ROWMAJOR, TILED: TILED, MX_ROWMAJOR: MX_ROWMAJOR, MX_TILED: MX_TILED}
+_LAYOUTS = {"rowmajor": ROWMAJOR, "tiled": TILED, "mx_rowmajor": MX_ROWMAJOR, "mx_tiled": MX_TILED, "mx_act": MX_ACT,
+            ROWMAJOR: ROWMAJOR, TILED: TILED, MX_ROWMAJOR: MX_ROWMAJOR, MX_TILED: MX_TILED, MX_ACT: MX_ACT}
 
 if not os.path.exists(LIB_PATH):
     raise ImportError("libfp4.so is not built: run `python -c 'import __graft_entry__ as g; g.build()'` "
@@ -176,15 +176,16 @@ class MXFP4Weight:
 
 
 def quantize_mx(W: torch.Tensor, layout="mx_tiled", out: Optional[MXFP4Weight] = None) -> MXFP4Weight:
-    """fp4_quantize_mx: bf16 W [N][K] (K % 32 == 0) -> MXFP4Weight in `layout`."""
+    """fp4_quantize_mx: bf16 W [N][K] (K % 32 == 0; "mx_act" K % 128 == 0) ->
+    MXFP4Weight in `layout` ("mx_act": the activation operand of gemm_mx_a4)."""
     N, K = W.shape
     lay = _LAYOUTS[layout]
-    if lay not in (MX_ROWMAJOR, MX_TILED):
+    if lay not in (MX_ROWMAJOR, MX_TILED, MX_ACT):
         raise ValueError("quantize_mx takes an MX layout")
     if out is None:
         pb, sb = layout_bytes(N, K, lay)
         out = MXFP4Weight(torch.empty(pb, dtype=torch.uint8, device=W.device),
-                          torch.empty(sb, dtype=torch.uint8, device=W.device) if lay == MX_ROWMAJOR else None, N, K, lay)
+                          torch.empty(sb, dtype=torch.uint8, device=W.device) if lay != MX_TILED else None, N, K, lay)
     _check(_lib.fp4_quantize_mx(_dev(W, "W", torch.bfloat16), N, K, lay, _dev(out.packed, "packed", torch.uint8),
                                 _opt(out.scales, "scales"), _stream(W.device)), "fp4_quantize_mx")
     return out
@@ -209,10 +210,10 @@ def gemv_mx(x: torch.Tensor, w: MXFP4Weight, out: Optional[torch.Tensor] = None)
 
 def gemm_mx_a4(xq: MXFP4Weight, w: MXFP4Weight, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """fp4_gemm_mx_a4: y[M][N] = dequant(xq) @ dequant(w)^T (fp32) with both
-    operands MXFP4: xq the activation rows from quantize_mx(x, "mx_rowmajor"),
+    operands MXFP4: xq the activation rows from quantize_mx(x, "mx_act"),
     w an MX tiled weight."""
-    if xq.layout != MX_ROWMAJOR or xq.scales is None:
-        raise ValueError("xq must come from quantize_mx(x, 'mx_rowmajor')")
+    if xq.layout != MX_ACT or xq.scales is None:
+        raise ValueError("xq must come from quantize_mx(x, 'mx_act')")
     if xq.K != w.K:
         raise ValueError("xq has K=%d, weight has K=%d" % (xq.K, w.K))
     _mx_tiled(w)

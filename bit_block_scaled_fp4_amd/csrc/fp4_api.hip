@@ -51,9 +51,9 @@ int fp4_layout_bytes(int64_t N, int64_t K, int layout, size_t* packed_bytes, siz
     const int64_t tiles = fp4::groups_of(N) * fp4::chunks_of(K);
     *packed_bytes = (size_t)(tiles * fp4::kTileBytes);   // codes and scales share each tile
     *scale_bytes = 0;
-  } else if (layout == FP4_LAYOUT_MX_ROWMAJOR || layout == FP4_LAYOUT_MX_TILED) {
-    if (K % 32 != 0) return FP4_ERR_SHAPE;
-    if (layout == FP4_LAYOUT_MX_ROWMAJOR) {
+  } else if (layout == FP4_LAYOUT_MX_ROWMAJOR || layout == FP4_LAYOUT_MX_TILED || layout == FP4_LAYOUT_MX_ACT) {
+    if (K % (layout == FP4_LAYOUT_MX_ACT ? 128 : 32) != 0) return FP4_ERR_SHAPE;
+    if (layout != FP4_LAYOUT_MX_TILED) {
       *packed_bytes = (size_t)(N * K / 2);
       *scale_bytes = (size_t)(N * K / 32);
     } else {
@@ -95,12 +95,14 @@ int fp4_quantize_fp8(const void* W_fp8, const float* w_scale, int64_t N, int64_t
 }
 
 int fp4_quantize_mx(const void* W_bf16, int64_t N, int64_t K, int layout, void* packed, void* scales, void* stream) {
-  if (layout != FP4_LAYOUT_MX_ROWMAJOR && layout != FP4_LAYOUT_MX_TILED) return FP4_ERR_LAYOUT;
-  if (!W_bf16 || !packed || (layout == FP4_LAYOUT_MX_ROWMAJOR && !scales)) return FP4_ERR_NULL;
+  if (layout != FP4_LAYOUT_MX_ROWMAJOR && layout != FP4_LAYOUT_MX_TILED && layout != FP4_LAYOUT_MX_ACT)
+    return FP4_ERR_LAYOUT;
+  if (!W_bf16 || !packed || (layout != FP4_LAYOUT_MX_TILED && !scales)) return FP4_ERR_NULL;
   if (int st = check_nk(N, K)) return st;
-  if (K % 32 != 0) return FP4_ERR_SHAPE;
+  if (K % (layout == FP4_LAYOUT_MX_ACT ? 128 : 32) != 0) return FP4_ERR_SHAPE;
   if (!aligned(W_bf16, 16) || !aligned(packed, 16)) return FP4_ERR_ALIGN;
-  return hip_status(fp4::launch_quantize_mx(static_cast<const uint16_t*>(W_bf16), N, K, layout == FP4_LAYOUT_MX_TILED,
+  return hip_status(fp4::launch_quantize_mx(static_cast<const uint16_t*>(W_bf16), N, K,
+                                            layout == FP4_LAYOUT_MX_TILED ? 1 : layout == FP4_LAYOUT_MX_ACT ? 2 : 0,
                                             static_cast<uint8_t*>(packed), static_cast<uint8_t*>(scales),
                                             static_cast<hipStream_t>(stream)));
 }
@@ -462,7 +464,8 @@ int fp4_gemm_mx_a4(float* y, const void* xq_packed, const void* xq_scales, const
                    int64_t K, void* stream) {
   if (!y || !xq_packed || !xq_scales || !packed) return FP4_ERR_NULL;
   if (int st = check_nk(N, K)) return st;
-  if (K % 128 != 0 || M < 1 || M > 65535 * 256 || M * N > kMaxElems) return FP4_ERR_SHAPE;
+  if (K % 128 != 0 || M < 1 || M > 65535 * 256 || M * N > kMaxElems || M * (K / 32) >= (int64_t(1) << 31))
+    return FP4_ERR_SHAPE;
   if ((N + 7) / 8 * fp4::chunks_of(K) * fp4::kMxTileBytes >= (int64_t(1) << 31)) return FP4_ERR_SHAPE;
   if (!aligned(xq_packed, 16) || !aligned(packed, 16) || !aligned(xq_scales, 4) || !aligned(y, 4)) return FP4_ERR_ALIGN;
   return hip_status(fp4::launch_mx_a4(y, static_cast<const uint8_t*>(xq_packed), static_cast<const uint8_t*>(xq_scales),

@@ -103,7 +103,7 @@ hipError_t launch_quantize(const uint16_t* W, int64_t N, int64_t K, bool tiled, 
 hipError_t launch_quantize_fp8(const uint8_t* W, const float* w_scale, int64_t N, int64_t K, bool tiled,
                                uint8_t* packed, uint8_t* scales, float* gscale, hipStream_t s);
 // MXFP4 quantisation of bf16 W (K % 32 == 0), one pass.
-hipError_t launch_quantize_mx(const uint16_t* W, int64_t N, int64_t K, bool tiled, uint8_t* packed, uint8_t* scales,
+hipError_t launch_quantize_mx(const uint16_t* W, int64_t N, int64_t K, int mode, uint8_t* packed, uint8_t* scales,
                               hipStream_t s);
 hipError_t launch_retile(const uint8_t* packed, const uint8_t* scales, int64_t N, int64_t K, uint8_t* tiles,
                          hipStream_t s);

@@ -52,7 +52,7 @@ constexpr int kBScales = (kBN / 8) * 2 * 16;   // 16 row groups x 2 row parities
 
 struct A4Args {
   const uint8_t* xa;   // activation codes [M][K/2]
-  const uint8_t* xs;   // activation scales [M][K/32]
+  const uint8_t* xs;   // activation scales [K/128][M][4]
   const uint8_t* w;    // MX tiled weights, G * C tiles of kMxTileBytes
   float* y;            // [M][ldy]
   int M, N, K, G, C;
@@ -100,7 +100,7 @@ __device__ __forceinline__ void dma_wait() {
 constexpr int kStages = 3;
 constexpr int kDmaPerStep = 8;   // per wave: 4 activation code, 2 weight code, 1 activation scale, 1 weight scale
 constexpr int kOffA = 0, kOffB = kACodes, kOffAS = kOffB + kBCodes, kOffBS = kOffAS + kAScales;
-constexpr int kStageBytes = kOffBS + 2 * kBScales;   // the weight scale load fills twice that (lanes 32..63: zeros)
+constexpr int kStageBytes = kOffBS + kBScales;
 constexpr int kLdsBytes = kStages * kStageBytes;
 
 __global__ __launch_bounds__(256) void k_mx_a4(const A4Args a) {
@@ -113,7 +113,9 @@ __global__ __launch_bounds__(256) void k_mx_a4(const A4Args a) {
   const int rows = min(kBM, a.M - m0);
   const int g0 = n0 >> 3, ngroups = min(kBN / 8, a.G - g0);
   const i32x4_t ra = rsrc4(a.xa + (int64_t)m0 * Kh, (uint32_t)rows * Kh);
-  const i32x4_t rs = rsrc4(a.xs + (int64_t)m0 * Ks, (uint32_t)rows * Ks);
+  // the whole scale array: a slab's rows past M read the next step's first
+  // rows (scales of zero codes, in rows never stored) or, at the end, zeros
+  const i32x4_t rs = rsrc4(a.xs, (uint32_t)a.M * Ks);
   const i32x4_t rw = rsrc4(a.w + (int64_t)g0 * C * kMxTileBytes, (uint32_t)ngroups * C * kMxTileBytes);
   const uint32_t sbase = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
 
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(256) void k_mx_a4(const A4Args a) {
   // (lane / 4) % 8 of the group: pair q = row / 2, parity h = row % 2
   const int bq = (dr & 7) >> 1, bh = dr & 1;
   constexpr uint32_t kOut = 0x80000000u;   // an offset past every resource
-  // weight scale chunk of lane L < 32: group L / 2, row parity L % 2
+  // weight scale chunk of lane L < 8: group 4 wave + L / 2, row parity L % 2
   const int sj = lane >> 1, sh = lane & 1;
   auto issue = [&](int step, int stage) {
     const int k0 = step * kKS, c = k0 >> 10, p0 = (k0 & 1023) >> 5;
@@ -140,11 +142,15 @@ __global__ __launch_bounds__(256) void k_mx_a4(const A4Args a) {
       const int e = 2 * wave + i, g = 2 * e + (lane >> 5);
       dma16(rw, (uint32_t)((g * C + c) * kMxTileBytes + bq * 1024 + bh * 512 + (p0 + dj) * 16), st + kOffB + e * 1024);
     }
-    // activation scales: rows 64 wave + lane, the step's 4 bytes (K / 32 is a multiple of 4)
-    dma4(rs, (uint32_t)((64 * wave + lane) * Ks + (k0 >> 5)), st + kOffAS + wave * 256);
-    // weight scales (every wave loads the same bytes; lanes 32..63 write zeros)
-    dma16(rw, lane < 32 && sj < ngroups ? (uint32_t)((sj * C + c) * kMxTileBytes + 4096 + sh * 128 + p0 * 4) : kOut,
-          st + kOffBS);
+    // activation scales: the step's 4 bytes of rows m0 + 64 wave + lane (contiguous rows)
+    dma4(rs, (uint32_t)((step * a.M + m0 + 64 * wave + lane) * 4), st + kOffAS + wave * 256);
+    // weight scales: wave w loads the 16-byte chunks of groups 4 w .. 4 w + 3
+    // with lanes 0..7 (the other lanes idle, so they write no LDS)
+    if (lane < 8) {
+      const int g = 4 * wave + sj;
+      dma16(rw, g < ngroups ? (uint32_t)((g * C + c) * kMxTileBytes + 4096 + sh * 128 + p0 * 4) : kOut,
+            st + kOffBS + wave * 128);
+    }
   };
 
   f32x16_t acc[4][2];
@@ -156,36 +162,54 @@ __global__ __launch_bounds__(256) void k_mx_a4(const A4Args a) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   const int r32 = lane & 31, kb = lane >> 5;
-  auto compute = [&](int stage) {
+  // One MFMA step's operands: 4 activation and 2 weight fragments with
+  // their scales, for 32-element block 2 ks + kb of the stage.
+  struct Frag {
+    i32x8_t av[4], bv[2];
+    int as[4], bs[2];
+  };
+  auto load = [&](int stage, int ks, Frag& f) {
     const uint8_t* s = lds + stage * kStageBytes;
+    const int j = 2 * ks + kb;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int j = 2 * ks + kb;   // this lane's 32-element block of the step
-      i32x8_t av[4], bv[2];
-      int as[4], bs[2];
+    for (int mt = 0; mt < 4; ++mt) {
+      const int row = 128 * wm + 32 * mt + r32;
+      const uint4 v = *reinterpret_cast<const uint4*>(s + kOffA + row * 64 + slot(row, j));
+      f.av[mt] = i32x8_t{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+      f.as[mt] = s[kOffAS + row * 4 + j];
+    }
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const int row = 128 * wm + 32 * mt + r32;
-        const uint4 v = *reinterpret_cast<const uint4*>(s + kOffA + row * 64 + slot(row, j));
-        av[mt] = i32x8_t{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-        as[mt] = s[kOffAS + row * 4 + j];
-      }
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int n = 64 * wn + 32 * nt + r32;
-        const uint4 v = *reinterpret_cast<const uint4*>(s + kOffB + n * 64 + slot(n, j));
-        bv[nt] = i32x8_t{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-        bs[nt] = s[kOffBS + ((n >> 3) * 2 + (n & 1)) * 16 + j * 4 + ((n & 7) >> 1)];
-      }
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[mt], bv[nt], acc[mt][nt], 4, 4, 0, as[mt], 0,
-                                                                          bs[nt]);
+    for (int nt = 0; nt < 2; ++nt) {
+      const int n = 64 * wn + 32 * nt + r32;
+      const uint4 v = *reinterpret_cast<const uint4*>(s + kOffB + n * 64 + slot(n, j));
+      f.bv[nt] = i32x8_t{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+      f.bs[nt] = s[kOffBS + ((n >> 3) * 2 + (n & 1)) * 16 + j * 4 + ((n & 7) >> 1)];
     }
   };
+  auto mma = [&](const Frag& f) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.av[mt], f.bv[nt], acc[mt][nt], 4, 4, 0,
+                                                                        f.as[mt], 0, f.bs[nt]);
+  };
+  // 8 MFMAs with the 12 LDS reads of the other half-step between them
+  auto interleave = [] {
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two LDS reads
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  };
 
+  // Software pipeline: the first half of a step multiplies fragments read
+  // before the barrier while the second half's fragments are read; the
+  // second half multiplies while the next step's first fragments are read
+  // (after the barrier that publishes that step's stage). The barrier's
+  // fence completes every LDS read issued before it, so a stage is free for
+  // the next load two steps later.
   const int nsteps = K / kKS;
   issue(0, 0);
   if (nsteps > 1) {
@@ -195,17 +219,24 @@ __global__ __launch_bounds__(256) void k_mx_a4(const A4Args a) {
     dma_wait<0>();
   }
   __syncthreads();
+  Frag f0, f1;
+  load(0, 0, f0);
   int stage = 0;
   for (int s = 0; s < nsteps; ++s) {
     const bool ahead = s + 2 < nsteps;
     if (ahead) issue(s + 2, stage == 0 ? 2 : stage - 1);   // the stage step s - 1 used
-    compute(stage);
+    load(stage, 1, f1);
+    mma(f0);
+    interleave();
     if (ahead)
       dma_wait<kDmaPerStep>();   // step s + 1 landed; step s + 2 may still be in flight
     else
       dma_wait<0>();
     __syncthreads();
     stage = stage == 2 ? 0 : stage + 1;
+    load(stage, 0, f0);   // past the last step this reads a stale stage, unused
+    mma(f1);
+    interleave();
   }
 
 #pragma unroll

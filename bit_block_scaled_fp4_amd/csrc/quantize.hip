@@ -211,12 +211,15 @@ __global__ __launch_bounds__(256) void k_encode(const Src src, int64_t N, int64_
 // and rounded to E2M1 as in k_encode. A block with amax 0 keeps scale 0 and
 // codes 0. Tiled layout: rows and blocks over the padded space; the tile is
 // kMxTileBytes with the scale of (row 2i + h, block l) at
-// kTileCodes + 128h + 4l + i.
+// kTileCodes + 128h + 4l + i. mode 0 row-major, 1 tiled, 2 the activation
+// operand layout (row-major codes; the scale of (row n, block b) at
+// ((b / 4) N + n) 4 + b % 4, K a multiple of 128).
 // grid: rows * segs workgroups, segs = ceil(bpr / 256); block 256.
-__global__ __launch_bounds__(256) void k_mx_encode(const uint16_t* __restrict__ W, int64_t N, int64_t K, int tiled,
+__global__ __launch_bounds__(256) void k_mx_encode(const uint16_t* __restrict__ W, int64_t N, int64_t K, int mode,
                                                    uint8_t* __restrict__ packed, uint8_t* __restrict__ scales) {
   const int64_t kb = K / 32;                          // blocks per row
   const int64_t C = chunks_of(K);
+  const bool tiled = mode == 1;
   const int64_t bpr = tiled ? C * 32 : kb;            // blocks per (padded) row
   const uint32_t segs = (uint32_t)((bpr + 255) / 256);
   const uint32_t wg = blockIdx.x;
@@ -256,7 +259,7 @@ __global__ __launch_bounds__(256) void k_mx_encode(const uint16_t* __restrict__ 
   }
   if (!tiled) {
     *reinterpret_cast<uint4*>(packed + n * (K / 2) + b * 16) = make_uint4(q[0], q[1], q[2], q[3]);
-    scales[n * kb + b] = (uint8_t)sc;
+    scales[mode == 2 ? ((b >> 2) * N + n) * 4 + (b & 3) : n * kb + b] = (uint8_t)sc;
   } else {
     const int64_t g = n / kGroupRows, r = n % kGroupRows;
     const int64_t c = b / 32, l = b % 32;
@@ -345,13 +348,14 @@ hipError_t launch_quantize_fp8(const uint8_t* W, const float* w_scale, int64_t N
   return launch_quantize_src(SrcFp8{W, w_scale}, W, N, K, tiled, packed, scales, gscale, s);
 }
 
-hipError_t launch_quantize_mx(const uint16_t* W, int64_t N, int64_t K, bool tiled, uint8_t* packed, uint8_t* scales,
+hipError_t launch_quantize_mx(const uint16_t* W, int64_t N, int64_t K, int mode, uint8_t* packed, uint8_t* scales,
                               hipStream_t s) {
+  const bool tiled = mode == 1;
   const int64_t rows = tiled ? groups_of(N) * kGroupRows : N;
   const int64_t bpr = tiled ? chunks_of(K) * 32 : K / 32;
   const int64_t wgs = rows * ((bpr + 255) / 256);
   if (wgs > UINT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_mx_encode, dim3((unsigned)wgs), dim3(256), 0, s, W, N, K, tiled ? 1 : 0, packed, scales);
+  hipLaunchKernelGGL(k_mx_encode, dim3((unsigned)wgs), dim3(256), 0, s, W, N, K, mode, packed, scales);
   return hipGetLastError();
 }
 

@@ -107,7 +107,8 @@ typedef enum {
     FP4_LAYOUT_ROWMAJOR = 0,     /* NVFP4, canonical */
     FP4_LAYOUT_TILED = 1,        /* NVFP4, device tiles */
     FP4_LAYOUT_MX_ROWMAJOR = 2,  /* MXFP4, canonical: packed [N][K/2], E8M0 scales [N][K/32] */
-    FP4_LAYOUT_MX_TILED = 3      /* MXFP4, device tiles of 4352 bytes (below) */
+    FP4_LAYOUT_MX_TILED = 3,     /* MXFP4, device tiles of 4352 bytes (below) */
+    FP4_LAYOUT_MX_ACT = 4        /* MXFP4 activation operand of fp4_gemm_mx_a4 (below) */
 } fp4_layout;
 
 /* Human-readable text for a status code (static storage, never NULL). */
@@ -115,8 +116,9 @@ FP4_API const char *fp4_status_string(int status);
 
 /* Bytes of the packed and scale arrays for an N x K weight in `layout`.
  * ROWMAJOR: N*K/2 and N*K/16. TILED: G*C*4608 and 0 (the scales live in
- * the tiles, see above). MX_ROWMAJOR: N*K/2 and N*K/32; MX_TILED: G*C*4352
- * and 0 (both need K % 32 == 0). Host-only; enqueues nothing. */
+ * the tiles, see above). MX_ROWMAJOR and MX_ACT: N*K/2 and N*K/32; MX_TILED:
+ * G*C*4352 and 0 (K % 32 == 0; MX_ACT K % 128 == 0). Host-only; enqueues
+ * nothing. */
 FP4_API int fp4_layout_bytes(int64_t N, int64_t K, int layout, size_t *packed_bytes, size_t *scale_bytes);
 
 /* Quantise a bf16 weight W [N][K] (device) to NVFP4 in `layout`, writing
@@ -147,7 +149,10 @@ FP4_API int fp4_quantize(const void *W_bf16, int64_t N, int64_t K, int layout, v
  * scales; MX_TILED writes the tiles into `packed` (scales unused): rows in
  * groups of 8, K in chunks of 1024, tile (g, c) the 4352 bytes at
  * (g*C + c)*4352, codes as in the NVFP4 tile, then byte 4096 + h*128 + l*4 + i
- * = scale of (row 8g + 2i + h, block 32c + l). The bytes are unique. */
+ * = scale of (row 8g + 2i + h, block 32c + l). MX_ACT (K % 128 == 0) writes
+ * the codes as MX_ROWMAJOR and the scales grouped by 128-column step: the
+ * scale of (row n, block b) at ((b / 4) * N + n) * 4 + b % 4, so one step's
+ * scales of consecutive rows are contiguous. The bytes are unique. */
 FP4_API int fp4_quantize_mx(const void *W_bf16, int64_t N, int64_t K, int layout, void *packed, void *scales,
                             void *stream);
 
@@ -167,14 +172,14 @@ FP4_API int fp4_gemm_prefill_mx(float *y, const void *x_bf16, const void *packed
  * "github.com/kekzl/imp", the feature table: MXFP4 in the quantisation
  * row, a block-scaled GEMM in the engine row). y[M][N] (fp32, ldy = N,
  * overwritten) = dequant(xq) * dequant(W)^T, where xq holds the activation
- * rows x[M][K] quantised by fp4_quantize_mx with layout MX_ROWMAJOR
- * (codes [M][K/2], E8M0 scales [M][K/32], device) and W is an MX_TILED
+ * rows x[M][K] quantised by fp4_quantize_mx with layout MX_ACT (codes
+ * [M][K/2], E8M0 scales [K/128][M][4], device) and W is an MX_TILED
  * weight. Each product of two scaled E2M1 values is exact and the sums
  * are fp32, so y matches that definition closely; against the product with
  * bf16 activations (fp4_gemm_prefill_mx) it carries the activations' own
  * quantisation error (E2M1 keeps one mantissa bit), in exchange for the
- * matrix cores' FP4 rate. K % 128 == 0 and M <= 16776960 (FP4_ERR_SHAPE
- * otherwise), the tiles below 2^31 bytes; xq_packed and packed 16-byte
+ * matrix cores' FP4 rate. K % 128 == 0, M <= 16776960 and M*K/32 < 2^31
+ * (FP4_ERR_SHAPE otherwise), the tiles below 2^31 bytes; xq_packed and packed 16-byte
  * aligned, xq_scales and y 4-byte aligned. No workspace, nothing
  * allocated. */
 FP4_API int fp4_gemm_mx_a4(float *y, const void *xq_packed, const void *xq_scales, const void *packed, int64_t M,

@@ -252,6 +252,10 @@ def test_mx_layout_bytes_and_argument_errors():
     assert fp4.layout_bytes(1024, 1024, "mx_rowmajor") == (1024 * 512, 1024 * 32)
     assert fp4.layout_bytes(1024, 1024, "mx_tiled") == (128 * 4352, 0)
     assert fp4.layout_bytes(11, 1056, "mx_tiled") == (2 * 2 * 4352, 0)
+    assert fp4.layout_bytes(1024, 1024, "mx_act") == (1024 * 512, 1024 * 32)
+    with pytest.raises(fp4.Fp4Error) as e:
+        fp4.layout_bytes(8, 96, "mx_act")                        # K % 128 != 0
+    assert e.value.status == ESHAPE
     with pytest.raises(fp4.Fp4Error) as e:
         fp4.layout_bytes(8, 48, "mx_tiled")                      # K % 32 != 0
     assert e.value.status == ESHAPE
@@ -259,6 +263,9 @@ def test_mx_layout_bytes_and_argument_errors():
     assert L.fp4_quantize_mx(A, 8, 64, 1, A, A, None) == ELAYOUT     # an NVFP4 layout
     assert L.fp4_quantize_mx(None, 8, 64, 3, A, None, None) == ENULL
     assert L.fp4_quantize_mx(A, 8, 64, 2, A, None, None) == ENULL     # row-major needs the scale array
+    assert L.fp4_quantize_mx(A, 8, 128, 4, A, None, None) == ENULL    # so does the activation layout
+    assert L.fp4_quantize_mx(A, 8, 96, 4, A, A, None) == ESHAPE       # activation layout: K % 128
+    assert L.fp4_quantize_mx(A, 8, 128, 5, A, A, None) == ELAYOUT
     assert L.fp4_quantize_mx(A, 8, 48, 3, A, None, None) == ESHAPE
     assert L.fp4_quantize_mx(A + 8, 8, 64, 3, A, None, None) == EALIGN
     assert L.fp4_gemv_mx(None, A, A, 1, 8, 64, None) == ENULL

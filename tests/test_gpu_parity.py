@@ -1201,12 +1201,14 @@ def test_mx_a4_small_shapes(M, N, K):
     bw = bf16_tensor((N, K), 9 * N + K, 0.03, outlier_p=0.002, outlier_scale=20.0)
     bx = bf16_tensor((M, K), 13 * M + K, 1.0, outlier_p=0.002, outlier_scale=20.0)
     w = fp4.quantize_mx(to_gpu_bf16(bw), "mx_tiled")
-    xq = fp4.quantize_mx(to_gpu_bf16(bx), "mx_rowmajor")
+    xq = fp4.quantize_mx(to_gpu_bf16(bx), "mx_act")
     y = fp4.gemm_mx_a4(xq, w)
     torch.cuda.synchronize()
     xp, xs = oracle.mx_quantize(bx)
     assert np.array_equal(xq.packed.cpu().numpy().reshape(M, K // 2), xp)
-    assert np.array_equal(xq.scales.cpu().numpy().reshape(M, K // 32), xs)
+    # activation layout: the scales of each 128-column step, rows consecutive
+    xs_gpu = xq.scales.cpu().numpy().reshape(K // 128, M, 4).transpose(1, 0, 2).reshape(M, K // 32)
+    assert np.array_equal(xs_gpu, xs)
     wp, ws = oracle.mx_quantize(bw)
     yr, l1 = oracle.mx_a4_product(xp, xs, wp, ws)
     check_mx_a4(y.cpu().numpy(), yr, l1, "mx a4 %dx%dx%d" % (M, N, K))
@@ -1217,7 +1219,7 @@ def test_mx_a4_full_size_sampled_rows():
     MXFP4, checked on 8 sampled token rows (all 17408 outputs each)."""
     bx = act_bits("prefill", "x")
     w = fp4.quantize_mx(to_gpu_bf16(weight_bits("dense27b_layer", "gate")), "mx_tiled")
-    xq = fp4.quantize_mx(to_gpu_bf16(bx), "mx_rowmajor")
+    xq = fp4.quantize_mx(to_gpu_bf16(bx), "mx_act")
     y = fp4.gemm_mx_a4(xq, w)
     torch.cuda.synchronize()
     rows = [0, 1, 255, 256, 1000, 1791, 1792, 2047]
