@@ -44,11 +44,11 @@ typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
-constexpr int kBM = 256, kBN = 128, kKS = 128;
-constexpr int kACodes = kBM * 64;              // one stage: 64 code bytes per row
-constexpr int kAScales = kBM * 4;              // 4 scale bytes per row
-constexpr int kBCodes = kBN * 64;
-constexpr int kBScales = (kBN / 8) * 2 * 16;   // 16 row groups x 2 row parities x 16 bytes
+constexpr int kBM = 256, kBN = 256, kKS = 256, kWaves = 8;
+constexpr int kACodes = kBM * 128;             // one stage: 128 code bytes per row
+constexpr int kAScales = kBM * 8;              // 8 scale bytes per row
+constexpr int kBCodes = kBN * 128;
+constexpr int kBScales = (kBN / 8) * 2 * 32;   // 32 row groups x 2 row parities x 32 bytes
 
 struct A4Args {
   const uint8_t* xa;   // activation codes [M][K/2]
@@ -62,7 +62,7 @@ struct A4Args {
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 
 // slot of 16-byte chunk j of LDS row r
-__device__ __forceinline__ int slot(int r, int j) { return (j ^ ((r >> 2) & 3)) << 4; }
+__device__ __forceinline__ int slot(int r, int j) { return (j ^ (r & 7)) << 4; }
 
 // Buffer resource as four scalars (base, num_records, raw 32-bit format):
 // num_records bytes are readable, anything past them reads as zero.
@@ -97,17 +97,17 @@ __device__ __forceinline__ void dma_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-constexpr int kStages = 3;
-constexpr int kDmaPerStep = 8;   // per wave: 4 activation code, 2 weight code, 1 activation scale, 1 weight scale
+constexpr int kStages = 2;
+constexpr int kDmaPerStep = 10;   // per wave: 4 activation code, 4 weight code, 1 activation scale, 1 weight scale
 constexpr int kOffA = 0, kOffB = kACodes, kOffAS = kOffB + kBCodes, kOffBS = kOffAS + kAScales;
 constexpr int kStageBytes = kOffBS + kBScales;
 constexpr int kLdsBytes = kStages * kStageBytes;
 
-__global__ __launch_bounds__(256) void k_mx_a4(const A4Args a) {
+__global__ __launch_bounds__(kWaves * 64) void k_mx_a4(const A4Args a) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int n0 = blockIdx.x * kBN, m0 = blockIdx.y * kBM;
   const int K = a.K, Kh = K >> 1, Ks = K >> 5, C = a.C;
   const int rows = min(kBM, a.M - m0);
@@ -119,37 +119,34 @@ __global__ __launch_bounds__(256) void k_mx_a4(const A4Args a) {
   const i32x4_t rw = rsrc4(a.w + (int64_t)g0 * C * kMxTileBytes, (uint32_t)ngroups * C * kMxTileBytes);
   const uint32_t sbase = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
 
-  // DMA lane roles. A code instruction fills 16 LDS rows of 64 bytes: lane
-  // -> row lane / 4 of the 16, slot lane % 4, which holds chunk (lane % 4) ^
-  // ((lane / 16) % 4) (rows of 16-aligned blocks: (row / 4) % 4 is lane / 16).
-  const int dr = lane >> 2, dj = (lane & 3) ^ ((lane >> 4) & 3);
-  // weight row n = 16 e + dr of the block: group 2 e + lane / 32, row
-  // (lane / 4) % 8 of the group: pair q = row / 2, parity h = row % 2
-  const int bq = (dr & 7) >> 1, bh = dr & 1;
+  // DMA lane roles. A code instruction fills 8 LDS rows of 128 bytes: lane
+  // -> row lane / 8 of the 8, slot lane % 8, which holds chunk (lane % 8) ^
+  // (lane / 8) (the rows are 8-aligned, so row % 8 is lane / 8).
+  const int dr = lane >> 3, dj = (lane & 7) ^ dr;
   constexpr uint32_t kOut = 0x80000000u;   // an offset past every resource
-  // weight scale chunk of lane L < 8: group 4 wave + L / 2, row parity L % 2
-  const int sj = lane >> 1, sh = lane & 1;
   auto issue = [&](int step, int stage) {
     const int k0 = step * kKS, c = k0 >> 10, p0 = (k0 & 1023) >> 5;
     const uint32_t st = sbase + stage * kStageBytes;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {   // activation codes: rows 16 d .. 16 d + 15, d = 4 wave + i
+    for (int i = 0; i < 4; ++i) {   // activation codes: rows 8 d .. 8 d + 7, d = 4 wave + i
       const int d = 4 * wave + i;
-      dma16(ra, (uint32_t)((16 * d + dr) * Kh + (k0 >> 1) + 16 * dj), st + kOffA + d * 1024);
+      dma16(ra, (uint32_t)((8 * d + dr) * Kh + (k0 >> 1) + 16 * dj), st + kOffA + d * 1024);
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {   // weight codes: rows 16 e .. 16 e + 15, e = 2 wave + i
-      const int e = 2 * wave + i, g = 2 * e + (lane >> 5);
-      dma16(rw, (uint32_t)((g * C + c) * kMxTileBytes + bq * 1024 + bh * 512 + (p0 + dj) * 16), st + kOffB + e * 1024);
+    for (int i = 0; i < 4; ++i) {   // weight codes: group e = 4 wave + i, its rows 2 q + h = lane / 8
+      const int e = 4 * wave + i;
+      dma16(rw, (uint32_t)((e * C + c) * kMxTileBytes + (dr >> 1) * 1024 + (dr & 1) * 512 + (p0 + dj) * 16),
+            st + kOffB + e * 1024);
     }
-    // activation scales: the step's 4 bytes of rows m0 + 64 wave + lane (contiguous rows)
-    dma4(rs, (uint32_t)((step * a.M + m0 + 64 * wave + lane) * 4), st + kOffAS + wave * 256);
-    // weight scales: wave w loads the 16-byte chunks of groups 4 w .. 4 w + 3
-    // with lanes 0..7 (the other lanes idle, so they write no LDS)
-    if (lane < 8) {
-      const int g = 4 * wave + sj;
-      dma16(rw, g < ngroups ? (uint32_t)((g * C + c) * kMxTileBytes + 4096 + sh * 128 + p0 * 4) : kOut,
-            st + kOffBS + wave * 128);
+    {   // activation scales: sub-step u = wave / 4 (128 columns), rows 64 (wave % 4) + lane
+      const int u = wave >> 2, r = 64 * (wave & 3) + lane;
+      dma4(rs, (uint32_t)(((2 * step + u) * a.M + m0 + r) * 4), st + kOffAS + u * 1024 + (wave & 3) * 256);
+    }
+    if (lane < 16) {   // weight scales: 16-byte piece P = 16 wave + lane: group P / 4, parity (P / 2) % 2, half P % 2
+      const int P = 16 * wave + lane, g = P >> 2;
+      dma16(rw, g < ngroups ? (uint32_t)((g * C + c) * kMxTileBytes + 4096 + ((P >> 1) & 1) * 128 + p0 * 4 + (P & 1) * 16)
+                            : kOut,
+            st + kOffBS + wave * 256);
     }
   };
 
@@ -174,16 +171,16 @@ __global__ __launch_bounds__(256) void k_mx_a4(const A4Args a) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       const int row = 128 * wm + 32 * mt + r32;
-      const uint4 v = *reinterpret_cast<const uint4*>(s + kOffA + row * 64 + slot(row, j));
+      const uint4 v = *reinterpret_cast<const uint4*>(s + kOffA + row * 128 + slot(row, j));
       f.av[mt] = i32x8_t{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-      f.as[mt] = s[kOffAS + row * 4 + j];
+      f.as[mt] = s[kOffAS + (j >> 2) * 1024 + row * 4 + (j & 3)];
     }
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int n = 64 * wn + 32 * nt + r32;
-      const uint4 v = *reinterpret_cast<const uint4*>(s + kOffB + n * 64 + slot(n, j));
+      const uint4 v = *reinterpret_cast<const uint4*>(s + kOffB + n * 128 + slot(n, j));
       f.bv[nt] = i32x8_t{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-      f.bs[nt] = s[kOffBS + ((n >> 3) * 2 + (n & 1)) * 16 + j * 4 + ((n & 7) >> 1)];
+      f.bs[nt] = s[kOffBS + ((n >> 3) * 2 + (n & 1)) * 32 + j * 4 + ((n & 7) >> 1)];
     }
   };
   auto mma = [&](const Frag& f) {
@@ -210,30 +207,30 @@ __global__ __launch_bounds__(256) void k_mx_a4(const A4Args a) {
   // (after the barrier that publishes that step's stage). The barrier's
   // fence completes every LDS read issued before it, so a stage is free for
   // the next load two steps later.
-  const int nsteps = K / kKS;
+  // K % 256 == 128 ends with a half step: its second half reads zero
+  // weight codes and scales (tile padding) and activation scales past the
+  // array (zeros), so it adds exact zeros
+  const int nsteps = (K + kKS - 1) / kKS;
   issue(0, 0);
-  if (nsteps > 1) {
-    issue(1, 1);
-    dma_wait<kDmaPerStep>();
-  } else {
-    dma_wait<0>();
-  }
+  dma_wait<0>();
   __syncthreads();
   Frag f0, f1;
   load(0, 0, f0);
   int stage = 0;
   for (int s = 0; s < nsteps; ++s) {
-    const bool ahead = s + 2 < nsteps;
-    if (ahead) issue(s + 2, stage == 0 ? 2 : stage - 1);   // the stage step s - 1 used
+    if (s + 1 < nsteps) issue(s + 1, stage ^ 1);   // the stage step s - 1 used
     load(stage, 1, f1);
     mma(f0);
     interleave();
-    if (ahead)
-      dma_wait<kDmaPerStep>();   // step s + 1 landed; step s + 2 may still be in flight
-    else
-      dma_wait<0>();
+    load(stage, 2, f0);
+    mma(f1);
+    interleave();
+    load(stage, 3, f1);
+    mma(f0);
+    interleave();
+    dma_wait<0>();   // step s + 1 landed
     __syncthreads();
-    stage = stage == 2 ? 0 : stage + 1;
+    stage ^= 1;
     load(stage, 0, f0);   // past the last step this reads a stale stage, unused
     mma(f1);
     interleave();
@@ -279,7 +276,7 @@ hipError_t launch_mx_a4(float* y, const uint8_t* xq_codes, const uint8_t* xq_sca
     if (e != hipSuccess) return e;
     attr_set[dev].store(true, std::memory_order_release);
   }
-  const dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM)), block(256);
+  const dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM)), block(kWaves * 64);
   hipLaunchKernelGGL(k_mx_a4, grid, block, kLdsBytes, s, a);
   return hipGetLastError();
 }
