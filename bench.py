@@ -41,6 +41,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_FP4_PEAK_TFLOPS = 10100.0   # dense FP4 matrix-core peak
 HIDDEN, INTER = 5120, 17408
 REPS = 7            # timed windows per measurement
 CPU_THREADS = 16    # the host cores one GPU's job may use
@@ -617,7 +618,16 @@ def other_configs(fp4, torch, timer, w27, gpu_bf16, dev, x_in0, x_mid0):
     res["mx_prefill_2048x17408x5120"] = line(timer.time_calls(lambda i: fp4.gemm_prefill_mx(xp, mxc[i % 6]["gate"],
                                                                                           out=ypm), 6, reps=5),
                                              flops=2.0 * 2048 * INTER * HIDDEN, mfma=True)
-    del mxb, mxc, lmx, lmxc, ypm, xp, g2
+    # the same product with both operands MXFP4 on the block-scaled FP4 matrix cores; the activations are
+    # quantised (fp4_quantize_mx, the activation operand layout) in a launch of their own, timed apart
+    xq4 = fp4.quantize_mx(xp, "mx_act")
+    fl4 = 2.0 * 2048 * INTER * HIDDEN
+    t4 = timer.time_calls(lambda i: fp4.gemm_mx_a4(xq4, mxc[i % 6]["gate"], out=ypm), 6, reps=5)
+    res["mx_a4_prefill_2048x17408x5120"] = dict(
+        line(t4, flops=fl4), frac_of_mfma_fp4_peak=round(fl4 / statistics.median(t4) / 1e6 / MFMA_FP4_PEAK_TFLOPS, 4))
+    res["mx_a4_quantise_x_2048x5120"] = line(timer.time_calls(lambda i: fp4.quantize_mx(xp, "mx_act", out=xq4), 6,
+                                                              reps=5))
+    del mxb, mxc, lmx, lmxc, ypm, xp, g2, xq4
     # ---- load-time quantisation of the down projection from bf16 and from an FP8 release (the
     # rule reads the input twice: algorithmic bytes = 2 input reads + 9/16 byte per element written)
     Wb = gpu_bf16(tensor_bits(workload("dense27b_layer").tensor("down")))
