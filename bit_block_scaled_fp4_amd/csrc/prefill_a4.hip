@@ -16,19 +16,23 @@
 // of the scale operand; B lane l likewise holds column l % 32; result lane
 // l holds column l % 32, rows (i % 4) + 8 (i / 4) + 4 (l / 32), i < 16.
 //
-// Tiling. A 256-thread workgroup computes 256 rows x 128 columns; its four
-// waves form a 2 x 2 grid of 128 x 64 (4 x 2 result blocks each). K
-// advances 128 per step (two MFMA steps). Every global read is a
-// direct-to-LDS buffer load into one of three stages, issued two steps
-// ahead: per stage 256 activation rows and 128 weight rows of 64 code bytes
-// (4 chunks of 16), the activations' 4 scale bytes per row and the weight
-// groups' scale chunks. A row's chunk j sits in slot j ^ ((row / 4) % 4),
-// which keeps the 16-byte operand reads of a half-wave in distinct bank
-// groups (rows r and r + 16 in the same group). Each wave issues the same
-// eight loads per step, so one wait for all but the newest eight and one
-// barrier close a step.
+// Tiling. A 512-thread workgroup (one per CU: 136 KB of LDS) computes 256
+// rows x 256 columns; its eight waves form a 2 x 4 grid of 128 x 64 (4 x 2
+// result blocks each). K advances 256 per step (four MFMA steps). Every
+// global read is a direct-to-LDS buffer load into one of two stages, issued
+// one step ahead: per stage 256 activation and 256 weight rows of 128 code
+// bytes (8 chunks of 16, a whole 128-byte line per row, so each load
+// request moves a full line), the activations' 8 scale bytes per row (two
+// contiguous runs in the activation layout) and the weight groups' 32-byte
+// scale runs. A row's chunk j sits in slot j ^ ((row / 2) % 8): the MFMA
+// operand reads (lane -> row lane % 32) then give 16 consecutive rows 16
+// distinct 16-byte bank groups of the 256-byte bank window (rows r and r + 1
+// fall in opposite halves). Each wave issues the same ten loads per step.
+// The fragments of the next quarter step are read from LDS while the
+// current quarter's MFMAs run.
 //
-// Bounds: K is a multiple of 128 (the launcher checks); activation rows
+// Bounds: K is a multiple of 128 (the launcher checks; a last half step adds
+// exact zeros); activation rows
 // past M and weight row groups past N read zeros (offsets past the
 // resource; the tiled layout pads a ragged last group with zero codes), and
 // the stores skip rows past M and columns past N.
@@ -62,7 +66,7 @@ struct A4Args {
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 
 // slot of 16-byte chunk j of LDS row r
-__device__ __forceinline__ int slot(int r, int j) { return (j ^ (r & 7)) << 4; }
+__device__ __forceinline__ int slot(int r, int j) { return (j ^ ((r >> 1) & 7)) << 4; }
 
 // Buffer resource as four scalars (base, num_records, raw 32-bit format):
 // num_records bytes are readable, anything past them reads as zero.
@@ -121,20 +125,21 @@ __global__ __launch_bounds__(kWaves * 64) void k_mx_a4(const A4Args a) {
 
   // DMA lane roles. A code instruction fills 8 LDS rows of 128 bytes: lane
   // -> row lane / 8 of the 8, slot lane % 8, which holds chunk (lane % 8) ^
-  // (lane / 8) (the rows are 8-aligned, so row % 8 is lane / 8).
-  const int dr = lane >> 3, dj = (lane & 7) ^ dr;
+  // ((row / 2) % 8): for rows 8 d .. 8 d + 7 that is (lane % 8) ^ (4 (d % 2)
+  // + lane / 16).
+  const int dr = lane >> 3, dj0 = (lane & 7) ^ (dr >> 1), dj1 = (lane & 7) ^ (4 + (dr >> 1));
   constexpr uint32_t kOut = 0x80000000u;   // an offset past every resource
   auto issue = [&](int step, int stage) {
     const int k0 = step * kKS, c = k0 >> 10, p0 = (k0 & 1023) >> 5;
     const uint32_t st = sbase + stage * kStageBytes;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {   // activation codes: rows 8 d .. 8 d + 7, d = 4 wave + i
-      const int d = 4 * wave + i;
+      const int d = 4 * wave + i, dj = (i & 1) ? dj1 : dj0;
       dma16(ra, (uint32_t)((8 * d + dr) * Kh + (k0 >> 1) + 16 * dj), st + kOffA + d * 1024);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {   // weight codes: group e = 4 wave + i, its rows 2 q + h = lane / 8
-      const int e = 4 * wave + i;
+      const int e = 4 * wave + i, dj = (i & 1) ? dj1 : dj0;
       dma16(rw, (uint32_t)((e * C + c) * kMxTileBytes + (dr >> 1) * 1024 + (dr & 1) * 512 + (p0 + dj) * 16),
             st + kOffB + e * 1024);
     }
