@@ -281,5 +281,6 @@ def test_mx_layout_bytes_and_argument_errors():
     assert L.fp4_gemm_mx_a4(A, A, A, A, 4, 8, 96, None) == ESHAPE        # K % 128 != 0
     assert L.fp4_gemm_mx_a4(A, A, A, A, 0, 8, 128, None) == ESHAPE
     assert L.fp4_gemm_mx_a4(A, A, A, A, 65535 * 256 + 1, 8, 128, None) == ESHAPE
+    assert L.fp4_gemm_mx_a4(A, A, A, A, 1 << 20, 8, 1 << 16, None) == ESHAPE   # M*K/32 reaches 2^31
     assert L.fp4_gemm_mx_a4(A, A + 8, A, A, 4, 8, 128, None) == EALIGN   # codes not 16-byte aligned
     assert L.fp4_gemm_mx_a4(A, A, A + 2, A, 4, 8, 128, None) == EALIGN   # scales not 4-byte aligned
