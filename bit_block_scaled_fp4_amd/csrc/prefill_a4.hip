@@ -3,7 +3,8 @@
 // The imp README's feature table names MXFP4 beside NVFP4 (quantisation row)
 // and a block-scaled matrix multiply (engine row). Here both operands are
 // MXFP4: the activation rows, quantised by the weights' own MXFP4 rule
-// (fp4_quantize_mx, row-major), and the weights in the MX tiled layout. One
+// (fp4_quantize_mx, activation layout: row-major codes, scales grouped by
+// 128-column step), and the weights in the MX tiled layout. One
 // v_mfma_scale_f32_32x32x64_f8f6f4 with both operands E2M1 multiplies a
 // 32 x 64 activation block by a 64 x 32 weight block, each lane supplying
 // the E8M0 scale of its own 32 elements, at the FP4 rate (10.1 PF/s dense on
