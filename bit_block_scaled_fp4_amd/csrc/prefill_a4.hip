@@ -30,7 +30,9 @@
 // distinct 16-byte bank groups of the 256-byte bank window (rows r and r + 1
 // fall in opposite halves). Each wave issues the same ten loads per step.
 // The fragments of the next quarter step are read from LDS while the
-// current quarter's MFMAs run.
+// current quarter's MFMAs run. The grid is persistent (one workgroup per
+// CU, tiles in row-major order, strided by the grid): a tile's fp32 results
+// go out as streaming stores while the next tile's first step loads.
 //
 // Bounds: K is a multiple of 128 (the launcher checks; a last half step adds
 // exact zeros); activation rows
@@ -61,6 +63,7 @@ struct A4Args {
   const uint8_t* w;    // MX tiled weights, G * C tiles of kMxTileBytes
   float* y;            // [M][ldy]
   int M, N, K, G, C;
+  int gx, gy;          // column and row tiles
   int64_t ldy;
 };
 
@@ -87,14 +90,28 @@ __device__ __forceinline__ i32x4_t rsrc4(const void* base, uint32_t bytes) {
 // awaited explicitly with dma_wait before the barrier that publishes it. M0
 // (reserved, so not listed as clobbered) is written by these statements
 // only: nothing else in this kernel uses it.
-__device__ __forceinline__ void dma16(const i32x4_t& rs, uint32_t voff, uint32_t lds) {
+// the resource (and below the LDS address) as scalars for the asm operands
+// (no-ops where the compiler already keeps them in scalar registers)
+__device__ __forceinline__ i32x4_t uniform(const i32x4_t& r) {
+  i32x4_t u;
+  u[0] = __builtin_amdgcn_readfirstlane(r[0]);
+  u[1] = __builtin_amdgcn_readfirstlane(r[1]);
+  u[2] = __builtin_amdgcn_readfirstlane(r[2]);
+  u[3] = __builtin_amdgcn_readfirstlane(r[3]);
+  return u;
+}
+__device__ __forceinline__ void dma16(const i32x4_t& r, uint32_t voff, uint32_t lds) {
+  const i32x4_t rs = uniform(r);
+  const uint32_t l = __builtin_amdgcn_readfirstlane(lds);
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs),
-               "s"(lds)
+               "s"(l)
                : "memory");
 }
-__device__ __forceinline__ void dma4(const i32x4_t& rs, uint32_t voff, uint32_t lds) {
+__device__ __forceinline__ void dma4(const i32x4_t& r, uint32_t voff, uint32_t lds) {
+  const i32x4_t rs = uniform(r);
+  const uint32_t l = __builtin_amdgcn_readfirstlane(lds);
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rs),
-               "s"(lds)
+               "s"(l)
                : "memory");
 }
 template <int N>
@@ -113,15 +130,28 @@ __global__ __launch_bounds__(kWaves * 64) void k_mx_a4(const A4Args a) {
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave >> 2, wn = wave & 3;
-  const int n0 = blockIdx.x * kBN, m0 = blockIdx.y * kBM;
   const int K = a.K, Kh = K >> 1, Ks = K >> 5, C = a.C;
-  const int rows = min(kBM, a.M - m0);
-  const int g0 = n0 >> 3, ngroups = min(kBN / 8, a.G - g0);
-  const i32x4_t ra = rsrc4(a.xa + (int64_t)m0 * Kh, (uint32_t)rows * Kh);
+  const int T = a.gx * a.gy;
   // the whole scale array: a slab's rows past M read the next step's first
   // rows (scales of zero codes, in rows never stored) or, at the end, zeros
   const i32x4_t rs = rsrc4(a.xs, (uint32_t)a.M * Ks);
-  const i32x4_t rw = rsrc4(a.w + (int64_t)g0 * C * kMxTileBytes, (uint32_t)ngroups * C * kMxTileBytes);
+  // one tile: its origin, weight row groups and buffer resources (tiles in
+  // row-major order, so consecutive workgroups share activation rows)
+  struct Tile {
+    int m0, n0, ngroups;
+    i32x4_t ra, rw;
+  };
+  auto tile_at = [&](int id) {
+    Tile u;
+    const int tm = id / a.gx;
+    u.m0 = tm * kBM;
+    u.n0 = (id - tm * a.gx) * kBN;
+    const int rows = min(kBM, a.M - u.m0), g0 = u.n0 >> 3;
+    u.ngroups = min(kBN / 8, a.G - g0);
+    u.ra = rsrc4(a.xa + (int64_t)u.m0 * Kh, (uint32_t)rows * Kh);
+    u.rw = rsrc4(a.w + (int64_t)g0 * C * kMxTileBytes, (uint32_t)u.ngroups * C * kMxTileBytes);
+    return u;
+  };
   const uint32_t sbase = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
 
   // DMA lane roles. A code instruction fills 8 LDS rows of 128 bytes: lane
@@ -130,39 +160,33 @@ __global__ __launch_bounds__(kWaves * 64) void k_mx_a4(const A4Args a) {
   // + lane / 16).
   const int dr = lane >> 3, dj0 = (lane & 7) ^ (dr >> 1), dj1 = (lane & 7) ^ (4 + (dr >> 1));
   constexpr uint32_t kOut = 0x80000000u;   // an offset past every resource
-  auto issue = [&](int step, int stage) {
+  auto issue = [&](const Tile& u, int step, int stage) {
     const int k0 = step * kKS, c = k0 >> 10, p0 = (k0 & 1023) >> 5;
     const uint32_t st = sbase + stage * kStageBytes;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {   // activation codes: rows 8 d .. 8 d + 7, d = 4 wave + i
       const int d = 4 * wave + i, dj = (i & 1) ? dj1 : dj0;
-      dma16(ra, (uint32_t)((8 * d + dr) * Kh + (k0 >> 1) + 16 * dj), st + kOffA + d * 1024);
+      dma16(u.ra, (uint32_t)((8 * d + dr) * Kh + (k0 >> 1) + 16 * dj), st + kOffA + d * 1024);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {   // weight codes: group e = 4 wave + i, its rows 2 q + h = lane / 8
       const int e = 4 * wave + i, dj = (i & 1) ? dj1 : dj0;
-      dma16(rw, (uint32_t)((e * C + c) * kMxTileBytes + (dr >> 1) * 1024 + (dr & 1) * 512 + (p0 + dj) * 16),
+      dma16(u.rw, (uint32_t)((e * C + c) * kMxTileBytes + (dr >> 1) * 1024 + (dr & 1) * 512 + (p0 + dj) * 16),
             st + kOffB + e * 1024);
     }
-    {   // activation scales: sub-step u = wave / 4 (128 columns), rows 64 (wave % 4) + lane
-      const int u = wave >> 2, r = 64 * (wave & 3) + lane;
-      dma4(rs, (uint32_t)(((2 * step + u) * a.M + m0 + r) * 4), st + kOffAS + u * 1024 + (wave & 3) * 256);
+    {   // activation scales: sub-step v = wave / 4 (128 columns), rows 64 (wave % 4) + lane
+      const int v = wave >> 2, r = 64 * (wave & 3) + lane;
+      dma4(rs, (uint32_t)(((2 * step + v) * a.M + u.m0 + r) * 4), st + kOffAS + v * 1024 + (wave & 3) * 256);
     }
     if (lane < 16) {   // weight scales: 16-byte piece P = 16 wave + lane: group P / 4, parity (P / 2) % 2, half P % 2
       const int P = 16 * wave + lane, g = P >> 2;
-      dma16(rw, g < ngroups ? (uint32_t)((g * C + c) * kMxTileBytes + 4096 + ((P >> 1) & 1) * 128 + p0 * 4 + (P & 1) * 16)
+      dma16(u.rw, g < u.ngroups ? (uint32_t)((g * C + c) * kMxTileBytes + 4096 + ((P >> 1) & 1) * 128 + p0 * 4 + (P & 1) * 16)
                             : kOut,
             st + kOffBS + wave * 256);
     }
   };
 
   f32x16_t acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   const int r32 = lane & 31, kb = lane >> 5;
   // One MFMA step's operands: 4 activation and 2 weight fragments with
@@ -216,43 +240,64 @@ __global__ __launch_bounds__(kWaves * 64) void k_mx_a4(const A4Args a) {
   // K % 256 == 128 ends with a half step: its second half reads zero
   // weight codes and scales (tile padding) and activation scales past the
   // array (zeros), so it adds exact zeros
+  // Persistent: one workgroup per CU walks tiles blockIdx.x, + gridDim.x, ...
+  // The next tile's first step is loaded (into the stage the last step used,
+  // free since the last barrier) while this tile's results are stored.
   const int nsteps = (K + kKS - 1) / kKS;
-  issue(0, 0);
-  dma_wait<0>();
-  __syncthreads();
-  Frag f0, f1;
-  load(0, 0, f0);
-  int stage = 0;
-  for (int s = 0; s < nsteps; ++s) {
-    if (s + 1 < nsteps) issue(s + 1, stage ^ 1);   // the stage step s - 1 used
-    load(stage, 1, f1);
-    mma(f0);
-    interleave();
-    load(stage, 2, f0);
-    mma(f1);
-    interleave();
-    load(stage, 3, f1);
-    mma(f0);
-    interleave();
-    dma_wait<0>();   // step s + 1 landed
+  int id = blockIdx.x, stage = 0;
+  Tile cur = tile_at(id);
+  issue(cur, 0, 0);
+  for (;;) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    dma_wait<0>();
     __syncthreads();
-    stage ^= 1;
-    load(stage, 0, f0);   // past the last step this reads a stale stage, unused
-    mma(f1);
-    interleave();
-  }
-
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int col = n0 + 64 * wn + 32 * nt + r32;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = m0 + 128 * wm + 32 * mt + (i & 3) + 8 * (i >> 2) + 4 * kb;
-        if (row < a.M && col < a.N) a.y[(int64_t)row * a.ldy + col] = acc[mt][nt][i];
-      }
+    Frag f0, f1;
+    load(stage, 0, f0);
+    for (int s = 0; s < nsteps; ++s) {
+      if (s + 1 < nsteps) issue(cur, s + 1, stage ^ 1);   // the stage step s - 1 used
+      load(stage, 1, f1);
+      mma(f0);
+      interleave();
+      load(stage, 2, f0);
+      mma(f1);
+      interleave();
+      load(stage, 3, f1);
+      mma(f0);
+      interleave();
+      dma_wait<0>();   // step s + 1 landed
+      __syncthreads();
+      stage ^= 1;
+      load(stage, 0, f0);   // past the last step this reads a stale stage, unused
+      mma(f1);
+      interleave();
     }
+    const int nid = id + (int)gridDim.x;
+    Tile nxt = cur;
+    if (nid < T) {
+      nxt = tile_at(nid);
+      issue(nxt, 0, stage ^ 1);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int col = cur.n0 + 64 * wn + 32 * nt + r32;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int row = cur.m0 + 128 * wm + 32 * mt + (i & 3) + 8 * (i >> 2) + 4 * kb;
+          if (row < a.M && col < a.N) __builtin_nontemporal_store(acc[mt][nt][i], &a.y[(int64_t)row * a.ldy + col]);
+        }
+      }
+    if (nid >= T) break;
+    id = nid;
+    cur = nxt;
+    stage ^= 1;
+  }
 }
 
 }  // namespace
@@ -270,19 +315,27 @@ hipError_t launch_mx_a4(float* y, const uint8_t* xq_codes, const uint8_t* xq_sca
   a.G = (int)((N + 7) / 8);
   a.C = (int)chunks_of(K);
   a.ldy = N;
+  a.gx = (int)((N + kBN - 1) / kBN);
+  a.gy = (int)((M + kBM - 1) / kBM);
   // more than 64 KB of dynamic LDS must be allowed once per device
   constexpr int kMaxDevices = 64;
-  static std::atomic<bool> attr_set[kMaxDevices];
+  // (and the CU count, one persistent workgroup per CU, is read once)
+  static std::atomic<int> cus_of[kMaxDevices];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  if (!attr_set[dev].load(std::memory_order_acquire)) {   // racing first calls set the same value
+  int cus = cus_of[dev].load(std::memory_order_acquire);
+  if (cus == 0) {   // racing first calls store the same values
     e = hipFuncSetAttribute((const void*)k_mx_a4, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (e != hipSuccess) return e;
-    attr_set[dev].store(true, std::memory_order_release);
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (cus < 1) return hipErrorInvalidDevice;
+    cus_of[dev].store(cus, std::memory_order_release);
   }
-  const dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM)), block(kWaves * 64);
+  const int64_t tiles = (int64_t)a.gx * a.gy;
+  const dim3 grid((unsigned)std::min<int64_t>(tiles, cus)), block(kWaves * 64);
   hipLaunchKernelGGL(k_mx_a4, grid, block, kLdsBytes, s, a);
   return hipGetLastError();
 }
