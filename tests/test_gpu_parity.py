@@ -1227,3 +1227,20 @@ def test_mx_a4_full_size_sampled_rows():
     xp, xs = oracle.mx_quantize(bx[rows])
     yr, l1 = oracle.mx_a4_product(xp, xs, p, s)
     check_mx_a4(y[rows].cpu().numpy(), yr, l1, "mx a4 full size")
+
+
+def test_mx_a4_8192_rows_sampled():
+    """8192 tokens x the gate projection: 2176 tiles, so each workgroup of the
+    persistent grid walks 8 or 9 of them; 6 sampled rows (first and last
+    rows, tile and band edges), all 17408 outputs each."""
+    print("mx a4 8192 rows", flush=True)
+    bx = bf16_tensor((8192, 5120), 8192 * 7 + 5, 1.0, outlier_p=0.001, outlier_scale=20.0)
+    w = fp4.quantize_mx(to_gpu_bf16(weight_bits("dense27b_layer", "gate")), "mx_tiled")
+    xq = fp4.quantize_mx(to_gpu_bf16(bx), "mx_act")
+    y = fp4.gemm_mx_a4(xq, w)
+    torch.cuda.synchronize()
+    rows = [0, 255, 256, 4095, 8064, 8191]
+    p, s = mx_oracle_quant("dense27b_layer", "gate")
+    xp, xs = oracle.mx_quantize(bx[rows])
+    yr, l1 = oracle.mx_a4_product(xp, xs, p, s)
+    check_mx_a4(y[rows].cpu().numpy(), yr, l1, "mx a4 8192 rows")
