@@ -214,18 +214,27 @@ __global__ __launch_bounds__(256) void k_encode(const Src src, int64_t N, int64_
 // kTileCodes + 128h + 4l + i. mode 0 row-major, 1 tiled, 2 the activation
 // operand layout (row-major codes; the scale of (row n, block b) at
 // ((b / 4) N + n) 4 + b % 4, K a multiple of 128).
-// grid: rows * segs workgroups, segs = ceil(bpr / 256); block 256.
+// Threads run over the blocks of all rows in order (row = index / bpr), so
+// no lane idles when a row has fewer than 256 blocks (K = 5120: 160).
+// grid: ceil(rows * bpr / 256) workgroups; block 256.
 __global__ __launch_bounds__(256) void k_mx_encode(const uint16_t* __restrict__ W, int64_t N, int64_t K, int mode,
                                                    uint8_t* __restrict__ packed, uint8_t* __restrict__ scales) {
   const int64_t kb = K / 32;                          // blocks per row
   const int64_t C = chunks_of(K);
   const bool tiled = mode == 1;
   const int64_t bpr = tiled ? C * 32 : kb;            // blocks per (padded) row
-  const uint32_t segs = (uint32_t)((bpr + 255) / 256);
-  const uint32_t wg = blockIdx.x;
-  const int64_t n = wg / segs;
-  const int64_t b = (int64_t)(wg - (uint32_t)n * segs) * 256 + threadIdx.x;
-  if (b >= bpr) return;
+  const int64_t rows = tiled ? groups_of(N) * kGroupRows : N;
+  const int64_t gb = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gb >= rows * bpr) return;
+  int64_t n, b;
+  if (rows * bpr <= (int64_t)UINT32_MAX) {   // 32-bit division where it suffices
+    const uint32_t q = (uint32_t)gb / (uint32_t)bpr;
+    n = q;
+    b = (int64_t)((uint32_t)gb - q * (uint32_t)bpr);
+  } else {
+    n = gb / bpr;
+    b = gb - n * bpr;
+  }
 
   uint32_t sc = 0, q[4] = {0u, 0u, 0u, 0u};
   if (n < N && b < kb) {
@@ -353,7 +362,7 @@ hipError_t launch_quantize_mx(const uint16_t* W, int64_t N, int64_t K, int mode,
   const bool tiled = mode == 1;
   const int64_t rows = tiled ? groups_of(N) * kGroupRows : N;
   const int64_t bpr = tiled ? chunks_of(K) * 32 : K / 32;
-  const int64_t wgs = rows * ((bpr + 255) / 256);
+  const int64_t wgs = (rows * bpr + 255) / 256;
   if (wgs > UINT32_MAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_mx_encode, dim3((unsigned)wgs), dim3(256), 0, s, W, N, K, mode, packed, scales);
   return hipGetLastError();
