@@ -31,8 +31,9 @@
 // fall in opposite halves). Each wave issues the same ten loads per step.
 // The fragments of the next quarter step are read from LDS while the
 // current quarter's MFMAs run. The grid is persistent (one workgroup per
-// CU, tiles in row-major order, strided by the grid): a tile's fp32 results
-// go out as streaming stores while the next tile's first step loads.
+// CU, tiles in row-major order, strided by the grid): a tile's last step
+// loads the next tile's first, and its fp32 results go out as streaming
+// stores.
 //
 // Bounds: K is a multiple of 128 (the launcher checks; a last half step adds
 // exact zeros); activation rows
@@ -241,12 +242,17 @@ __global__ __launch_bounds__(kWaves * 64) void k_mx_a4(const A4Args a) {
   // weight codes and scales (tile padding) and activation scales past the
   // array (zeros), so it adds exact zeros
   // Persistent: one workgroup per CU walks tiles blockIdx.x, + gridDim.x, ...
-  // The next tile's first step is loaded (into the stage the last step used,
-  // free since the last barrier) while this tile's results are stored.
+  // A tile's last step loads the next tile's first step, and the read after
+  // its barrier takes that step's first fragments, so the next tile starts
+  // at once while this tile's results are stored.
   const int nsteps = (K + kKS - 1) / kKS;
   int id = blockIdx.x, stage = 0;
   Tile cur = tile_at(id);
   issue(cur, 0, 0);
+  dma_wait<0>();
+  __syncthreads();
+  Frag f0, f1;
+  load(stage, 0, f0);
   for (;;) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -254,12 +260,14 @@ __global__ __launch_bounds__(kWaves * 64) void k_mx_a4(const A4Args a) {
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-    dma_wait<0>();
-    __syncthreads();
-    Frag f0, f1;
-    load(stage, 0, f0);
+    const int nid = id + (int)gridDim.x;
+    Tile nxt = cur;
+    if (nid < T) nxt = tile_at(nid);
     for (int s = 0; s < nsteps; ++s) {
-      if (s + 1 < nsteps) issue(cur, s + 1, stage ^ 1);   // the stage step s - 1 used
+      if (s + 1 < nsteps)
+        issue(cur, s + 1, stage ^ 1);   // the stage step s - 1 used
+      else if (nid < T)
+        issue(nxt, 0, stage ^ 1);       // the next tile's first step
       load(stage, 1, f1);
       mma(f0);
       interleave();
@@ -272,15 +280,9 @@ __global__ __launch_bounds__(kWaves * 64) void k_mx_a4(const A4Args a) {
       dma_wait<0>();   // step s + 1 landed
       __syncthreads();
       stage ^= 1;
-      load(stage, 0, f0);   // past the last step this reads a stale stage, unused
+      load(stage, 0, f0);   // past the last step: the next tile's first fragments (or unused)
       mma(f1);
       interleave();
-    }
-    const int nid = id + (int)gridDim.x;
-    Tile nxt = cur;
-    if (nid < T) {
-      nxt = tile_at(nid);
-      issue(nxt, 0, stage ^ 1);
     }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
@@ -296,7 +298,6 @@ __global__ __launch_bounds__(kWaves * 64) void k_mx_a4(const A4Args a) {
     if (nid >= T) break;
     id = nid;
     cur = nxt;
-    stage ^= 1;
   }
 }
 
